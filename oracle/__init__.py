@@ -1,0 +1,215 @@
+"""CPU oracle for the 1-bit Adam step -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may import
+this package.  The product library (``adam_ob_compress_amd``) never imports, links or runs it, and it
+imports nothing from the product.  Arithmetic lives in ``ob_oracle.c`` (plain single-threaded C,
+double-precision arithmetic on fp32 state, built with ``-ffp-contract=off``); this module only
+marshals numpy arrays and holds the host-side step schedules.
+
+Pages cited (by title and section):
+  [P1] "1bit Adam" tutorial (intelliparadigm.com article 2150495), sections 2.1, 2.2, 3.1, 3.2, 6.1.
+  [P2] "DeepSpeed Communication Compression and Hiding", sections "1-bit Adam: warmup, frozen
+       variance, error feedback" and "0/1 Adam".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ob_oracle.c")
+_LIB = os.path.join(_HERE, "libob_oracle.so")
+# A test may point the wrapper at a rebuilt copy of the oracle (the planted-mistake test does).
+_LIB_OVERRIDE = os.environ.get("OB_ORACLE_LIB")
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-Wall"]
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ob_oracle.c into libob_oracle.so with gcc (always recompiles)."""
+    cmd = ["gcc", *CFLAGS, "-o", _LIB + ".tmp", _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    global _lib
+    _lib = None
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    F = ctypes.c_float
+    I = ctypes.c_int
+    lib.or_pack.argtypes = [P, I, I64, P]
+    lib.or_unpack.argtypes = [P, I64, I64, P, P, P]
+    lib.or_compress_step.argtypes = [I64, I64, P, P, I, P, P, P, P, P, P, P, P,
+                                     F, F, F, F, I, F]
+    lib.or_warmup_step.argtypes = [I64, P, I, P, P, P, F, F, F, F, I, I64]
+    lib.or_server_reduce.argtypes = [I64, I64, P, I, P, P, P, P, P]
+    lib.or_server_average.argtypes = [I64, I64, P, I, P, P, P]
+    lib.or_chunk_sumsq.argtypes = [P, I64, I64]
+    lib.or_chunk_sumsq.restype = ctypes.c_double
+    lib.or_chunk_scale.argtypes = [P, I64, I64]
+    lib.or_chunk_scale.restype = ctypes.c_float
+    for name in ("or_pack", "or_unpack", "or_compress_step", "or_warmup_step",
+                 "or_server_reduce", "or_server_average"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def _grad(g):
+    """Return (array, is_bf16).  bf16 gradients travel as their raw uint16 bit patterns."""
+    if g.dtype == np.float32:
+        return g, 0
+    if g.dtype == np.uint16:
+        return g, 1
+    raise TypeError(f"gradient must be float32 or uint16 (bf16 bits), got {g.dtype}")
+
+
+# ----------------------------------------------------------------------------------------------
+# chunk tables
+# ----------------------------------------------------------------------------------------------
+
+def uniform_offsets(n: int, chunk: int) -> np.ndarray:
+    """Offsets of uniform chunks of `chunk` elements; the last chunk ends at n."""
+    k = (n + chunk - 1) // chunk
+    off = [min(c * chunk, n) for c in range(k)] + [n]
+    return np.asarray(off, dtype=np.int64)
+
+
+def n_words(n: int) -> int:
+    return (n + 31) // 32
+
+
+# ----------------------------------------------------------------------------------------------
+# the method
+# ----------------------------------------------------------------------------------------------
+
+def pack(x: np.ndarray) -> np.ndarray:
+    x, bf = _grad(np.ascontiguousarray(x))
+    out = np.zeros(n_words(x.size), dtype=np.uint32)
+    _check(_load().or_pack(_ptr(x), bf, x.size, _ptr(out)), "pack")
+    return out
+
+
+def unpack(words: np.ndarray, n: int, offsets: np.ndarray | None = None,
+           scales: np.ndarray | None = None) -> np.ndarray:
+    out = np.empty(n, dtype=np.float32)
+    k = 0 if offsets is None else offsets.size - 1
+    _check(_load().or_unpack(_ptr(words), n, k, _ptr(offsets), _ptr(scales), _ptr(out)), "unpack")
+    return out
+
+
+def chunk_sumsq(x: np.ndarray, begin: int, end: int) -> float:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return _load().or_chunk_sumsq(_ptr(x), begin, end)
+
+
+def chunk_scale(x: np.ndarray, begin: int, end: int) -> float:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return _load().or_chunk_scale(_ptr(x), begin, end)
+
+
+def compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef_mode=0, ef_beta=0.9,
+                  want_signs=False, count_nonfinite=False):
+    """One compressed step.  err, m, p are updated in place (fp32); v is read only.
+
+    Returns (words uint32[ceil(n/32)], scales fp32[K], signs int8[n] or None, nonfinite int or None).
+    """
+    g, bf = _grad(np.ascontiguousarray(g))
+    n = g.size
+    for a in (err, m, v, p):
+        assert a.dtype == np.float32 and a.size == n and a.flags["C_CONTIGUOUS"]
+    k = offsets.size - 1
+    words = np.zeros(n_words(n), dtype=np.uint32)
+    scales = np.zeros(max(k, 0), dtype=np.float32)
+    signs = np.zeros(n, dtype=np.int8) if want_signs else None
+    nf = np.zeros(1, dtype=np.int64) if count_nonfinite else None
+    rc = _load().or_compress_step(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), _ptr(m), _ptr(v),
+                                  _ptr(p), _ptr(words), _ptr(scales), _ptr(signs), _ptr(nf),
+                                  lr, beta1, eps, clip, ef_mode, ef_beta)
+    _check(rc, "compress_step")
+    return words, scales, signs, (int(nf[0]) if nf is not None else None)
+
+
+def warmup_step(g, m, v, p, *, lr, beta1, beta2, eps, bias_correction=False, step=0):
+    """One dense Adam step; m, v, p updated in place."""
+    g, bf = _grad(np.ascontiguousarray(g))
+    n = g.size
+    for a in (m, v, p):
+        assert a.dtype == np.float32 and a.size == n and a.flags["C_CONTIGUOUS"]
+    rc = _load().or_warmup_step(n, _ptr(g), bf, _ptr(m), _ptr(v), _ptr(p), lr, beta1, beta2, eps,
+                                1 if bias_correction else 0, step)
+    _check(rc, "warmup_step")
+
+
+def server_reduce(worker_words, worker_scales, server_err, offsets):
+    """Server half on one share: worker_words uint32[W, ceil(n/32)], worker_scales fp32[W, K].
+
+    server_err (fp32[n]) is updated in place; returns (words_out, scales_out)."""
+    n = server_err.size
+    k = offsets.size - 1
+    W = worker_words.shape[0]
+    assert worker_words.shape == (W, n_words(n)) and worker_words.dtype == np.uint32
+    assert worker_scales.shape == (W, k) and worker_scales.dtype == np.float32
+    words = np.zeros(n_words(n), dtype=np.uint32)
+    scales = np.zeros(k, dtype=np.float32)
+    rc = _load().or_server_reduce(n, k, _ptr(offsets), W, _ptr(np.ascontiguousarray(worker_words)),
+                                  _ptr(np.ascontiguousarray(worker_scales)), _ptr(server_err),
+                                  _ptr(words), _ptr(scales))
+    _check(rc, "server_reduce")
+    return words, scales
+
+
+def server_average(worker_words, worker_scales, n, offsets):
+    k = offsets.size - 1
+    W = worker_words.shape[0]
+    out = np.empty(n, dtype=np.float32)
+    rc = _load().or_server_average(n, k, _ptr(offsets), W,
+                                   _ptr(np.ascontiguousarray(worker_words)),
+                                   _ptr(np.ascontiguousarray(worker_scales)), _ptr(out))
+    _check(rc, "server_average")
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# host schedules
+# ----------------------------------------------------------------------------------------------
+
+def one_bit_adam_kind(step: int, freeze_step: int) -> str:
+    """[P2] 1-bit Adam: dense Adam while step < freeze_step, compressed afterwards (step from 0)."""
+    return "dense" if step < freeze_step else "compressed"
+
+
+def zero_one_adam_kind(t: int, period: int) -> str:
+    """[P2] 0/1 Adam: a full-precision variance refresh on every period-th step (t from 1)."""
+    return "dense" if t % period == 0 else "compressed"

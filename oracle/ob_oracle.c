@@ -1,0 +1,283 @@
+/*
+ * ob_oracle.c -- CPU oracle for the 1-bit Adam optimizer step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Plain, single-threaded, slow and meant to be checked by eye against
+ * the pages.  Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py may load or
+ * call it.  The HIP library never links, includes or executes anything from this folder, and this
+ * file takes no code, header, table or constant from that library.
+ *
+ * Pages (cited by title and section; no line numbers):
+ *   [P1] "1bit Adam" tutorial (intelliparadigm.com, article 2150495):
+ *        sec. 2.1 (sign quantization, error computation, EMA error compensation),
+ *        sec. 2.2 (first moment driven by the compressed gradient),
+ *        sec. 3.1 (per-parameter state: error buffer, momentum, variance, beta1/beta2/eps),
+ *        sec. 3.2 (compress routine; clipping at +/-5 before quantizing, NaN check after the error
+ *                  update, int8 storage of the signs),
+ *        sec. 5.1 (BERT-base table: 3.12% communication volume => one bit per fp32 element).
+ *   [P2] "DeepSpeed Communication Compression and Hiding" (shaojiemike.top):
+ *        section "baseline: why Adam is hard to compress" (the Adam moment equations),
+ *        section "1-bit Adam: warmup, frozen variance, error feedback" (the two-phase pseudo-code),
+ *        section "0/1 Adam" (periodic variance refresh alternating with 1-bit steps).
+ *   [P3] gradient-compression survey (bmjup.com post 14450), section on the core principle
+ *        (plain error feedback: the residual of the compressor is added to the next gradient).
+ *
+ * Readings taken where the pages leave a step open (each is listed with its reason in the design
+ * notes of the repository):
+ *   R1 scale: one fp32 scale per chunk, scale_c = ||x_c||_2 / sqrt(n_c).  ||x||^2 is summed in
+ *      double in ascending index order; sqrt(S / n_c) is taken in double and rounded once to fp32.
+ *   R2 sign(x) = +1 iff x >= 0.0f (IEEE ordered compare): +0 and -0 give +1, NaN gives -1.
+ *   R3 packing: bit j of uint32 word w is the sign bit of flat element 32*w + j (1 <=> +1), bits of
+ *      indices >= n are 0; the packing ignores chunk boundaries.
+ *   R4 precision: every tensor the method keeps or hands on (compensated x, g_hat, error, m, v, p,
+ *      scales) is fp32, as the state of [P1] sec. 3.1 and the in-place fp32 compensation of
+ *      [P1] sec. 3.2 are.  Each formula of the pages is evaluated here in double from its fp32
+ *      operands and rounded once to fp32 when its tensor is written.  bf16 gradients are widened
+ *      exactly to fp32 first.
+ *   R5 the update uses the new m (and in the dense step the new v).
+ *   R6 the error in plain mode is replaced (x - g_hat) as in [P2]/[P3]; in EMA mode ([P1] sec. 2.1)
+ *      it is ef_beta*err_old + (1-ef_beta)*delta with delta = fl32(x - g_hat), g_hat scaled.
+ *   R7 clipping ([P1] sec. 3.2) clamps the widened gradient elementwise to [-clip, clip] before the
+ *      error is added; clip <= 0 means off; NaN passes through.
+ *   R8 the NaN check of [P1] sec. 3.2 counts non-finite new-error elements; it changes nothing.
+ *   R9 server: avg_i = sum_w (+/- s_{w,c}) / W, summed in double over w = 0..W-1 and rounded once
+ *      to fp32; x = fl32(avg + e_srv); then the same scale/pack/plain error as the worker.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_ERR_ARG 1
+#define OR_ERR_OOM 5
+
+/* ---------- element helpers ---------- */
+
+/* bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits. */
+static float bf16_bits_to_float(uint16_t b)
+{
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static float load_grad(const void* g, int g_is_bf16, int64_t i)
+{
+    if (g_is_bf16)
+        return bf16_bits_to_float(((const uint16_t*)g)[i]);
+    return ((const float*)g)[i];
+}
+
+/* R2: the sign decision, made on the fp32 compensated value. */
+static int sign_bit(float x)
+{
+    return x >= 0.0f ? 1 : 0;
+}
+
+static int check_offsets(int64_t n, int64_t K, const int64_t* off)
+{
+    if (n < 0 || K < 0 || off == NULL) return 0;
+    if (n == 0) return K == 0 || (K >= 0 && off[0] == 0);
+    if (K < 1 || off[0] != 0 || off[K] != n) return 0;
+    for (int64_t c = 0; c < K; ++c)
+        if (off[c + 1] <= off[c]) return 0;
+    return 1;
+}
+
+/* ---------- R1: per-chunk scale ---------- */
+
+double or_chunk_sumsq(const float* x, int64_t begin, int64_t end)
+{
+    double s = 0.0;
+    for (int64_t i = begin; i < end; ++i)
+        s += (double)x[i] * (double)x[i];
+    return s;
+}
+
+float or_chunk_scale(const float* x, int64_t begin, int64_t end)
+{
+    double s = or_chunk_sumsq(x, begin, end);
+    return (float)sqrt(s / (double)(end - begin));
+}
+
+/* ---------- R3: packing and unpacking ---------- */
+
+int or_pack(const void* x, int x_is_bf16, int64_t n, uint32_t* words)
+{
+    if (n < 0 || (n > 0 && (x == NULL || words == NULL))) return OR_ERR_ARG;
+    int64_t nw = (n + 31) / 32;
+    for (int64_t w = 0; w < nw; ++w) words[w] = 0u;
+    for (int64_t i = 0; i < n; ++i)
+        if (sign_bit(load_grad(x, x_is_bf16, i)))
+            words[i / 32] |= (uint32_t)1u << (i % 32);
+    return OR_OK;
+}
+
+static int word_bit(const uint32_t* words, int64_t i)
+{
+    return (int)((words[i / 32] >> (i % 32)) & 1u);
+}
+
+/* out_i = +s_c or -s_c by the bit of i; s_c = 1 when scales == NULL.  [P2] 1-bit Adam: dequantize. */
+int or_unpack(const uint32_t* words, int64_t n, int64_t K, const int64_t* off, const float* scales,
+              float* out)
+{
+    if (n < 0 || (n > 0 && (words == NULL || out == NULL))) return OR_ERR_ARG;
+    if (scales != NULL) {
+        if (!check_offsets(n, K, off)) return OR_ERR_ARG;
+        for (int64_t c = 0; c < K; ++c)
+            for (int64_t i = off[c]; i < off[c + 1]; ++i)
+                out[i] = word_bit(words, i) ? scales[c] : -scales[c];
+    } else {
+        for (int64_t i = 0; i < n; ++i)
+            out[i] = word_bit(words, i) ? 1.0f : -1.0f;
+    }
+    return OR_OK;
+}
+
+/* ---------- compressed step ([P2] 1-bit Adam, compressed branch; [P1] sec. 2.1, 2.2, 3.2) ---------- */
+
+int or_compress_step(int64_t n, int64_t K, const int64_t* off,
+                     const void* g, int g_is_bf16,
+                     float* err, float* m, const float* v, float* p,
+                     uint32_t* words, float* scales, int8_t* signs, int64_t* nonfinite,
+                     float lr, float beta1, float eps, float clip, int ef_mode, float ef_beta)
+{
+    if (!check_offsets(n, K, off)) return OR_ERR_ARG;
+    if (n == 0) return OR_OK;
+    if (!g || !err || !m || !v || !p || !words || !scales) return OR_ERR_ARG;
+
+    float* x = (float*)calloc((size_t)n, sizeof(float));
+    if (x == NULL) return OR_ERR_OOM;
+
+    /* compensated = grad (+clip, R7) + error, kept as an fp32 tensor (R4). */
+    for (int64_t i = 0; i < n; ++i) {
+        double gi = (double)load_grad(g, g_is_bf16, i);
+        if (clip > 0.0f) {
+            double c = (double)clip;
+            if (gi > c)
+                gi = c;
+            else if (gi < -c)
+                gi = -c;
+        }
+        x[i] = (float)(gi + (double)err[i]);
+    }
+
+    /* q, scale = one_bit_quantize(compensated): R1 scale per chunk, R2/R3 sign bits. */
+    for (int64_t c = 0; c < K; ++c)
+        scales[c] = or_chunk_scale(x, off[c], off[c + 1]);
+    or_pack(x, 0, n, words);
+
+    const double b1 = (double)beta1;
+    const double eb = (double)ef_beta;
+    for (int64_t c = 0; c < K; ++c) {
+        for (int64_t i = off[c]; i < off[c + 1]; ++i) {
+            int b = sign_bit(x[i]);
+            /* g_hat = dequantize(q): +scale or -scale. */
+            float gh = b ? scales[c] : -scales[c];
+            /* error = compensated - g_hat (plain, [P2]/[P3]), or its EMA ([P1] sec. 2.1). */
+            float delta = (float)((double)x[i] - (double)gh);
+            float e_new;
+            if (ef_mode == 1)
+                e_new = (float)(eb * (double)err[i] + (1.0 - eb) * (double)delta);
+            else
+                e_new = delta;
+            err[i] = e_new;
+            /* m = beta1*m + (1-beta1)*g_hat ([P2]; [P1] sec. 2.2). */
+            m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)gh);
+            /* param -= lr * m / (sqrt(v_frozen) + eps), v untouched ([P2]). */
+            p[i] = (float)((double)p[i] -
+                           (double)lr * ((double)m[i] / (sqrt((double)v[i]) + (double)eps)));
+            if (signs != NULL) signs[i] = (int8_t)(b ? 1 : -1);
+            if (nonfinite != NULL && !isfinite(e_new)) *nonfinite += 1;
+        }
+    }
+    free(x);
+    return OR_OK;
+}
+
+/* ---------- dense Adam step (warmup before freeze_step, and the 0/1 Adam refresh) ----------
+ * [P2] baseline section: m = b1 m + (1-b1) g, v = b2 v + (1-b2) g^2; update as in the 1-bit Adam
+ * pseudo-code with the new m and v.  bias_correction != 0 divides m and v by (1 - b^t), t = step
+ * (textbook Adam); the pages' pseudo-code has no bias correction, so it is off by default.
+ * The error buffer is not touched. */
+int or_warmup_step(int64_t n, const void* g, int g_is_bf16, float* m, float* v, float* p,
+                   float lr, float beta1, float beta2, float eps, int bias_correction, int64_t step)
+{
+    if (n < 0) return OR_ERR_ARG;
+    if (n == 0) return OR_OK;
+    if (!g || !m || !v || !p) return OR_ERR_ARG;
+    if (bias_correction && step < 1) return OR_ERR_ARG;
+    const double b1 = (double)beta1, b2 = (double)beta2;
+    double bc1 = 1.0, bc2 = 1.0;
+    if (bias_correction) {
+        bc1 = 1.0 - pow(b1, (double)step);
+        bc2 = 1.0 - pow(b2, (double)step);
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        double gi = (double)load_grad(g, g_is_bf16, i);
+        m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * gi);
+        v[i] = (float)(b2 * (double)v[i] + (1.0 - b2) * (gi * gi));
+        double mh = (double)m[i] / bc1;
+        double vh = (double)v[i] / bc2;
+        p[i] = (float)((double)p[i] - (double)lr * (mh / (sqrt(vh) + (double)eps)));
+    }
+    return OR_OK;
+}
+
+/* ---------- server half of the compressed allreduce on one GPU's share ([P2] compressed_allreduce) ----
+ * worker_words: W rows of ceil(n/32) words; worker_scales: W rows of K scales.  R9. */
+int or_server_reduce(int64_t n, int64_t K, const int64_t* off, int W,
+                     const uint32_t* worker_words, const float* worker_scales,
+                     float* server_err, uint32_t* words_out, float* scales_out)
+{
+    if (!check_offsets(n, K, off) || W < 1) return OR_ERR_ARG;
+    if (n == 0) return OR_OK;
+    if (!worker_words || !worker_scales || !server_err || !words_out || !scales_out) return OR_ERR_ARG;
+    const int64_t nw = (n + 31) / 32;
+    float* x = (float*)calloc((size_t)n, sizeof(float));
+    if (x == NULL) return OR_ERR_OOM;
+
+    for (int64_t c = 0; c < K; ++c) {
+        for (int64_t i = off[c]; i < off[c + 1]; ++i) {
+            double a = 0.0;
+            for (int w = 0; w < W; ++w) {
+                double s = (double)worker_scales[(int64_t)w * K + c];
+                a += word_bit(worker_words + (int64_t)w * nw, i) ? s : -s;
+            }
+            float avg = (float)(a / (double)W);
+            x[i] = (float)((double)avg + (double)server_err[i]);
+        }
+    }
+    for (int64_t c = 0; c < K; ++c)
+        scales_out[c] = or_chunk_scale(x, off[c], off[c + 1]);
+    or_pack(x, 0, n, words_out);
+    for (int64_t c = 0; c < K; ++c) {
+        for (int64_t i = off[c]; i < off[c + 1]; ++i) {
+            float gh = sign_bit(x[i]) ? scales_out[c] : -scales_out[c];
+            server_err[i] = (float)((double)x[i] - (double)gh);
+        }
+    }
+    free(x);
+    return OR_OK;
+}
+
+/* Per-element server average alone (for checking the exact-average reading R9 by itself). */
+int or_server_average(int64_t n, int64_t K, const int64_t* off, int W,
+                      const uint32_t* worker_words, const float* worker_scales, float* avg_out)
+{
+    if (!check_offsets(n, K, off) || W < 1) return OR_ERR_ARG;
+    const int64_t nw = (n + 31) / 32;
+    for (int64_t c = 0; c < K; ++c) {
+        for (int64_t i = off[c]; i < off[c + 1]; ++i) {
+            double a = 0.0;
+            for (int w = 0; w < W; ++w) {
+                double s = (double)worker_scales[(int64_t)w * K + c];
+                a += word_bit(worker_words + (int64_t)w * nw, i) ? s : -s;
+            }
+            avg_out[i] = (float)(a / (double)W);
+        }
+    }
+    return OR_OK;
+}

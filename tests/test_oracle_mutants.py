@@ -1,0 +1,90 @@
+"""Planted mistakes: each plausible slip in the oracle must make its pin tests fail.
+
+Each case copies oracle/ob_oracle.c to a temporary folder, applies one textual change (a dropped
+term, a wrong sign or index, a transposed operand, a wrong constant), builds it with the oracle's own
+flags and runs tests/test_oracle.py against that copy in a subprocess.  The real oracle is never
+modified.  CPU only.
+"""
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "ob_oracle.c")
+
+MUTANTS = {
+    "sign_of_zero": ("return x >= 0.0f ? 1 : 0;", "return x > 0.0f ? 1 : 0;"),
+    "bit_order": ("words[i / 32] |= (uint32_t)1u << (i % 32);",
+                  "words[i / 32] |= (uint32_t)1u << (31 - i % 32);"),
+    "dense_drops_eps": ("(mh / (sqrt(vh) + (double)eps))", "(mh / (sqrt(vh)))"),
+    "scale_count": ("return (float)sqrt(s / (double)(end - begin));",
+                    "return (float)sqrt(s / (double)(end - begin + 1));"),
+    "scale_no_sqrt": ("return (float)sqrt(s / (double)(end - begin));",
+                      "return (float)(s / (double)(end - begin));"),
+    "error_sign": ("float delta = (float)((double)x[i] - (double)gh);",
+                   "float delta = (float)((double)gh - (double)x[i]);"),
+    "momentum_uses_x": ("m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)gh);",
+                        "m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)x[i]);"),
+    "momentum_coeffs_swapped": ("m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)gh);",
+                                "m[i] = (float)((1.0 - b1) * (double)m[i] + b1 * (double)gh);"),
+    "update_sign": ("p[i] = (float)((double)p[i] -\n                           (double)lr",
+                    "p[i] = (float)((double)p[i] +\n                           (double)lr"),
+    "update_drops_eps": ("(sqrt((double)v[i]) + (double)eps)));\n            if (signs",
+                         "(sqrt((double)v[i]))));\n            if (signs"),
+    "update_no_sqrt": ("((double)m[i] / (sqrt((double)v[i]) + (double)eps)",
+                       "((double)m[i] / ((double)v[i] + (double)eps)"),
+    "ema_coeffs_swapped": ("e_new = (float)(eb * (double)err[i] + (1.0 - eb) * (double)delta);",
+                           "e_new = (float)((1.0 - eb) * (double)err[i] + eb * (double)delta);"),
+    "ema_unscaled_sign": ("float delta = (float)((double)x[i] - (double)gh);",
+                          "float delta = (float)((double)x[i] - (b ? 1.0 : -1.0));"),
+    "clip_lower_bound": ("gi = -c;", "gi = c;"),
+    "gh_wrong_chunk": ("float gh = b ? scales[c] : -scales[c];",
+                       "float gh = b ? scales[0] : -scales[0];"),
+    "nonfinite_nan_only": ("!isfinite(e_new)", "isnan(e_new)"),
+    "int8_zero_for_plus": ("signs[i] = (int8_t)(b ? 1 : -1);", "signs[i] = (int8_t)(b ? 0 : -1);"),
+    "dense_v_not_squared": ("(1.0 - b2) * (gi * gi)", "(1.0 - b2) * gi"),
+    "dense_v_uses_beta1": ("v[i] = (float)(b2 * (double)v[i]", "v[i] = (float)(b1 * (double)v[i]"),
+    "dense_bias_corr_power": ("bc2 = 1.0 - pow(b2, (double)step);", "bc2 = 1.0 - pow(b1, (double)step);"),
+    "dense_old_m_in_update": ("double mh = (double)m[i] / bc1;", "double mh = (double)m[i] / bc1 / b1;"),
+    "server_bit_polarity": ("a += word_bit(worker_words + (int64_t)w * nw, i) ? s : -s;",
+                            "a += word_bit(worker_words + (int64_t)w * nw, i) ? -s : s;", 2),
+    "server_row_stride": ("a += word_bit(worker_words + (int64_t)w * nw, i) ? s : -s;",
+                          "a += word_bit(worker_words + (int64_t)w * K, i) ? s : -s;", 2),
+    "server_scale_row_stride": ("double s = (double)worker_scales[(int64_t)w * K + c];",
+                                "double s = (double)worker_scales[(int64_t)c * W + w];", 2),
+    "server_divisor": ("float avg = (float)(a / (double)W);", "float avg = (float)(a / (double)(W + 1));"),
+    "server_error_uses_avg": ("server_err[i] = (float)((double)x[i] - (double)gh);",
+                              "server_err[i] = (float)((double)x[i] - (double)gh + (double)server_err[i]);"),
+    "unpack_polarity": ("out[i] = word_bit(words, i) ? scales[c] : -scales[c];",
+                        "out[i] = word_bit(words, i) ? -scales[c] : scales[c];"),
+}
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    with tempfile.TemporaryDirectory(prefix="ob_mutants_") as d:
+        yield d
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, workdir):
+    old, new, *count = MUTANTS[name]
+    count = count[0] if count else 1
+    src = open(SRC).read()
+    assert src.count(old) == count, f"mutation anchor for {name} does not match {count} time(s)"
+    csrc = os.path.join(workdir, f"{name}.c")
+    lib = os.path.join(workdir, f"lib_{name}.so")
+    with open(csrc, "w") as f:
+        f.write(src.replace(old, new))
+    subprocess.run(["gcc", *oracle.CFLAGS, "-o", lib, csrc, "-lm"], check=True,
+                   stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    env = dict(os.environ, OB_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode != 0, f"planted mistake '{name}' passed every pin:\n{r.stdout[-2000:]}"
