@@ -1,0 +1,433 @@
+// ob_api.cpp -- host runtime and C ABI of libobadam.so (declarations and contracts in ob_adam.h).
+//
+// The host side only validates arguments, owns the plan's small device tables and enqueues kernels
+// on the caller's stream; every step of the optimizer runs in ob_kernels.hip.
+#include "ob_adam.h"
+#include "ob_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <new>
+#include <vector>
+
+struct ob_plan_s {
+    int device = 0;
+    int64_t n = 0;
+    int32_t K = 0;
+    int64_t block_elems = 0;
+    int64_t n_items = 0;
+    ob::Item* d_items = nullptr;
+    int32_t* d_chunk_first = nullptr;
+    int64_t* d_chunk_off = nullptr;
+    double* d_partials = nullptr;
+
+    // kernel timing
+    bool timing = false;
+    struct Rec {
+        int kernel;
+        hipEvent_t a, b;
+    };
+    std::vector<Rec> pending;
+    std::vector<hipEvent_t> pool;
+    double total_ms[OB_KERNEL_COUNT] = {};
+    int64_t launches[OB_KERNEL_COUNT] = {};
+
+    ob::PlanDev dev() const
+    {
+        ob::PlanDev pd;
+        pd.items = d_items;
+        pd.chunk_first = d_chunk_first;
+        pd.chunk_off = d_chunk_off;
+        pd.partials = d_partials;
+        pd.n = n;
+        pd.n_items = n_items;
+        pd.K = K;
+        return pd;
+    }
+};
+
+namespace {
+
+constexpr int64_t kMaxBlockElems = int64_t(1) << 20;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Make the plan's device current for the duration of a call.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev) != hipSuccess) {
+            ok = false;
+            return;
+        }
+        if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+    }
+    ~DeviceGuard()
+    {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+// Elements per work block: enough blocks to fill 256 CUs several times over, whole tiles, at most
+// 64 tiles.  OB_BLOCK_ELEMS (a multiple of 1024) overrides the choice for tuning sweeps.
+int64_t choose_block_elems(int64_t n)
+{
+    if (const char* env = std::getenv("OB_BLOCK_ELEMS")) {
+        const long long v = std::atoll(env);
+        if (v >= ob::kTile && v <= kMaxBlockElems && v % ob::kTile == 0) return v;
+    }
+    const int64_t target_blocks = 8192;
+    int64_t e = (n + target_blocks - 1) / target_blocks;
+    e = (e + ob::kTile - 1) / ob::kTile * ob::kTile;
+    return std::min<int64_t>(std::max<int64_t>(e, 4 * ob::kTile), 64 * ob::kTile);
+}
+
+void free_plan(ob_plan p)
+{
+    if (!p) return;
+    for (auto& r : p->pending) {
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    for (auto e : p->pool) (void)hipEventDestroy(e);
+    if (p->d_items) (void)hipFree(p->d_items);
+    if (p->d_chunk_first) (void)hipFree(p->d_chunk_first);
+    if (p->d_chunk_off) (void)hipFree(p->d_chunk_off);
+    if (p->d_partials) (void)hipFree(p->d_partials);
+    delete p;
+}
+
+hipEvent_t take_event(ob_plan p)
+{
+    if (!p->pool.empty()) {
+        hipEvent_t e = p->pool.back();
+        p->pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Enqueue one kernel via `launch`, bracketed by events when timing is on.
+template <class F>
+ob_status timed(ob_plan p, int kernel, hipStream_t s, F&& launch)
+{
+    hipEvent_t a = nullptr, b = nullptr;
+    if (p && p->timing) {
+        a = take_event(p);
+        b = take_event(p);
+        if (a && b) (void)hipEventRecord(a, s);
+    }
+    (void)hipGetLastError();  // clear a stale error so the check below sees this launch only
+    const hipError_t err = launch();
+    if (a && b) {
+        (void)hipEventRecord(b, s);
+        p->pending.push_back({kernel, a, b});
+    } else {
+        if (a) p->pool.push_back(a);
+        if (b) p->pool.push_back(b);
+    }
+    return err == hipSuccess ? OB_OK : OB_ERR_HIP;
+}
+
+ob_status drain_timing(ob_plan p)
+{
+    ob_status st = OB_OK;
+    for (auto& r : p->pending) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+            st = OB_ERR_HIP;
+        else {
+            p->total_ms[r.kernel] += ms;
+            p->launches[r.kernel] += 1;
+        }
+        p->pool.push_back(r.a);
+        p->pool.push_back(r.b);
+    }
+    p->pending.clear();
+    return st;
+}
+
+bool valid_dtype(int d) { return d == OB_F32 || d == OB_BF16; }
+
+ob_status check_grad(const void* g, int dt)
+{
+    if (!valid_dtype(dt)) return OB_ERR_DTYPE;
+    if (!g) return OB_ERR_ARG;
+    return aligned(g, dt == OB_BF16 ? 8 : 16) ? OB_OK : OB_ERR_ALIGN;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ob_status_str(ob_status s)
+{
+    switch (s) {
+    case OB_OK: return "ok";
+    case OB_ERR_ARG: return "invalid argument";
+    case OB_ERR_ALIGN: return "misaligned pointer or chunk boundary";
+    case OB_ERR_DTYPE: return "unknown dtype";
+    case OB_ERR_HIP: return "HIP runtime error";
+    case OB_ERR_OOM: return "device allocation failed";
+    }
+    return "unknown status";
+}
+
+ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_offsets, int64_t n_chunks,
+                         ob_plan* out)
+{
+    if (!out) return OB_ERR_ARG;
+    *out = nullptr;
+    if (n < 0) return OB_ERR_ARG;
+
+    // chunk table (host)
+    std::vector<int64_t> off;
+    if (chunk_offsets == nullptr) {
+        if (chunk_size <= 0) return OB_ERR_ARG;
+        if (n > 0) {
+            const int64_t K = (n + chunk_size - 1) / chunk_size;
+            if (K > 1 && chunk_size % 64 != 0) return OB_ERR_ALIGN;
+            if (K > INT32_MAX - 1) return OB_ERR_ARG;
+            off.resize(static_cast<size_t>(K) + 1);
+            for (int64_t c = 0; c < K; ++c) off[c] = c * chunk_size;
+            off[K] = n;
+        } else {
+            off.push_back(0);
+        }
+    } else {
+        if (n_chunks < 0 || n_chunks > INT32_MAX - 1) return OB_ERR_ARG;
+        if (n > 0 && n_chunks < 1) return OB_ERR_ARG;
+        off.assign(chunk_offsets, chunk_offsets + n_chunks + 1);
+        if (off[0] != 0 || off.back() != n) return OB_ERR_ARG;
+        for (int64_t c = 0; c < n_chunks; ++c)
+            if (off[c + 1] <= off[c]) return OB_ERR_ARG;
+        for (int64_t c = 1; c < n_chunks; ++c)
+            if (off[c] % 64 != 0) return OB_ERR_ALIGN;
+    }
+    const int64_t K = static_cast<int64_t>(off.size()) - 1;
+
+    ob_plan p = new (std::nothrow) ob_plan_s;
+    if (!p) return OB_ERR_OOM;
+    p->n = n;
+    p->K = static_cast<int32_t>(K);
+    p->block_elems = choose_block_elems(n);
+
+    // work blocks: consecutive per chunk
+    std::vector<ob::Item> items;
+    std::vector<int32_t> first(static_cast<size_t>(K) + 1, 0);
+    for (int64_t c = 0; c < K; ++c) {
+        first[c] = static_cast<int32_t>(items.size());
+        for (int64_t s = off[c]; s < off[c + 1]; s += p->block_elems) {
+            ob::Item it;
+            it.start = s;
+            it.len = static_cast<int32_t>(std::min<int64_t>(p->block_elems, off[c + 1] - s));
+            it.chunk = static_cast<int32_t>(c);
+            items.push_back(it);
+            if (items.size() > static_cast<size_t>(INT32_MAX)) {
+                delete p;
+                return OB_ERR_ARG;
+            }
+        }
+    }
+    first[K] = static_cast<int32_t>(items.size());
+    p->n_items = static_cast<int64_t>(items.size());
+
+    if (hipGetDevice(&p->device) != hipSuccess) {
+        delete p;
+        return OB_ERR_HIP;
+    }
+    if (p->n_items > 0) {
+        const hipError_t e1 = hipMalloc(&p->d_items, items.size() * sizeof(ob::Item));
+        const hipError_t e2 = hipMalloc(&p->d_chunk_first, first.size() * sizeof(int32_t));
+        const hipError_t e3 = hipMalloc(&p->d_chunk_off, off.size() * sizeof(int64_t));
+        const hipError_t e4 = hipMalloc(&p->d_partials, items.size() * sizeof(double));
+        if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess || e4 != hipSuccess) {
+            const bool oom = e1 == hipErrorOutOfMemory || e2 == hipErrorOutOfMemory ||
+                             e3 == hipErrorOutOfMemory || e4 == hipErrorOutOfMemory;
+            free_plan(p);
+            return oom ? OB_ERR_OOM : OB_ERR_HIP;
+        }
+        if (hipMemcpy(p->d_items, items.data(), items.size() * sizeof(ob::Item), hipMemcpyHostToDevice) !=
+                hipSuccess ||
+            hipMemcpy(p->d_chunk_first, first.data(), first.size() * sizeof(int32_t),
+                      hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(p->d_chunk_off, off.data(), off.size() * sizeof(int64_t), hipMemcpyHostToDevice) !=
+                hipSuccess) {
+            free_plan(p);
+            return OB_ERR_HIP;
+        }
+    }
+    *out = p;
+    return OB_OK;
+}
+
+ob_status ob_plan_destroy(ob_plan plan)
+{
+    if (!plan) return OB_ERR_ARG;
+    DeviceGuard g(plan->device);
+    free_plan(plan);
+    return OB_OK;
+}
+
+int64_t ob_plan_num_elements(ob_plan plan) { return plan ? plan->n : -1; }
+int64_t ob_plan_num_chunks(ob_plan plan) { return plan ? plan->K : -1; }
+int64_t ob_plan_num_blocks(ob_plan plan) { return plan ? plan->n_items : -1; }
+int64_t ob_plan_block_elems(ob_plan plan) { return plan ? plan->block_elems : -1; }
+
+ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* m, float* v, float* p,
+                              const ob_hparams* hp, hipStream_t stream)
+{
+    if (!plan || !hp) return OB_ERR_ARG;
+    if (!valid_dtype(g_dtype)) return OB_ERR_DTYPE;
+    if (plan->n == 0) return OB_OK;
+    if (ob_status st = check_grad(g, g_dtype)) return st;
+    if (!m || !v || !p) return OB_ERR_ARG;
+    if (!aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16)) return OB_ERR_ALIGN;
+    if (hp->bias_correction && hp->step < 1) return OB_ERR_ARG;
+
+    ob::DenseParams dp;
+    dp.lr = hp->lr;
+    dp.beta1 = hp->beta1;
+    dp.one_m_beta1 = 1.0 - static_cast<double>(hp->beta1);
+    dp.beta2 = hp->beta2;
+    dp.one_m_beta2 = 1.0 - static_cast<double>(hp->beta2);
+    dp.eps = hp->eps;
+    dp.bias_correction = hp->bias_correction ? 1 : 0;
+    dp.bc1 = 1.0;
+    dp.bc2 = 1.0;
+    if (hp->bias_correction) {
+        dp.bc1 = 1.0 - std::pow(static_cast<double>(hp->beta1), static_cast<double>(hp->step));
+        dp.bc2 = 1.0 - std::pow(static_cast<double>(hp->beta2), static_cast<double>(hp->step));
+    }
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return OB_ERR_HIP;
+    const ob::PlanDev pd = plan->dev();
+    const int bf = g_dtype == OB_BF16;
+    return timed(plan, OB_KERNEL_DENSE, stream, [&] { return ob::launch_dense(pd, g, bf, m, v, p, dp, stream); });
+}
+
+ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* err, float* m,
+                                const float* v, float* p, uint32_t* words_out, float* scales_out,
+                                int8_t* signs_out, uint64_t* nonfinite_out, const ob_hparams* hp,
+                                hipStream_t stream)
+{
+    if (!plan || !hp) return OB_ERR_ARG;
+    if (!valid_dtype(g_dtype)) return OB_ERR_DTYPE;
+    if (plan->n == 0) return OB_OK;
+    if (ob_status st = check_grad(g, g_dtype)) return st;
+    if (!err || !m || !v || !p || !words_out || !scales_out) return OB_ERR_ARG;
+    if (!aligned(err, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16)) return OB_ERR_ALIGN;
+    if (!aligned(words_out, 4) || !aligned(scales_out, 4)) return OB_ERR_ALIGN;
+    if (signs_out && !aligned(signs_out, 4)) return OB_ERR_ALIGN;
+    if (nonfinite_out && !aligned(nonfinite_out, 8)) return OB_ERR_ALIGN;
+    if (hp->ef_mode != OB_EF_PLAIN && hp->ef_mode != OB_EF_EMA) return OB_ERR_ARG;
+
+    ob::CompressParams cp;
+    cp.lr = hp->lr;
+    cp.beta1 = hp->beta1;
+    cp.one_m_beta1 = 1.0 - static_cast<double>(hp->beta1);
+    cp.eps = hp->eps;
+    cp.clip = hp->clip > 0.0f ? hp->clip : 0.0f;
+    cp.ef_beta = hp->ef_beta;
+    cp.one_m_ef_beta = 1.0 - static_cast<double>(hp->ef_beta);
+
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return OB_ERR_HIP;
+    const ob::PlanDev pd = plan->dev();
+    const int bf = g_dtype == OB_BF16;
+    ob_status st = timed(plan, OB_KERNEL_CHUNK_SUMSQ, stream,
+                         [&] { return ob::launch_chunk_sumsq(pd, g, bf, err, cp.clip, stream); });
+    if (st != OB_OK) return st;
+    return timed(plan, OB_KERNEL_COMPRESS, stream, [&] {
+        return ob::launch_compress(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out,
+                                   reinterpret_cast<unsigned long long*>(nonfinite_out),
+                                   hp->ef_mode == OB_EF_EMA, cp, stream);
+    });
+}
+
+ob_status ob_server_reduce(ob_plan plan, int32_t W, const uint32_t* worker_words, const float* worker_scales,
+                           float* server_err, uint32_t* words_out, float* scales_out, hipStream_t stream)
+{
+    if (!plan) return OB_ERR_ARG;
+    if (W < 1 || W > 1024) return OB_ERR_ARG;
+    if (plan->n == 0) return OB_OK;
+    if (!worker_words || !worker_scales || !server_err || !words_out || !scales_out) return OB_ERR_ARG;
+    if (!aligned(worker_words, 4) || !aligned(worker_scales, 4) || !aligned(server_err, 16) ||
+        !aligned(words_out, 4) || !aligned(scales_out, 4))
+        return OB_ERR_ALIGN;
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return OB_ERR_HIP;
+    const ob::PlanDev pd = plan->dev();
+    ob_status st = timed(plan, OB_KERNEL_SERVER_SUMSQ, stream, [&] {
+        return ob::launch_server_sumsq(pd, W, worker_words, worker_scales, server_err, stream);
+    });
+    if (st != OB_OK) return st;
+    return timed(plan, OB_KERNEL_SERVER_APPLY, stream, [&] {
+        return ob::launch_server_apply(pd, W, worker_words, worker_scales, server_err, words_out, scales_out,
+                                       stream);
+    });
+}
+
+ob_status ob_pack(const void* x, ob_dtype x_dtype, int64_t n, uint32_t* words_out, hipStream_t stream)
+{
+    if (!valid_dtype(x_dtype)) return OB_ERR_DTYPE;
+    if (n < 0) return OB_ERR_ARG;
+    if (n == 0) return OB_OK;
+    if (!x || !words_out) return OB_ERR_ARG;
+    if (!aligned(x, x_dtype == OB_BF16 ? 8 : 16) || !aligned(words_out, 4)) return OB_ERR_ALIGN;
+    (void)hipGetLastError();
+    return ob::launch_pack(x, x_dtype == OB_BF16, n, words_out, stream) == hipSuccess ? OB_OK : OB_ERR_HIP;
+}
+
+ob_status ob_unpack(ob_plan plan, const uint32_t* words, int64_t n, const float* scales, float* out,
+                    hipStream_t stream)
+{
+    if (n < 0) return OB_ERR_ARG;
+    if (scales && !plan) return OB_ERR_ARG;
+    if (plan && plan->n != n) return OB_ERR_ARG;
+    if (n == 0) return OB_OK;
+    if (!words || !out) return OB_ERR_ARG;
+    if (!aligned(words, 4) || !aligned(out, 16) || (scales && !aligned(scales, 4))) return OB_ERR_ALIGN;
+    if (plan && scales) {
+        DeviceGuard guard(plan->device);
+        if (!guard.ok) return OB_ERR_HIP;
+        const ob::PlanDev pd = plan->dev();
+        return timed(plan, OB_KERNEL_UNPACK, stream,
+                     [&] { return ob::launch_unpack(&pd, words, n, scales, out, stream); });
+    }
+    (void)hipGetLastError();
+    return ob::launch_unpack(nullptr, words, n, nullptr, out, stream) == hipSuccess ? OB_OK : OB_ERR_HIP;
+}
+
+ob_status ob_plan_set_timing(ob_plan plan, int32_t enable)
+{
+    if (!plan) return OB_ERR_ARG;
+    DeviceGuard guard(plan->device);
+    ob_status st = drain_timing(plan);
+    plan->timing = enable != 0;
+    for (int k = 0; k < OB_KERNEL_COUNT; ++k) {
+        plan->total_ms[k] = 0.0;
+        plan->launches[k] = 0;
+    }
+    return st;
+}
+
+ob_status ob_plan_read_timing(ob_plan plan, int32_t kernel, double* total_ms, int64_t* launches)
+{
+    if (!plan || kernel < 0 || kernel >= OB_KERNEL_COUNT || !total_ms || !launches) return OB_ERR_ARG;
+    DeviceGuard guard(plan->device);
+    const ob_status st = drain_timing(plan);
+    *total_ms = plan->total_ms[kernel];
+    *launches = plan->launches[kernel];
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// ob_internal.h -- shared between the host runtime (ob_api.cpp) and the kernels (ob_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ob {
+
+// Launch geometry of every per-element kernel: 256 threads (four 64-wide waves), each lane owning
+// 4 consecutive elements per tile, so one tile is 1024 consecutive elements and one 16-byte access
+// per lane per fp32 array.
+constexpr int kBlock = 256;
+constexpr int kVec = 4;
+constexpr int kTile = kBlock * kVec;
+
+// One work block: a contiguous run of elements inside one chunk.  Blocks of a chunk are consecutive,
+// start at multiples of 64 elements and (except a chunk's last) hold a whole number of tiles.
+struct Item {
+    int64_t start;
+    int32_t len;
+    int32_t chunk;
+};
+
+// Device-side view of a plan.
+struct PlanDev {
+    const Item* items;          // [n_items]
+    const int32_t* chunk_first; // [K + 1]: blocks of chunk c are [chunk_first[c], chunk_first[c+1])
+    const int64_t* chunk_off;   // [K + 1]: element offsets
+    double* partials;           // [n_items]: per-block sum of squares (workspace)
+    int64_t n;
+    int64_t n_items;
+    int32_t K;
+};
+
+// Hyperparameters widened to double: each state line is evaluated in double from fp32 operands and
+// rounded once to fp32 when stored (1 - beta is exact in double for beta in [0.5, 1]).
+struct CompressParams {
+    double lr, beta1, one_m_beta1, eps, ef_beta, one_m_ef_beta;
+    float clip;
+};
+
+struct DenseParams {
+    double lr, beta1, one_m_beta1, beta2, one_m_beta2, eps, bc1, bc2;
+    int bias_correction;
+};
+
+hipError_t launch_chunk_sumsq(const PlanDev& pd, const void* g, int g_bf16, const float* err,
+                              float clip, hipStream_t s);
+hipError_t launch_compress(const PlanDev& pd, const void* g, int g_bf16, float* err, float* m,
+                           const float* v, float* p, uint32_t* words, float* scales, int8_t* signs,
+                           unsigned long long* nonfinite, int ema, const CompressParams& cp,
+                           hipStream_t s);
+hipError_t launch_dense(const PlanDev& pd, const void* g, int g_bf16, float* m, float* v, float* p,
+                        const DenseParams& dp, hipStream_t s);
+hipError_t launch_server_sumsq(const PlanDev& pd, int W, const uint32_t* ww, const float* ws,
+                               const float* e, hipStream_t s);
+hipError_t launch_server_apply(const PlanDev& pd, int W, const uint32_t* ww, const float* ws,
+                               float* e, uint32_t* words, float* scales, hipStream_t s);
+hipError_t launch_unpack(const PlanDev* pd, const uint32_t* words, int64_t n, const float* scales,
+                         float* out, hipStream_t s);
+hipError_t launch_pack(const void* x, int x_bf16, int64_t n, uint32_t* words, hipStream_t s);
+
+}  // namespace ob

@@ -1,0 +1,717 @@
+// ob_kernels.hip -- HIP kernels of the 1-bit Adam step for gfx950 (MI355X).
+//
+// Pages cited (title and section):
+//   [P1] "1bit Adam" tutorial (intelliparadigm.com article 2150495): sec. 2.1 (sign quantization and
+//        EMA error compensation), sec. 2.2 (first moment on the compressed gradient), sec. 3.2
+//        (clip to +/-5 before quantizing, NaN check, int8 signs).
+//   [P2] "DeepSpeed Communication Compression and Hiding": "baseline" section (Adam moments),
+//        "1-bit Adam: warmup, frozen variance, error feedback" (compressed branch, dequantize,
+//        compressed_allreduce), "0/1 Adam" (refresh step = dense step).
+//
+// Design (memory bound: ~30 bytes and a few dozen ALU ops per element, no dense contraction, so no
+// MFMA):
+//   * every per-element kernel walks work blocks ("items") of one chunk each; a block of 256 threads
+//     = four wave64s; each lane owns 4 consecutive elements per 1024-element tile, so each fp32
+//     array moves as one 16-byte load/store per lane and a wave covers 1 KiB contiguous per array;
+//   * the per-chunk scale needs the whole chunk before any element can be finished, hence two
+//     passes: pass 1 writes one double partial sum of squares per block (wave butterfly in registers,
+//     LDS across the four waves); pass 2 reduces the chunk's partials in a fixed order at its start
+//     (every block of the chunk gets bit-identical scales), then does the fused streaming update;
+//   * sign bits: each lane forms a 4-bit nibble; an OR across 8 neighbouring lanes with DPP row
+//     permutes (no LDS) builds the 32-bit word of 32 consecutive elements, written by one lane;
+//   * all fp32 arithmetic is plain IEEE (no fast-math, denormals kept: a negative denormal must give
+//     sign -1).
+#include "ob_internal.h"
+
+#include <math.h>
+
+namespace ob {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPlainItem = 16 * kTile;  // elements per block for the plan-less pack/unpack
+
+// ------------------------------------------------------------------------------------------------
+// loads and stores
+// ------------------------------------------------------------------------------------------------
+
+struct GradF32 {
+    using T = float;
+    static __device__ __forceinline__ f4 load4(const float* __restrict__ g, int64_t i)
+    {
+        return *reinterpret_cast<const f4*>(g + i);
+    }
+    static __device__ __forceinline__ float load1(const float* __restrict__ g, int64_t i) { return g[i]; }
+};
+
+// bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits.
+struct GradBF16 {
+    using T = uint16_t;
+    static __device__ __forceinline__ f4 load4(const uint16_t* __restrict__ g, int64_t i)
+    {
+        const u2 u = *reinterpret_cast<const u2*>(g + i);
+        f4 r;
+        r.x = __uint_as_float(u.x << 16);
+        r.y = __uint_as_float(u.x & 0xffff0000u);
+        r.z = __uint_as_float(u.y << 16);
+        r.w = __uint_as_float(u.y & 0xffff0000u);
+        return r;
+    }
+    static __device__ __forceinline__ float load1(const uint16_t* __restrict__ g, int64_t i)
+    {
+        return __uint_as_float(static_cast<uint32_t>(g[i]) << 16);
+    }
+};
+
+__device__ __forceinline__ f4 ld4(const float* __restrict__ p, int64_t i)
+{
+    return *reinterpret_cast<const f4*>(p + i);
+}
+
+__device__ __forceinline__ void st4(float* __restrict__ p, int64_t i, f4 v)
+{
+    *reinterpret_cast<f4*>(p + i) = v;
+}
+
+// ------------------------------------------------------------------------------------------------
+// reductions and bit packing
+// ------------------------------------------------------------------------------------------------
+
+// Butterfly over the 64 lanes: each step adds two equal-content partial sums, so every lane ends
+// with the same bits.
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sum over the block in a fixed order; every thread returns the same value.
+__device__ __forceinline__ double block_sum(double v, double* lds)
+{
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double s = lds[0];
+#pragma unroll
+    for (int w = 1; w < kBlock / 64; ++w) s += lds[w];
+    return s;
+}
+
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* lds)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t s = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) s += lds[w];
+    return s;
+}
+
+// OR of a value across each group of 8 consecutive lanes, via DPP:
+// quad_perm[1,0,3,2], quad_perm[2,3,0,1], then row_half_mirror (lane j <-> 7-j in each 8-lane half
+// row).  After the call every lane of the group holds the group's OR.  Must run with all lanes active.
+__device__ __forceinline__ uint32_t or8(uint32_t v)
+{
+    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false));
+    return v;
+}
+
+// Lane tid holds the 4 sign bits of elements i..i+3 (i = tile start + 4*tid, tile start a multiple of
+// 32).  Lanes 8k..8k+7 together hold the 32 bits of one word; lane 8k writes it if `valid`.
+__device__ __forceinline__ void store_word(uint32_t* __restrict__ words, int64_t i, uint32_t nib, bool valid)
+{
+    const uint32_t w = or8(nib << (4 * (threadIdx.x & 7)));
+    if ((threadIdx.x & 7) == 0 && valid) words[i >> 5] = w;
+}
+
+__device__ __forceinline__ uint32_t signs4(uint32_t nib)
+{
+    // byte k = +1 (0x01) or -1 (0xFF) by bit k
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r |= ((nib >> k) & 1u ? 0x01u : 0xFFu) << (8 * k);
+    return r;
+}
+
+// ------------------------------------------------------------------------------------------------
+// element rules
+// ------------------------------------------------------------------------------------------------
+
+// compensated = clip(g) + err ([P2] 1-bit Adam; clip of [P1] sec. 3.2).  NaN passes the clip.
+template <bool CLIP>
+__device__ __forceinline__ float compensate(float g, float e, float clip)
+{
+    if (CLIP) g = g > clip ? clip : (g < -clip ? -clip : g);
+    return g + e;
+}
+
+// One element of the compressed step; returns the sign bit (1 <=> +1).
+// x, g_hat and delta are single fp32 operations; the error (EMA), m and p lines are evaluated in
+// double and rounded once, so a large update that nearly cancels p keeps full fp32 accuracy.
+template <bool EMA>
+__device__ __forceinline__ uint32_t compress_elem(float x, float& e, float& mm, float vv, float& pp,
+                                                  float scale, const CompressParams& cp)
+{
+    const bool b = x >= 0.0f;
+    const float gh = b ? scale : -scale;              // g_hat = dequantize(q)
+    const float delta = x - gh;                       // compensated - g_hat
+    if (EMA)
+        e = static_cast<float>(cp.ef_beta * static_cast<double>(e) + cp.one_m_ef_beta * static_cast<double>(delta));
+    else
+        e = delta;
+    // m on g_hat ([P1] sec. 2.2; [P2]), then the frozen-v update with the stored (new) m ([P2])
+    mm = static_cast<float>(cp.beta1 * static_cast<double>(mm) + cp.one_m_beta1 * static_cast<double>(gh));
+    const double den = sqrt(static_cast<double>(vv)) + cp.eps;
+    pp = static_cast<float>(static_cast<double>(pp) - cp.lr * (static_cast<double>(mm) / den));
+    return b ? 1u : 0u;
+}
+
+// Chunk scale from the chunk's block partials, reduced in a fixed order.
+__device__ __forceinline__ float chunk_scale(const PlanDev& pd, int c, double* lds)
+{
+    const int f0 = pd.chunk_first[c], f1 = pd.chunk_first[c + 1];
+    double s = 0.0;
+    for (int i = f0 + static_cast<int>(threadIdx.x); i < f1; i += kBlock) s += pd.partials[i];
+    s = block_sum(s, lds);
+    const int64_t nc = pd.chunk_off[c + 1] - pd.chunk_off[c];
+    return static_cast<float>(sqrt(s / static_cast<double>(nc)));
+}
+
+// ------------------------------------------------------------------------------------------------
+// compressed step, pass 1: per-block sum of squares of x = clip(g) + err
+// ------------------------------------------------------------------------------------------------
+
+template <class G, bool CLIP>
+__global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typename G::T* __restrict__ g,
+                                                        const float* __restrict__ err, float clip)
+{
+    __shared__ double lds[kBlock / 64];
+    const Item it = pd.items[blockIdx.x];
+    const int tid = threadIdx.x;
+    double acc = 0.0;
+    constexpr int U = 4;
+    int base = 0;
+    for (; base + U * kTile <= it.len; base += U * kTile) {
+        f4 gv[U], ev[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            gv[u] = G::load4(g, i);
+            ev[u] = ld4(err, i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                const double x = compensate<CLIP>(gv[u][k], ev[u][k], clip);
+                acc = fma(x, x, acc);
+            }
+        }
+    }
+    for (; base < it.len; base += kTile) {
+        const int cnt = it.len - base - kVec * tid;
+        const int64_t i = it.start + base + kVec * tid;
+        if (cnt >= kVec) {
+            const f4 gv = G::load4(g, i), ev = ld4(err, i);
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                const double x = compensate<CLIP>(gv[k], ev[k], clip);
+                acc = fma(x, x, acc);
+            }
+        } else {
+            for (int k = 0; k < cnt; ++k) {
+                const double x = compensate<CLIP>(G::load1(g, i + k), err[i + k], clip);
+                acc = fma(x, x, acc);
+            }
+        }
+    }
+    const double s = block_sum(acc, lds);
+    if (tid == 0) pd.partials[blockIdx.x] = s;
+}
+
+// ------------------------------------------------------------------------------------------------
+// compressed step, pass 2: scale, sign bits, error, m, p in one streaming pass
+// ------------------------------------------------------------------------------------------------
+
+template <class G, bool CLIP, bool EMA, bool SIGNS, bool NONFIN>
+__global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename G::T* __restrict__ g,
+                                                     float* __restrict__ err, float* __restrict__ m,
+                                                     const float* __restrict__ v, float* __restrict__ p,
+                                                     uint32_t* __restrict__ words, float* __restrict__ scales,
+                                                     int8_t* __restrict__ signs,
+                                                     unsigned long long* __restrict__ nonfinite,
+                                                     CompressParams cp)
+{
+    __shared__ double lds[kBlock / 64];
+    const Item it = pd.items[blockIdx.x];
+    const int tid = threadIdx.x;
+    const float scale = chunk_scale(pd, it.chunk, lds);
+    if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
+
+    uint32_t nf = 0;
+    constexpr int U = 2;
+    int base = 0;
+    for (; base + U * kTile <= it.len; base += U * kTile) {
+        f4 gv[U], ev[U], mv[U], vv[U], pv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            gv[u] = G::load4(g, i);
+            ev[u] = ld4(err, i);
+            mv[u] = ld4(m, i);
+            vv[u] = ld4(v, i);
+            pv[u] = ld4(p, i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            uint32_t nib = 0;
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                const float x = compensate<CLIP>(gv[u][k], ev[u][k], cp.clip);
+                float e = ev[u][k], mm = mv[u][k], pp = pv[u][k];
+                nib |= compress_elem<EMA>(x, e, mm, vv[u][k], pp, scale, cp) << k;
+                ev[u][k] = e;
+                mv[u][k] = mm;
+                pv[u][k] = pp;
+                if (NONFIN) nf += __builtin_isfinite(e) ? 0u : 1u;
+            }
+            st4(err, i, ev[u]);
+            st4(m, i, mv[u]);
+            st4(p, i, pv[u]);
+            if (SIGNS) *reinterpret_cast<uint32_t*>(signs + i) = signs4(nib);
+            store_word(words, i, nib, true);
+        }
+    }
+    for (; base < it.len; base += kTile) {
+        const int rem = it.len - base;
+        const int cnt = rem - kVec * tid;
+        const int64_t i = it.start + base + kVec * tid;
+        uint32_t nib = 0;
+        if (cnt >= kVec) {
+            const f4 gv = G::load4(g, i), vv = ld4(v, i);
+            f4 ev = ld4(err, i), mv = ld4(m, i), pv = ld4(p, i);
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                const float x = compensate<CLIP>(gv[k], ev[k], cp.clip);
+                float e = ev[k], mm = mv[k], pp = pv[k];
+                nib |= compress_elem<EMA>(x, e, mm, vv[k], pp, scale, cp) << k;
+                ev[k] = e;
+                mv[k] = mm;
+                pv[k] = pp;
+                if (NONFIN) nf += __builtin_isfinite(e) ? 0u : 1u;
+            }
+            st4(err, i, ev);
+            st4(m, i, mv);
+            st4(p, i, pv);
+            if (SIGNS) *reinterpret_cast<uint32_t*>(signs + i) = signs4(nib);
+        } else if (cnt > 0) {
+            for (int k = 0; k < cnt; ++k) {
+                const float x = compensate<CLIP>(G::load1(g, i + k), err[i + k], cp.clip);
+                float e = err[i + k], mm = m[i + k], pp = p[i + k];
+                const uint32_t b = compress_elem<EMA>(x, e, mm, v[i + k], pp, scale, cp);
+                nib |= b << k;
+                err[i + k] = e;
+                m[i + k] = mm;
+                p[i + k] = pp;
+                if (SIGNS) signs[i + k] = b ? int8_t(1) : int8_t(-1);
+                if (NONFIN) nf += __builtin_isfinite(e) ? 0u : 1u;
+            }
+        }
+        store_word(words, i, nib, 32 * (tid >> 3) < rem);
+    }
+    if (NONFIN) {
+        __shared__ uint32_t ldsu[kBlock / 64];
+        const uint32_t t = block_sum_u32(nf, ldsu);
+        if (tid == 0 && t) atomicAdd(nonfinite, static_cast<unsigned long long>(t));
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// dense Adam step ([P2] baseline section; warmup / 0-1 Adam refresh)
+// ------------------------------------------------------------------------------------------------
+
+// Each line in double from fp32 operands, rounded once when stored; p uses the stored m and v.
+template <bool BC>
+__device__ __forceinline__ void dense_elem(float g, float& mm, float& vv, float& pp, const DenseParams& dp)
+{
+    const double gd = static_cast<double>(g);
+    mm = static_cast<float>(dp.beta1 * static_cast<double>(mm) + dp.one_m_beta1 * gd);
+    vv = static_cast<float>(dp.beta2 * static_cast<double>(vv) + dp.one_m_beta2 * (gd * gd));
+    double mh = static_cast<double>(mm), vh = static_cast<double>(vv);
+    if (BC) {
+        mh = mh / dp.bc1;
+        vh = vh / dp.bc2;
+    }
+    pp = static_cast<float>(static_cast<double>(pp) - dp.lr * (mh / (sqrt(vh) + dp.eps)));
+}
+
+template <class G, bool BC>
+__global__ __launch_bounds__(kBlock) void k_dense(PlanDev pd, const typename G::T* __restrict__ g,
+                                                  float* __restrict__ m, float* __restrict__ v,
+                                                  float* __restrict__ p, DenseParams dp)
+{
+    const Item it = pd.items[blockIdx.x];
+    const int tid = threadIdx.x;
+    constexpr int U = 2;
+    int base = 0;
+    for (; base + U * kTile <= it.len; base += U * kTile) {
+        f4 gv[U], mv[U], vv[U], pv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            gv[u] = G::load4(g, i);
+            mv[u] = ld4(m, i);
+            vv[u] = ld4(v, i);
+            pv[u] = ld4(p, i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                float mm = mv[u][k], vq = vv[u][k], pp = pv[u][k];
+                dense_elem<BC>(gv[u][k], mm, vq, pp, dp);
+                mv[u][k] = mm;
+                vv[u][k] = vq;
+                pv[u][k] = pp;
+            }
+            st4(m, i, mv[u]);
+            st4(v, i, vv[u]);
+            st4(p, i, pv[u]);
+        }
+    }
+    for (; base < it.len; base += kTile) {
+        const int cnt = it.len - base - kVec * tid;
+        const int64_t i = it.start + base + kVec * tid;
+        if (cnt >= kVec) {
+            const f4 gv = G::load4(g, i);
+            f4 mv = ld4(m, i), vv = ld4(v, i), pv = ld4(p, i);
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                float mm = mv[k], vq = vv[k], pp = pv[k];
+                dense_elem<BC>(gv[k], mm, vq, pp, dp);
+                mv[k] = mm;
+                vv[k] = vq;
+                pv[k] = pp;
+            }
+            st4(m, i, mv);
+            st4(v, i, vv);
+            st4(p, i, pv);
+        } else {
+            for (int k = 0; k < cnt; ++k) {
+                float mm = m[i + k], vq = v[i + k], pp = p[i + k];
+                dense_elem<BC>(G::load1(g, i + k), mm, vq, pp, dp);
+                m[i + k] = mm;
+                v[i + k] = vq;
+                p[i + k] = pp;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// server half of compressed_allreduce ([P2] 1-bit Adam)
+// ------------------------------------------------------------------------------------------------
+
+// Averages of the 4 elements i..i+3 (one nibble of one word) over W workers: exact double sum of
+// +-s in ascending worker order, one division by W, one rounding to fp32.
+__device__ __forceinline__ f4 server_avg4(int W, const uint32_t* __restrict__ ww, int64_t nw,
+                                          const float* __restrict__ ws, int K, int c, int64_t i)
+{
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    const int64_t wi = i >> 5;
+    const int sh = static_cast<int>(i & 31);
+    for (int w = 0; w < W; ++w) {
+        const uint32_t bits = ww[static_cast<int64_t>(w) * nw + wi] >> sh;
+        const double s = static_cast<double>(ws[static_cast<int64_t>(w) * K + c]);
+        a0 += (bits & 1u) ? s : -s;
+        a1 += (bits & 2u) ? s : -s;
+        a2 += (bits & 4u) ? s : -s;
+        a3 += (bits & 8u) ? s : -s;
+    }
+    const double dw = static_cast<double>(W);
+    f4 r;
+    r.x = static_cast<float>(a0 / dw);
+    r.y = static_cast<float>(a1 / dw);
+    r.z = static_cast<float>(a2 / dw);
+    r.w = static_cast<float>(a3 / dw);
+    return r;
+}
+
+template <bool APPLY>
+__global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint32_t* __restrict__ ww,
+                                                   int64_t nw, const float* __restrict__ ws,
+                                                   float* __restrict__ e, uint32_t* __restrict__ words,
+                                                   float* __restrict__ scales)
+{
+    __shared__ double lds[kBlock / 64];
+    const Item it = pd.items[blockIdx.x];
+    const int tid = threadIdx.x;
+    const int c = it.chunk;
+    float scale = 0.0f;
+    if (APPLY) {
+        scale = chunk_scale(pd, c, lds);
+        if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[c]) scales[c] = scale;
+    }
+    double acc = 0.0;
+    for (int base = 0; base < it.len; base += kTile) {
+        const int rem = it.len - base;
+        const int cnt = rem - kVec * tid;
+        const int64_t i = it.start + base + kVec * tid;
+        uint32_t nib = 0;
+        if (cnt > 0) {
+            const f4 avg = server_avg4(W, ww, nw, ws, pd.K, c, i);
+            if (cnt >= kVec) {
+                f4 ev = ld4(e, i);
+                f4 x;
+#pragma unroll
+                for (int k = 0; k < kVec; ++k) x[k] = avg[k] + ev[k];
+                if (APPLY) {
+#pragma unroll
+                    for (int k = 0; k < kVec; ++k) {
+                        const bool b = x[k] >= 0.0f;
+                        ev[k] = x[k] - (b ? scale : -scale);
+                        nib |= (b ? 1u : 0u) << k;
+                    }
+                    st4(e, i, ev);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < kVec; ++k) acc = fma(static_cast<double>(x[k]), static_cast<double>(x[k]), acc);
+                }
+            } else {
+                for (int k = 0; k < cnt; ++k) {
+                    const float x = avg[k] + e[i + k];
+                    if (APPLY) {
+                        const bool b = x >= 0.0f;
+                        e[i + k] = x - (b ? scale : -scale);
+                        nib |= (b ? 1u : 0u) << k;
+                    } else {
+                        acc = fma(static_cast<double>(x), static_cast<double>(x), acc);
+                    }
+                }
+            }
+        }
+        if (APPLY) store_word(words, i, nib, 32 * (tid >> 3) < rem);
+    }
+    if (!APPLY) {
+        const double s = block_sum(acc, lds);
+        if (tid == 0) pd.partials[blockIdx.x] = s;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// unpack + dequantize, and plain pack
+// ------------------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void k_unpack(const Item* __restrict__ items, int64_t n,
+                                                   const uint32_t* __restrict__ words,
+                                                   const float* __restrict__ scales, float* __restrict__ out)
+{
+    int64_t start;
+    int len;
+    float s = 1.0f;
+    if (items != nullptr) {
+        const Item it = items[blockIdx.x];
+        start = it.start;
+        len = it.len;
+        s = scales[it.chunk];
+    } else {
+        start = static_cast<int64_t>(blockIdx.x) * kPlainItem;
+        len = static_cast<int>(min(static_cast<int64_t>(kPlainItem), n - start));
+    }
+    const int tid = threadIdx.x;
+    for (int base = 0; base < len; base += kTile) {
+        const int cnt = len - base - kVec * tid;
+        const int64_t i = start + base + kVec * tid;
+        if (cnt <= 0) continue;
+        const uint32_t bits = words[i >> 5] >> (i & 31);
+        f4 r;
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) r[k] = ((bits >> k) & 1u) ? s : -s;
+        if (cnt >= kVec) {
+            st4(out, i, r);
+        } else {
+            for (int k = 0; k < cnt; ++k) out[i + k] = r[k];
+        }
+    }
+}
+
+template <class G>
+__global__ __launch_bounds__(kBlock) void k_pack(const typename G::T* __restrict__ x, int64_t n,
+                                                 uint32_t* __restrict__ words)
+{
+    const int64_t start = static_cast<int64_t>(blockIdx.x) * kPlainItem;
+    const int len = static_cast<int>(min(static_cast<int64_t>(kPlainItem), n - start));
+    const int tid = threadIdx.x;
+    for (int base = 0; base < len; base += kTile) {
+        const int rem = len - base;
+        const int cnt = rem - kVec * tid;
+        const int64_t i = start + base + kVec * tid;
+        uint32_t nib = 0;
+        if (cnt >= kVec) {
+            const f4 xv = G::load4(x, i);
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) nib |= (xv[k] >= 0.0f ? 1u : 0u) << k;
+        } else {
+            for (int k = 0; k < cnt; ++k) nib |= (G::load1(x, i + k) >= 0.0f ? 1u : 0u) << k;
+        }
+        store_word(words, i, nib, 32 * (tid >> 3) < rem);
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------------------
+
+hipError_t launch_chunk_sumsq(const PlanDev& pd, const void* g, int g_bf16, const float* err,
+                              float clip, hipStream_t s)
+{
+    const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
+    const bool cl = clip > 0.0f;
+    if (g_bf16) {
+        auto gp = static_cast<const uint16_t*>(g);
+        if (cl)
+            hipLaunchKernelGGL((k_chunk_sumsq<GradBF16, true>), grid, block, 0, s, pd, gp, err, clip);
+        else
+            hipLaunchKernelGGL((k_chunk_sumsq<GradBF16, false>), grid, block, 0, s, pd, gp, err, clip);
+    } else {
+        auto gp = static_cast<const float*>(g);
+        if (cl)
+            hipLaunchKernelGGL((k_chunk_sumsq<GradF32, true>), grid, block, 0, s, pd, gp, err, clip);
+        else
+            hipLaunchKernelGGL((k_chunk_sumsq<GradF32, false>), grid, block, 0, s, pd, gp, err, clip);
+    }
+    return hipGetLastError();
+}
+
+namespace {
+template <class G, bool CLIP, bool EMA>
+void compress_dispatch(const PlanDev& pd, const typename G::T* g, float* err, float* m, const float* v,
+                       float* p, uint32_t* words, float* scales, int8_t* signs,
+                       unsigned long long* nonfinite, const CompressParams& cp, hipStream_t s)
+{
+    const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
+    const int sel = (signs ? 1 : 0) | (nonfinite ? 2 : 0);
+    switch (sel) {
+    case 0:
+        hipLaunchKernelGGL((k_compress<G, CLIP, EMA, false, false>), grid, block, 0, s, pd, g, err, m, v,
+                           p, words, scales, signs, nonfinite, cp);
+        break;
+    case 1:
+        hipLaunchKernelGGL((k_compress<G, CLIP, EMA, true, false>), grid, block, 0, s, pd, g, err, m, v,
+                           p, words, scales, signs, nonfinite, cp);
+        break;
+    case 2:
+        hipLaunchKernelGGL((k_compress<G, CLIP, EMA, false, true>), grid, block, 0, s, pd, g, err, m, v,
+                           p, words, scales, signs, nonfinite, cp);
+        break;
+    default:
+        hipLaunchKernelGGL((k_compress<G, CLIP, EMA, true, true>), grid, block, 0, s, pd, g, err, m, v,
+                           p, words, scales, signs, nonfinite, cp);
+        break;
+    }
+}
+
+template <class G>
+void compress_dispatch_g(const PlanDev& pd, const typename G::T* g, float* err, float* m, const float* v,
+                         float* p, uint32_t* words, float* scales, int8_t* signs,
+                         unsigned long long* nonfinite, int ema, const CompressParams& cp, hipStream_t s)
+{
+    const bool cl = cp.clip > 0.0f;
+    if (cl && ema)
+        compress_dispatch<G, true, true>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
+    else if (cl)
+        compress_dispatch<G, true, false>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
+    else if (ema)
+        compress_dispatch<G, false, true>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
+    else
+        compress_dispatch<G, false, false>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
+}
+}  // namespace
+
+hipError_t launch_compress(const PlanDev& pd, const void* g, int g_bf16, float* err, float* m,
+                           const float* v, float* p, uint32_t* words, float* scales, int8_t* signs,
+                           unsigned long long* nonfinite, int ema, const CompressParams& cp,
+                           hipStream_t s)
+{
+    if (g_bf16)
+        compress_dispatch_g<GradBF16>(pd, static_cast<const uint16_t*>(g), err, m, v, p, words, scales,
+                                      signs, nonfinite, ema, cp, s);
+    else
+        compress_dispatch_g<GradF32>(pd, static_cast<const float*>(g), err, m, v, p, words, scales,
+                                     signs, nonfinite, ema, cp, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense(const PlanDev& pd, const void* g, int g_bf16, float* m, float* v, float* p,
+                        const DenseParams& dp, hipStream_t s)
+{
+    const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
+    if (g_bf16) {
+        auto gp = static_cast<const uint16_t*>(g);
+        if (dp.bias_correction)
+            hipLaunchKernelGGL((k_dense<GradBF16, true>), grid, block, 0, s, pd, gp, m, v, p, dp);
+        else
+            hipLaunchKernelGGL((k_dense<GradBF16, false>), grid, block, 0, s, pd, gp, m, v, p, dp);
+    } else {
+        auto gp = static_cast<const float*>(g);
+        if (dp.bias_correction)
+            hipLaunchKernelGGL((k_dense<GradF32, true>), grid, block, 0, s, pd, gp, m, v, p, dp);
+        else
+            hipLaunchKernelGGL((k_dense<GradF32, false>), grid, block, 0, s, pd, gp, m, v, p, dp);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_server_sumsq(const PlanDev& pd, int W, const uint32_t* ww, const float* ws,
+                               const float* e, hipStream_t s)
+{
+    const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
+    const int64_t nw = (pd.n + 31) / 32;
+    hipLaunchKernelGGL((k_server<false>), grid, block, 0, s, pd, W, ww, nw, ws, const_cast<float*>(e),
+                       static_cast<uint32_t*>(nullptr), static_cast<float*>(nullptr));
+    return hipGetLastError();
+}
+
+hipError_t launch_server_apply(const PlanDev& pd, int W, const uint32_t* ww, const float* ws,
+                               float* e, uint32_t* words, float* scales, hipStream_t s)
+{
+    const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
+    const int64_t nw = (pd.n + 31) / 32;
+    hipLaunchKernelGGL((k_server<true>), grid, block, 0, s, pd, W, ww, nw, ws, e, words, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const PlanDev* pd, const uint32_t* words, int64_t n, const float* scales,
+                         float* out, hipStream_t s)
+{
+    const int64_t blocks = pd ? pd->n_items : (n + kPlainItem - 1) / kPlainItem;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kBlock);
+    hipLaunchKernelGGL(k_unpack, grid, block, 0, s, pd ? pd->items : nullptr, n, words, scales, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const void* x, int x_bf16, int64_t n, uint32_t* words, hipStream_t s)
+{
+    const int64_t blocks = (n + kPlainItem - 1) / kPlainItem;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kBlock);
+    if (x_bf16)
+        hipLaunchKernelGGL((k_pack<GradBF16>), grid, block, 0, s, static_cast<const uint16_t*>(x), n, words);
+    else
+        hipLaunchKernelGGL((k_pack<GradF32>), grid, block, 0, s, static_cast<const float*>(x), n, words);
+    return hipGetLastError();
+}
+
+}  // namespace ob

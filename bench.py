@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Throughput of the 1-bit Adam step on one MI355X.
+
+Default workload: the BERT-base parameter list (197 fp32 tensors, 108,891,648 elements, one scale
+chunk per tensor).  The schedule's dense steps (step < freeze_step) run first and are timed on their
+own; then `--warmup` untimed compressed steps; then `--steps` timed steps.  One JSON line is printed.
+
+Inputs are synthetic and resident in HBM before timing starts: a ring of up to 4 pre-drawn gradients
+(seeded) is cycled, so no random generation runs inside the timed region.
+
+Other modes:
+  --rocprof-summary DIR   summarise rocprofv3 CSV output found under DIR (kernel stats, and
+                          FETCH_SIZE / WRITE_SIZE counters per dispatch) as markdown on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "elements/s and achieved HBM GB/s (% of peak) of fused 1-bit Adam step, 1 GPU"
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "bert-base-110M-fp32"
+KERNEL_SOURCES = ("adam_ob_compress_amd/csrc/ob_kernels.hip", "adam_ob_compress_amd/csrc/ob_internal.h")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def bytes_per_elem(w, kernel: str) -> float:
+    """Algorithmic (compulsory) HBM bytes per element of one launch of `kernel` on workload w."""
+    gb = 2.0 if w.grad_dtype == "bf16" else 4.0
+    if kernel == "compress":          # read g err m v p, write err m p + 1 bit (+ int8 sign)
+        return gb + 16.0 + 12.0 + 0.125 + (1.0 if w.int8_signs else 0.0)
+    if kernel == "chunk_sumsq":       # read g err
+        return gb + 4.0
+    if kernel == "dense":             # read g m v p, write m v p
+        return gb + 12.0 + 12.0
+    if kernel == "server_sumsq":      # read W sign bits and the server error
+        return w.workers / 8.0 + 4.0
+    if kernel == "server_apply":      # read W bits + error, write error + 1 bit
+        return w.workers / 8.0 + 4.0 + 4.0 + 0.125
+    if kernel == "unpack":            # read 1 bit, write fp32
+        return 0.125 + 4.0
+    raise KeyError(kernel)
+
+
+def step_compulsory_bytes(w, kind: str) -> float:
+    """Bytes per element the method must move once per step (the two-pass re-read not counted)."""
+    if kind == "dense":
+        return bytes_per_elem(w, "dense")
+    if w.workers:
+        return w.workers / 8.0 + 4.0 + 4.0 + 0.125 + bytes_per_elem(w, "unpack")
+    return bytes_per_elem(w, "compress")
+
+
+def load_traffic(kernel: str, workload: str):
+    """Counter-derived HBM bytes per launch from profiles/, or None if absent or stale."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("traffic-json:"):
+            rec = json.loads(line.split(":", 1)[1])
+            if rec.get("kernel_src_sha") != kernel_source_sha():
+                return None
+            return rec.get("bytes_per_launch")
+    return None
+
+
+# ------------------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, single thread, on a bounded sample
+# ------------------------------------------------------------------------------------------------
+
+def cpu_baseline(w, seconds: float):
+    import numpy as np
+
+    import oracle
+    from adam_ob_compress_amd import synth
+
+    off = w.chunk_offsets()
+    # whole chunks from the start until ~2^27 elements (all of BERT-base)
+    K = 1
+    while K < w.n_chunks and off[K] < (1 << 27):
+        K += 1
+    n_s = int(off[K])
+    sub = synth.scaled(w, n_s, w.chunk) if w.offsets is None else None
+    if sub is None:
+        import dataclasses
+        sub = dataclasses.replace(w, n=n_s, offsets=tuple(int(o) for o in off[:K + 1]))
+    err, m, v, p = (synth.host(t) for t in synth.draw_state(sub, "cpu"))
+    g = synth.host(synth.draw_grad(sub, 0, "cpu"))
+    offs = sub.chunk_offsets()
+    times = []
+    t_end = time.perf_counter() + seconds
+    while len(times) < 2 or (time.perf_counter() < t_end and len(times) < 20):
+        t0 = time.perf_counter()
+        if w.workers:
+            raise NotImplementedError
+        oracle.compress_step(g, err, m, v, p, offs, lr=w.lr, beta1=w.beta1, eps=w.eps, clip=w.clip,
+                             ef_mode=w.ef_mode, ef_beta=w.ef_beta, want_signs=w.int8_signs)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": n_s / t, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(times)} compressed steps of the oracle on the first {K} chunks "
+                      f"({n_s} elements) of {w.name}, single thread, median step {t:.3f} s"}
+
+
+# ------------------------------------------------------------------------------------------------
+# GPU run
+# ------------------------------------------------------------------------------------------------
+
+def run(args):
+    import torch
+
+    import adam_ob_compress_amd as ob
+    from adam_ob_compress_amd import schedule, synth
+
+    w = synth.WORKLOADS[args.workload]
+    if w.workers:
+        raise SystemExit("bench.py times the optimizer step; the server workload is a parity case")
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    plan = ob.ob_plan_create(w.n, chunk_size=w.chunk if w.offsets is None else 0, chunk_offsets=w.offsets)
+    err, m, v, p = synth.draw_state(w, dev)
+    ring = 1 if w.n > (1 << 31) else min(4, max(1, args.steps))
+    grads = [synth.draw_grad(w, s, dev) for s in range(ring)]
+    opt = schedule.OneBitAdam(plan, err, m, v, p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                              clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta, int8_signs=w.int8_signs,
+                              freeze_step=w.freeze_step, refresh_period=w.refresh_period)
+    stream = torch.cuda.current_stream()
+    print(f"# {w.name}: n={w.n} chunks={plan.num_chunks} blocks={plan.num_blocks} "
+          f"block_elems={plan.block_elems}", file=sys.stderr, flush=True)
+
+    # the schedule's dense steps before freeze_step (timed on their own with events)
+    dense_ms = None
+    if w.freeze_step:
+        ob.ob_plan_set_timing(plan, True)
+        for s in range(w.freeze_step):
+            opt.step(grads[s % ring])
+        torch.cuda.synchronize()
+        ms, cnt = ob.ob_plan_read_timing(plan, ob.OB_KERNEL_DENSE)
+        dense_ms = ms / max(cnt, 1)
+        ob.ob_plan_set_timing(plan, False)
+
+    for k in range(args.warmup):
+        opt.step(grads[k % ring])
+    torch.cuda.synchronize()
+
+    ob.ob_plan_set_timing(plan, True)
+    kinds = {"dense": 0, "compressed": 0}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        kinds[opt.step(grads[k % ring], stream)] += 1
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    kern = {}
+    for kid, name in ob.KERNEL_NAMES.items():
+        ms, cnt = ob.ob_plan_read_timing(plan, kid)
+        if cnt:
+            kern[name] = {"avg_ms": ms / cnt, "launches": cnt,
+                          "GBps": bytes_per_elem(w, name) * w.n / (ms / cnt * 1e-3) / 1e9}
+    ob.ob_plan_set_timing(plan, False)
+
+    if args.copy_probe_mib:
+        nb = args.copy_probe_mib << 20
+        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        ev1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * nb / (ev0.elapsed_time(ev1) / 5 * 1e-3) / 1e9
+        kern["torch_copy_probe"] = {"bytes_per_launch": 2 * nb, "GBps": copy_gbps}
+        del src, dst
+
+    dom = "compress"
+    avg = kern[dom]["avg_ms"]
+    bpe = bytes_per_elem(w, dom)
+    achieved = bpe * w.n / (avg * 1e-3) / 1e9
+    traffic = load_traffic(dom, w.name)
+    value = w.n / (ms_per_step * 1e-3)
+    step_gbps = step_compulsory_bytes(w, "compressed") * w.n / (ms_per_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": ("bf16 grads + f32 state" if w.grad_dtype == "bf16" else "f32"),
+        "data": "synthetic (seeded; ring of pre-drawn gradients)",
+        "config": {"workload": w.name, "elements": w.n, "chunks": plan.num_chunks,
+                   "grad_dtype": w.grad_dtype, "clip": w.clip,
+                   "error_feedback": "ema" if w.ef_mode else "plain", "int8_signs": w.int8_signs,
+                   "freeze_step": w.freeze_step, "refresh_period": w.refresh_period,
+                   "block_elems": plan.block_elems, "work_blocks": plan.num_blocks},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "bytes_per_elem": bpe, "traffic": traffic},
+        "step_compulsory_GBps": step_gbps,
+        "step_hbm_frac": step_gbps / PEAK_HBM_GBPS,
+        "timed_step_kinds": kinds,
+        "dense_step_ms": dense_ms,
+        "kernels": kern,
+        "kernel_src_sha": kernel_source_sha(),
+        "cpu_baseline": None,
+    }
+    return w, res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain torch copy of this many MiB (counter calibration)")
+    ap.add_argument("--rocprof-summary", metavar="DIR")
+    args = ap.parse_args()
+
+    if args.rocprof_summary:
+        print(rocprof_summary(args.rocprof_summary))
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): the "
+              "compressed step is one GPU's share; the multi-GPU exchange is not part of this build.",
+              file=sys.stderr)
+        return 2
+    w, res = run(args)
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+# ------------------------------------------------------------------------------------------------
+# rocprofv3 CSV summaries
+# ------------------------------------------------------------------------------------------------
+
+def _short(name: str) -> str:
+    for key in ("k_chunk_sumsq", "k_compress", "k_dense", "k_server", "k_unpack", "k_pack"):
+        if key in name:
+            tmpl = name.split(key, 1)[1]
+            return key + (tmpl[:60] if tmpl else "")
+    return name[:80]
+
+
+def rocprof_summary(d: str) -> str:
+    out = []
+    stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
+    for f in stats:
+        rows = list(csv.DictReader(open(f)))
+        out.append(f"### kernel stats: {os.path.relpath(f, d)}\n")
+        out.append("| kernel | calls | avg us | min us | max us | total % |")
+        out.append("|---|---|---|---|---|---|")
+        for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+            out.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                       f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                       f"{float(r['Percentage']):.1f} |")
+        out.append("")
+    ctr = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    for f in ctr:
+        agg = {}
+        for r in csv.DictReader(open(f)):
+            key = (_short(r["Kernel_Name"]), r["Counter_Name"])
+            a = agg.setdefault(key, [0.0, set()])
+            a[0] += float(r["Counter_Value"])
+            a[1].add(r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        out.append(f"### counters: {os.path.relpath(f, d)}\n")
+        out.append("| kernel | counter | dispatches | per dispatch (KiB) |")
+        out.append("|---|---|---|---|")
+        for (k, c), (tot, ids) in sorted(agg.items()):
+            out.append(f"| {k} | {c} | {len(ids)} | {tot / max(len(ids), 1):.1f} |")
+        out.append("")
+    return "\n".join(out) if out else f"no rocprofv3 CSV output under {d}"
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,168 @@
+/*
+ * ob_adam.h -- C ABI of the 1-bit Adam step on one AMD MI355X (gfx950).
+ *
+ * The library (libobadam.so) runs every step of the optimizer in hand-written HIP kernels.  All data
+ * pointers are DEVICE pointers owned by the caller; every call is asynchronous on the caller's
+ * `stream` and returns once its kernels are enqueued.  No torch types cross this boundary.
+ *
+ * Pages cited (title and section):
+ *   [P1] "1bit Adam" tutorial (intelliparadigm.com article 2150495): sec. 2.1 quantization and error
+ *        compensation, sec. 2.2 momentum on the compressed gradient, sec. 3.1 per-parameter state,
+ *        sec. 3.2 compress routine (clip, NaN check, int8 signs), sec. 4.2 packing into one buffer.
+ *   [P2] "DeepSpeed Communication Compression and Hiding": section "baseline: why Adam is hard to
+ *        compress" (Adam moments), section "1-bit Adam: warmup, frozen variance, error feedback"
+ *        (the two-phase step and compressed_allreduce), section "0/1 Adam" (variance refresh).
+ *
+ * Definitions used by every call
+ *   - Elements are a flat index 0..n-1 over one contiguous buffer per state array (the parameters
+ *     packed into one block, [P1] sec. 4.2).  n may exceed 2^32.
+ *   - A plan splits 0..n-1 into K chunks; every chunk has its own fp32 scale.  Chunk c spans
+ *     [o_c, o_{c+1}).  Interior chunk boundaries must be multiples of 64.
+ *   - sign(x) = +1 iff x >= 0.0f (so +0 and -0 give +1, NaN gives -1).
+ *   - Packed signs: bit j of uint32 word w is 1 iff sign(x[32w + j]) = +1; ceil(n/32) words; bits
+ *     for indices >= n are 0.  The packing ignores chunk boundaries.
+ *   - scale_c = ||x_c||_2 / sqrt(n_c), with ||x_c||^2 accumulated in double and sqrt(S/n_c) taken in
+ *     double, then rounded to fp32.  g_hat = +scale_c or -scale_c by the sign.
+ *
+ * Alignment: fp32 state and fp32 gradient pointers 16 bytes; bf16 gradient 8 bytes; words, scales
+ * and int8 signs 4 bytes; the non-finite counter 8 bytes.  (torch allocations are 256-byte aligned.)
+ *
+ * Errors: arguments are validated on the host before anything is enqueued, and a failed check
+ * returns a status without touching the GPU: OB_ERR_ARG (null required pointer, bad size, bad chunk
+ * table, W < 1, n differs from the plan), OB_ERR_ALIGN (pointer or chunk-boundary alignment),
+ * OB_ERR_DTYPE (unknown dtype).  A failed launch returns OB_ERR_HIP; faults during execution surface
+ * at the caller's next synchronisation.  OB_ERR_OOM: a plan allocation failed.  n = 0 is a no-op.
+ * No C++ exception crosses the ABI and nothing aborts.  NaN and Inf propagate per IEEE.
+ *
+ * Threads and streams: distinct plans are independent.  A plan holds a small workspace (one double
+ * per work block), so one plan must not be used by two calls that may run concurrently on the GPU;
+ * calls on one stream are ordered and therefore safe.
+ */
+#ifndef OB_ADAM_H
+#define OB_ADAM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    OB_OK = 0,
+    OB_ERR_ARG = 1,
+    OB_ERR_ALIGN = 2,
+    OB_ERR_DTYPE = 3,
+    OB_ERR_HIP = 4,
+    OB_ERR_OOM = 5
+} ob_status;
+
+/* Gradient / packed-input element type. */
+typedef enum { OB_F32 = 0, OB_BF16 = 1 } ob_dtype;
+
+/* Error feedback rule: PLAIN replaces the error with x - g_hat ([P2] 1-bit Adam pseudo-code);
+ * EMA keeps ef_beta*err + (1-ef_beta)*(x - g_hat) ([P1] sec. 2.1). */
+typedef enum { OB_EF_PLAIN = 0, OB_EF_EMA = 1 } ob_ef_mode;
+
+/* Hyperparameters, fp32 as in the per-parameter state of [P1] sec. 3.1. */
+typedef struct {
+    float lr;
+    float beta1;
+    float beta2;            /* dense step only */
+    float eps;
+    float clip;             /* compressed step: clamp g to [-clip, clip] before adding the error
+                               ([P1] sec. 3.2); <= 0 disables; NaN passes through */
+    int32_t ef_mode;        /* ob_ef_mode */
+    float ef_beta;          /* EMA coefficient ([P1] sec. 2.1 uses beta1 = 0.9) */
+    int32_t bias_correction;/* dense step only: divide m, v by 1 - beta^step (textbook Adam);
+                               the pages' step has none, so 0 is the default */
+    int64_t step;           /* dense step with bias_correction: t >= 1 */
+} ob_hparams;
+
+typedef struct ob_plan_s* ob_plan;
+
+/* Create a plan for n elements on the current HIP device.
+ *   chunk_offsets == NULL: uniform chunks of chunk_size elements (the last one ends at n);
+ *                          chunk_size > 0 and, when n > chunk_size, a multiple of 64.
+ *   chunk_offsets != NULL: n_chunks + 1 host int64 offsets, 0 = o_0 < o_1 < ... < o_K = n, interior
+ *                          offsets multiples of 64 (one chunk per parameter tensor).
+ * The plan owns its device tables and workspace (hipMalloc here, hipFree in ob_plan_destroy);
+ * *out is set to NULL on failure. */
+ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_offsets,
+                         int64_t n_chunks, ob_plan* out);
+ob_status ob_plan_destroy(ob_plan plan);
+int64_t ob_plan_num_elements(ob_plan plan);   /* -1 for a NULL plan */
+int64_t ob_plan_num_chunks(ob_plan plan);     /* -1 for a NULL plan */
+int64_t ob_plan_num_blocks(ob_plan plan);     /* work blocks = grid size of the per-element kernels */
+int64_t ob_plan_block_elems(ob_plan plan);    /* elements per work block (except chunk tails) */
+
+/* Dense Adam step ([P2] baseline section; the step used before freeze_step in [P2] 1-bit Adam and for
+ * the variance refresh of [P2] 0/1 Adam):
+ *   m = beta1*m + (1-beta1)*g;  v = beta2*v + (1-beta2)*g^2;
+ *   p -= lr * mh / (sqrt(vh) + eps)   with mh = m, vh = v, or m/(1-beta1^t), v/(1-beta2^t) when
+ *   hp->bias_correction.  The error buffer is not touched.
+ * g: n elements of `g_dtype` (read only); m, v, p: fp32[n], updated in place. */
+ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* m, float* v,
+                              float* p, const ob_hparams* hp, hipStream_t stream);
+
+/* Compressed step ([P2] 1-bit Adam, compressed branch with W = 1; [P1] sec. 2.1-2.2, 3.2):
+ *   g' = clip(widen(g));  x = g' + err (fp32);  words = pack(sign(x));  scales_c per chunk;
+ *   g_hat = +-scale_c;  err = x - g_hat (PLAIN) or ef_beta*err + (1-ef_beta)*(x - g_hat) (EMA);
+ *   m = beta1*m + (1-beta1)*g_hat;  p -= lr * m / (sqrt(v) + eps)  (v frozen, read only).
+ * Runs two kernels: a per-chunk sum of squares, then one fused streaming pass.
+ * g: n elements (read only); err, m, p: fp32[n] in place; v: fp32[n] read only;
+ * words_out: uint32[ceil(n/32)]; scales_out: fp32[K];
+ * signs_out (optional, NULL = off): int8[n] of +1/-1 ([P1] sec. 3.2);
+ * nonfinite_out (optional, NULL = off): device uint64 counter to which the number of non-finite new
+ * error elements is added ([P1] sec. 3.2 NaN check; the caller zeroes it).
+ * Outputs must not alias inputs. */
+ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* err, float* m,
+                                const float* v, float* p, uint32_t* words_out, float* scales_out,
+                                int8_t* signs_out, uint64_t* nonfinite_out, const ob_hparams* hp,
+                                hipStream_t stream);
+
+/* Server half of compressed_allreduce ([P2] 1-bit Adam) on this GPU's share of n elements:
+ *   avg_i = (sum_{w<W} (bit_w(i) ? s_{w,c} : -s_{w,c})) / W, summed in double in ascending w and
+ *           rounded once to fp32;
+ *   x = avg + server_err;  words_out = pack(sign(x));  scales_out per chunk of x;
+ *   server_err = x - g_hat (plain error feedback kept by the server).
+ * worker_words: W rows of ceil(n/32) uint32 (row w starts at w*ceil(n/32)); pad bits are ignored;
+ * worker_scales: W rows of K fp32; server_err: fp32[n] in place; words_out: uint32[ceil(n/32)];
+ * scales_out: fp32[K].  1 <= W <= 1024. */
+ob_status ob_server_reduce(ob_plan plan, int32_t W, const uint32_t* worker_words,
+                           const float* worker_scales, float* server_err, uint32_t* words_out,
+                           float* scales_out, hipStream_t stream);
+
+/* Pack signs of x (fp32 or bf16, n elements) into ceil(n/32) words ([P2] one_bit_quantize, sign part). */
+ob_status ob_pack(const void* x, ob_dtype x_dtype, int64_t n, uint32_t* words_out, hipStream_t stream);
+
+/* Unpack + dequantize ([P2] dequantize): out_i = bit(i) ? s_c : -s_c, s_c = scales[c] for the plan's
+ * chunk c of i; with scales == NULL, s = 1 and plan may be NULL.  With scales, plan is required and n
+ * must equal the plan's n.  out: fp32[n]. */
+ob_status ob_unpack(ob_plan plan, const uint32_t* words, int64_t n, const float* scales, float* out,
+                    hipStream_t stream);
+
+const char* ob_status_str(ob_status s);
+
+/* ---- kernel timing (measurement support) ----
+ * With timing on, every call made with this plan records a hipEvent pair around each kernel it
+ * launches, on the call's stream.  ob_plan_read_timing waits for the recorded events and returns the
+ * summed milliseconds and launch count of one kernel kind since timing was switched on. */
+typedef enum {
+    OB_KERNEL_CHUNK_SUMSQ = 0,     /* compressed step, pass 1 */
+    OB_KERNEL_COMPRESS = 1,        /* compressed step, pass 2 (fused streaming pass) */
+    OB_KERNEL_DENSE = 2,           /* dense Adam step */
+    OB_KERNEL_SERVER_SUMSQ = 3,    /* server reduce, pass 1 */
+    OB_KERNEL_SERVER_APPLY = 4,    /* server reduce, pass 2 */
+    OB_KERNEL_UNPACK = 5,
+    OB_KERNEL_COUNT = 6
+} ob_kernel;
+
+ob_status ob_plan_set_timing(ob_plan plan, int32_t enable);
+ob_status ob_plan_read_timing(ob_plan plan, int32_t kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OB_ADAM_H */

@@ -1,0 +1,186 @@
+"""Parity harness: the HIP path against the CPU oracle, per step, from identical input state.
+
+Each step: the oracle's own state for the checked chunks is written into the GPU buffers, the GPU
+step runs over the whole buffer (the launch configuration the bench times), the oracle runs the same
+step on host copies of the checked chunks, and the outputs of those chunks are compared.  The oracle
+never receives anything the HIP path computed: its inputs come from the seeded generators
+(adam_ob_compress_amd.synth) and from its own previous steps.
+
+Every chunk's outputs depend only on that chunk (pinned on the CPU by
+tests/test_oracle.py::test_chunks_are_independent), so checking a subset of chunks is exact for them,
+and the oracle may run on different chunks in parallel threads (ctypes releases the GIL).
+
+Tolerances:
+  * packed words and int8 signs: bit-exact;
+  * scales: equal, or 1 ulp apart (the double sum of squares is reduced in a different order);
+    mismatches are counted and returned;
+  * fp32 state: |gpu - ref| <= 2e-6*|ref| + 1e-9 (+ the exact propagation of a scale difference:
+    err moves by |dscale| (EMA: (1-ef_beta)|dscale|), m by (1-beta1)|dscale|, p by
+    lr*(1-beta1)|dscale|/(sqrt(v)+eps)); NaN must match NaN and +-Inf must match exactly.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+
+import numpy as np
+import torch
+
+import oracle
+from adam_ob_compress_amd import schedule, synth
+import adam_ob_compress_amd as ob
+
+REL, ABS = 2e-6, 1e-9
+_POOL = cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+
+
+def ulp_diff(a, b):
+    ai = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    bi = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    # map sign-magnitude to a monotone integer line
+    ai = np.where(ai < 0, -(ai & 0x7FFFFFFF), ai)
+    bi = np.where(bi < 0, -(bi & 0x7FFFFFFF), bi)
+    return np.abs(ai - bi)
+
+
+def assert_f32_close(gpu, ref, what, slack=0.0):
+    gpu = np.asarray(gpu, np.float32)
+    ref = np.asarray(ref, np.float32)
+    assert gpu.shape == ref.shape, what
+    gn, rn = np.isnan(gpu), np.isnan(ref)
+    assert np.array_equal(gn, rn), f"{what}: NaN positions differ ({int(np.sum(gn != rn))})"
+    gi, ri = np.isinf(gpu), np.isinf(ref)
+    assert np.array_equal(gi, ri) and np.array_equal(gpu[gi], ref[ri]), f"{what}: Inf differ"
+    fin = ~(rn | ri)
+    g64 = gpu[fin].astype(np.float64)
+    r64 = ref[fin].astype(np.float64)
+    tol = REL * np.abs(r64) + ABS
+    if not np.isscalar(slack):
+        slack = np.asarray(slack, np.float64)[fin]
+    tol = tol + slack
+    bad = np.abs(g64 - r64) > tol
+    if np.any(bad):
+        k = int(np.argmax(np.abs(g64 - r64) - tol))
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; worst gpu="
+                             f"{g64[k]!r} ref={r64[k]!r} tol={tol[k]!r}")
+
+
+class ChunkRef:
+    """The oracle's state for one chunk [a, b)."""
+
+    def __init__(self, c, a, b, err, m, v, p):
+        self.c, self.a, self.b = c, a, b
+        self.err, self.m, self.v, self.p = err, m, v, p
+        self.out = None
+
+
+def host_chunks(w, chunks, err, m, v, p):
+    off = w.chunk_offsets()
+    refs = []
+    for c in chunks:
+        a, b = int(off[c]), int(off[c + 1])
+        refs.append(ChunkRef(c, a, b, *(synth.host(t[a:b]) for t in (err, m, v, p))))
+    return refs
+
+
+def upload(refs, err, m, v, p):
+    """Write the oracle's chunk state into the GPU buffers (identical input state)."""
+    for r in refs:
+        for dst, src in ((err, r.err), (m, r.m), (v, r.v), (p, r.p)):
+            dst[r.a:r.b].copy_(torch.from_numpy(src), non_blocking=False)
+
+
+def _oracle_compress(r, g, w):
+    words, scales, signs, nf = oracle.compress_step(
+        g, r.err, r.m, r.v, r.p, np.asarray([0, r.b - r.a], np.int64), lr=w.lr, beta1=w.beta1,
+        eps=w.eps, clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta, want_signs=w.int8_signs,
+        count_nonfinite=True)
+    r.out = dict(words=words, scale=scales[0], signs=signs, nf=nf)
+
+
+def _oracle_dense(r, g, w, bias_correction, t):
+    oracle.warmup_step(g, r.m, r.v, r.p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                       bias_correction=bias_correction, step=t)
+    r.out = {}
+
+
+def oracle_step(refs, g_dev, w, kind, bias_correction=False, t=0):
+    gs = [synth.host(g_dev[r.a:r.b]) for r in refs]
+    if kind == "compressed":
+        futs = [_POOL.submit(_oracle_compress, r, g, w) for r, g in zip(refs, gs)]
+    else:
+        futs = [_POOL.submit(_oracle_dense, r, g, w, bias_correction, t) for r, g in zip(refs, gs)]
+    for f in futs:
+        f.result()
+
+
+def compare_chunks(refs, w, kind, err, m, v, p, words=None, scales=None, signs=None):
+    """Compare the GPU buffers on the checked chunks with the oracle; returns scale-ulp mismatches."""
+    mism = 0
+    b1 = np.float64(np.float32(w.beta1))
+    eb = np.float64(np.float32(w.ef_beta))
+    lr = np.float64(np.float32(w.lr))
+    eps = np.float64(np.float32(w.eps))
+    for r in refs:
+        tag = f"{w.name} chunk {r.c} [{r.a},{r.b}) {kind}"
+        ge, gm, gv, gp = (synth.host(t[r.a:r.b]) for t in (err, m, v, p))
+        ds = 0.0
+        if kind == "compressed":
+            ws = synth.host(words[r.a // 32:(r.b + 31) // 32])
+            assert np.array_equal(ws, r.out["words"]), f"{tag}: packed words differ"
+            sc = np.float32(scales[r.c].item())
+            d = int(ulp_diff(sc, r.out["scale"]))
+            assert d <= 1 or (np.isnan(sc) and np.isnan(r.out["scale"])), \
+                f"{tag}: scale {sc!r} vs {r.out['scale']!r} ({d} ulp)"
+            if d == 1:
+                mism += 1
+                ds = abs(float(sc) - float(r.out["scale"]))
+            if signs is not None:
+                assert np.array_equal(synth.host(signs[r.a:r.b]), r.out["signs"]), f"{tag}: int8 signs differ"
+            assert np.array_equal(gv, r.v), f"{tag}: v changed in the compressed step"
+        else:
+            assert_f32_close(gv, r.v, f"{tag}: v")
+        err_slack = ds * ((1 - eb) if w.ef_mode == 1 else 1.0)
+        m_slack = ds * (1 - b1)
+        p_slack = lr * m_slack / (np.sqrt(r.v.astype(np.float64)) + eps) if ds else 0.0
+        assert_f32_close(ge, r.err, f"{tag}: err", err_slack)
+        assert_f32_close(gm, r.m, f"{tag}: m", m_slack)
+        assert_f32_close(gp, r.p, f"{tag}: p", p_slack)
+    return mism
+
+
+def run_workload(w, chunks=None, steps=None, device="cuda:0", log=print):
+    """Run w's schedule on the GPU and check the given chunks (all if None) every step.
+
+    Returns a dict of counts (steps by kind, scale mismatches)."""
+    K = w.n_chunks
+    chunks = list(range(K)) if chunks is None else sorted(set(chunks))
+    steps = w.steps if steps is None else steps
+    plan = ob.ob_plan_create(w.n, chunk_size=w.chunk if w.offsets is None else 0,
+                             chunk_offsets=w.offsets)
+    err, m, v, p = synth.draw_state(w, device)
+    opt = schedule.OneBitAdam(plan, err, m, v, p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                              clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta,
+                              int8_signs=w.int8_signs, count_nonfinite=True,
+                              freeze_step=w.freeze_step, refresh_period=w.refresh_period)
+    refs = host_chunks(w, chunks, err, m, v, p)
+    g = None
+    counts = {"dense": 0, "compressed": 0, "scale_ulp_mismatch": 0}
+    nf_ref = 0
+    for s in range(steps):
+        g = synth.draw_grad(w, s, device, out=g)
+        upload(refs, err, m, v, p)
+        torch.cuda.synchronize()
+        kind = opt.step(g)
+        torch.cuda.synchronize()
+        oracle_step(refs, g, w, kind, t=opt.dense_steps)
+        counts[kind] += 1
+        counts["scale_ulp_mismatch"] += compare_chunks(refs, w, kind, err, m, v, p, opt.words,
+                                                       opt.scales, opt.signs)
+        if kind == "compressed":
+            nf_ref += sum(r.out["nf"] for r in refs)
+        log(f"{w.name} step {s} {kind}: {len(refs)} chunks match")
+    if len(chunks) == K:
+        assert int(opt.nonfinite.item()) == nf_ref
+    del plan
+    return counts

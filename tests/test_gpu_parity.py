@@ -1,0 +1,371 @@
+"""GPU parity: every entry point of libobadam.so against the CPU oracle (marked gpu).
+
+Sizes: brute force over n = 1..130; several tiles and work blocks with ragged tails; and the five
+workloads at full size in the launch configuration the bench uses (checked chunks listed per test).
+Inputs come only from adam_ob_compress_amd.synth; nothing the HIP path computes is fed to the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import adam_ob_compress_amd as ob
+from adam_ob_compress_amd import synth
+
+import _parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    ob.lib()  # raises if the HIP library was not built
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    _require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _t(a, dtype=None):
+    """Host numpy -> device tensor (bf16 from uint16 bits, uint32 into int32 storage)."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).to(DEV).view(torch.bfloat16)
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32).copy()).to(DEV)
+    return torch.from_numpy(a.copy()).to(DEV)
+
+
+def _bf16_bits(x):
+    """Round fp32 to bf16 (nearest even) and return the uint16 bit patterns (NaN kept quiet)."""
+    return synth.host(torch.from_numpy(x).to(torch.bfloat16))
+
+
+# ------------------------------------------------------------------------------------------------
+# pack / unpack
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("pattern", ["normal", "signed_zeros", "denormals", "special", "alternating"])
+def test_pack_bruteforce(pattern):
+    for n in list(range(1, 131)) + [1023, 1024, 1025, 16384 + 4, 100003]:
+        x = synth.draw_values(n, 17, pattern)
+        for arr in (x, _bf16_bits(x)):
+            words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+            ob.ob_pack(_t(arr), words)
+            assert np.array_equal(synth.host(words), oracle.pack(arr)), (pattern, n, arr.dtype)
+
+
+def test_unpack_with_and_without_scales():
+    for n, chunk in ((1, 64), (33, 64), (130, 64), (5000, 1024), (100003, 4096)):
+        x = synth.draw_values(n, 23, "special")
+        words_np = oracle.pack(x)
+        off = oracle.uniform_offsets(n, chunk)
+        sc = synth.draw_values(off.size - 1, 29, "normal") * np.float32(7)
+        plan = ob.ob_plan_create(n, chunk_size=chunk)
+        out = torch.empty(n, dtype=torch.float32, device=DEV)
+        ob.ob_unpack(plan, _t(words_np), n, out, scales=_t(sc))
+        assert np.array_equal(synth.host(out), oracle.unpack(words_np, n, off, sc))
+        ob.ob_unpack(None, _t(words_np), n, out)
+        assert np.array_equal(synth.host(out), oracle.unpack(words_np, n))
+
+
+# ------------------------------------------------------------------------------------------------
+# compressed / dense step: brute force on tiny and multi-tile inputs
+# ------------------------------------------------------------------------------------------------
+
+VARIANTS = {
+    "fp32_plain": dict(gdt="f32", clip=0.0, ef_mode=0, signs=False),
+    "bf16_ema_clip_int8": dict(gdt="bf16", clip=5.0, ef_mode=1, signs=True),
+    "fp32_ema": dict(gdt="f32", clip=0.0, ef_mode=1, signs=True),
+    "bf16_plain": dict(gdt="bf16", clip=0.0, ef_mode=0, signs=False),
+}
+
+
+def _small_state(n, seed, wide=False):
+    rng = np.random.default_rng([seed, n])
+    s = 20.0 if wide else 1e-3
+    g = (rng.standard_normal(n) * s).astype(np.float32)
+    err = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (np.abs(rng.standard_normal(n)) * 1e-6 + 1e-8).astype(np.float32)
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    return g, err, m, v, p
+
+
+def _gpu_vs_oracle_compress(n, chunk, var, seed, g=None, state=None, steps=1, lr=1e-4):
+    gnp, err, m, v, p = _small_state(n, seed, wide=var["clip"] > 0)
+    if g is not None:
+        gnp = g
+    if state is not None:
+        err, m, v, p = state
+    if var["gdt"] == "bf16":
+        gnp = _bf16_bits(gnp)
+    off = oracle.uniform_offsets(n, chunk)
+    plan = ob.ob_plan_create(n, chunk_size=chunk)
+    hp = ob.hparams(lr=lr, beta1=0.9, eps=1e-8, clip=var["clip"], ef_mode=var["ef_mode"], ef_beta=0.9)
+    for _ in range(steps):
+        d = [_t(a) for a in (gnp, err, m, v, p)]
+        words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+        scales = torch.zeros(off.size - 1, dtype=torch.float32, device=DEV)
+        signs = torch.zeros(n, dtype=torch.int8, device=DEV) if var["signs"] else None
+        nf = torch.zeros(1, dtype=torch.int64, device=DEV)
+        ob.ob_adam_compress_step(plan, d[0], d[1], d[2], d[3], d[4], words, scales, hp, signs, nf)
+        rw, rs, rsg, rnf = oracle.compress_step(gnp, err, m, v, p, off, lr=lr, beta1=0.9, eps=1e-8,
+                                                clip=var["clip"], ef_mode=var["ef_mode"], ef_beta=0.9,
+                                                want_signs=var["signs"], count_nonfinite=True)
+        tag = f"n={n} chunk={chunk} {var}"
+        assert np.array_equal(synth.host(words), rw), f"{tag}: words"
+        if signs is not None:
+            assert np.array_equal(synth.host(signs), rsg), f"{tag}: signs"
+        gs = synth.host(scales)
+        d_ulp = P.ulp_diff(gs, rs)
+        assert np.all(d_ulp <= 1), f"{tag}: scales {gs} vs {rs}"
+        cidx = np.repeat(np.arange(off.size - 1), np.diff(off))
+        ds = np.abs(gs.astype(np.float64) - rs.astype(np.float64))[cidx]
+        ds = np.where(np.isfinite(ds), ds, 0.0)
+        eslack = ds * (0.1 if var["ef_mode"] else 1.0)
+        P.assert_f32_close(synth.host(d[1]), err, f"{tag}: err", eslack)
+        P.assert_f32_close(synth.host(d[2]), m, f"{tag}: m", 0.1 * ds)
+        P.assert_f32_close(synth.host(d[4]), p, f"{tag}: p",
+                           lr * 0.1 * ds / (np.sqrt(v.astype(np.float64)) + 1e-8))
+        assert np.array_equal(synth.host(d[3]), v), f"{tag}: v changed"
+        assert int(nf.item()) == rnf, f"{tag}: non-finite count"
+        gnp = _small_state(n, seed + 1000 + _, wide=var["clip"] > 0)[0]
+        if var["gdt"] == "bf16":
+            gnp = _bf16_bits(gnp)
+
+
+@pytest.mark.parametrize("vname", sorted(VARIANTS))
+def test_compress_bruteforce_small(vname):
+    var = VARIANTS[vname]
+    for n in range(1, 131):
+        for chunk in sorted({64, 128, n}):
+            _gpu_vs_oracle_compress(n, chunk, var, seed=n * 7 + chunk)
+
+
+@pytest.mark.parametrize("vname", sorted(VARIANTS))
+@pytest.mark.parametrize("n,chunk", [(1 << 20, 1 << 20), (1_000_003, 1 << 16), (300_037, 4096),
+                                     (70_000, 64 * 1000)])
+def test_compress_multi_tile(vname, n, chunk):
+    """Several tiles and work blocks per chunk, ragged chunk and buffer tails, 3 steps each from the
+    oracle's state."""
+    _gpu_vs_oracle_compress(n, chunk, VARIANTS[vname], seed=n, steps=3)
+
+
+def test_compress_edge_values():
+    """Negative denormals, both zeros, NaN and Inf in g and in the error buffer."""
+    n = 4096 + 17
+    rng = np.random.default_rng(5)
+    for pattern in ("denormals", "signed_zeros", "special"):
+        g = synth.draw_values(n, 31, pattern)
+        err = np.where(rng.random(n) < 0.5, np.float32(0.0), synth.draw_values(n, 37, pattern))
+        state = (err.astype(np.float32), np.zeros(n, np.float32),
+                 np.ones(n, np.float32), np.zeros(n, np.float32))
+        for vname in ("fp32_plain", "fp32_ema"):
+            _gpu_vs_oracle_compress(n, 1024, VARIANTS[vname], seed=1, g=g,
+                                    state=tuple(a.copy() for a in state))
+
+
+@pytest.mark.parametrize("gdt", ["f32", "bf16"])
+@pytest.mark.parametrize("bias_correction", [False, True])
+def test_dense_step(gdt, bias_correction):
+    for n in (1, 7, 130, 5000, 1_000_003):
+        g, _, m, v, p = _small_state(n, 3)
+        if gdt == "bf16":
+            g = _bf16_bits(g)
+        plan = ob.ob_plan_create(n, chunk_size=1 << 16)
+        d = [_t(a) for a in (g, m, v, p)]
+        hp = ob.hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, bias_correction=bias_correction,
+                        step=3)
+        ob.ob_adam_warmup_step(plan, d[0], d[1], d[2], d[3], hp)
+        oracle.warmup_step(g, m, v, p, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                           bias_correction=bias_correction, step=3)
+        for name, dev_t, ref in (("m", d[1], m), ("v", d[2], v), ("p", d[3], p)):
+            P.assert_f32_close(synth.host(dev_t), ref, f"dense n={n} {gdt} bc={bias_correction}: {name}")
+
+
+def test_server_bruteforce_small():
+    for W in (1, 2, 3, 8):
+        for n, chunk in ((1, 64), (31, 64), (130, 64), (1000, 128), (5000, 1024), (70001, 1 << 14)):
+            off = oracle.uniform_offsets(n, chunk)
+            K = off.size - 1
+            rng = np.random.default_rng([W, n])
+            ww = rng.integers(0, 1 << 32, size=(W, (n + 31) // 32), dtype=np.uint64).astype(np.uint32)
+            ws = rng.uniform(1e-4, 1e-2, size=(W, K)).astype(np.float32)
+            e = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+            plan = ob.ob_plan_create(n, chunk_size=chunk)
+            de = _t(e)
+            words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+            scales = torch.zeros(K, dtype=torch.float32, device=DEV)
+            ob.ob_server_reduce(plan, _t(ww).view(W, -1), _t(ws), de, words, scales)
+            rw, rs = oracle.server_reduce(ww, ws, e, off)
+            tag = f"server W={W} n={n}"
+            assert np.array_equal(synth.host(words), rw), tag
+            gs = synth.host(scales)
+            assert np.all(P.ulp_diff(gs, rs) <= 1), tag
+            ds = np.abs(gs.astype(np.float64) - rs)[np.repeat(np.arange(K), np.diff(off))]
+            P.assert_f32_close(synth.host(de), e, tag + ": server err", ds)
+
+
+# ------------------------------------------------------------------------------------------------
+# edge cases of the boundary
+# ------------------------------------------------------------------------------------------------
+
+def test_zero_size_is_noop():
+    plan = ob.ob_plan_create(0, chunk_size=64)
+    z = torch.zeros(0, dtype=torch.float32, device=DEV)
+    zi = torch.zeros(0, dtype=torch.int32, device=DEV)
+    hp = ob.hparams()
+    ob.ob_adam_compress_step(plan, z, z, z, z, z, zi, torch.zeros(0, device=DEV), hp)
+    ob.ob_adam_warmup_step(plan, z, z, z, z, hp)
+    ob.ob_pack(z, zi)
+    ob.ob_unpack(None, zi, 0, z)
+
+
+def test_misaligned_and_invalid_arguments():
+    n = 1024
+    plan = ob.ob_plan_create(n, chunk_size=256)
+    big = torch.zeros(n + 4, dtype=torch.float32, device=DEV)
+    ok = [torch.zeros(n, dtype=torch.float32, device=DEV) for _ in range(5)]
+    words = torch.zeros(n // 32, dtype=torch.int32, device=DEV)
+    scales = torch.zeros(4, dtype=torch.float32, device=DEV)
+    hp = ob.hparams()
+    with pytest.raises(ob.ObError) as e:
+        ob.ob_adam_compress_step(plan, big[1:n + 1], *ok[1:], words, scales, hp)   # g + 4 bytes
+    assert e.value.status == 2
+    with pytest.raises(ob.ObError) as e:
+        ob.ob_adam_compress_step(plan, ok[0], big[2:n + 2], *ok[2:], words, scales, hp)
+    assert e.value.status == 2
+    with pytest.raises(ob.ObError) as e:       # interior chunk boundary not a multiple of 64
+        ob.ob_plan_create(200, chunk_offsets=[0, 100, 200])
+    assert e.value.status == 2
+    with pytest.raises(ob.ObError) as e:       # offsets do not end at n
+        ob.ob_plan_create(200, chunk_offsets=[0, 64, 199])
+    assert e.value.status == 1
+    with pytest.raises(ob.ObError) as e:
+        ob.ob_plan_create(-1, chunk_size=64)
+    assert e.value.status == 1
+    with pytest.raises(ob.ObError) as e:       # W = 0 workers
+        ob.ob_server_reduce(plan, torch.zeros((0, n // 32), dtype=torch.int32, device=DEV),
+                            torch.zeros((0, 4), device=DEV), ok[0], words, scales)
+    assert e.value.status == 1
+    with pytest.raises(ob.ObError) as e:       # unpack n differs from the plan
+        ob.ob_unpack(plan, torch.zeros(n // 64, dtype=torch.int32, device=DEV), n // 2,
+                     torch.zeros(n // 2, device=DEV), scales=scales)
+    assert e.value.status == 1
+    with pytest.raises(ValueError):            # host tensors are refused: no CPU path
+        ob.ob_pack(torch.zeros(64), words[:2])
+
+
+def test_deterministic():
+    n = 3_000_017
+    var = VARIANTS["bf16_ema_clip_int8"]
+    g, err, m, v, p = _small_state(n, 77, wide=True)
+    gb = _bf16_bits(g)
+    plan = ob.ob_plan_create(n, chunk_size=1 << 18)
+    hp = ob.hparams(lr=1e-4, clip=5.0, ef_mode=1, ef_beta=0.9)
+    outs = []
+    for _ in range(2):
+        d = [_t(a) for a in (gb, err, m, v, p)]
+        words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+        scales = torch.zeros(plan.num_chunks, dtype=torch.float32, device=DEV)
+        signs = torch.zeros(n, dtype=torch.int8, device=DEV)
+        ob.ob_adam_compress_step(plan, d[0], d[1], d[2], d[3], d[4], words, scales, hp, signs)
+        outs.append([synth.host(t) for t in (d[1], d[2], d[4], words, scales, signs)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    assert var["signs"]
+
+
+def test_kernel_timing_api():
+    n = 1 << 20
+    plan = ob.ob_plan_create(n, chunk_size=1 << 18)
+    d = [torch.ones(n, dtype=torch.float32, device=DEV) for _ in range(5)]
+    words = torch.zeros(n // 32, dtype=torch.int32, device=DEV)
+    scales = torch.zeros(4, dtype=torch.float32, device=DEV)
+    ob.ob_plan_set_timing(plan, True)
+    for _ in range(3):
+        ob.ob_adam_compress_step(plan, *d, words, scales, ob.hparams())
+    ob.ob_adam_warmup_step(plan, d[0], d[2], d[3], d[4], ob.hparams())
+    ms, cnt = ob.ob_plan_read_timing(plan, ob.OB_KERNEL_COMPRESS)
+    assert cnt == 3 and ms > 0
+    assert ob.ob_plan_read_timing(plan, ob.OB_KERNEL_CHUNK_SUMSQ)[1] == 3
+    assert ob.ob_plan_read_timing(plan, ob.OB_KERNEL_DENSE)[1] == 1
+
+
+# ------------------------------------------------------------------------------------------------
+# the workloads at full size
+# ------------------------------------------------------------------------------------------------
+
+def test_workload_single_1m():
+    """2^20 fp32 elements, one chunk, 10 compressed steps, every output checked every step."""
+    counts = P.run_workload(synth.SINGLE_1M, log=lambda *_: None)
+    assert counts["compressed"] == 10 and counts["dense"] == 0
+
+
+def test_workload_bert_base():
+    """197 per-tensor chunks (108,891,648 fp32 elements): 5 dense steps, then 20 compressed; every
+    chunk checked every step."""
+    counts = P.run_workload(synth.BERT_BASE, log=lambda *_: None)
+    assert counts["dense"] == 5 and counts["compressed"] == 20
+
+
+def test_workload_server_2p28_w8():
+    """n = 2^28, W = 8, chunks of 2^20: 10 rounds of server reduce + unpack; the server error carries
+    across rounds; 33 chunks checked each round (every 8th and the last)."""
+    w = synth.SERVER_W8
+    off = w.chunk_offsets()
+    K = w.n_chunks
+    plan = ob.ob_plan_create(w.n, chunk_size=w.chunk)
+    e = torch.zeros(w.n, dtype=torch.float32, device=DEV)
+    words = torch.zeros((w.n + 31) // 32, dtype=torch.int32, device=DEV)
+    scales = torch.zeros(K, dtype=torch.float32, device=DEV)
+    out = torch.empty(w.n, dtype=torch.float32, device=DEV)
+    chunks = sorted(set(range(0, K, 8)) | {K - 1})
+    ref_e = {c: np.zeros(int(off[c + 1] - off[c]), np.float32) for c in chunks}
+    for r in range(w.steps):
+        ww = synth.draw_worker_words(w, r, DEV)
+        ws = synth.draw_worker_scales(w, r, DEV)
+        for c in chunks:
+            e[int(off[c]):int(off[c + 1])].copy_(torch.from_numpy(ref_e[c]))
+        ob.ob_server_reduce(plan, ww, ws, e, words, scales)
+        ob.ob_unpack(plan, words, w.n, out, scales=scales)
+        torch.cuda.synchronize()
+        wwh, wsh = synth.host(ww), synth.host(ws)
+        for c in chunks:
+            a, b = int(off[c]), int(off[c + 1])
+            rw, rs = oracle.server_reduce(np.ascontiguousarray(wwh[:, a // 32:b // 32]),
+                                          np.ascontiguousarray(wsh[:, c:c + 1]), ref_e[c],
+                                          np.asarray([0, b - a], np.int64))
+            tag = f"server round {r} chunk {c}"
+            assert np.array_equal(synth.host(words[a // 32:b // 32]), rw), tag
+            gs = np.float32(scales[c].item())
+            assert P.ulp_diff(gs, rs[0]) <= 1, tag
+            ds = abs(float(gs) - float(rs[0]))
+            P.assert_f32_close(synth.host(e[a:b]), ref_e[c], tag + ": server err", ds)
+            ro = oracle.unpack(rw, b - a, np.asarray([0, b - a], np.int64), rs)
+            P.assert_f32_close(synth.host(out[a:b]), ro, tag + ": unpack", ds)
+            if ds == 0.0:
+                assert np.array_equal(synth.host(out[a:b]), ro), tag + ": unpack"
+
+
+@pytest.mark.slow
+def test_workload_gpt2_1p5b():
+    """1,557,611,200 bf16-gradient elements, chunks of 2^24 (93 chunks, ragged tail): 10 compressed
+    steps; chunks 0, 1, 46 and the tail chunk 92 checked every step."""
+    w = synth.GPT2_XL
+    counts = P.run_workload(w, chunks=[0, 1, 46, w.n_chunks - 1], log=lambda *_: None)
+    assert counts["compressed"] == 10
+
+
+@pytest.mark.slow
+def test_workload_llama2_7b():
+    """6,738,415,616 bf16-gradient elements (~129 GB resident), chunks of 2^24 (402 chunks), clip 5,
+    EMA error, int8 signs, dense refresh at t = 16, 32, 48: chunks 0, 200 and the tail 401 checked
+    on all 48 steps."""
+    w = synth.LLAMA2_7B
+    counts = P.run_workload(w, chunks=[0, 200, w.n_chunks - 1], log=lambda *_: None)
+    assert counts["dense"] == 3 and counts["compressed"] == 45
