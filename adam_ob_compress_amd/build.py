@@ -10,7 +10,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libobadam.so")
-SOURCES = [os.path.join(CSRC, "ob_kernels.hip"), os.path.join(CSRC, "ob_api.cpp")]
+# (source, extra defines): compiled to objects in parallel, then linked into one library
+UNITS = [
+    ("ob_kernels.hip", []),
+    ("ob_api.cpp", []),
+]
+BUILD_DIR = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -23,12 +28,25 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra: list[str] | None = None, out: str | None = None) -> str:
-    """Compile every source into one shared library (always recompiles)."""
+    """Compile every unit (in parallel) and link one shared library; always recompiles."""
     target = out or LIB
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-o", target + ".tmp", *SOURCES]
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    procs, objs = [], []
+    for i, (src, defs) in enumerate(UNITS):
+        obj = os.path.join(BUILD_DIR, f"{i}_{os.path.splitext(src)[0]}.o")
+        cmd = [HIPCC, *FLAGS, *defs, *(extra or []), "-c", "-o", obj, os.path.join(CSRC, src)]
+        cmd.remove("-shared")
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((subprocess.Popen(cmd), cmd))
+        objs.append(obj)
+    failed = [cmd for p, cmd in procs if p.wait() != 0]
+    if failed:
+        raise RuntimeError("hipcc failed: " + " ".join(failed[0]))
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", target + ".tmp", *objs]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+        print(" ".join(link), flush=True)
+    subprocess.run(link, check=True)
     os.replace(target + ".tmp", target)
     return target
 

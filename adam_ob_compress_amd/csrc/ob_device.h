@@ -1,0 +1,209 @@
+// ob_device.h -- device helpers shared by the kernel translation units (loads and stores, wave and
+// block reductions, DPP bit packing, and the per-element rules of the compressed step).
+#pragma once
+
+#include "ob_internal.h"
+
+#include <math.h>
+
+namespace ob {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPlainItem = 16 * kTile;  // elements per block for the plan-less pack/unpack
+
+// Tuning knobs (compile-time; every setting computes the same results):
+//   OB_P1_UNROLL / OB_P2_UNROLL   tiles in flight per loop trip in pass 1 / pass 2
+//   OB_NT_P1                      nontemporal loads in pass 1
+//   OB_NT_P2                      nontemporal loads of the pass-2 inputs (read once more, then dead)
+//   OB_NT_ST                      nontemporal stores of the pass-2 outputs
+#ifndef OB_P1_UNROLL
+#define OB_P1_UNROLL 4
+#endif
+#ifndef OB_P2_UNROLL
+#define OB_P2_UNROLL 2
+#endif
+#ifndef OB_NT_P1
+#define OB_NT_P1 1
+#endif
+#ifndef OB_NT_P2
+#define OB_NT_P2 0
+#endif
+#ifndef OB_NT_ST
+#define OB_NT_ST 0
+#endif
+
+// ------------------------------------------------------------------------------------------------
+// loads and stores
+// ------------------------------------------------------------------------------------------------
+
+template <bool NT, class V>
+__device__ __forceinline__ V ldv(const V* __restrict__ p)
+{
+    if (NT) return __builtin_nontemporal_load(p);
+    return *p;
+}
+
+struct GradF32 {
+    using T = float;
+    template <bool NT = false, class I>
+    static __device__ __forceinline__ f4 load4(const float* __restrict__ g, I i)
+    {
+        return ldv<NT>(reinterpret_cast<const f4*>(g + i));
+    }
+    template <class I>
+    static __device__ __forceinline__ float load1(const float* __restrict__ g, I i) { return g[i]; }
+};
+
+// bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits.
+struct GradBF16 {
+    using T = uint16_t;
+    template <bool NT = false, class I>
+    static __device__ __forceinline__ f4 load4(const uint16_t* __restrict__ g, I i)
+    {
+        const u2 u = ldv<NT>(reinterpret_cast<const u2*>(g + i));
+        f4 r;
+        r.x = __uint_as_float(u.x << 16);
+        r.y = __uint_as_float(u.x & 0xffff0000u);
+        r.z = __uint_as_float(u.y << 16);
+        r.w = __uint_as_float(u.y & 0xffff0000u);
+        return r;
+    }
+    template <class I>
+    static __device__ __forceinline__ float load1(const uint16_t* __restrict__ g, I i)
+    {
+        return __uint_as_float(static_cast<uint32_t>(g[i]) << 16);
+    }
+};
+
+template <bool NT = false, class I>
+__device__ __forceinline__ f4 ld4(const float* __restrict__ p, I i)
+{
+    return ldv<NT>(reinterpret_cast<const f4*>(p + i));
+}
+
+template <bool NT = false, class I>
+__device__ __forceinline__ void st4(float* __restrict__ p, I i, f4 v)
+{
+    if (NT)
+        __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p + i));
+    else
+        *reinterpret_cast<f4*>(p + i) = v;
+}
+
+// ------------------------------------------------------------------------------------------------
+// reductions and bit packing
+// ------------------------------------------------------------------------------------------------
+
+// Butterfly over the 64 lanes: each step adds two equal-content partial sums, so every lane ends
+// with the same bits.
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Sum over the block in a fixed order; every thread returns the same value.
+__device__ __forceinline__ double block_sum(double v, double* lds)
+{
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double s = lds[0];
+#pragma unroll
+    for (int w = 1; w < kBlock / 64; ++w) s += lds[w];
+    return s;
+}
+
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* lds)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t s = 0;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) s += lds[w];
+    return s;
+}
+
+// OR of a value across each group of 8 consecutive lanes, via DPP:
+// quad_perm[1,0,3,2], quad_perm[2,3,0,1], then row_half_mirror (lane j <-> 7-j in each 8-lane half
+// row).  After the call every lane of the group holds the group's OR.  Must run with all lanes active.
+__device__ __forceinline__ uint32_t or8(uint32_t v)
+{
+    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false));
+    return v;
+}
+
+// Lane tid holds the 4 sign bits of elements i..i+3 (i = tile start + 4*tid, tile start a multiple of
+// 32).  Lanes 8k..8k+7 together hold the 32 bits of one word; lane 8k writes it if `valid`.
+template <class I>
+__device__ __forceinline__ void store_word(uint32_t* __restrict__ words, I i, uint32_t nib, bool valid)
+{
+    const uint32_t w = or8(nib << (4 * (threadIdx.x & 7)));
+    if ((threadIdx.x & 7) == 0 && valid) words[i >> 5] = w;
+}
+
+__device__ __forceinline__ uint32_t signs4(uint32_t nib)
+{
+    // byte k = +1 (0x01) or -1 (0xFF) by bit k
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r |= ((nib >> k) & 1u ? 0x01u : 0xFFu) << (8 * k);
+    return r;
+}
+
+// ------------------------------------------------------------------------------------------------
+// element rules
+// ------------------------------------------------------------------------------------------------
+
+// compensated = clip(g) + err ([P2] 1-bit Adam; clip of [P1] sec. 3.2).  NaN passes the clip.
+template <bool CLIP>
+__device__ __forceinline__ float compensate(float g, float e, float clip)
+{
+    if (CLIP) g = g > clip ? clip : (g < -clip ? -clip : g);
+    return g + e;
+}
+
+// One element of the compressed step; returns the sign bit (1 <=> +1).
+// x, g_hat and delta are single fp32 operations; the error (EMA), m and p lines are evaluated in
+// double and rounded once, so a large update that nearly cancels p keeps full fp32 accuracy.
+template <bool EMA>
+__device__ __forceinline__ uint32_t compress_elem(float x, float& e, float& mm, float vv, float& pp,
+                                                  float scale, const CompressParams& cp)
+{
+    const bool b = x >= 0.0f;
+    const float gh = b ? scale : -scale;              // g_hat = dequantize(q)
+    const float delta = x - gh;                       // compensated - g_hat
+    if (EMA)
+        e = static_cast<float>(cp.ef_beta * static_cast<double>(e) + cp.one_m_ef_beta * static_cast<double>(delta));
+    else
+        e = delta;
+    // m on g_hat ([P1] sec. 2.2; [P2]), then the frozen-v update with the stored (new) m ([P2])
+    mm = static_cast<float>(cp.beta1 * static_cast<double>(mm) + cp.one_m_beta1 * static_cast<double>(gh));
+    const double den = sqrt(static_cast<double>(vv)) + cp.eps;
+    pp = static_cast<float>(static_cast<double>(pp) - cp.lr * (static_cast<double>(mm) / den));
+    return b ? 1u : 0u;
+}
+
+// Chunk scale from the chunk's block partials, reduced in a fixed order.
+__device__ __forceinline__ float chunk_scale(const PlanDev& pd, int c, double* lds)
+{
+    const int f0 = pd.chunk_first[c], f1 = pd.chunk_first[c + 1];
+    double s = 0.0;
+    for (int i = f0 + static_cast<int>(threadIdx.x); i < f1; i += kBlock) s += pd.partials[i];
+    s = block_sum(s, lds);
+    const int64_t nc = pd.chunk_off[c + 1] - pd.chunk_off[c];
+    return static_cast<float>(sqrt(s / static_cast<double>(nc)));
+}
+
+}  // namespace
+}  // namespace ob

@@ -21,170 +21,10 @@
 //     permutes (no LDS) builds the 32-bit word of 32 consecutive elements, written by one lane;
 //   * all fp32 arithmetic is plain IEEE (no fast-math, denormals kept: a negative denormal must give
 //     sign -1).
-#include "ob_internal.h"
-
-#include <math.h>
+#include "ob_device.h"
 
 namespace ob {
 namespace {
-
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u2 __attribute__((ext_vector_type(2)));
-
-constexpr int kPlainItem = 16 * kTile;  // elements per block for the plan-less pack/unpack
-
-// ------------------------------------------------------------------------------------------------
-// loads and stores
-// ------------------------------------------------------------------------------------------------
-
-struct GradF32 {
-    using T = float;
-    static __device__ __forceinline__ f4 load4(const float* __restrict__ g, int64_t i)
-    {
-        return *reinterpret_cast<const f4*>(g + i);
-    }
-    static __device__ __forceinline__ float load1(const float* __restrict__ g, int64_t i) { return g[i]; }
-};
-
-// bf16 -> fp32 is exact: the bf16 bits are the high half of the fp32 bits.
-struct GradBF16 {
-    using T = uint16_t;
-    static __device__ __forceinline__ f4 load4(const uint16_t* __restrict__ g, int64_t i)
-    {
-        const u2 u = *reinterpret_cast<const u2*>(g + i);
-        f4 r;
-        r.x = __uint_as_float(u.x << 16);
-        r.y = __uint_as_float(u.x & 0xffff0000u);
-        r.z = __uint_as_float(u.y << 16);
-        r.w = __uint_as_float(u.y & 0xffff0000u);
-        return r;
-    }
-    static __device__ __forceinline__ float load1(const uint16_t* __restrict__ g, int64_t i)
-    {
-        return __uint_as_float(static_cast<uint32_t>(g[i]) << 16);
-    }
-};
-
-__device__ __forceinline__ f4 ld4(const float* __restrict__ p, int64_t i)
-{
-    return *reinterpret_cast<const f4*>(p + i);
-}
-
-__device__ __forceinline__ void st4(float* __restrict__ p, int64_t i, f4 v)
-{
-    *reinterpret_cast<f4*>(p + i) = v;
-}
-
-// ------------------------------------------------------------------------------------------------
-// reductions and bit packing
-// ------------------------------------------------------------------------------------------------
-
-// Butterfly over the 64 lanes: each step adds two equal-content partial sums, so every lane ends
-// with the same bits.
-__device__ __forceinline__ double wave_sum(double v)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
-// Sum over the block in a fixed order; every thread returns the same value.
-__device__ __forceinline__ double block_sum(double v, double* lds)
-{
-    v = wave_sum(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
-    __syncthreads();
-    double s = lds[0];
-#pragma unroll
-    for (int w = 1; w < kBlock / 64; ++w) s += lds[w];
-    return s;
-}
-
-__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* lds)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
-    __syncthreads();
-    uint32_t s = 0;
-#pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) s += lds[w];
-    return s;
-}
-
-// OR of a value across each group of 8 consecutive lanes, via DPP:
-// quad_perm[1,0,3,2], quad_perm[2,3,0,1], then row_half_mirror (lane j <-> 7-j in each 8-lane half
-// row).  After the call every lane of the group holds the group's OR.  Must run with all lanes active.
-__device__ __forceinline__ uint32_t or8(uint32_t v)
-{
-    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false));
-    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false));
-    v |= static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false));
-    return v;
-}
-
-// Lane tid holds the 4 sign bits of elements i..i+3 (i = tile start + 4*tid, tile start a multiple of
-// 32).  Lanes 8k..8k+7 together hold the 32 bits of one word; lane 8k writes it if `valid`.
-__device__ __forceinline__ void store_word(uint32_t* __restrict__ words, int64_t i, uint32_t nib, bool valid)
-{
-    const uint32_t w = or8(nib << (4 * (threadIdx.x & 7)));
-    if ((threadIdx.x & 7) == 0 && valid) words[i >> 5] = w;
-}
-
-__device__ __forceinline__ uint32_t signs4(uint32_t nib)
-{
-    // byte k = +1 (0x01) or -1 (0xFF) by bit k
-    uint32_t r = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) r |= ((nib >> k) & 1u ? 0x01u : 0xFFu) << (8 * k);
-    return r;
-}
-
-// ------------------------------------------------------------------------------------------------
-// element rules
-// ------------------------------------------------------------------------------------------------
-
-// compensated = clip(g) + err ([P2] 1-bit Adam; clip of [P1] sec. 3.2).  NaN passes the clip.
-template <bool CLIP>
-__device__ __forceinline__ float compensate(float g, float e, float clip)
-{
-    if (CLIP) g = g > clip ? clip : (g < -clip ? -clip : g);
-    return g + e;
-}
-
-// One element of the compressed step; returns the sign bit (1 <=> +1).
-// x, g_hat and delta are single fp32 operations; the error (EMA), m and p lines are evaluated in
-// double and rounded once, so a large update that nearly cancels p keeps full fp32 accuracy.
-template <bool EMA>
-__device__ __forceinline__ uint32_t compress_elem(float x, float& e, float& mm, float vv, float& pp,
-                                                  float scale, const CompressParams& cp)
-{
-    const bool b = x >= 0.0f;
-    const float gh = b ? scale : -scale;              // g_hat = dequantize(q)
-    const float delta = x - gh;                       // compensated - g_hat
-    if (EMA)
-        e = static_cast<float>(cp.ef_beta * static_cast<double>(e) + cp.one_m_ef_beta * static_cast<double>(delta));
-    else
-        e = delta;
-    // m on g_hat ([P1] sec. 2.2; [P2]), then the frozen-v update with the stored (new) m ([P2])
-    mm = static_cast<float>(cp.beta1 * static_cast<double>(mm) + cp.one_m_beta1 * static_cast<double>(gh));
-    const double den = sqrt(static_cast<double>(vv)) + cp.eps;
-    pp = static_cast<float>(static_cast<double>(pp) - cp.lr * (static_cast<double>(mm) / den));
-    return b ? 1u : 0u;
-}
-
-// Chunk scale from the chunk's block partials, reduced in a fixed order.
-__device__ __forceinline__ float chunk_scale(const PlanDev& pd, int c, double* lds)
-{
-    const int f0 = pd.chunk_first[c], f1 = pd.chunk_first[c + 1];
-    double s = 0.0;
-    for (int i = f0 + static_cast<int>(threadIdx.x); i < f1; i += kBlock) s += pd.partials[i];
-    s = block_sum(s, lds);
-    const int64_t nc = pd.chunk_off[c + 1] - pd.chunk_off[c];
-    return static_cast<float>(sqrt(s / static_cast<double>(nc)));
-}
 
 // ------------------------------------------------------------------------------------------------
 // compressed step, pass 1: per-block sum of squares of x = clip(g) + err
@@ -198,15 +38,15 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
     const Item it = pd.items[blockIdx.x];
     const int tid = threadIdx.x;
     double acc = 0.0;
-    constexpr int U = 4;
+    constexpr int U = OB_P1_UNROLL;
     int base = 0;
     for (; base + U * kTile <= it.len; base += U * kTile) {
         f4 gv[U], ev[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = it.start + base + u * kTile + kVec * tid;
-            gv[u] = G::load4(g, i);
-            ev[u] = ld4(err, i);
+            gv[u] = G::template load4<OB_NT_P1>(g, i);
+            ev[u] = ld4<OB_NT_P1>(err, i);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -228,7 +68,9 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
                 acc = fma(x, x, acc);
             }
         } else {
-            for (int k = 0; k < cnt; ++k) {
+            #pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                if (k >= cnt) continue;
                 const double x = compensate<CLIP>(G::load1(g, i + k), err[i + k], clip);
                 acc = fma(x, x, acc);
             }
@@ -258,18 +100,18 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
     if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
 
     uint32_t nf = 0;
-    constexpr int U = 2;
+    constexpr int U = OB_P2_UNROLL;
     int base = 0;
     for (; base + U * kTile <= it.len; base += U * kTile) {
         f4 gv[U], ev[U], mv[U], vv[U], pv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = it.start + base + u * kTile + kVec * tid;
-            gv[u] = G::load4(g, i);
-            ev[u] = ld4(err, i);
-            mv[u] = ld4(m, i);
-            vv[u] = ld4(v, i);
-            pv[u] = ld4(p, i);
+            gv[u] = G::template load4<OB_NT_P2>(g, i);
+            ev[u] = ld4<OB_NT_P2>(err, i);
+            mv[u] = ld4<OB_NT_P2>(m, i);
+            vv[u] = ld4<OB_NT_P2>(v, i);
+            pv[u] = ld4<OB_NT_P2>(p, i);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -285,9 +127,9 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
                 pv[u][k] = pp;
                 if (NONFIN) nf += __builtin_isfinite(e) ? 0u : 1u;
             }
-            st4(err, i, ev[u]);
-            st4(m, i, mv[u]);
-            st4(p, i, pv[u]);
+            st4<OB_NT_ST>(err, i, ev[u]);
+            st4<OB_NT_ST>(m, i, mv[u]);
+            st4<OB_NT_ST>(p, i, pv[u]);
             if (SIGNS) *reinterpret_cast<uint32_t*>(signs + i) = signs4(nib);
             store_word(words, i, nib, true);
         }
@@ -315,7 +157,9 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
             st4(p, i, pv);
             if (SIGNS) *reinterpret_cast<uint32_t*>(signs + i) = signs4(nib);
         } else if (cnt > 0) {
-            for (int k = 0; k < cnt; ++k) {
+            #pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                if (k >= cnt) continue;
                 const float x = compensate<CLIP>(G::load1(g, i + k), err[i + k], cp.clip);
                 float e = err[i + k], mm = m[i + k], pp = p[i + k];
                 const uint32_t b = compress_elem<EMA>(x, e, mm, v[i + k], pp, scale, cp);
@@ -408,7 +252,9 @@ __global__ __launch_bounds__(kBlock) void k_dense(PlanDev pd, const typename G::
             st4(v, i, vv);
             st4(p, i, pv);
         } else {
-            for (int k = 0; k < cnt; ++k) {
+            #pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                if (k >= cnt) continue;
                 float mm = m[i + k], vq = v[i + k], pp = p[i + k];
                 dense_elem<BC>(G::load1(g, i + k), mm, vq, pp, dp);
                 m[i + k] = mm;
@@ -425,26 +271,52 @@ __global__ __launch_bounds__(kBlock) void k_dense(PlanDev pd, const typename G::
 
 // Averages of the 4 elements i..i+3 (one nibble of one word) over W workers: exact double sum of
 // +-s in ascending worker order, one division by W, one rounding to fp32.
+// Workers are taken kWorkerBatch at a time: the batch's word loads are all issued before the sums
+// use them, so the memory latency is paid once per batch, not once per worker.  The additions stay
+// in ascending worker order.
+constexpr int kWorkerBatch = 8;
+
 __device__ __forceinline__ f4 server_avg4(int W, const uint32_t* __restrict__ ww, int64_t nw,
                                           const float* __restrict__ ws, int K, int c, int64_t i)
 {
     double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
     const int64_t wi = i >> 5;
     const int sh = static_cast<int>(i & 31);
-    for (int w = 0; w < W; ++w) {
-        const uint32_t bits = ww[static_cast<int64_t>(w) * nw + wi] >> sh;
-        const double s = static_cast<double>(ws[static_cast<int64_t>(w) * K + c]);
-        a0 += (bits & 1u) ? s : -s;
-        a1 += (bits & 2u) ? s : -s;
-        a2 += (bits & 4u) ? s : -s;
-        a3 += (bits & 8u) ? s : -s;
+    for (int w0 = 0; w0 < W; w0 += kWorkerBatch) {
+        uint32_t bits[kWorkerBatch];
+        double s[kWorkerBatch];
+#pragma unroll
+        for (int j = 0; j < kWorkerBatch; ++j) {
+            const int w = w0 + j < W ? w0 + j : W - 1;  // in-range index; surplus lanes of the batch unused
+            bits[j] = ww[static_cast<int64_t>(w) * nw + wi] >> sh;
+            s[j] = static_cast<double>(ws[static_cast<int64_t>(w) * K + c]);
+        }
+        // past the last worker the batch adds +0.0, an exact no-op (the sums start at +0 and an IEEE
+        // sum is never -0 unless both terms are), so the loop has no branch the loads must wait for
+#pragma unroll
+        for (int j = 0; j < kWorkerBatch; ++j) {
+            const double sj = w0 + j < W ? s[j] : 0.0;
+            a0 += (bits[j] & 1u) ? sj : -sj;
+            a1 += (bits[j] & 2u) ? sj : -sj;
+            a2 += (bits[j] & 4u) ? sj : -sj;
+            a3 += (bits[j] & 8u) ? sj : -sj;
+        }
     }
-    const double dw = static_cast<double>(W);
     f4 r;
-    r.x = static_cast<float>(a0 / dw);
-    r.y = static_cast<float>(a1 / dw);
-    r.z = static_cast<float>(a2 / dw);
-    r.w = static_cast<float>(a3 / dw);
+    if ((W & (W - 1)) == 0) {
+        // W a power of two: 1/W is exact, so the product equals the IEEE quotient
+        const double rw = 1.0 / static_cast<double>(W);
+        r.x = static_cast<float>(a0 * rw);
+        r.y = static_cast<float>(a1 * rw);
+        r.z = static_cast<float>(a2 * rw);
+        r.w = static_cast<float>(a3 * rw);
+    } else {
+        const double dw = static_cast<double>(W);
+        r.x = static_cast<float>(a0 / dw);
+        r.y = static_cast<float>(a1 / dw);
+        r.z = static_cast<float>(a2 / dw);
+        r.w = static_cast<float>(a3 / dw);
+    }
     return r;
 }
 
@@ -470,9 +342,11 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
         const int64_t i = it.start + base + kVec * tid;
         uint32_t nib = 0;
         if (cnt > 0) {
+            // the error load is issued before the worker loads so that all are in flight together
+            f4 ev = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (cnt >= kVec) ev = ld4(e, i);
             const f4 avg = server_avg4(W, ww, nw, ws, pd.K, c, i);
             if (cnt >= kVec) {
-                f4 ev = ld4(e, i);
                 f4 x;
 #pragma unroll
                 for (int k = 0; k < kVec; ++k) x[k] = avg[k] + ev[k];
@@ -489,7 +363,9 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
                     for (int k = 0; k < kVec; ++k) acc = fma(static_cast<double>(x[k]), static_cast<double>(x[k]), acc);
                 }
             } else {
-                for (int k = 0; k < cnt; ++k) {
+                #pragma unroll
+                for (int k = 0; k < kVec; ++k) {
+                    if (k >= cnt) continue;
                     const float x = avg[k] + e[i + k];
                     if (APPLY) {
                         const bool b = x >= 0.0f;
@@ -541,7 +417,9 @@ __global__ __launch_bounds__(kBlock) void k_unpack(const Item* __restrict__ item
         if (cnt >= kVec) {
             st4(out, i, r);
         } else {
-            for (int k = 0; k < cnt; ++k) out[i + k] = r[k];
+            #pragma unroll
+            for (int k = 0; k < kVec; ++k)
+                if (k < cnt) out[i + k] = r[k];
         }
     }
 }
@@ -563,7 +441,9 @@ __global__ __launch_bounds__(kBlock) void k_pack(const typename G::T* __restrict
 #pragma unroll
             for (int k = 0; k < kVec; ++k) nib |= (xv[k] >= 0.0f ? 1u : 0u) << k;
         } else {
-            for (int k = 0; k < cnt; ++k) nib |= (G::load1(x, i + k) >= 0.0f ? 1u : 0u) << k;
+            #pragma unroll
+            for (int k = 0; k < kVec; ++k)
+                if (k < cnt) nib |= (G::load1(x, i + k) >= 0.0f ? 1u : 0u) << k;
         }
         store_word(words, i, nib, 32 * (tid >> 3) < rem);
     }

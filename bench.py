@@ -30,7 +30,8 @@ if ROOT not in sys.path:
 METRIC = "elements/s and achieved HBM GB/s (% of peak) of fused 1-bit Adam step, 1 GPU"
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "bert-base-110M-fp32"
-KERNEL_SOURCES = ("adam_ob_compress_amd/csrc/ob_kernels.hip", "adam_ob_compress_amd/csrc/ob_internal.h")
+KERNEL_SOURCES = ("adam_ob_compress_amd/csrc/ob_kernels.hip", "adam_ob_compress_amd/csrc/ob_device.h",
+                  "adam_ob_compress_amd/csrc/ob_internal.h")
 
 
 def kernel_source_sha() -> str:

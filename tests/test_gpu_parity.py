@@ -148,7 +148,7 @@ def test_compress_bruteforce_small(vname):
 
 @pytest.mark.parametrize("vname", sorted(VARIANTS))
 @pytest.mark.parametrize("n,chunk", [(1 << 20, 1 << 20), (1_000_003, 1 << 16), (300_037, 4096),
-                                     (70_000, 64 * 1000)])
+                                     (70_000, 64 * 1000), (5_000_000, 5_000_000 - 64 * 7)])
 def test_compress_multi_tile(vname, n, chunk):
     """Several tiles and work blocks per chunk, ragged chunk and buffer tails, 3 steps each from the
     oracle's state."""
