@@ -320,6 +320,31 @@ __device__ __forceinline__ f4 server_avg4(int W, const uint32_t* __restrict__ ww
     return r;
 }
 
+// Sign patterns of the 4 elements of a lane, one byte each: byte k holds bit k of worker w's nibble
+// at bit w.  The 8 nibbles are packed as bits 4w+k and the 32-bit index is rotated right by two
+// index bits (4w+k -> 8k+w) with four delta swaps.
+__device__ __forceinline__ uint32_t delta_swap(uint32_t x, int d, uint32_t mask)
+{
+    const uint32_t t = ((x >> d) ^ x) & mask;
+    return x ^ t ^ (t << d);
+}
+
+__device__ __forceinline__ uint32_t patterns4(const uint32_t (&nib)[kWorkerBatch])
+{
+    uint32_t x = 0;
+#pragma unroll
+    for (int w = 0; w < kWorkerBatch; ++w) x |= (nib[w] & 0xFu) << (4 * w);
+    x = delta_swap(x, 3, 0x0A0A0A0Au);   // index bits 0 <-> 2
+    x = delta_swap(x, 6, 0x00CC00CCu);   // index bits 1 <-> 3
+    x = delta_swap(x, 12, 0x0000F0F0u);  // index bits 2 <-> 4
+    x = delta_swap(x, 8, 0x0000FF00u);   // index bits 3 <-> 4
+    return x;
+}
+
+// The server average of an element depends only on its W sign bits and the chunk's W scales.  For
+// W <= 8 each block tabulates all 2^W averages of its chunk in LDS, each computed exactly as
+// server_avg4 does (double sum in ascending worker order, one division, one rounding), and looks
+// them up; for larger W it sums per element.
 template <bool APPLY>
 __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint32_t* __restrict__ ww,
                                                    int64_t nw, const float* __restrict__ ws,
@@ -327,9 +352,23 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
                                                    float* __restrict__ scales)
 {
     __shared__ double lds[kBlock / 64];
+    __shared__ float table[1 << kWorkerBatch];
     const Item it = pd.items[blockIdx.x];
     const int tid = threadIdx.x;
     const int c = it.chunk;
+    const bool tabulate = W <= kWorkerBatch;
+    if (tabulate) {
+        const bool pow2 = (W & (W - 1)) == 0;
+        for (int pat = tid; pat < (1 << W); pat += kBlock) {
+            double a = 0.0;
+            for (int w = 0; w < W; ++w) {
+                const double s = static_cast<double>(ws[static_cast<int64_t>(w) * pd.K + c]);
+                a += ((pat >> w) & 1) ? s : -s;
+            }
+            table[pat] = static_cast<float>(pow2 ? a * (1.0 / static_cast<double>(W)) : a / static_cast<double>(W));
+        }
+        __syncthreads();
+    }
     float scale = 0.0f;
     if (APPLY) {
         scale = chunk_scale(pd, c, lds);
@@ -342,10 +381,26 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
         const int64_t i = it.start + base + kVec * tid;
         uint32_t nib = 0;
         if (cnt > 0) {
-            // the error load is issued before the worker loads so that all are in flight together
+            // the error and worker loads are all issued before any of them is used
             f4 ev = {0.0f, 0.0f, 0.0f, 0.0f};
             if (cnt >= kVec) ev = ld4(e, i);
-            const f4 avg = server_avg4(W, ww, nw, ws, pd.K, c, i);
+            f4 avg;
+            if (tabulate) {
+                uint32_t nb[kWorkerBatch];
+                const int64_t wi = i >> 5;
+                const int sh = static_cast<int>(i & 31);
+                // unconditional loads (clamped worker index) so that all are issued before the first use
+#pragma unroll
+                for (int w = 0; w < kWorkerBatch; ++w) {
+                    const int wc = w < W ? w : W - 1;
+                    nb[w] = (ww[static_cast<int64_t>(wc) * nw + wi] >> sh) & (w < W ? 0xFu : 0u);
+                }
+                const uint32_t pats = patterns4(nb);
+#pragma unroll
+                for (int k = 0; k < kVec; ++k) avg[k] = table[(pats >> (8 * k)) & 0xFFu];
+            } else {
+                avg = server_avg4(W, ww, nw, ws, pd.K, c, i);
+            }
             if (cnt >= kVec) {
                 f4 x;
 #pragma unroll
@@ -363,7 +418,7 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
                     for (int k = 0; k < kVec; ++k) acc = fma(static_cast<double>(x[k]), static_cast<double>(x[k]), acc);
                 }
             } else {
-                #pragma unroll
+#pragma unroll
                 for (int k = 0; k < kVec; ++k) {
                     if (k >= cnt) continue;
                     const float x = avg[k] + e[i + k];

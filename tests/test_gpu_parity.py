@@ -188,7 +188,8 @@ def test_dense_step(gdt, bias_correction):
 
 
 def test_server_bruteforce_small():
-    for W in (1, 2, 3, 8):
+    """W <= 8 takes the kernels' per-chunk table of averages, W > 8 the per-element sums."""
+    for W in (1, 2, 3, 5, 8, 9, 16):
         for n, chunk in ((1, 64), (31, 64), (130, 64), (1000, 128), (5000, 1024), (70001, 1 << 14)):
             off = oracle.uniform_offsets(n, chunk)
             K = off.size - 1
