@@ -17,12 +17,16 @@ struct ob_plan_s {
     int device = 0;
     int64_t n = 0;
     int32_t K = 0;
-    int64_t block_elems = 0;
-    int64_t n_items = 0;
-    ob::Item* d_items = nullptr;
-    int32_t* d_chunk_first = nullptr;
     int64_t* d_chunk_off = nullptr;
-    double* d_partials = nullptr;
+    double* d_partials = nullptr;  // one per pass-1 block
+
+    // block tables, one per kernel kind (kTables)
+    struct Table {
+        int64_t block_elems = 0;
+        int64_t n_items = 0;
+        ob::Item* d_items = nullptr;
+        int32_t* d_first = nullptr;
+    } t[4];
 
     // kernel timing
     bool timing = false;
@@ -35,15 +39,16 @@ struct ob_plan_s {
     double total_ms[OB_KERNEL_COUNT] = {};
     int64_t launches[OB_KERNEL_COUNT] = {};
 
-    ob::PlanDev dev() const
+    ob::PlanDev dev(int table) const
     {
         ob::PlanDev pd;
-        pd.items = d_items;
-        pd.chunk_first = d_chunk_first;
+        pd.items = t[table].d_items;
+        pd.chunk_first = t[table].d_first;
+        pd.p1_first = t[0].d_first;
         pd.chunk_off = d_chunk_off;
         pd.partials = d_partials;
         pd.n = n;
-        pd.n_items = n_items;
+        pd.n_items = t[table].n_items;
         pd.K = K;
         return pd;
     }
@@ -74,14 +79,30 @@ struct DeviceGuard {
     }
 };
 
-// Elements per work block: enough blocks to fill 256 CUs several times over, whole tiles, at most
-// 64 tiles.  OB_BLOCK_ELEMS (a multiple of 1024) overrides the choice for tuning sweeps.
-int64_t choose_block_elems(int64_t n)
+// Block tables by kernel kind.  Elements per block (from sweeps of 1-128 tiles of 1024 on MI355X):
+//   pass 1 (sums of squares): large blocks, so a chunk has few partial sums: enough blocks to fill
+//     256 CUs several times over, whole tiles, at most 64 tiles;
+//   compressed pass 2: 4 tiles;  dense step: 2 tiles;  server pass 2 and unpack: 8 tiles.
+// Environment overrides for tuning sweeps (multiples of 1024): OB_BLOCK_ELEMS, OB_BLOCK_ELEMS2,
+// OB_BLOCK_ELEMS_DENSE, OB_BLOCK_ELEMS_SERVER.
+enum { T_PASS1 = 0, T_COMPRESS = 1, T_DENSE = 2, T_SERVER = 3, kTables = 4 };
+
+int64_t env_block_elems(const char* name)
 {
-    if (const char* env = std::getenv("OB_BLOCK_ELEMS")) {
+    if (const char* env = std::getenv(name)) {
         const long long v = std::atoll(env);
         if (v >= ob::kTile && v <= kMaxBlockElems && v % ob::kTile == 0) return v;
     }
+    return 0;
+}
+
+int64_t choose_block_elems(int64_t n, int table)
+{
+    static const char* const env[kTables] = {"OB_BLOCK_ELEMS", "OB_BLOCK_ELEMS2", "OB_BLOCK_ELEMS_DENSE",
+                                             "OB_BLOCK_ELEMS_SERVER"};
+    static const int64_t tiles[kTables] = {0, 4, 2, 8};
+    if (const int64_t e = env_block_elems(env[table])) return e;
+    if (table != T_PASS1) return tiles[table] * ob::kTile;
     const int64_t target_blocks = 8192;
     int64_t e = (n + target_blocks - 1) / target_blocks;
     e = (e + ob::kTile - 1) / ob::kTile * ob::kTile;
@@ -96,8 +117,10 @@ void free_plan(ob_plan p)
         (void)hipEventDestroy(r.b);
     }
     for (auto e : p->pool) (void)hipEventDestroy(e);
-    if (p->d_items) (void)hipFree(p->d_items);
-    if (p->d_chunk_first) (void)hipFree(p->d_chunk_first);
+    for (auto& t : p->t) {
+        if (t.d_items) (void)hipFree(t.d_items);
+        if (t.d_first) (void)hipFree(t.d_first);
+    }
     if (p->d_chunk_off) (void)hipFree(p->d_chunk_off);
     if (p->d_partials) (void)hipFree(p->d_partials);
     delete p;
@@ -218,52 +241,58 @@ ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_off
     if (!p) return OB_ERR_OOM;
     p->n = n;
     p->K = static_cast<int32_t>(K);
-    p->block_elems = choose_block_elems(n);
 
-    // work blocks: consecutive per chunk
-    std::vector<ob::Item> items;
-    std::vector<int32_t> first(static_cast<size_t>(K) + 1, 0);
-    for (int64_t c = 0; c < K; ++c) {
-        first[c] = static_cast<int32_t>(items.size());
-        for (int64_t s = off[c]; s < off[c + 1]; s += p->block_elems) {
-            ob::Item it;
-            it.start = s;
-            it.len = static_cast<int32_t>(std::min<int64_t>(p->block_elems, off[c + 1] - s));
-            it.chunk = static_cast<int32_t>(c);
-            items.push_back(it);
-            if (items.size() > static_cast<size_t>(INT32_MAX)) {
-                delete p;
-                return OB_ERR_ARG;
+    // block tables: consecutive blocks per chunk
+    std::vector<ob::Item> items[kTables];
+    std::vector<int32_t> first[kTables];
+    for (int pass = 0; pass < kTables; ++pass) {
+        ob_plan_s::Table& t = p->t[pass];
+        t.block_elems = choose_block_elems(n, pass);
+        first[pass].assign(static_cast<size_t>(K) + 1, 0);
+        for (int64_t c = 0; c < K; ++c) {
+            first[pass][c] = static_cast<int32_t>(items[pass].size());
+            for (int64_t s = off[c]; s < off[c + 1]; s += t.block_elems) {
+                ob::Item it;
+                it.start = s;
+                it.len = static_cast<int32_t>(std::min<int64_t>(t.block_elems, off[c + 1] - s));
+                it.chunk = static_cast<int32_t>(c);
+                items[pass].push_back(it);
+                if (items[pass].size() > static_cast<size_t>(INT32_MAX)) {
+                    delete p;
+                    return OB_ERR_ARG;
+                }
             }
         }
+        first[pass][K] = static_cast<int32_t>(items[pass].size());
+        t.n_items = static_cast<int64_t>(items[pass].size());
     }
-    first[K] = static_cast<int32_t>(items.size());
-    p->n_items = static_cast<int64_t>(items.size());
 
     if (hipGetDevice(&p->device) != hipSuccess) {
         delete p;
         return OB_ERR_HIP;
     }
-    if (p->n_items > 0) {
-        const hipError_t e1 = hipMalloc(&p->d_items, items.size() * sizeof(ob::Item));
-        const hipError_t e2 = hipMalloc(&p->d_chunk_first, first.size() * sizeof(int32_t));
-        const hipError_t e3 = hipMalloc(&p->d_chunk_off, off.size() * sizeof(int64_t));
-        const hipError_t e4 = hipMalloc(&p->d_partials, items.size() * sizeof(double));
-        if (e1 != hipSuccess || e2 != hipSuccess || e3 != hipSuccess || e4 != hipSuccess) {
-            const bool oom = e1 == hipErrorOutOfMemory || e2 == hipErrorOutOfMemory ||
-                             e3 == hipErrorOutOfMemory || e4 == hipErrorOutOfMemory;
+    if (n > 0) {
+        auto fail = [&](hipError_t e) {
             free_plan(p);
-            return oom ? OB_ERR_OOM : OB_ERR_HIP;
+            return e == hipErrorOutOfMemory ? OB_ERR_OOM : OB_ERR_HIP;
+        };
+        hipError_t e;
+        for (int pass = 0; pass < kTables; ++pass) {
+            ob_plan_s::Table& t = p->t[pass];
+            if ((e = hipMalloc(&t.d_items, items[pass].size() * sizeof(ob::Item))) != hipSuccess) return fail(e);
+            if ((e = hipMalloc(&t.d_first, first[pass].size() * sizeof(int32_t))) != hipSuccess) return fail(e);
+            if ((e = hipMemcpy(t.d_items, items[pass].data(), items[pass].size() * sizeof(ob::Item),
+                               hipMemcpyHostToDevice)) != hipSuccess)
+                return fail(e);
+            if ((e = hipMemcpy(t.d_first, first[pass].data(), first[pass].size() * sizeof(int32_t),
+                               hipMemcpyHostToDevice)) != hipSuccess)
+                return fail(e);
         }
-        if (hipMemcpy(p->d_items, items.data(), items.size() * sizeof(ob::Item), hipMemcpyHostToDevice) !=
-                hipSuccess ||
-            hipMemcpy(p->d_chunk_first, first.data(), first.size() * sizeof(int32_t),
-                      hipMemcpyHostToDevice) != hipSuccess ||
-            hipMemcpy(p->d_chunk_off, off.data(), off.size() * sizeof(int64_t), hipMemcpyHostToDevice) !=
-                hipSuccess) {
-            free_plan(p);
-            return OB_ERR_HIP;
-        }
+        if ((e = hipMalloc(&p->d_partials, items[0].size() * sizeof(double))) != hipSuccess) return fail(e);
+        if ((e = hipMalloc(&p->d_chunk_off, off.size() * sizeof(int64_t))) != hipSuccess) return fail(e);
+        if ((e = hipMemcpy(p->d_chunk_off, off.data(), off.size() * sizeof(int64_t), hipMemcpyHostToDevice)) !=
+            hipSuccess)
+            return fail(e);
     }
     *out = p;
     return OB_OK;
@@ -279,8 +308,8 @@ ob_status ob_plan_destroy(ob_plan plan)
 
 int64_t ob_plan_num_elements(ob_plan plan) { return plan ? plan->n : -1; }
 int64_t ob_plan_num_chunks(ob_plan plan) { return plan ? plan->K : -1; }
-int64_t ob_plan_num_blocks(ob_plan plan) { return plan ? plan->n_items : -1; }
-int64_t ob_plan_block_elems(ob_plan plan) { return plan ? plan->block_elems : -1; }
+int64_t ob_plan_num_blocks(ob_plan plan) { return plan ? plan->t[T_COMPRESS].n_items : -1; }
+int64_t ob_plan_block_elems(ob_plan plan) { return plan ? plan->t[T_COMPRESS].block_elems : -1; }
 
 ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* m, float* v, float* p,
                               const ob_hparams* hp, hipStream_t stream)
@@ -309,7 +338,7 @@ ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, flo
     }
     DeviceGuard guard(plan->device);
     if (!guard.ok) return OB_ERR_HIP;
-    const ob::PlanDev pd = plan->dev();
+    const ob::PlanDev pd = plan->dev(T_DENSE);
     const int bf = g_dtype == OB_BF16;
     return timed(plan, OB_KERNEL_DENSE, stream, [&] { return ob::launch_dense(pd, g, bf, m, v, p, dp, stream); });
 }
@@ -341,10 +370,10 @@ ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, f
 
     DeviceGuard guard(plan->device);
     if (!guard.ok) return OB_ERR_HIP;
-    const ob::PlanDev pd = plan->dev();
+    const ob::PlanDev pd1 = plan->dev(T_PASS1), pd = plan->dev(T_COMPRESS);
     const int bf = g_dtype == OB_BF16;
     ob_status st = timed(plan, OB_KERNEL_CHUNK_SUMSQ, stream,
-                         [&] { return ob::launch_chunk_sumsq(pd, g, bf, err, cp.clip, stream); });
+                         [&] { return ob::launch_chunk_sumsq(pd1, g, bf, err, cp.clip, stream); });
     if (st != OB_OK) return st;
     return timed(plan, OB_KERNEL_COMPRESS, stream, [&] {
         return ob::launch_compress(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out,
@@ -365,9 +394,9 @@ ob_status ob_server_reduce(ob_plan plan, int32_t W, const uint32_t* worker_words
         return OB_ERR_ALIGN;
     DeviceGuard guard(plan->device);
     if (!guard.ok) return OB_ERR_HIP;
-    const ob::PlanDev pd = plan->dev();
+    const ob::PlanDev pd1 = plan->dev(T_PASS1), pd = plan->dev(T_SERVER);
     ob_status st = timed(plan, OB_KERNEL_SERVER_SUMSQ, stream, [&] {
-        return ob::launch_server_sumsq(pd, W, worker_words, worker_scales, server_err, stream);
+        return ob::launch_server_sumsq(pd1, W, worker_words, worker_scales, server_err, stream);
     });
     if (st != OB_OK) return st;
     return timed(plan, OB_KERNEL_SERVER_APPLY, stream, [&] {
@@ -399,7 +428,7 @@ ob_status ob_unpack(ob_plan plan, const uint32_t* words, int64_t n, const float*
     if (plan && scales) {
         DeviceGuard guard(plan->device);
         if (!guard.ok) return OB_ERR_HIP;
-        const ob::PlanDev pd = plan->dev();
+        const ob::PlanDev pd = plan->dev(T_SERVER);
         return timed(plan, OB_KERNEL_UNPACK, stream,
                      [&] { return ob::launch_unpack(&pd, words, n, scales, out, stream); });
     }

@@ -23,16 +23,36 @@ constexpr int kPlainItem = 16 * kTile;  // elements per block for the plan-less 
 #define OB_P1_UNROLL 4
 #endif
 #ifndef OB_P2_UNROLL
-#define OB_P2_UNROLL 2
+#define OB_P2_UNROLL 4
 #endif
 #ifndef OB_NT_P1
 #define OB_NT_P1 1
 #endif
 #ifndef OB_NT_P2
-#define OB_NT_P2 0
+#define OB_NT_P2 1
 #endif
 #ifndef OB_NT_ST
-#define OB_NT_ST 0
+#define OB_NT_ST 1
+#endif
+//   OB_NT_SRV                     nontemporal loads in server pass 1
+//   OB_NT_UNPACK                  nontemporal stores in unpack
+//   OB_NT_DENSE                   nontemporal loads and stores in the dense step
+#ifndef OB_NT_SRV
+#define OB_NT_SRV 1
+#endif
+#ifndef OB_NT_UNPACK
+#define OB_NT_UNPACK 1
+#endif
+#ifndef OB_NT_DENSE
+#define OB_NT_DENSE 1
+#endif
+//   OB_NT_SRV2                    nontemporal loads and stores in server pass 2
+//   OB_NT_BITS                    nontemporal stores of packed words and int8 signs
+#ifndef OB_NT_SRV2
+#define OB_NT_SRV2 0
+#endif
+#ifndef OB_NT_BITS
+#define OB_NT_BITS 0
 #endif
 
 // ------------------------------------------------------------------------------------------------
@@ -149,7 +169,12 @@ template <class I>
 __device__ __forceinline__ void store_word(uint32_t* __restrict__ words, I i, uint32_t nib, bool valid)
 {
     const uint32_t w = or8(nib << (4 * (threadIdx.x & 7)));
-    if ((threadIdx.x & 7) == 0 && valid) words[i >> 5] = w;
+    if ((threadIdx.x & 7) == 0 && valid) {
+        if (OB_NT_BITS)
+            __builtin_nontemporal_store(w, words + (i >> 5));
+        else
+            words[i >> 5] = w;
+    }
 }
 
 __device__ __forceinline__ uint32_t signs4(uint32_t nib)
@@ -194,10 +219,11 @@ __device__ __forceinline__ uint32_t compress_elem(float x, float& e, float& mm, 
     return b ? 1u : 0u;
 }
 
-// Chunk scale from the chunk's block partials, reduced in a fixed order.
+// Chunk scale from the chunk's pass-1 partials, reduced in a fixed order (so every pass-2 block of
+// the chunk computes the same bits).
 __device__ __forceinline__ float chunk_scale(const PlanDev& pd, int c, double* lds)
 {
-    const int f0 = pd.chunk_first[c], f1 = pd.chunk_first[c + 1];
+    const int f0 = pd.p1_first[c], f1 = pd.p1_first[c + 1];
     double s = 0.0;
     for (int i = f0 + static_cast<int>(threadIdx.x); i < f1; i += kBlock) s += pd.partials[i];
     s = block_sum(s, lds);

@@ -21,19 +21,21 @@ struct Item {
     int32_t chunk;
 };
 
-// Device-side view of a plan.
+// Device-side view of a plan for one launch.  Pass-1 kernels (sums of squares) and pass-2 kernels
+// (everything that needs a chunk's scale, and the dense step) use different block tables: pass 1
+// takes large blocks so that a chunk has few partial sums, pass 2 small blocks; a pass-2 block
+// forms its chunk's scale from the pass-1 partials.
 struct PlanDev {
-    const Item* items;          // [n_items]
-    const int32_t* chunk_first; // [K + 1]: blocks of chunk c are [chunk_first[c], chunk_first[c+1])
+    const Item* items;          // [n_items] blocks of this launch
+    const int32_t* chunk_first; // [K + 1]: blocks of chunk c in `items` are [chunk_first[c], chunk_first[c+1])
+    const int32_t* p1_first;    // [K + 1]: the same for the pass-1 table (indexes `partials`)
     const int64_t* chunk_off;   // [K + 1]: element offsets
-    double* partials;           // [n_items]: per-block sum of squares (workspace)
+    double* partials;           // [pass-1 blocks]: per-block sum of squares (workspace)
     int64_t n;
     int64_t n_items;
     int32_t K;
 };
 
-// Hyperparameters widened to double: each state line is evaluated in double from fp32 operands and
-// rounded once to fp32 when stored (1 - beta is exact in double for beta in [0.5, 1]).
 struct CompressParams {
     double lr, beta1, one_m_beta1, eps, ef_beta, one_m_ef_beta;
     float clip;

@@ -130,7 +130,13 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
             st4<OB_NT_ST>(err, i, ev[u]);
             st4<OB_NT_ST>(m, i, mv[u]);
             st4<OB_NT_ST>(p, i, pv[u]);
-            if (SIGNS) *reinterpret_cast<uint32_t*>(signs + i) = signs4(nib);
+            if (SIGNS) {
+                uint32_t* sp = reinterpret_cast<uint32_t*>(signs + i);
+                if (OB_NT_BITS)
+                    __builtin_nontemporal_store(signs4(nib), sp);
+                else
+                    *sp = signs4(nib);
+            }
             store_word(words, i, nib, true);
         }
     }
@@ -213,10 +219,10 @@ __global__ __launch_bounds__(kBlock) void k_dense(PlanDev pd, const typename G::
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = it.start + base + u * kTile + kVec * tid;
-            gv[u] = G::load4(g, i);
-            mv[u] = ld4(m, i);
-            vv[u] = ld4(v, i);
-            pv[u] = ld4(p, i);
+            gv[u] = G::template load4<OB_NT_DENSE>(g, i);
+            mv[u] = ld4<OB_NT_DENSE>(m, i);
+            vv[u] = ld4<OB_NT_DENSE>(v, i);
+            pv[u] = ld4<OB_NT_DENSE>(p, i);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -229,9 +235,9 @@ __global__ __launch_bounds__(kBlock) void k_dense(PlanDev pd, const typename G::
                 vv[u][k] = vq;
                 pv[u][k] = pp;
             }
-            st4(m, i, mv[u]);
-            st4(v, i, vv[u]);
-            st4(p, i, pv[u]);
+            st4<OB_NT_DENSE>(m, i, mv[u]);
+            st4<OB_NT_DENSE>(v, i, vv[u]);
+            st4<OB_NT_DENSE>(p, i, pv[u]);
         }
     }
     for (; base < it.len; base += kTile) {
@@ -383,7 +389,7 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
         if (cnt > 0) {
             // the error and worker loads are all issued before any of them is used
             f4 ev = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (cnt >= kVec) ev = ld4(e, i);
+            if (cnt >= kVec) ev = ld4 < (!APPLY && OB_NT_SRV) || (APPLY && OB_NT_SRV2) > (e, i);
             f4 avg;
             if (tabulate) {
                 uint32_t nb[kWorkerBatch];
@@ -393,7 +399,9 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
 #pragma unroll
                 for (int w = 0; w < kWorkerBatch; ++w) {
                     const int wc = w < W ? w : W - 1;
-                    nb[w] = (ww[static_cast<int64_t>(wc) * nw + wi] >> sh) & (w < W ? 0xFu : 0u);
+                    const uint32_t* wp = ww + static_cast<int64_t>(wc) * nw + wi;
+                    const uint32_t word = ((!APPLY && OB_NT_SRV) || (APPLY && OB_NT_SRV2)) ? __builtin_nontemporal_load(wp) : *wp;
+                    nb[w] = (word >> sh) & (w < W ? 0xFu : 0u);
                 }
                 const uint32_t pats = patterns4(nb);
 #pragma unroll
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
                         ev[k] = x[k] - (b ? scale : -scale);
                         nib |= (b ? 1u : 0u) << k;
                     }
-                    st4(e, i, ev);
+                    st4<OB_NT_SRV2>(e, i, ev);
                 } else {
 #pragma unroll
                     for (int k = 0; k < kVec; ++k) acc = fma(static_cast<double>(x[k]), static_cast<double>(x[k]), acc);
@@ -470,7 +478,7 @@ __global__ __launch_bounds__(kBlock) void k_unpack(const Item* __restrict__ item
 #pragma unroll
         for (int k = 0; k < kVec; ++k) r[k] = ((bits >> k) & 1u) ? s : -s;
         if (cnt >= kVec) {
-            st4(out, i, r);
+            st4<OB_NT_UNPACK>(out, i, r);
         } else {
             #pragma unroll
             for (int k = 0; k < kVec; ++k)

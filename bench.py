@@ -11,6 +11,9 @@ Inputs are synthetic and resident in HBM before timing starts: a ring of up to 4
 Other modes:
   --rocprof-summary DIR   summarise rocprofv3 CSV output found under DIR (kernel stats, and
                           FETCH_SIZE / WRITE_SIZE counters per dispatch) as markdown on stdout.
+  --traffic-profile DIR   from the FETCH_SIZE and WRITE_SIZE runs under DIR (made with
+                          --copy-probe-mib 1024), write the calibrated HBM traffic of --kernel on
+                          --workload as markdown on stdout (the profiles/traffic_*.md format).
 """
 from __future__ import annotations
 
@@ -247,10 +250,15 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain torch copy of this many MiB (counter calibration)")
     ap.add_argument("--rocprof-summary", metavar="DIR")
+    ap.add_argument("--traffic-profile", metavar="DIR")
+    ap.add_argument("--kernel", default="compress")
     args = ap.parse_args()
 
     if args.rocprof_summary:
         print(rocprof_summary(args.rocprof_summary))
+        return 0
+    if args.traffic_profile:
+        print(traffic_profile(args.traffic_profile, args.kernel, args.workload))
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -275,6 +283,63 @@ def _short(name: str) -> str:
             tmpl = name.split(key, 1)[1]
             return key + (tmpl[:60] if tmpl else "")
     return name[:80]
+
+
+KERNEL_SYMBOL = {"compress": "k_compress<", "chunk_sumsq": "k_chunk_sumsq<", "dense": "k_dense<",
+                 "server_sumsq": "k_server<false>", "server_apply": "k_server<true>", "unpack": "k_unpack"}
+
+
+def _counter_rows(d: str, counter: str):
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                yield r
+
+
+def traffic_profile(d: str, kernel: str, workload: str) -> str:
+    """Calibrated HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE runs under d."""
+    from adam_ob_compress_amd import synth
+
+    w = synth.WORKLOADS[workload]
+    probe_kib = 1 << 20  # the --copy-probe-mib 1024 copy reads and writes 1 GiB each
+    res = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = list(_counter_rows(d, counter))
+        # the probe is the run's last 8 copy dispatches of grid 131072 (3 warm-up + 5 timed copies)
+        copies = sorted((r for r in rows if "copyBuffer" in r["Kernel_Name"] and r["Grid_Size"] == "131072"),
+                        key=lambda r: int(r["Dispatch_Id"]))
+        probe = [float(r["Counter_Value"]) for r in copies[-8:]]
+        kern = [float(r["Counter_Value"]) for r in rows if KERNEL_SYMBOL[kernel] in r["Kernel_Name"]]
+        if not probe or not kern:
+            raise SystemExit(f"no {counter} rows for the copy probe or {kernel} under {d}")
+        res[counter] = (sum(kern) / len(kern), len(kern), sum(probe) / len(probe) / probe_kib)
+    (fk, fn, ff), (wk, wn, wf) = res["FETCH_SIZE"], res["WRITE_SIZE"]
+    traffic = (fk / ff + wk / wf) * 1024
+    alg = bytes_per_elem(w, kernel) * w.n
+    rec = {"kernel": kernel, "workload": w.name, "kernel_src_sha": kernel_source_sha(),
+           "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+           "fetch_factor": round(ff, 5), "write_factor": round(wf, 5), "bytes_per_launch": round(traffic),
+           "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 4)}
+    return f"""# HBM traffic of `{kernel}` on {w.name}
+
+Kernel source sha (ob_kernels.hip, ob_device.h, ob_internal.h): {rec['kernel_src_sha']}.
+
+Commands (each its own run on one MI355X, from the repository root, `export TMPDIR=/tmp`):
+
+    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o run --output-format csv -- python bench.py --workload {w.name} --steps 5 --warmup 2 --no-cpu --copy-probe-mib 1024
+    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o run --output-format csv -- python bench.py --workload {w.name} --steps 5 --warmup 2 --no-cpu --copy-probe-mib 1024
+    python bench.py --traffic-profile gpurun_out --kernel {kernel} --workload {w.name}
+
+Calibration: the run also copies 1 GiB with torch (`__amd_rocclr_copyBuffer`, grid 131072), which
+reads and writes 1,048,576 KiB.  The counters read {ff * probe_kib:,.1f} KiB (FETCH_SIZE) and
+{wf * probe_kib:,.1f} KiB (WRITE_SIZE) per such dispatch: fetch factor {ff:.5f}, write factor {wf:.5f}.
+
+| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/launch (calibrated) | algorithmic bytes/launch | ratio |
+|---|---|---|---|---|---|---|
+| {kernel} | {fn} / {wn} | {fk:,.1f} | {wk:,.1f} | {traffic:,.0f} | {alg:,.0f} ({bytes_per_elem(w, kernel)} B x n) | {traffic / alg:.4f} |
+
+traffic-json: {json.dumps(rec)}
+"""
 
 
 def rocprof_summary(d: str) -> str:
