@@ -58,8 +58,10 @@ def _load():
     I = ctypes.c_int
     lib.or_pack.argtypes = [P, I, I64, P]
     lib.or_unpack.argtypes = [P, I64, I64, P, P, P]
-    lib.or_compress_step.argtypes = [I64, I64, P, P, I, P, P, P, P, P, P, P, P,
+    lib.or_compress_step.argtypes = [I64, I64, P, P, I, P, I, P, P, P, P, P, P, P,
                                      F, F, F, F, I, F]
+    lib.or_to_format.argtypes = [P, I64, I, P]
+    lib.or_from_format.argtypes = [P, I64, I, P]
     lib.or_warmup_step.argtypes = [I64, P, I, P, P, P, F, F, F, F, I, I64]
     lib.or_server_reduce.argtypes = [I64, I64, P, I, P, P, P, P, P]
     lib.or_server_average.argtypes = [I64, I64, P, I, P, P, P]
@@ -68,7 +70,7 @@ def _load():
     lib.or_chunk_scale.argtypes = [P, I64, I64]
     lib.or_chunk_scale.restype = ctypes.c_float
     for name in ("or_pack", "or_unpack", "or_compress_step", "or_warmup_step",
-                 "or_server_reduce", "or_server_average"):
+                 "or_server_reduce", "or_server_average", "or_to_format", "or_from_format"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -93,6 +95,38 @@ def _grad(g):
     if g.dtype == np.uint16:
         return g, 1
     raise TypeError(f"gradient must be float32 or uint16 (bf16 bits), got {g.dtype}")
+
+
+# Storage formats of the error buffer (reading R15 in ob_oracle.c).  fp16 travels as numpy float16,
+# bf16 as its raw uint16 bit patterns.
+ERR_FORMATS = {"f32": 0, "bf16": 1, "f16": 2}
+
+
+def _err(e):
+    """Return (array, format code) of an error buffer: float32, float16, or uint16 (bf16 bits)."""
+    if e.dtype == np.float32:
+        return e, 0
+    if e.dtype == np.uint16:
+        return e, 1
+    if e.dtype == np.float16:
+        return e, 2
+    raise TypeError(f"error buffer must be float32, float16 or uint16 (bf16 bits), got {e.dtype}")
+
+
+def to_format(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Round fp32 values to "bf16" (uint16 bits) or "f16" (float16), nearest, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = np.zeros(x.size, dtype=np.uint16)
+    _check(_load().or_to_format(_ptr(x), x.size, ERR_FORMATS[fmt], _ptr(bits)), "to_format")
+    return bits.view(np.float16) if fmt == "f16" else bits
+
+
+def from_format(bits: np.ndarray, fmt: str) -> np.ndarray:
+    """Widen "bf16" bits (uint16) or "f16" values (float16 or their uint16 bits) to fp32, exactly."""
+    bits = np.ascontiguousarray(bits).view(np.uint16)
+    out = np.zeros(bits.size, dtype=np.float32)
+    _check(_load().or_from_format(_ptr(bits), bits.size, ERR_FORMATS[fmt], _ptr(out)), "from_format")
+    return out
 
 
 # ----------------------------------------------------------------------------------------------
@@ -141,20 +175,23 @@ def chunk_scale(x: np.ndarray, begin: int, end: int) -> float:
 
 def compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef_mode=0, ef_beta=0.9,
                   want_signs=False, count_nonfinite=False):
-    """One compressed step.  err, m, p are updated in place (fp32); v is read only.
+    """One compressed step.  err, m, p are updated in place; v is read only.  m, v, p are fp32; the
+    error buffer is fp32, fp16 (numpy float16) or bf16 (uint16 bits), see R15.
 
     Returns (words uint32[ceil(n/32)], scales fp32[K], signs int8[n] or None, nonfinite int or None).
     """
     g, bf = _grad(np.ascontiguousarray(g))
     n = g.size
-    for a in (err, m, v, p):
+    err, efmt = _err(err)
+    assert err.size == n and err.flags["C_CONTIGUOUS"]
+    for a in (m, v, p):
         assert a.dtype == np.float32 and a.size == n and a.flags["C_CONTIGUOUS"]
     k = offsets.size - 1
     words = np.zeros(n_words(n), dtype=np.uint32)
     scales = np.zeros(max(k, 0), dtype=np.float32)
     signs = np.zeros(n, dtype=np.int8) if want_signs else None
     nf = np.zeros(1, dtype=np.int64) if count_nonfinite else None
-    rc = _load().or_compress_step(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), _ptr(m), _ptr(v),
+    rc = _load().or_compress_step(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m), _ptr(v),
                                   _ptr(p), _ptr(words), _ptr(scales), _ptr(signs), _ptr(nf),
                                   lr, beta1, eps, clip, ef_mode, ef_beta)
     _check(rc, "compress_step")

@@ -41,6 +41,12 @@
  *   R8 the NaN check of [P1] sec. 3.2 counts non-finite new-error elements; it changes nothing.
  *   R9 server: avg_i = sum_w (+/- s_{w,c}) / W, summed in double over w = 0..W-1 and rounded once
  *      to fp32; x = fl32(avg + e_srv); then the same scale/pack/plain error as the worker.
+ *   R15 error storage ([P3] Q&A on the memory cost of error feedback, which suggests keeping the
+ *      fp32 error term in a 16-bit format such as FP16): the error buffer may be held as fp32, bf16
+ *      or fp16.  A stored value is widened exactly when read; the new error is computed in fp32 as
+ *      in R4/R6 and then rounded to the storage format to nearest, ties to even (IEEE 754's default
+ *      rounding), overflowing to +-Inf.  The R8 check counts non-finite STORED values, so an fp16
+ *      overflow is reported.
  */
 #include <math.h>
 #include <stdint.h>
@@ -69,10 +75,114 @@ static float load_grad(const void* g, int g_is_bf16, int64_t i)
     return ((const float*)g)[i];
 }
 
+/* ---------- R15: storage formats of the error buffer ---------- */
+
+#define OR_FMT_F32 0
+#define OR_FMT_BF16 1
+#define OR_FMT_F16 2
+
+/* Nearest value of a binary floating-point format with `prec` significand bits (the implicit bit
+ * included), smallest normal exponent emin and largest finite value maxf, ties to even; a result
+ * beyond maxf becomes +-Inf.  x is an fp32 value, so every step below is exact in double. */
+static double round_to_format(double x, int prec, int emin, double maxf)
+{
+    if (isnan(x) || isinf(x)) return x;
+    double a = fabs(x);
+    int e;
+    frexp(a, &e);                 /* a in [2^(e-1), 2^e) */
+    int E = e - 1;
+    if (a == 0.0 || E < emin) E = emin;   /* subnormals: the quantum of the lowest normal binade */
+    double q = ldexp(1.0, E - (prec - 1));
+    double r = nearbyint(a / q) * q;      /* default rounding mode: nearest, ties to even */
+    if (r > maxf) r = INFINITY;
+    return copysign(r, x);
+}
+
+#define BF16_MAXF ((2.0 - ldexp(1.0, -7)) * ldexp(1.0, 127))
+#define F16_MAXF 65504.0
+
+/* bf16 bits of a value of the bf16 format: bf16 values are fp32 values whose low 16 bits are 0. */
+static uint16_t bf16_bits_of(double r)
+{
+    if (isnan(r)) return (uint16_t)(signbit(r) ? 0xFFC0u : 0x7FC0u);
+    float f = (float)r;           /* exact */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* fp16 (IEEE binary16) bits of a value of the fp16 format: 1 sign, 5 exponent (bias 15), 10 bits. */
+static uint16_t f16_bits_of(double r)
+{
+    uint16_t s = signbit(r) ? 0x8000u : 0u;
+    if (isnan(r)) return (uint16_t)(s | 0x7E00u);
+    if (isinf(r)) return (uint16_t)(s | 0x7C00u);
+    double a = fabs(r);
+    if (a < ldexp(1.0, -14)) return (uint16_t)(s | (uint16_t)ldexp(a, 24));   /* zero, subnormal */
+    int e;
+    frexp(a, &e);
+    int E = e - 1;
+    return (uint16_t)(s | (uint16_t)((E + 15) << 10) | (uint16_t)(ldexp(a, 10 - E) - 1024.0));
+}
+
+static float f16_bits_to_float(uint16_t h)
+{
+    int ex = (h >> 10) & 0x1F, mant = h & 0x3FF;
+    double v;
+    if (ex == 0x1F)
+        v = mant ? NAN : INFINITY;
+    else if (ex == 0)
+        v = ldexp((double)mant, -24);
+    else
+        v = ldexp((double)(mant + 1024), ex - 25);
+    return (float)((h & 0x8000u) ? -v : v);
+}
+
 /* R2: the sign decision, made on the fp32 compensated value. */
 static int sign_bit(float x)
 {
     return x >= 0.0f ? 1 : 0;
+}
+
+/* Element i of an error buffer in format fmt, widened exactly to fp32. */
+static float load_err(const void* buf, int fmt, int64_t i)
+{
+    if (fmt == OR_FMT_BF16) return bf16_bits_to_float(((const uint16_t*)buf)[i]);
+    if (fmt == OR_FMT_F16) return f16_bits_to_float(((const uint16_t*)buf)[i]);
+    return ((const float*)buf)[i];
+}
+
+/* Store e (fp32) as element i of an error buffer in format fmt; returns the stored value, widened. */
+static float store_err(void* buf, int fmt, int64_t i, float e)
+{
+    if (fmt == OR_FMT_BF16) {
+        uint16_t b = bf16_bits_of(round_to_format(e, 8, -126, BF16_MAXF));
+        ((uint16_t*)buf)[i] = b;
+        return bf16_bits_to_float(b);
+    }
+    if (fmt == OR_FMT_F16) {
+        uint16_t h = f16_bits_of(round_to_format(e, 11, -14, F16_MAXF));
+        ((uint16_t*)buf)[i] = h;
+        return f16_bits_to_float(h);
+    }
+    ((float*)buf)[i] = e;
+    return e;
+}
+
+/* Narrow n fp32 values to a 16-bit error format (bits out), or widen bits back: exposed so the
+ * conversions can be checked on their own. */
+int or_to_format(const float* x, int64_t n, int fmt, uint16_t* bits)
+{
+    if (n < 0 || (fmt != OR_FMT_BF16 && fmt != OR_FMT_F16)) return 1;
+    for (int64_t i = 0; i < n; ++i) store_err(bits, fmt, i, x[i]);
+    return 0;
+}
+
+int or_from_format(const uint16_t* bits, int64_t n, int fmt, float* out)
+{
+    if (n < 0 || (fmt != OR_FMT_BF16 && fmt != OR_FMT_F16)) return 1;
+    for (int64_t i = 0; i < n; ++i) out[i] = load_err(bits, fmt, i);
+    return 0;
 }
 
 static int check_offsets(int64_t n, int64_t K, const int64_t* off)
@@ -140,16 +250,24 @@ int or_unpack(const uint32_t* words, int64_t n, int64_t K, const int64_t* off, c
 
 int or_compress_step(int64_t n, int64_t K, const int64_t* off,
                      const void* g, int g_is_bf16,
-                     float* err, float* m, const float* v, float* p,
+                     void* err_store, int err_fmt, float* m, const float* v, float* p,
                      uint32_t* words, float* scales, int8_t* signs, int64_t* nonfinite,
                      float lr, float beta1, float eps, float clip, int ef_mode, float ef_beta)
 {
     if (!check_offsets(n, K, off)) return OR_ERR_ARG;
+    if (err_fmt != OR_FMT_F32 && err_fmt != OR_FMT_BF16 && err_fmt != OR_FMT_F16) return OR_ERR_ARG;
     if (n == 0) return OR_OK;
-    if (!g || !err || !m || !v || !p || !words || !scales) return OR_ERR_ARG;
+    if (!g || !err_store || !m || !v || !p || !words || !scales) return OR_ERR_ARG;
 
     float* x = (float*)calloc((size_t)n, sizeof(float));
-    if (x == NULL) return OR_ERR_OOM;
+    float* err = (float*)calloc((size_t)n, sizeof(float));
+    if (x == NULL || err == NULL) {
+        free(x);
+        free(err);
+        return OR_ERR_OOM;
+    }
+    /* R15: the error as fp32 (exact widening of the stored values). */
+    for (int64_t i = 0; i < n; ++i) err[i] = load_err(err_store, err_fmt, i);
 
     /* compensated = grad (+clip, R7) + error, kept as an fp32 tensor (R4). */
     for (int64_t i = 0; i < n; ++i) {
@@ -190,10 +308,15 @@ int or_compress_step(int64_t n, int64_t K, const int64_t* off,
             p[i] = (float)((double)p[i] -
                            (double)lr * ((double)m[i] / (sqrt((double)v[i]) + (double)eps)));
             if (signs != NULL) signs[i] = (int8_t)(b ? 1 : -1);
-            if (nonfinite != NULL && !isfinite(e_new)) *nonfinite += 1;
         }
     }
+    /* R15: store the new error in its format; R8: count non-finite stored values. */
+    for (int64_t i = 0; i < n; ++i) {
+        float stored = store_err(err_store, err_fmt, i, err[i]);
+        if (nonfinite != NULL && !isfinite(stored)) *nonfinite += 1;
+    }
     free(x);
+    free(err);
     return OR_OK;
 }
 

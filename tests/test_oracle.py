@@ -9,7 +9,12 @@ Pins used (none retypes the oracle's formula):
     the EMA identity err_new - err_old == (1-beta)(g - g_hat), v untouched, chunk independence;
   * special cases: one-element chunk, constant magnitude, all-zero chunk, EMA with beta 0 == plain,
     clip 0 == off, W = 1 server idempotence, identical workers, cancellation;
-  * brute force over n = 1..130 with edge patterns (zeros of both signs, negative denormals, NaN, Inf).
+  * brute force over n = 1..130 with edge patterns (zeros of both signs, negative denormals, NaN, Inf);
+  * 16-bit error storage (R15): the narrowing against numpy's float32->float16 and torch's
+    float32->bfloat16 conversions (both round to nearest, ties to even) on every rounding boundary of
+    the two formats, the widening against the same libraries on all 65536 patterns, hand-derived
+    tie and overflow examples, and the reduction of a 16-bit-error step to the fp32 step followed by
+    the library rounding.
 """
 import math
 from fractions import Fraction
@@ -532,3 +537,124 @@ def test_invalid_arguments_rejected():
         oracle.compress_step(g, *s, np.asarray([0, 5], np.int64), **HP)        # does not end at n
     with pytest.raises(ValueError):
         oracle.compress_step(g, *s, np.asarray([0, 5, 5, 10], np.int64), **HP)  # empty chunk
+
+
+# ------------------------------------------------------------------------------------------------
+# R15: 16-bit storage of the error buffer
+# ------------------------------------------------------------------------------------------------
+
+def _lib_narrow(x32, fmt):
+    """Library rounding of fp32 to the format (numpy float16 / torch bfloat16), as uint16 bits."""
+    if fmt == "f16":
+        with np.errstate(over="ignore"):
+            return x32.astype(np.float16).view(np.uint16)
+    return torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _lib_widen(bits, fmt):
+    bits = np.asarray(bits).view(np.uint16)
+    if fmt == "f16":
+        return bits.view(np.float16).astype(np.float32)
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+
+
+def _boundary_sample(fmt):
+    """Every finite non-negative value of the format, every midpoint between neighbours (including
+    the overflow midpoint), one fp32 ulp either side of each, both signs, plus random fp32 patterns
+    and the special values."""
+    if fmt == "f16":
+        v = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+        top = 65536.0
+    else:
+        v = (np.arange(0, 0x7F80, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+        top = 2.0 ** 128
+    nxt = np.append(v[1:], top)
+    cand = np.concatenate([v, (v + nxt) / 2]).astype(np.float32)     # midpoints are exact in fp32
+    with np.errstate(over="ignore"):
+        s = np.concatenate([cand, np.nextafter(cand, np.float32(np.inf)),
+                            np.nextafter(cand, np.float32(-np.inf))])
+    rnd = np.random.default_rng(15).integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64)
+    rnd = rnd.astype(np.uint32).view(np.float32)
+    special = np.asarray([np.inf, -np.inf, np.nan, 0.0, -0.0, 3.4028235e38, -3.4028235e38, 1e-45],
+                         np.float32)
+    return np.concatenate([s, -s, rnd, special]).astype(np.float32)
+
+
+def _same_bits_or_nan(a_bits, b_bits, fmt):
+    wa, wb = _lib_widen(a_bits, fmt), _lib_widen(b_bits, fmt)
+    na, nb = np.isnan(wa), np.isnan(wb)
+    assert np.array_equal(na, nb)
+    assert np.array_equal(np.asarray(a_bits).view(np.uint16)[~na], np.asarray(b_bits).view(np.uint16)[~nb])
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_error_narrowing_matches_library_rounding(fmt):
+    x = _boundary_sample(fmt)
+    _same_bits_or_nan(oracle.to_format(x, fmt), _lib_narrow(x, fmt), fmt)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_error_widening_exhaustive(fmt):
+    bits = np.arange(0, 1 << 16, dtype=np.uint32).astype(np.uint16)
+    a = oracle.from_format(bits, fmt)
+    b = _lib_widen(bits, fmt)
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    fin = ~np.isnan(b)
+    assert np.array_equal(a[fin].view(np.uint32), b[fin].view(np.uint32))   # -0 keeps its sign
+
+
+def _err_buffer(values, fmt):
+    x = np.asarray(values, np.float32)
+    bits = _lib_narrow(x, fmt)
+    assert np.array_equal(_lib_widen(bits, fmt), x), "worked-example inputs must be exact"
+    return bits.view(np.float16).copy() if fmt == "f16" else bits.copy()
+
+
+@pytest.mark.parametrize("name", ["compress_f16_err_ties_overflow", "compress_bf16_err_ties",
+                                  "compress_bf16_err_ema_ties"])
+def test_worked_compress_16bit_error(golden, name):
+    case = golden[name]
+    fmt = case["err_format"]
+    g = _arr(case["g"])
+    m, v, p = (_arr(case[k]) for k in ("m", "v", "p"))
+    err = _err_buffer(case["err"], fmt)
+    off = np.asarray(case["offsets"], dtype=np.int64)
+    words, scales, signs, nf = oracle.compress_step(
+        g, err, m, v, p, off, lr=case["lr"], beta1=case["beta1"], eps=case["eps"], clip=case["clip"],
+        ef_mode=case["ef_mode"], ef_beta=case["ef_beta"], want_signs=True, count_nonfinite=True)
+    assert words.tolist() == case["expect_words"]
+    assert scales.tolist() == case["expect_scales"]
+    assert _lib_widen(err, fmt).tolist() == [float(e) for e in case["expect_err"]]
+    assert m.tolist() == case["expect_m"]
+    assert p.tolist() == case["expect_p"]
+    assert signs.tolist() == case["expect_signs"]
+    assert nf == case["expect_nonfinite"]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("ef_mode", [0, 1])
+def test_compress_16bit_error_is_fp32_step_then_rounding(fmt, ef_mode):
+    """R15 as a relation: a step on a 16-bit error buffer equals the fp32 step on its exact widening,
+    with the new error rounded by the library; the NaN check counts non-finite rounded values."""
+    n = 3 * 1024 + 77
+    off = oracle.uniform_offsets(n, 1024)
+    g, err32, m, v, p = _random_state(n, 16, sigma=1.0)
+    err32 *= 0.1
+    g[::97] *= 3e5                      # large enough that fp16 overflows
+    g[5] = np.nan
+    bits = _lib_narrow(err32, fmt)
+    err16 = bits.view(np.float16).copy() if fmt == "f16" else bits.copy()
+    e_ref = _lib_widen(bits, fmt)
+    m2, p2 = m.copy(), p.copy()
+    hp = dict(HP, ef_mode=ef_mode, ef_beta=0.9, want_signs=True, count_nonfinite=True)
+    wa, sa, ga, nfa = oracle.compress_step(g, err16, m, v, p, off, **hp)
+    wb, sb, gb, _ = oracle.compress_step(g, e_ref, m2, v, p2, off, **hp)
+    assert np.array_equal(wa, wb) and np.array_equal(ga, gb)
+    assert np.array_equal(sa.view(np.uint32), sb.view(np.uint32))
+    assert np.array_equal(m, m2, equal_nan=True)
+    assert np.array_equal(p, p2, equal_nan=True)
+    expect = _lib_narrow(e_ref, fmt)
+    _same_bits_or_nan(err16.view(np.uint16), expect, fmt)
+    assert nfa == int(np.sum(~np.isfinite(_lib_widen(expect, fmt))))
+    if fmt == "f16":
+        assert nfa > 1, "the fp16 case must exercise overflow to Inf"

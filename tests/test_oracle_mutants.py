@@ -45,7 +45,20 @@ MUTANTS = {
     "clip_lower_bound": ("gi = -c;", "gi = c;"),
     "gh_wrong_chunk": ("float gh = b ? scales[c] : -scales[c];",
                        "float gh = b ? scales[0] : -scales[0];"),
-    "nonfinite_nan_only": ("!isfinite(e_new)", "isnan(e_new)"),
+    "nonfinite_nan_only": ("!isfinite(stored)", "isnan(stored)"),
+    "nonfinite_counts_unrounded": ("!isfinite(stored)", "!isfinite(err[i])"),
+    "format_ties_away": ("nearbyint(a / q)", "round(a / q)"),
+    "format_truncates": ("nearbyint(a / q)", "trunc(a / q)"),
+    "overflow_saturates": ("if (r > maxf) r = INFINITY;", "if (r > maxf) r = maxf;"),
+    "f16_emin": ("round_to_format(e, 11, -14, F16_MAXF)", "round_to_format(e, 11, -15, F16_MAXF)"),
+    "f16_precision": ("round_to_format(e, 11, -14, F16_MAXF)", "round_to_format(e, 10, -14, F16_MAXF)"),
+    "bf16_precision": ("round_to_format(e, 8, -126, BF16_MAXF)", "round_to_format(e, 9, -126, BF16_MAXF)"),
+    "f16_decode_bias": ("v = ldexp((double)(mant + 1024), ex - 25);", "v = ldexp((double)(mant + 1024), ex - 24);"),
+    "f16_subnormal_decode": ("v = ldexp((double)mant, -24);", "v = ldexp((double)mant, -25);"),
+    "error_not_widened": ("for (int64_t i = 0; i < n; ++i) err[i] = load_err(err_store, err_fmt, i);",
+                          "for (int64_t i = 0; i < n; ++i) err[i] = 0.0f;"),
+    "error_stored_unrounded_bf16": ("uint16_t b = bf16_bits_of(round_to_format(e, 8, -126, BF16_MAXF));",
+                                    "uint16_t b = bf16_bits_of((double)(float)((double)e));"),
     "int8_zero_for_plus": ("signs[i] = (int8_t)(b ? 1 : -1);", "signs[i] = (int8_t)(b ? 0 : -1);"),
     "dense_v_not_squared": ("(1.0 - b2) * (gi * gi)", "(1.0 - b2) * gi"),
     "dense_v_uses_beta1": ("v[i] = (float)(b2 * (double)v[i]", "v[i] = (float)(b1 * (double)v[i]"),
