@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libobadam.so")
 
 OB_OK, OB_ERR_ARG, OB_ERR_ALIGN, OB_ERR_DTYPE, OB_ERR_HIP, OB_ERR_OOM = range(6)
-OB_F32, OB_BF16 = 0, 1
+OB_F32, OB_BF16, OB_F16 = 0, 1, 2
 OB_EF_PLAIN, OB_EF_EMA = 0, 1
 (OB_KERNEL_CHUNK_SUMSQ, OB_KERNEL_COMPRESS, OB_KERNEL_DENSE, OB_KERNEL_SERVER_SUMSQ,
  OB_KERNEL_SERVER_APPLY, OB_KERNEL_UNPACK) = range(6)
@@ -66,7 +66,7 @@ def lib() -> ctypes.CDLL:
         "ob_plan_num_blocks": (I64, [P]),
         "ob_plan_block_elems": (I64, [P]),
         "ob_adam_warmup_step": (I32, [P, P, I32, P, P, P, HP, P]),
-        "ob_adam_compress_step": (I32, [P, P, I32, P, P, P, P, P, P, P, P, HP, P]),
+        "ob_adam_compress_step": (I32, [P, P, I32, P, I32, P, P, P, P, P, P, P, HP, P]),
         "ob_server_reduce": (I32, [P, I32, P, P, P, P, P, P]),
         "ob_pack": (I32, [P, I32, I64, P, P]),
         "ob_unpack": (I32, [P, P, I64, P, P, P]),
@@ -119,6 +119,15 @@ def _gdtype(g: torch.Tensor) -> int:
     if g.dtype == torch.bfloat16:
         return OB_BF16
     raise TypeError(f"gradient dtype must be float32 or bfloat16, got {g.dtype}")
+
+
+_ERR_DTYPES = {torch.float32: OB_F32, torch.bfloat16: OB_BF16, torch.float16: OB_F16}
+
+
+def _errdtype(err: torch.Tensor) -> int:
+    if err.dtype not in _ERR_DTYPES:
+        raise TypeError(f"error buffer dtype must be float32, bfloat16 or float16, got {err.dtype}")
+    return _ERR_DTYPES[err.dtype]
 
 
 def _stream(stream):
@@ -184,14 +193,16 @@ def ob_adam_compress_step(plan: Plan, g, err, m, v, p, words_out, scales_out, hp
                           signs_out=None, nonfinite_out=None, stream=None):
     n = plan.n
     _want(g, "g", g.dtype, n)
-    for name, t in (("err", err), ("m", m), ("v", v), ("p", p)):
+    _want(err, "err", err.dtype, n)
+    for name, t in (("m", m), ("v", v), ("p", p)):
         _want(t, name, torch.float32, n)
     _want(words_out, "words_out", torch.int32, (n + 31) // 32)
     _want(scales_out, "scales_out", torch.float32, plan.num_chunks)
     _want(signs_out, "signs_out", torch.int8, n)
     _want(nonfinite_out, "nonfinite_out", torch.int64, 1)
     _check(lib().ob_adam_compress_step(
-        plan.handle, _dev(g, "g"), _gdtype(g), _dev(err, "err"), _dev(m, "m"), _dev(v, "v"), _dev(p, "p"),
+        plan.handle, _dev(g, "g"), _gdtype(g), _dev(err, "err"), _errdtype(err), _dev(m, "m"), _dev(v, "v"),
+        _dev(p, "p"),
         _dev(words_out, "words_out"), _dev(scales_out, "scales_out"), _dev(signs_out, "signs_out"),
         _dev(nonfinite_out, "nonfinite_out"), ctypes.byref(hp), _stream(stream)), "ob_adam_compress_step")
 

@@ -12,6 +12,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libobadam.so")
 # (source, extra defines): compiled to objects in parallel, then linked into one library
 UNITS = [
+    ("ob_compress.hip", ["-DOB_ERR_FMT=0"]),   # fp32 error buffer
+    ("ob_compress.hip", ["-DOB_ERR_FMT=1"]),   # bf16
+    ("ob_compress.hip", ["-DOB_ERR_FMT=2"]),   # fp16
     ("ob_kernels.hip", []),
     ("ob_api.cpp", []),
 ]

@@ -178,7 +178,10 @@ ob_status drain_timing(ob_plan p)
     return st;
 }
 
+// gradient / packed-input types
 bool valid_dtype(int d) { return d == OB_F32 || d == OB_BF16; }
+// error-buffer storage formats
+bool valid_err_dtype(int d) { return d == OB_F32 || d == OB_BF16 || d == OB_F16; }
 
 ob_status check_grad(const void* g, int dt)
 {
@@ -343,17 +346,18 @@ ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, flo
     return timed(plan, OB_KERNEL_DENSE, stream, [&] { return ob::launch_dense(pd, g, bf, m, v, p, dp, stream); });
 }
 
-ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* err, float* m,
-                                const float* v, float* p, uint32_t* words_out, float* scales_out,
+ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
+                                float* m, const float* v, float* p, uint32_t* words_out, float* scales_out,
                                 int8_t* signs_out, uint64_t* nonfinite_out, const ob_hparams* hp,
                                 hipStream_t stream)
 {
     if (!plan || !hp) return OB_ERR_ARG;
-    if (!valid_dtype(g_dtype)) return OB_ERR_DTYPE;
+    if (!valid_dtype(g_dtype) || !valid_err_dtype(err_dtype)) return OB_ERR_DTYPE;
     if (plan->n == 0) return OB_OK;
     if (ob_status st = check_grad(g, g_dtype)) return st;
     if (!err || !m || !v || !p || !words_out || !scales_out) return OB_ERR_ARG;
-    if (!aligned(err, 16) || !aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16)) return OB_ERR_ALIGN;
+    if (!aligned(err, err_dtype == OB_F32 ? 16 : 8)) return OB_ERR_ALIGN;
+    if (!aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16)) return OB_ERR_ALIGN;
     if (!aligned(words_out, 4) || !aligned(scales_out, 4)) return OB_ERR_ALIGN;
     if (signs_out && !aligned(signs_out, 4)) return OB_ERR_ALIGN;
     if (nonfinite_out && !aligned(nonfinite_out, 8)) return OB_ERR_ALIGN;
@@ -372,13 +376,28 @@ ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, f
     if (!guard.ok) return OB_ERR_HIP;
     const ob::PlanDev pd1 = plan->dev(T_PASS1), pd = plan->dev(T_COMPRESS);
     const int bf = g_dtype == OB_BF16;
-    ob_status st = timed(plan, OB_KERNEL_CHUNK_SUMSQ, stream,
-                         [&] { return ob::launch_chunk_sumsq(pd1, g, bf, err, cp.clip, stream); });
+    const int ema = hp->ef_mode == OB_EF_EMA;
+    auto nf = reinterpret_cast<unsigned long long*>(nonfinite_out);
+    ob_status st = timed(plan, OB_KERNEL_CHUNK_SUMSQ, stream, [&] {
+        switch (err_dtype) {
+        case OB_BF16: return ob::launch_chunk_sumsq<OB_BF16>(pd1, g, bf, err, cp.clip, stream);
+        case OB_F16: return ob::launch_chunk_sumsq<OB_F16>(pd1, g, bf, err, cp.clip, stream);
+        default: return ob::launch_chunk_sumsq<OB_F32>(pd1, g, bf, err, cp.clip, stream);
+        }
+    });
     if (st != OB_OK) return st;
     return timed(plan, OB_KERNEL_COMPRESS, stream, [&] {
-        return ob::launch_compress(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out,
-                                   reinterpret_cast<unsigned long long*>(nonfinite_out),
-                                   hp->ef_mode == OB_EF_EMA, cp, stream);
+        switch (err_dtype) {
+        case OB_BF16:
+            return ob::launch_compress<OB_BF16>(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf,
+                                                ema, cp, stream);
+        case OB_F16:
+            return ob::launch_compress<OB_F16>(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf,
+                                               ema, cp, stream);
+        default:
+            return ob::launch_compress<OB_F32>(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf,
+                                               ema, cp, stream);
+        }
     });
 }
 

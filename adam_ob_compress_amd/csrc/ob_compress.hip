@@ -1,0 +1,297 @@
+// ob_compress.hip -- the compressed step (pass 1: per-block sums of squares; pass 2: the fused
+// streaming update) for one storage format of the error buffer.  Built once per format with
+// -DOB_ERR_FMT=0 (fp32), 1 (bf16) or 2 (fp16); each build defines that format's launchers.
+//
+// Pages cited (title and section):
+//   [P1] "1bit Adam" tutorial (intelliparadigm.com article 2150495): sec. 2.1 (sign quantization and
+//        EMA error compensation), sec. 2.2 (first moment on the compressed gradient), sec. 3.2
+//        (clip before quantizing, NaN check, int8 signs).
+//   [P2] "DeepSpeed Communication Compression and Hiding": "1-bit Adam: warmup, frozen variance,
+//        error feedback" (compressed branch of the two-phase step, dequantize).
+//   [P3] gradient-compression survey (bmjup.com post 14450): Q&A on the memory cost of error
+//        feedback (a 16-bit error term).
+//
+// Design (memory bound: ~30 bytes and a few dozen ALU ops per element, no dense contraction, so no
+// MFMA):
+//   * every kernel walks work blocks ("items") of one chunk each; a block of 256 threads = four
+//     wave64s; each lane owns 4 consecutive elements per 1024-element tile, so each fp32 array moves
+//     as one 16-byte access per lane (8 bytes for 16-bit arrays) and a wave covers a contiguous run;
+//   * the per-chunk scale needs the whole chunk before any element can be finished, hence two
+//     passes: pass 1 writes one double partial sum of squares per block (wave butterfly in registers,
+//     LDS across the four waves); pass 2 reduces the chunk's partials in a fixed order at its start
+//     (every block of the chunk gets bit-identical scales), then does the fused streaming update;
+//   * sign bits: each lane forms a 4-bit nibble; an OR across 8 neighbouring lanes with DPP row
+//     permutes (no LDS) builds the 32-bit word of 32 consecutive elements, written by one lane;
+//   * all fp32 arithmetic is plain IEEE (no fast-math, denormals kept: a negative denormal must give
+//     sign -1).
+#include "ob_device.h"
+
+#ifndef OB_ERR_FMT
+#error "build with -DOB_ERR_FMT=0 (fp32), 1 (bf16) or 2 (fp16)"
+#endif
+
+namespace ob {
+namespace {
+
+// ------------------------------------------------------------------------------------------------
+// compressed step, pass 1: per-block sum of squares of x = clip(g) + err
+// ------------------------------------------------------------------------------------------------
+
+template <class G, class E, bool CLIP>
+__global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typename G::T* __restrict__ g,
+                                                        const typename E::T* __restrict__ err, float clip)
+{
+    __shared__ double lds[kBlock / 64];
+    const Item it = pd.items[blockIdx.x];
+    const int tid = threadIdx.x;
+    double acc = 0.0;
+    constexpr int U = OB_P1_UNROLL;
+    int base = 0;
+    for (; base + U * kTile <= it.len; base += U * kTile) {
+        f4 gv[U], ev[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            gv[u] = G::template load4<OB_NT_P1>(g, i);
+            ev[u] = E::template load4<OB_NT_P1>(err, i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                const double x = compensate<CLIP>(gv[u][k], ev[u][k], clip);
+                acc = fma(x, x, acc);
+            }
+        }
+    }
+    for (; base < it.len; base += kTile) {
+        const int cnt = it.len - base - kVec * tid;
+        const int64_t i = it.start + base + kVec * tid;
+        if (cnt >= kVec) {
+            const f4 gv = G::load4(g, i), ev = E::load4(err, i);
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                const double x = compensate<CLIP>(gv[k], ev[k], clip);
+                acc = fma(x, x, acc);
+            }
+        } else {
+            #pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                if (k >= cnt) continue;
+                const double x = compensate<CLIP>(G::load1(g, i + k), E::load1(err, i + k), clip);
+                acc = fma(x, x, acc);
+            }
+        }
+    }
+    const double s = block_sum(acc, lds);
+    if (tid == 0) pd.partials[blockIdx.x] = s;
+}
+
+// ------------------------------------------------------------------------------------------------
+// compressed step, pass 2: scale, sign bits, error, m, p in one streaming pass
+// ------------------------------------------------------------------------------------------------
+
+template <class G, class E, bool CLIP, bool EMA, bool SIGNS, bool NONFIN>
+__global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename G::T* __restrict__ g,
+                                                     typename E::T* __restrict__ err, float* __restrict__ m,
+                                                     const float* __restrict__ v, float* __restrict__ p,
+                                                     uint32_t* __restrict__ words, float* __restrict__ scales,
+                                                     int8_t* __restrict__ signs,
+                                                     unsigned long long* __restrict__ nonfinite,
+                                                     CompressParams cp)
+{
+    __shared__ double lds[kBlock / 64];
+    const Item it = pd.items[blockIdx.x];
+    const int tid = threadIdx.x;
+    const float scale = chunk_scale(pd, it.chunk, lds);
+    if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
+
+    uint32_t nf = 0;
+    constexpr int U = OB_P2_UNROLL;
+    int base = 0;
+    for (; base + U * kTile <= it.len; base += U * kTile) {
+        f4 gv[U], ev[U], mv[U], vv[U], pv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            gv[u] = G::template load4<OB_NT_P2>(g, i);
+            ev[u] = E::template load4<OB_NT_P2>(err, i);
+            mv[u] = ld4<OB_NT_P2>(m, i);
+            vv[u] = ld4<OB_NT_P2>(v, i);
+            pv[u] = ld4<OB_NT_P2>(p, i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            uint32_t nib = 0;
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                const float x = compensate<CLIP>(gv[u][k], ev[u][k], cp.clip);
+                float e = ev[u][k], mm = mv[u][k], pp = pv[u][k];
+                nib |= compress_elem<EMA>(x, e, mm, vv[u][k], pp, scale, cp) << k;
+                e = E::rounded(e);
+                ev[u][k] = e;
+                mv[u][k] = mm;
+                pv[u][k] = pp;
+                if (NONFIN) nf += __builtin_isfinite(e) ? 0u : 1u;
+            }
+            E::template store4<OB_NT_ST>(err, i, ev[u]);
+            st4<OB_NT_ST>(m, i, mv[u]);
+            st4<OB_NT_ST>(p, i, pv[u]);
+            if (SIGNS) {
+                uint32_t* sp = reinterpret_cast<uint32_t*>(signs + i);
+                if (OB_NT_BITS)
+                    __builtin_nontemporal_store(signs4(nib), sp);
+                else
+                    *sp = signs4(nib);
+            }
+            store_word(words, i, nib, true);
+        }
+    }
+    for (; base < it.len; base += kTile) {
+        const int rem = it.len - base;
+        const int cnt = rem - kVec * tid;
+        const int64_t i = it.start + base + kVec * tid;
+        uint32_t nib = 0;
+        if (cnt >= kVec) {
+            const f4 gv = G::load4(g, i), vv = ld4(v, i);
+            f4 ev = E::load4(err, i), mv = ld4(m, i), pv = ld4(p, i);
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                const float x = compensate<CLIP>(gv[k], ev[k], cp.clip);
+                float e = ev[k], mm = mv[k], pp = pv[k];
+                nib |= compress_elem<EMA>(x, e, mm, vv[k], pp, scale, cp) << k;
+                e = E::rounded(e);
+                ev[k] = e;
+                mv[k] = mm;
+                pv[k] = pp;
+                if (NONFIN) nf += __builtin_isfinite(e) ? 0u : 1u;
+            }
+            E::store4(err, i, ev);
+            st4(m, i, mv);
+            st4(p, i, pv);
+            if (SIGNS) *reinterpret_cast<uint32_t*>(signs + i) = signs4(nib);
+        } else if (cnt > 0) {
+            #pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                if (k >= cnt) continue;
+                float e = E::load1(err, i + k), mm = m[i + k], pp = p[i + k];
+                const float x = compensate<CLIP>(G::load1(g, i + k), e, cp.clip);
+                const uint32_t b = compress_elem<EMA>(x, e, mm, v[i + k], pp, scale, cp);
+                nib |= b << k;
+                e = E::rounded(e);
+                E::store1(err, i + k, e);
+                m[i + k] = mm;
+                p[i + k] = pp;
+                if (SIGNS) signs[i + k] = b ? int8_t(1) : int8_t(-1);
+                if (NONFIN) nf += __builtin_isfinite(e) ? 0u : 1u;
+            }
+        }
+        store_word(words, i, nib, 32 * (tid >> 3) < rem);
+    }
+    if (NONFIN) {
+        __shared__ uint32_t ldsu[kBlock / 64];
+        const uint32_t t = block_sum_u32(nf, ldsu);
+        if (tid == 0 && t) atomicAdd(nonfinite, static_cast<unsigned long long>(t));
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------------------
+
+template <int EF>
+hipError_t launch_chunk_sumsq(const PlanDev& pd, const void* g, int g_bf16, const void* err_v, float clip,
+                              hipStream_t s)
+{
+    using E = typename ErrOf<EF>::type;
+    auto err = static_cast<const typename E::T*>(err_v);
+    const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
+    const bool cl = clip > 0.0f;
+    if (g_bf16) {
+        auto gp = static_cast<const uint16_t*>(g);
+        if (cl)
+            hipLaunchKernelGGL((k_chunk_sumsq<GradBF16, E, true>), grid, block, 0, s, pd, gp, err, clip);
+        else
+            hipLaunchKernelGGL((k_chunk_sumsq<GradBF16, E, false>), grid, block, 0, s, pd, gp, err, clip);
+    } else {
+        auto gp = static_cast<const float*>(g);
+        if (cl)
+            hipLaunchKernelGGL((k_chunk_sumsq<GradF32, E, true>), grid, block, 0, s, pd, gp, err, clip);
+        else
+            hipLaunchKernelGGL((k_chunk_sumsq<GradF32, E, false>), grid, block, 0, s, pd, gp, err, clip);
+    }
+    return hipGetLastError();
+}
+
+namespace {
+template <class G, class E, bool CLIP, bool EMA>
+void compress_dispatch(const PlanDev& pd, const typename G::T* g, typename E::T* err, float* m, const float* v,
+                       float* p, uint32_t* words, float* scales, int8_t* signs,
+                       unsigned long long* nonfinite, const CompressParams& cp, hipStream_t s)
+{
+    const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
+    const int sel = (signs ? 1 : 0) | (nonfinite ? 2 : 0);
+    switch (sel) {
+    case 0:
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, false, false>), grid, block, 0, s, pd, g, err, m, v,
+                           p, words, scales, signs, nonfinite, cp);
+        break;
+    case 1:
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, true, false>), grid, block, 0, s, pd, g, err, m, v,
+                           p, words, scales, signs, nonfinite, cp);
+        break;
+    case 2:
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, false, true>), grid, block, 0, s, pd, g, err, m, v,
+                           p, words, scales, signs, nonfinite, cp);
+        break;
+    default:
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, true, true>), grid, block, 0, s, pd, g, err, m, v,
+                           p, words, scales, signs, nonfinite, cp);
+        break;
+    }
+}
+
+template <class G, class E>
+void compress_dispatch_g(const PlanDev& pd, const typename G::T* g, typename E::T* err, float* m, const float* v,
+                         float* p, uint32_t* words, float* scales, int8_t* signs,
+                         unsigned long long* nonfinite, int ema, const CompressParams& cp, hipStream_t s)
+{
+    const bool cl = cp.clip > 0.0f;
+    if (cl && ema)
+        compress_dispatch<G, E, true, true>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
+    else if (cl)
+        compress_dispatch<G, E, true, false>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
+    else if (ema)
+        compress_dispatch<G, E, false, true>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
+    else
+        compress_dispatch<G, E, false, false>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
+}
+}  // namespace
+
+template <int EF>
+hipError_t launch_compress(const PlanDev& pd, const void* g, int g_bf16, void* err_v, float* m, const float* v,
+                           float* p, uint32_t* words, float* scales, int8_t* signs,
+                           unsigned long long* nonfinite, int ema, const CompressParams& cp, hipStream_t s)
+{
+    using E = typename ErrOf<EF>::type;
+    auto err = static_cast<typename E::T*>(err_v);
+    if (g_bf16)
+        compress_dispatch_g<GradBF16, E>(pd, static_cast<const uint16_t*>(g), err, m, v, p, words, scales,
+                                      signs, nonfinite, ema, cp, s);
+    else
+        compress_dispatch_g<GradF32, E>(pd, static_cast<const float*>(g), err, m, v, p, words, scales,
+                                     signs, nonfinite, ema, cp, s);
+    return hipGetLastError();
+}
+
+// this build's format
+template hipError_t launch_chunk_sumsq<OB_ERR_FMT>(const PlanDev&, const void*, int, const void*, float,
+                                                   hipStream_t);
+template hipError_t launch_compress<OB_ERR_FMT>(const PlanDev&, const void*, int, void*, float*, const float*,
+                                                float*, uint32_t*, float*, int8_t*, unsigned long long*, int,
+                                                const CompressParams&, hipStream_t);
+
+}  // namespace ob

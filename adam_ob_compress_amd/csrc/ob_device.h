@@ -98,6 +98,122 @@ struct GradBF16 {
     }
 };
 
+// ------------------------------------------------------------------------------------------------
+// storage formats of the error buffer ([P3] Q&A on the memory cost of error feedback: the fp32 error
+// term may be kept in a 16-bit format).  A stored value is widened exactly; a new error is computed
+// in fp32 and `rounded` to the format (nearest, ties to even, overflow to +-Inf) before it is stored
+// and before the non-finite check sees it; store4/store1 take already rounded values.
+// ------------------------------------------------------------------------------------------------
+
+struct ErrF32 {
+    using T = float;
+    template <bool NT = false, class I>
+    static __device__ __forceinline__ f4 load4(const float* __restrict__ p, I i)
+    {
+        return ldv<NT>(reinterpret_cast<const f4*>(p + i));
+    }
+    template <class I>
+    static __device__ __forceinline__ float load1(const float* __restrict__ p, I i) { return p[i]; }
+    static __device__ __forceinline__ float rounded(float e) { return e; }
+    template <bool NT = false, class I>
+    static __device__ __forceinline__ void store4(float* __restrict__ p, I i, f4 v)
+    {
+        if (NT)
+            __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p + i));
+        else
+            *reinterpret_cast<f4*>(p + i) = v;
+    }
+    template <class I>
+    static __device__ __forceinline__ void store1(float* __restrict__ p, I i, float e) { p[i] = e; }
+};
+
+// bf16 = the high half of the fp32 bits; rounding adds just under half a bf16 ulp plus the low bit
+// of the kept half (ties to even), which carries into the exponent where it must (up to Inf).
+struct ErrBF16 {
+    using T = uint16_t;
+    template <bool NT = false, class I>
+    static __device__ __forceinline__ f4 load4(const uint16_t* __restrict__ p, I i)
+    {
+        return GradBF16::load4<NT>(p, i);
+    }
+    template <class I>
+    static __device__ __forceinline__ float load1(const uint16_t* __restrict__ p, I i)
+    {
+        return GradBF16::load1(p, i);
+    }
+    static __device__ __forceinline__ float rounded(float e)
+    {
+        const uint32_t u = __float_as_uint(e);
+        if ((u & 0x7fffffffu) > 0x7f800000u) return __uint_as_float((u & 0x80000000u) | 0x7fc00000u);
+        return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+    }
+    template <bool NT = false, class I>
+    static __device__ __forceinline__ void store4(uint16_t* __restrict__ p, I i, f4 v)
+    {
+        u2 r;
+        r.x = (__float_as_uint(v.x) >> 16) | (__float_as_uint(v.y) & 0xffff0000u);
+        r.y = (__float_as_uint(v.z) >> 16) | (__float_as_uint(v.w) & 0xffff0000u);
+        if (NT)
+            __builtin_nontemporal_store(r, reinterpret_cast<u2*>(p + i));
+        else
+            *reinterpret_cast<u2*>(p + i) = r;
+    }
+    template <class I>
+    static __device__ __forceinline__ void store1(uint16_t* __restrict__ p, I i, float e)
+    {
+        p[i] = static_cast<uint16_t>(__float_as_uint(e) >> 16);
+    }
+};
+
+// IEEE binary16 through the hardware conversions (round to nearest even; fp16 denormals kept).
+struct ErrF16 {
+    using T = uint16_t;
+    static __device__ __forceinline__ float widen(uint32_t h)
+    {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+    }
+    static __device__ __forceinline__ uint32_t bits(float e)
+    {
+        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(e));
+    }
+    template <bool NT = false, class I>
+    static __device__ __forceinline__ f4 load4(const uint16_t* __restrict__ p, I i)
+    {
+        const u2 u = ldv<NT>(reinterpret_cast<const u2*>(p + i));
+        f4 r;
+        r.x = widen(u.x & 0xffffu);
+        r.y = widen(u.x >> 16);
+        r.z = widen(u.y & 0xffffu);
+        r.w = widen(u.y >> 16);
+        return r;
+    }
+    template <class I>
+    static __device__ __forceinline__ float load1(const uint16_t* __restrict__ p, I i) { return widen(p[i]); }
+    static __device__ __forceinline__ float rounded(float e) { return static_cast<float>(static_cast<_Float16>(e)); }
+    template <bool NT = false, class I>
+    static __device__ __forceinline__ void store4(uint16_t* __restrict__ p, I i, f4 v)
+    {
+        u2 r;
+        r.x = bits(v.x) | (bits(v.y) << 16);
+        r.y = bits(v.z) | (bits(v.w) << 16);
+        if (NT)
+            __builtin_nontemporal_store(r, reinterpret_cast<u2*>(p + i));
+        else
+            *reinterpret_cast<u2*>(p + i) = r;
+    }
+    template <class I>
+    static __device__ __forceinline__ void store1(uint16_t* __restrict__ p, I i, float e)
+    {
+        p[i] = static_cast<uint16_t>(bits(e));
+    }
+};
+
+// ob_dtype code of the error buffer -> its format
+template <int EF> struct ErrOf;
+template <> struct ErrOf<0> { using type = ErrF32; };
+template <> struct ErrOf<1> { using type = ErrBF16; };
+template <> struct ErrOf<2> { using type = ErrF16; };
+
 template <bool NT = false, class I>
 __device__ __forceinline__ f4 ld4(const float* __restrict__ p, I i)
 {

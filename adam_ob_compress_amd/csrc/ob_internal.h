@@ -46,12 +46,15 @@ struct DenseParams {
     int bias_correction;
 };
 
-hipError_t launch_chunk_sumsq(const PlanDev& pd, const void* g, int g_bf16, const float* err,
-                              float clip, hipStream_t s);
-hipError_t launch_compress(const PlanDev& pd, const void* g, int g_bf16, float* err, float* m,
-                           const float* v, float* p, uint32_t* words, float* scales, int8_t* signs,
-                           unsigned long long* nonfinite, int ema, const CompressParams& cp,
-                           hipStream_t s);
+// Compressed-step launchers for error-buffer format EF (0 fp32, 1 bf16, 2 fp16); ob_compress.hip,
+// built once per format, instantiates each.
+template <int EF>
+hipError_t launch_chunk_sumsq(const PlanDev& pd, const void* g, int g_bf16, const void* err, float clip,
+                              hipStream_t s);
+template <int EF>
+hipError_t launch_compress(const PlanDev& pd, const void* g, int g_bf16, void* err, float* m, const float* v,
+                           float* p, uint32_t* words, float* scales, int8_t* signs,
+                           unsigned long long* nonfinite, int ema, const CompressParams& cp, hipStream_t s);
 hipError_t launch_dense(const PlanDev& pd, const void* g, int g_bf16, float* m, float* v, float* p,
                         const DenseParams& dp, hipStream_t s);
 hipError_t launch_server_sumsq(const PlanDev& pd, int W, const uint32_t* ww, const float* ws,

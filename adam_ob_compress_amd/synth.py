@@ -50,6 +50,7 @@ class Workload:
     refresh_period: int = 0    # dense refresh when t % period == 0 (t from 1); 0 = never
     steps: int = 10
     workers: int = 0           # > 0: server-stage workload
+    err_dtype: str = "f32"     # storage of the error buffer: "f32" | "bf16" | "f16"
 
     @property
     def n_chunks(self) -> int:
@@ -96,6 +97,9 @@ LLAMA2_7B = Workload("llama2-7B-bf16-ema", 6_738_415_616, None, 1 << 24, "bf16",
                      refresh_period=16, steps=48)
 
 WORKLOADS = {w.name: w for w in (SINGLE_1M, BERT_BASE, SERVER_W8, GPT2_XL, LLAMA2_7B)}
+# the same optimizer workloads with the error buffer stored in 16 bits ("<name>-err-bf16", "-err-f16")
+WORKLOADS.update({f"{w.name}-err-{e}": dataclasses.replace(w, name=f"{w.name}-err-{e}", err_dtype=e)
+                  for w in (BERT_BASE, GPT2_XL, LLAMA2_7B) for e in ("bf16", "f16")})
 
 
 def scaled(w: Workload, n: int, chunk: int | None = None) -> Workload:
@@ -159,10 +163,13 @@ def draw_grad(w: Workload, step: int, device, out: torch.Tensor | None = None) -
     return out
 
 
+ERR_TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
 def draw_state(w: Workload, device):
-    """Initial (err, m, v, p): err = 0, m = 0, v = |N(0,1e-6)| + 1e-8, p ~ N(0, 0.02)."""
+    """Initial (err, m, v, p): err = 0 (in w.err_dtype), m = 0, v = |N(0,1e-6)| + 1e-8, p ~ N(0, 0.02)."""
     n = w.n
-    err = torch.zeros(n, dtype=torch.float32, device=device)
+    err = torch.zeros(n, dtype=ERR_TORCH_DTYPES[w.err_dtype], device=device)
     m = torch.zeros(n, dtype=torch.float32, device=device)
     v = torch.empty(n, dtype=torch.float32, device=device)
     p = torch.empty(n, dtype=torch.float32, device=device)

@@ -33,8 +33,8 @@ if ROOT not in sys.path:
 METRIC = "elements/s and achieved HBM GB/s (% of peak) of fused 1-bit Adam step, 1 GPU"
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "bert-base-110M-fp32"
-KERNEL_SOURCES = ("adam_ob_compress_amd/csrc/ob_kernels.hip", "adam_ob_compress_amd/csrc/ob_device.h",
-                  "adam_ob_compress_amd/csrc/ob_internal.h")
+KERNEL_SOURCES = ("adam_ob_compress_amd/csrc/ob_compress.hip", "adam_ob_compress_amd/csrc/ob_kernels.hip",
+                  "adam_ob_compress_amd/csrc/ob_device.h", "adam_ob_compress_amd/csrc/ob_internal.h")
 
 
 def kernel_source_sha() -> str:
@@ -48,10 +48,11 @@ def kernel_source_sha() -> str:
 def bytes_per_elem(w, kernel: str) -> float:
     """Algorithmic (compulsory) HBM bytes per element of one launch of `kernel` on workload w."""
     gb = 2.0 if w.grad_dtype == "bf16" else 4.0
+    eb = 4.0 if w.err_dtype == "f32" else 2.0
     if kernel == "compress":          # read g err m v p, write err m p + 1 bit (+ int8 sign)
-        return gb + 16.0 + 12.0 + 0.125 + (1.0 if w.int8_signs else 0.0)
+        return gb + eb + 12.0 + eb + 8.0 + 0.125 + (1.0 if w.int8_signs else 0.0)
     if kernel == "chunk_sumsq":       # read g err
-        return gb + 4.0
+        return gb + eb
     if kernel == "dense":             # read g m v p, write m v p
         return gb + 12.0 + 12.0
     if kernel == "server_sumsq":      # read W sign bits and the server error
@@ -218,10 +219,11 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("bf16 grads + f32 state" if w.grad_dtype == "bf16" else "f32"),
+        "dtype": (("bf16 grads + f32 state" if w.grad_dtype == "bf16" else "f32")
+                  + ("" if w.err_dtype == "f32" else f", {w.err_dtype} error buffer")),
         "data": "synthetic (seeded; ring of pre-drawn gradients)",
         "config": {"workload": w.name, "elements": w.n, "chunks": plan.num_chunks,
-                   "grad_dtype": w.grad_dtype, "clip": w.clip,
+                   "grad_dtype": w.grad_dtype, "err_dtype": w.err_dtype, "clip": w.clip,
                    "error_feedback": "ema" if w.ef_mode else "plain", "int8_signs": w.int8_signs,
                    "freeze_step": w.freeze_step, "refresh_period": w.refresh_period,
                    "block_elems": plan.block_elems, "work_blocks": plan.num_blocks},
@@ -322,7 +324,7 @@ def traffic_profile(d: str, kernel: str, workload: str) -> str:
            "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 4)}
     return f"""# HBM traffic of `{kernel}` on {w.name}
 
-Kernel source sha (ob_kernels.hip, ob_device.h, ob_internal.h): {rec['kernel_src_sha']}.
+Kernel source sha (ob_compress.hip, ob_kernels.hip, ob_device.h, ob_internal.h): {rec['kernel_src_sha']}.
 
 Commands (each its own run on one MI355X, from the repository root, `export TMPDIR=/tmp`):
 

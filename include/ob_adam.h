@@ -12,6 +12,8 @@
  *   [P2] "DeepSpeed Communication Compression and Hiding": section "baseline: why Adam is hard to
  *        compress" (Adam moments), section "1-bit Adam: warmup, frozen variance, error feedback"
  *        (the two-phase step and compressed_allreduce), section "0/1 Adam" (variance refresh).
+ *   [P3] gradient-compression survey (bmjup.com post 14450): Q&A on the memory cost of error
+ *        feedback (the error term kept in a 16-bit format such as FP16).
  *
  * Definitions used by every call
  *   - Elements are a flat index 0..n-1 over one contiguous buffer per state array (the parameters
@@ -24,8 +26,9 @@
  *   - scale_c = ||x_c||_2 / sqrt(n_c), with ||x_c||^2 accumulated in double and sqrt(S/n_c) taken in
  *     double, then rounded to fp32.  g_hat = +scale_c or -scale_c by the sign.
  *
- * Alignment: fp32 state and fp32 gradient pointers 16 bytes; bf16 gradient 8 bytes; words, scales
- * and int8 signs 4 bytes; the non-finite counter 8 bytes.  (torch allocations are 256-byte aligned.)
+ * Alignment: fp32 state and fp32 gradient pointers 16 bytes; bf16 gradient and 16-bit error buffer
+ * 8 bytes; words, scales and int8 signs 4 bytes; the non-finite counter 8 bytes.  (torch allocations
+ * are 256-byte aligned.)
  *
  * Errors: arguments are validated on the host before anything is enqueued, and a failed check
  * returns a status without touching the GPU: OB_ERR_ARG (null required pointer, bad size, bad chunk
@@ -57,8 +60,9 @@ typedef enum {
     OB_ERR_OOM = 5
 } ob_status;
 
-/* Gradient / packed-input element type. */
-typedef enum { OB_F32 = 0, OB_BF16 = 1 } ob_dtype;
+/* Element types.  Gradients and packed inputs: OB_F32 or OB_BF16.  The error buffer of the compressed
+ * step may also be OB_F16 (IEEE binary16). */
+typedef enum { OB_F32 = 0, OB_BF16 = 1, OB_F16 = 2 } ob_dtype;
 
 /* Error feedback rule: PLAIN replaces the error with x - g_hat ([P2] 1-bit Adam pseudo-code);
  * EMA keeps ef_beta*err + (1-ef_beta)*(x - g_hat) ([P1] sec. 2.1). */
@@ -110,14 +114,18 @@ ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, flo
  *   g_hat = +-scale_c;  err = x - g_hat (PLAIN) or ef_beta*err + (1-ef_beta)*(x - g_hat) (EMA);
  *   m = beta1*m + (1-beta1)*g_hat;  p -= lr * m / (sqrt(v) + eps)  (v frozen, read only).
  * Runs two kernels: a per-chunk sum of squares, then one fused streaming pass.
- * g: n elements (read only); err, m, p: fp32[n] in place; v: fp32[n] read only;
- * words_out: uint32[ceil(n/32)]; scales_out: fp32[K];
+ * g: n elements (read only); err: n elements of err_dtype, in place; m, p: fp32[n] in place;
+ * v: fp32[n] read only; words_out: uint32[ceil(n/32)]; scales_out: fp32[K];
+ * err_dtype ([P3] Q&A on error-feedback memory): OB_F32, or OB_BF16 / OB_F16 -- the stored error is
+ *   widened exactly when read, and the new error, computed in fp32 as above, is rounded to the format
+ *   (nearest, ties to even; beyond the largest finite value, +-Inf) when stored;
  * signs_out (optional, NULL = off): int8[n] of +1/-1 ([P1] sec. 3.2);
- * nonfinite_out (optional, NULL = off): device uint64 counter to which the number of non-finite new
- * error elements is added ([P1] sec. 3.2 NaN check; the caller zeroes it).
+ * nonfinite_out (optional, NULL = off): device uint64 counter to which the number of non-finite
+ * STORED new error elements is added ([P1] sec. 3.2 NaN check; the caller zeroes it), so an fp16
+ * overflow is counted.
  * Outputs must not alias inputs. */
-ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* err, float* m,
-                                const float* v, float* p, uint32_t* words_out, float* scales_out,
+ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
+                                float* m, const float* v, float* p, uint32_t* words_out, float* scales_out,
                                 int8_t* signs_out, uint64_t* nonfinite_out, const ob_hparams* hp,
                                 hipStream_t stream);
 
@@ -133,7 +141,7 @@ ob_status ob_server_reduce(ob_plan plan, int32_t W, const uint32_t* worker_words
                            const float* worker_scales, float* server_err, uint32_t* words_out,
                            float* scales_out, hipStream_t stream);
 
-/* Pack signs of x (fp32 or bf16, n elements) into ceil(n/32) words ([P2] one_bit_quantize, sign part). */
+/* Pack signs of x (OB_F32 or OB_BF16, n elements) into ceil(n/32) words ([P2] one_bit_quantize, sign part). */
 ob_status ob_pack(const void* x, ob_dtype x_dtype, int64_t n, uint32_t* words_out, hipStream_t stream);
 
 /* Unpack + dequantize ([P2] dequantize): out_i = bit(i) ? s_c : -s_c, s_c = scales[c] for the plan's

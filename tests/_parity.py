@@ -12,6 +12,8 @@ and the oracle may run on different chunks in parallel threads (ctypes releases 
 
 Tolerances:
   * packed words and int8 signs: bit-exact;
+  * a 16-bit error buffer: the fp32 bound below plus one unit in the last place of the storage format
+    (the two sides round fp32 values that may differ in their last bits);
   * scales: equal, or 1 ulp apart (the double sum of squares is reduced in a different order);
     mismatches are counted and returned;
   * fp32 state: |gpu - ref| <= 2e-6*|ref| + 1e-9 (+ the exact propagation of a scale difference:
@@ -65,6 +67,35 @@ def assert_f32_close(gpu, ref, what, slack=0.0):
                              f"{g64[k]!r} ref={r64[k]!r} tol={tol[k]!r}")
 
 
+# significand bits (implicit bit included) and the smallest subnormal of the 16-bit error formats
+_FMT = {"bf16": (8, 2.0 ** -133), "f16": (11, 2.0 ** -24)}
+
+
+def err_format(a: np.ndarray) -> str:
+    return {np.dtype(np.float32): "f32", np.dtype(np.uint16): "bf16", np.dtype(np.float16): "f16"}[a.dtype]
+
+
+def widen_err(a: np.ndarray) -> np.ndarray:
+    """A host error buffer as fp32: float16 by numpy, bf16 bits by shifting into the high half."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32)
+    return a.astype(np.float32)
+
+
+def assert_err_close(gpu, ref, what, slack=0.0):
+    """Error buffers of any storage format: fp32 by assert_f32_close; 16-bit with one extra ulp."""
+    fmt = err_format(np.asarray(ref))
+    assert err_format(np.asarray(gpu)) == fmt, what
+    g32, r32 = widen_err(np.asarray(gpu)), widen_err(np.asarray(ref))
+    if fmt == "f32":
+        return assert_f32_close(g32, r32, what, slack)
+    prec, tiny = _FMT[fmt]
+    ulp = np.abs(r32.astype(np.float64)) * 2.0 ** (1 - prec) + tiny
+    if not np.isscalar(slack):
+        slack = np.asarray(slack, np.float64)
+    assert_f32_close(g32, r32, what, np.where(np.isfinite(ulp), ulp, 0.0) + slack)
+
+
 class ChunkRef:
     """The oracle's state for one chunk [a, b)."""
 
@@ -84,10 +115,14 @@ def host_chunks(w, chunks, err, m, v, p):
 
 
 def upload(refs, err, m, v, p):
-    """Write the oracle's chunk state into the GPU buffers (identical input state)."""
+    """Write the oracle's chunk state into the GPU buffers (identical input state, bit for bit)."""
     for r in refs:
         for dst, src in ((err, r.err), (m, r.m), (v, r.v), (p, r.p)):
-            dst[r.a:r.b].copy_(torch.from_numpy(src), non_blocking=False)
+            d = dst[r.a:r.b]
+            if src.dtype == np.uint16:          # bf16 bits
+                d.view(torch.int16).copy_(torch.from_numpy(src.view(np.int16)), non_blocking=False)
+            else:
+                d.copy_(torch.from_numpy(src), non_blocking=False)
 
 
 def _oracle_compress(r, g, w):
@@ -143,7 +178,7 @@ def compare_chunks(refs, w, kind, err, m, v, p, words=None, scales=None, signs=N
         err_slack = ds * ((1 - eb) if w.ef_mode == 1 else 1.0)
         m_slack = ds * (1 - b1)
         p_slack = lr * m_slack / (np.sqrt(r.v.astype(np.float64)) + eps) if ds else 0.0
-        assert_f32_close(ge, r.err, f"{tag}: err", err_slack)
+        assert_err_close(ge, r.err, f"{tag}: err", err_slack)
         assert_f32_close(gm, r.m, f"{tag}: m", m_slack)
         assert_f32_close(gp, r.p, f"{tag}: p", p_slack)
     return mism

@@ -58,7 +58,7 @@ def test_validation_before_any_gpu_work(lib):
     assert lib.ob_unpack(None, None, 0, None, None, None) == 0
     assert lib.ob_unpack(None, P(0x1000), 64, P(0x2000), P(0x3000), None) == 1   # scales need a plan
     hp = ob.hparams()
-    assert lib.ob_adam_compress_step(None, P(0x1000), 0, None, None, None, None, None, None, None,
+    assert lib.ob_adam_compress_step(None, P(0x1000), 0, None, 0, None, None, None, None, None, None,
                                      None, ctypes.byref(hp), None) == 1
     assert lib.ob_adam_warmup_step(None, None, 0, None, None, None, ctypes.byref(hp), None) == 1
     assert lib.ob_server_reduce(None, 8, None, None, None, None, None, None) == 1

@@ -4,6 +4,8 @@ Sizes: brute force over n = 1..130; several tiles and work blocks with ragged ta
 workloads at full size in the launch configuration the bench uses (checked chunks listed per test).
 Inputs come only from adam_ob_compress_amd.synth; nothing the HIP path computes is fed to the oracle.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -81,7 +83,22 @@ VARIANTS = {
     "bf16_ema_clip_int8": dict(gdt="bf16", clip=5.0, ef_mode=1, signs=True),
     "fp32_ema": dict(gdt="f32", clip=0.0, ef_mode=1, signs=True),
     "bf16_plain": dict(gdt="bf16", clip=0.0, ef_mode=0, signs=False),
+    # 16-bit error buffers
+    "fp32_plain_f16err": dict(gdt="f32", clip=0.0, ef_mode=0, signs=False, edt="f16"),
+    "fp32_ema_bf16err": dict(gdt="f32", clip=0.0, ef_mode=1, signs=True, edt="bf16"),
+    "bf16_ema_clip_int8_f16err": dict(gdt="bf16", clip=5.0, ef_mode=1, signs=True, edt="f16"),
+    "bf16_plain_bf16err": dict(gdt="bf16", clip=0.0, ef_mode=0, signs=False, edt="bf16"),
 }
+
+
+def _as_err_format(err32, edt):
+    """An fp32 error array rounded (nearest even, by numpy / torch) to the variant's storage format."""
+    if edt == "f16":
+        with np.errstate(over="ignore"):
+            return err32.astype(np.float16)
+    if edt == "bf16":
+        return _bf16_bits(err32)
+    return err32
 
 
 def _small_state(n, seed, wide=False):
@@ -101,6 +118,7 @@ def _gpu_vs_oracle_compress(n, chunk, var, seed, g=None, state=None, steps=1, lr
         gnp = g
     if state is not None:
         err, m, v, p = state
+    err = _as_err_format(err, var.get("edt", "f32"))
     if var["gdt"] == "bf16":
         gnp = _bf16_bits(gnp)
     off = oracle.uniform_offsets(n, chunk)
@@ -127,7 +145,7 @@ def _gpu_vs_oracle_compress(n, chunk, var, seed, g=None, state=None, steps=1, lr
         ds = np.abs(gs.astype(np.float64) - rs.astype(np.float64))[cidx]
         ds = np.where(np.isfinite(ds), ds, 0.0)
         eslack = ds * (0.1 if var["ef_mode"] else 1.0)
-        P.assert_f32_close(synth.host(d[1]), err, f"{tag}: err", eslack)
+        P.assert_err_close(synth.host(d[1]), err, f"{tag}: err", eslack)
         P.assert_f32_close(synth.host(d[2]), m, f"{tag}: m", 0.1 * ds)
         P.assert_f32_close(synth.host(d[4]), p, f"{tag}: p",
                            lr * 0.1 * ds / (np.sqrt(v.astype(np.float64)) + 1e-8))
@@ -136,6 +154,7 @@ def _gpu_vs_oracle_compress(n, chunk, var, seed, g=None, state=None, steps=1, lr
         gnp = _small_state(n, seed + 1000 + _, wide=var["clip"] > 0)[0]
         if var["gdt"] == "bf16":
             gnp = _bf16_bits(gnp)
+    return rnf
 
 
 @pytest.mark.parametrize("vname", sorted(VARIANTS))
@@ -164,9 +183,24 @@ def test_compress_edge_values():
         err = np.where(rng.random(n) < 0.5, np.float32(0.0), synth.draw_values(n, 37, pattern))
         state = (err.astype(np.float32), np.zeros(n, np.float32),
                  np.ones(n, np.float32), np.zeros(n, np.float32))
-        for vname in ("fp32_plain", "fp32_ema"):
+        for vname in ("fp32_plain", "fp32_ema", "fp32_plain_f16err", "fp32_ema_bf16err"):
             _gpu_vs_oracle_compress(n, 1024, VARIANTS[vname], seed=1, g=g,
                                     state=tuple(a.copy() for a in state))
+
+
+def test_compress_f16_error_overflow_is_counted():
+    """New errors beyond fp16's range are stored as +-Inf and counted as non-finite."""
+    n = 10_000 + 3
+    rng = np.random.default_rng(9)
+    g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    hit = rng.random(n) < 0.01
+    # |g| = 1e6 on 1% of elements: scale ~ 1e5, so |x - g_hat| ~ 9e5 and the EMA's (1-0.9) share
+    # ~ 9e4, both past fp16's largest finite value 65504
+    g[hit] = np.where(rng.random(int(hit.sum())) < 0.5, -1e6, 1e6).astype(np.float32)
+    for vname in ("fp32_plain_f16err", "bf16_ema_clip_int8_f16err"):
+        var = dict(VARIANTS[vname], clip=0.0)
+        nf = _gpu_vs_oracle_compress(n, 1024, var, seed=2, g=g)
+        assert nf > 0, vname
 
 
 @pytest.mark.parametrize("gdt", ["f32", "bf16"])
@@ -259,6 +293,22 @@ def test_misaligned_and_invalid_arguments():
     assert e.value.status == 1
     with pytest.raises(ValueError):            # host tensors are refused: no CPU path
         ob.ob_pack(torch.zeros(64), words[:2])
+    e16 = torch.zeros(n + 4, dtype=torch.float16, device=DEV)
+    with pytest.raises(ob.ObError) as e:       # 16-bit error buffer 2 bytes off an 8-byte boundary
+        ob.ob_adam_compress_step(plan, ok[0], e16[1:n + 1], *ok[2:], words, scales, hp)
+    assert e.value.status == 2
+    with pytest.raises(TypeError):
+        ob.ob_adam_compress_step(plan, ok[0], torch.zeros(n, dtype=torch.int16, device=DEV), *ok[2:],
+                                 words, scales, hp)
+    # through the C ABI: an unknown error dtype, and fp16 gradients (not supported), are OB_ERR_DTYPE
+    import ctypes
+    L = ob.lib()
+    ptrs = [ctypes.c_void_p(t.data_ptr()) for t in ok]
+    for gdt, edt in ((0, 3), (2, 0), (0, -1)):
+        st = L.ob_adam_compress_step(plan.handle, ptrs[0], gdt, ptrs[1], edt, ptrs[2], ptrs[3], ptrs[4],
+                                     ctypes.c_void_p(words.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                                     None, None, ctypes.byref(hp), None)
+        assert st == 3, (gdt, edt, st)
 
 
 def test_deterministic():
@@ -311,6 +361,14 @@ def test_workload_bert_base():
     """197 per-tensor chunks (108,891,648 fp32 elements): 5 dense steps, then 20 compressed; every
     chunk checked every step."""
     counts = P.run_workload(synth.BERT_BASE, log=lambda *_: None)
+    assert counts["dense"] == 5 and counts["compressed"] == 20
+
+
+@pytest.mark.parametrize("edt", ["bf16", "f16"])
+def test_workload_bert_base_16bit_error(edt):
+    """The BERT-base workload with its error buffer stored in bf16 / fp16; every chunk every step."""
+    w = synth.WORKLOADS[f"{synth.BERT_BASE.name}-err-{edt}"]
+    counts = P.run_workload(w, log=lambda *_: None)
     assert counts["dense"] == 5 and counts["compressed"] == 20
 
 
@@ -370,3 +428,12 @@ def test_workload_llama2_7b():
     w = synth.LLAMA2_7B
     counts = P.run_workload(w, chunks=[0, 200, w.n_chunks - 1], log=lambda *_: None)
     assert counts["dense"] == 3 and counts["compressed"] == 45
+
+
+@pytest.mark.slow
+def test_workload_llama2_7b_bf16_error():
+    """The Llama-2-7B workload with a bf16 error buffer, 20 steps (one dense refresh at t = 16):
+    chunks 0, 200 and the tail 401 checked every step."""
+    w = dataclasses.replace(synth.WORKLOADS[f"{synth.LLAMA2_7B.name}-err-bf16"], steps=20)
+    counts = P.run_workload(w, chunks=[0, 200, w.n_chunks - 1], log=lambda *_: None)
+    assert counts["dense"] == 1 and counts["compressed"] == 19
