@@ -60,6 +60,9 @@ def _load():
     lib.or_unpack.argtypes = [P, I64, I64, P, P, P]
     lib.or_compress_step.argtypes = [I64, I64, P, P, I, P, I, P, P, P, P, P, P, P,
                                      F, F, F, F, I, F]
+    lib.or_lamb_compress_step.argtypes = [I64, I64, P, P, I, P, I, P, P, P, P, P, P, P, P,
+                                          F, F, F, F, I, F]
+    lib.or_lamb_warmup_step.argtypes = [I64, I64, P, P, I, P, P, P, P, F, F, F, F, I, I64]
     lib.or_to_format.argtypes = [P, I64, I, P]
     lib.or_from_format.argtypes = [P, I64, I, P]
     lib.or_warmup_step.argtypes = [I64, P, I, P, P, P, F, F, F, F, I, I64]
@@ -70,7 +73,8 @@ def _load():
     lib.or_chunk_scale.argtypes = [P, I64, I64]
     lib.or_chunk_scale.restype = ctypes.c_float
     for name in ("or_pack", "or_unpack", "or_compress_step", "or_warmup_step",
-                 "or_server_reduce", "or_server_average", "or_to_format", "or_from_format"):
+                 "or_server_reduce", "or_server_average", "or_to_format", "or_from_format",
+                 "or_lamb_compress_step", "or_lamb_warmup_step"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -207,6 +211,46 @@ def warmup_step(g, m, v, p, *, lr, beta1, beta2, eps, bias_correction=False, ste
     rc = _load().or_warmup_step(n, _ptr(g), bf, _ptr(m), _ptr(v), _ptr(p), lr, beta1, beta2, eps,
                                 1 if bias_correction else 0, step)
     _check(rc, "warmup_step")
+
+
+def lamb_compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef_mode=0, ef_beta=0.9,
+                       want_signs=False, count_nonfinite=False):
+    """One compressed 1-bit LAMB step (reading R16): as compress_step up to the momentum, then the
+    per-chunk (layer) trust ratio and update.  err, m, p in place; v read only.
+
+    Returns (words, scales fp32[K], ratios fp32[K], signs or None, nonfinite or None)."""
+    g, bf = _grad(np.ascontiguousarray(g))
+    n = g.size
+    err, efmt = _err(err)
+    assert err.size == n and err.flags["C_CONTIGUOUS"]
+    for a in (m, v, p):
+        assert a.dtype == np.float32 and a.size == n and a.flags["C_CONTIGUOUS"]
+    k = offsets.size - 1
+    words = np.zeros(n_words(n), dtype=np.uint32)
+    scales = np.zeros(max(k, 0), dtype=np.float32)
+    ratios = np.zeros(max(k, 0), dtype=np.float32)
+    signs = np.zeros(n, dtype=np.int8) if want_signs else None
+    nf = np.zeros(1, dtype=np.int64) if count_nonfinite else None
+    rc = _load().or_lamb_compress_step(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m),
+                                       _ptr(v), _ptr(p), _ptr(words), _ptr(scales), _ptr(ratios),
+                                       _ptr(signs), _ptr(nf), lr, beta1, eps, clip, ef_mode, ef_beta)
+    _check(rc, "lamb_compress_step")
+    return words, scales, ratios, signs, (int(nf[0]) if nf is not None else None)
+
+
+def lamb_warmup_step(g, m, v, p, offsets, *, lr, beta1, beta2, eps, bias_correction=False, step=0):
+    """One dense LAMB step (the warmup of 1-bit LAMB); m, v, p in place.  Returns ratios fp32[K]."""
+    g, bf = _grad(np.ascontiguousarray(g))
+    n = g.size
+    for a in (m, v, p):
+        assert a.dtype == np.float32 and a.size == n and a.flags["C_CONTIGUOUS"]
+    k = offsets.size - 1
+    ratios = np.zeros(max(k, 0), dtype=np.float32)
+    rc = _load().or_lamb_warmup_step(n, k, _ptr(offsets), _ptr(g), bf, _ptr(m), _ptr(v), _ptr(p),
+                                     _ptr(ratios), lr, beta1, beta2, eps, 1 if bias_correction else 0,
+                                     step)
+    _check(rc, "lamb_warmup_step")
+    return ratios
 
 
 def server_reduce(worker_words, worker_scales, server_err, offsets):

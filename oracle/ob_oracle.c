@@ -47,6 +47,15 @@
  *      in R4/R6 and then rounded to the storage format to nearest, ties to even (IEEE 754's default
  *      rounding), overflowing to +-Inf.  The R8 check counts non-finite STORED values, so an fp16
  *      overflow is reported.
+ *   R16 1-bit LAMB ([P2] section "1-bit LAMB: also protect the layer-wise trust ratio"): a layer is a
+ *      chunk (one chunk per parameter tensor).  The direction is u_i = m_i / (sqrt(v_i) + eps) with
+ *      the new m (compressed step: v frozen, m driven by g_hat as in R5/R6; dense step: the new m and
+ *      v, divided by 1 - beta^t when bias correction is on), evaluated in double and not stored.
+ *      S_w = sum p_i^2 over the layer's parameters before the update and S_u = sum u_i^2, both in
+ *      double in ascending index order; r = fl32(sqrt(S_w) / sqrt(S_u)), and r = 1 when S_w == 0 or
+ *      S_u == 0 (the ratio is undefined there, and a zero-initialised layer must still move);
+ *      p_i = fl32(p_i - lr * (r * u_i)) in double.  No weight decay and no clamp of r: the pages
+ *      give neither.
  */
 #include <math.h>
 #include <stdint.h>
@@ -248,11 +257,13 @@ int or_unpack(const uint32_t* words, int64_t n, int64_t K, const int64_t* off, c
 
 /* ---------- compressed step ([P2] 1-bit Adam, compressed branch; [P1] sec. 2.1, 2.2, 3.2) ---------- */
 
-int or_compress_step(int64_t n, int64_t K, const int64_t* off,
-                     const void* g, int g_is_bf16,
-                     void* err_store, int err_fmt, float* m, const float* v, float* p,
-                     uint32_t* words, float* scales, int8_t* signs, int64_t* nonfinite,
-                     float lr, float beta1, float eps, float clip, int ef_mode, float ef_beta)
+/* The compressed step; adam_update = 0 stops before the parameter update (1-bit LAMB, R16). */
+static int compress_core(int64_t n, int64_t K, const int64_t* off,
+                         const void* g, int g_is_bf16,
+                         void* err_store, int err_fmt, float* m, const float* v, float* p,
+                         uint32_t* words, float* scales, int8_t* signs, int64_t* nonfinite,
+                         float lr, float beta1, float eps, float clip, int ef_mode, float ef_beta,
+                         int adam_update)
 {
     if (!check_offsets(n, K, off)) return OR_ERR_ARG;
     if (err_fmt != OR_FMT_F32 && err_fmt != OR_FMT_BF16 && err_fmt != OR_FMT_F16) return OR_ERR_ARG;
@@ -305,8 +316,9 @@ int or_compress_step(int64_t n, int64_t K, const int64_t* off,
             /* m = beta1*m + (1-beta1)*g_hat ([P2]; [P1] sec. 2.2). */
             m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)gh);
             /* param -= lr * m / (sqrt(v_frozen) + eps), v untouched ([P2]). */
-            p[i] = (float)((double)p[i] -
-                           (double)lr * ((double)m[i] / (sqrt((double)v[i]) + (double)eps)));
+            if (adam_update)
+                p[i] = (float)((double)p[i] -
+                               (double)lr * ((double)m[i] / (sqrt((double)v[i]) + (double)eps)));
             if (signs != NULL) signs[i] = (int8_t)(b ? 1 : -1);
         }
     }
@@ -320,13 +332,25 @@ int or_compress_step(int64_t n, int64_t K, const int64_t* off,
     return OR_OK;
 }
 
+int or_compress_step(int64_t n, int64_t K, const int64_t* off,
+                     const void* g, int g_is_bf16,
+                     void* err_store, int err_fmt, float* m, const float* v, float* p,
+                     uint32_t* words, float* scales, int8_t* signs, int64_t* nonfinite,
+                     float lr, float beta1, float eps, float clip, int ef_mode, float ef_beta)
+{
+    return compress_core(n, K, off, g, g_is_bf16, err_store, err_fmt, m, v, p, words, scales, signs,
+                         nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 1);
+}
+
 /* ---------- dense Adam step (warmup before freeze_step, and the 0/1 Adam refresh) ----------
  * [P2] baseline section: m = b1 m + (1-b1) g, v = b2 v + (1-b2) g^2; update as in the 1-bit Adam
  * pseudo-code with the new m and v.  bias_correction != 0 divides m and v by (1 - b^t), t = step
  * (textbook Adam); the pages' pseudo-code has no bias correction, so it is off by default.
  * The error buffer is not touched. */
-int or_warmup_step(int64_t n, const void* g, int g_is_bf16, float* m, float* v, float* p,
-                   float lr, float beta1, float beta2, float eps, int bias_correction, int64_t step)
+/* The dense step; adam_update = 0 stops after the moments (1-bit LAMB warmup, R16). */
+static int warmup_core(int64_t n, const void* g, int g_is_bf16, float* m, float* v, float* p,
+                       float lr, float beta1, float beta2, float eps, int bias_correction, int64_t step,
+                       int adam_update)
 {
     if (n < 0) return OR_ERR_ARG;
     if (n == 0) return OR_OK;
@@ -344,8 +368,73 @@ int or_warmup_step(int64_t n, const void* g, int g_is_bf16, float* m, float* v, 
         v[i] = (float)(b2 * (double)v[i] + (1.0 - b2) * (gi * gi));
         double mh = (double)m[i] / bc1;
         double vh = (double)v[i] / bc2;
-        p[i] = (float)((double)p[i] - (double)lr * (mh / (sqrt(vh) + (double)eps)));
+        if (adam_update)
+            p[i] = (float)((double)p[i] - (double)lr * (mh / (sqrt(vh) + (double)eps)));
     }
+    return OR_OK;
+}
+
+int or_warmup_step(int64_t n, const void* g, int g_is_bf16, float* m, float* v, float* p,
+                   float lr, float beta1, float beta2, float eps, int bias_correction, int64_t step)
+{
+    return warmup_core(n, g, g_is_bf16, m, v, p, lr, beta1, beta2, eps, bias_correction, step, 1);
+}
+
+/* ---------- 1-bit LAMB ([P2] section "1-bit LAMB"; reading R16) ---------- */
+
+/* Per layer (chunk) c: trust ratio r_c = ||w_c|| / ||u_c|| of the parameters before the update and
+ * the direction u_i = (m_i / bc1) / (sqrt(v_i / bc2) + eps); then p_i -= lr * r_c * u_i. */
+static void lamb_update(int64_t K, const int64_t* off, const float* m, const float* v, float* p,
+                        float* ratios, float lr, float eps, double bc1, double bc2)
+{
+    for (int64_t c = 0; c < K; ++c) {
+        double sw = 0.0, su = 0.0;
+        for (int64_t i = off[c]; i < off[c + 1]; ++i) {
+            double u = ((double)m[i] / bc1) / (sqrt((double)v[i] / bc2) + (double)eps);
+            sw += (double)p[i] * (double)p[i];
+            su += u * u;
+        }
+        float r = (sw == 0.0 || su == 0.0) ? 1.0f : (float)(sqrt(sw) / sqrt(su));
+        ratios[c] = r;
+        for (int64_t i = off[c]; i < off[c + 1]; ++i) {
+            double u = ((double)m[i] / bc1) / (sqrt((double)v[i] / bc2) + (double)eps);
+            p[i] = (float)((double)p[i] - (double)lr * ((double)r * u));
+        }
+    }
+}
+
+/* Compressed 1-bit LAMB step: the compressed step's compensate / quantize / error / momentum on the
+ * reconstructed direction, then the layer-wise trust ratio and the update (v frozen). */
+int or_lamb_compress_step(int64_t n, int64_t K, const int64_t* off,
+                          const void* g, int g_is_bf16,
+                          void* err_store, int err_fmt, float* m, const float* v, float* p,
+                          uint32_t* words, float* scales, float* ratios, int8_t* signs,
+                          int64_t* nonfinite, float lr, float beta1, float eps, float clip,
+                          int ef_mode, float ef_beta)
+{
+    if (n > 0 && ratios == NULL) return OR_ERR_ARG;
+    int rc = compress_core(n, K, off, g, g_is_bf16, err_store, err_fmt, m, v, p, words, scales, signs,
+                           nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 0);
+    if (rc != OR_OK || n == 0) return rc;
+    lamb_update(K, off, m, v, p, ratios, lr, eps, 1.0, 1.0);
+    return OR_OK;
+}
+
+/* Dense LAMB step (the warmup of 1-bit LAMB): Adam moments, then the trust ratio and update. */
+int or_lamb_warmup_step(int64_t n, int64_t K, const int64_t* off, const void* g, int g_is_bf16,
+                        float* m, float* v, float* p, float* ratios, float lr, float beta1, float beta2,
+                        float eps, int bias_correction, int64_t step)
+{
+    if (!check_offsets(n, K, off)) return OR_ERR_ARG;
+    if (n > 0 && ratios == NULL) return OR_ERR_ARG;
+    int rc = warmup_core(n, g, g_is_bf16, m, v, p, lr, beta1, beta2, eps, bias_correction, step, 0);
+    if (rc != OR_OK || n == 0) return rc;
+    double bc1 = 1.0, bc2 = 1.0;
+    if (bias_correction) {
+        bc1 = 1.0 - pow((double)beta1, (double)step);
+        bc2 = 1.0 - pow((double)beta2, (double)step);
+    }
+    lamb_update(K, off, m, v, p, ratios, lr, eps, bc1, bc2);
     return OR_OK;
 }
 

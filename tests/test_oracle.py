@@ -14,7 +14,11 @@ Pins used (none retypes the oracle's formula):
     float32->bfloat16 conversions (both round to nearest, ties to even) on every rounding boundary of
     the two formats, the widening against the same libraries on all 65536 patterns, hand-derived
     tie and overflow examples, and the reduction of a 16-bit-error step to the fp32 step followed by
-    the library rounding.
+    the library rounding;
+  * 1-bit LAMB (R16): hand-derived two-layer examples (compressed and dense, with a zero layer and a
+    zero direction), the reduction of each layer's update to the already pinned Adam steps with
+    lr * r (exact when lr is a power of two), the ratio against math.fsum norms, exact scale
+    invariances (p x 2, v x 4, and g, err, m x 2), and layer independence.
 """
 import math
 from fractions import Fraction
@@ -658,3 +662,146 @@ def test_compress_16bit_error_is_fp32_step_then_rounding(fmt, ef_mode):
     assert nfa == int(np.sum(~np.isfinite(_lib_widen(expect, fmt))))
     if fmt == "f16":
         assert nfa > 1, "the fp16 case must exercise overflow to Inf"
+
+
+# ------------------------------------------------------------------------------------------------
+# R16: 1-bit LAMB
+# ------------------------------------------------------------------------------------------------
+
+def test_worked_lamb_compress(golden):
+    case = golden["lamb_compress_two_layers"]
+    g = _arr(case["g"])
+    err, m, v, p = (_arr(case[k]) for k in ("err", "m", "v", "p"))
+    v0 = v.copy()
+    off = np.asarray(case["offsets"], dtype=np.int64)
+    words, scales, ratios, signs, nf = oracle.lamb_compress_step(
+        g, err, m, v, p, off, lr=case["lr"], beta1=case["beta1"], eps=case["eps"], clip=case["clip"],
+        ef_mode=case["ef_mode"], ef_beta=case["ef_beta"], want_signs=True, count_nonfinite=True)
+    assert words.tolist() == case["expect_words"]
+    assert scales.tolist() == case["expect_scales"]
+    assert ratios.tolist() == case["expect_ratios"]
+    assert err.tolist() == case["expect_err"]
+    assert m.tolist() == case["expect_m"]
+    assert p.tolist() == case["expect_p"]
+    assert signs.tolist() == case["expect_signs"]
+    assert np.array_equal(v, v0) and nf == 0
+
+
+def test_worked_lamb_dense(golden):
+    case = golden["lamb_dense_two_layers"]
+    g = _arr(case["g"])
+    m, v, p = (_arr(case[k]) for k in ("m", "v", "p"))
+    off = np.asarray(case["offsets"], dtype=np.int64)
+    ratios = oracle.lamb_warmup_step(g, m, v, p, off, lr=case["lr"], beta1=case["beta1"],
+                                     beta2=case["beta2"], eps=case["eps"])
+    assert ratios.tolist() == case["expect_ratios"]
+    assert m.tolist() == case["expect_m"]
+    assert v.tolist() == case["expect_v"]
+    assert p.tolist() == case["expect_p"]
+
+
+def _lamb_layers(seed, sizes=(64, 1000, 4096 + 37, 128)):
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    n = int(off[-1])
+    g, err, m, v, p = _random_state(n, seed)
+    return off, g, err, m, v, p
+
+
+LR2 = 2.0 ** -10       # a power of two: lr * r is exact in fp32
+
+
+@pytest.mark.parametrize("ef_mode", [0, 1])
+def test_lamb_compress_equals_adam_with_scaled_lr(ef_mode):
+    """Per layer, 1-bit LAMB's step is the pinned compressed Adam step with lr' = lr * r."""
+    off, g, err, m, v, p = _lamb_layers(21)
+    a = [t.copy() for t in (err, m, p)]
+    hp = dict(lr=LR2, beta1=0.9, eps=1e-8, clip=0.0, ef_mode=ef_mode, ef_beta=0.9, want_signs=True)
+    words, scales, ratios, signs, _ = oracle.lamb_compress_step(g, a[0], a[1], v, a[2], off, **hp)
+    assert np.all(ratios > 0) and not np.all(ratios == 1.0)
+    for c in range(off.size - 1):
+        lo, hi = int(off[c]), int(off[c + 1])
+        r = float(ratios[c])
+        assert np.float32(LR2 * r) == LR2 * r
+        e2, m2, p2 = (t[lo:hi].copy() for t in (err, m, p))
+        hp2 = dict(hp, lr=LR2 * r)
+        w2, s2, sg2, _ = oracle.compress_step(g[lo:hi].copy(), e2, m2, v[lo:hi].copy(), p2,
+                                              np.asarray([0, hi - lo], np.int64), **hp2)
+        assert s2[0] == scales[c]
+        assert np.array_equal(sg2, signs[lo:hi])
+        assert np.array_equal(e2, a[0][lo:hi]) and np.array_equal(m2, a[1][lo:hi])
+        assert np.array_equal(p2, a[2][lo:hi]), f"layer {c}"
+    assert np.array_equal(words, oracle.pack(np.where(signs > 0, 1.0, -1.0).astype(np.float32)))
+
+
+@pytest.mark.parametrize("bias_correction,step", [(False, 0), (True, 1), (True, 7)])
+def test_lamb_dense_equals_adam_with_scaled_lr(bias_correction, step):
+    off, g, _, m, v, p = _lamb_layers(22)
+    a = [t.copy() for t in (m, v, p)]
+    hp = dict(lr=LR2, beta1=0.9, beta2=0.999, eps=1e-8, bias_correction=bias_correction, step=step)
+    ratios = oracle.lamb_warmup_step(g, a[0], a[1], a[2], off, **hp)
+    for c in range(off.size - 1):
+        lo, hi = int(off[c]), int(off[c + 1])
+        m2, v2, p2 = (t[lo:hi].copy() for t in (m, v, p))
+        oracle.warmup_step(g[lo:hi].copy(), m2, v2, p2, **dict(hp, lr=LR2 * float(ratios[c])))
+        for x, y in ((m2, a[0]), (v2, a[1]), (p2, a[2])):
+            assert np.array_equal(x, y[lo:hi]), f"layer {c}"
+
+
+def test_lamb_ratio_vs_fsum():
+    """r = ||w|| / ||u|| per layer, from correctly rounded sums (within 2 ulp of the double path)."""
+    off, g, err, m, v, p = _lamb_layers(23)
+    p0 = p.copy()
+    eps = 1e-8
+    _, _, ratios, _, _ = oracle.lamb_compress_step(g, err, m, v, p, off, lr=LR2, beta1=0.9, eps=eps)
+    for c in range(off.size - 1):
+        lo, hi = int(off[c]), int(off[c + 1])
+        u = m[lo:hi].astype(np.float64) / (np.sqrt(v[lo:hi].astype(np.float64)) + np.float64(np.float32(eps)))
+        w = p0[lo:hi].astype(np.float64)
+        r = math.sqrt(math.fsum(w * w)) / math.sqrt(math.fsum(u * u))
+        assert abs(float(ratios[c]) - r) <= 2 * float(np.spacing(np.float32(r))), f"layer {c}"
+
+
+def test_lamb_scale_invariances():
+    """Exact consequences of r = ||w|| / ||u|| (eps = 0, powers of two): p x 2 doubles r and the new
+    p; v x 4 halves u, doubles r and leaves the new p unchanged; g, err, m x 2 double x, the scale, m
+    and u, halve r, and leave the new p unchanged."""
+    off, g, err, m, v, p = _lamb_layers(24)
+    hp = dict(lr=1e-3, beta1=0.9, eps=0.0)
+
+    def run(g_, e_, m_, v_, p_):
+        e_, m_, p_ = e_.copy(), m_.copy(), p_.copy()
+        _, sc, r, _, _ = oracle.lamb_compress_step(g_, e_, m_, v_, p_, off, **hp)
+        return sc, r, e_, m_, p_
+
+    sc, r, e1, m1, p1 = run(g, err, m, v, p)
+    _, r2, _, _, p2 = run(g, err, m, v, 2 * p)
+    assert np.array_equal(r2, 2 * r) and np.array_equal(p2, 2 * p1)
+    _, r3, _, _, p3 = run(g, err, m, 4 * v, p)
+    assert np.array_equal(r3, 2 * r) and np.array_equal(p3, p1)
+    sc4, r4, e4, m4, p4 = run(2 * g, 2 * err, 2 * m, v, p)
+    assert np.array_equal(sc4, 2 * sc) and np.array_equal(r4, r / 2)
+    assert np.array_equal(e4, 2 * e1) and np.array_equal(m4, 2 * m1) and np.array_equal(p4, p1)
+
+
+def test_lamb_degenerate_layers_and_independence():
+    off, g, err, m, v, p = _lamb_layers(25)
+    p[int(off[1]):int(off[2])] = 0.0                    # a zero layer: r = 1
+    g[int(off[3]):int(off[4])] = 0.0                    # a zero direction: x = err only ...
+    err[int(off[3]):int(off[4])] = 0.0                  # ... and err = 0, m = 0 -> u = 0, r = 1
+    m[int(off[3]):int(off[4])] = 0.0
+    p[5] = np.nan                                       # NaN stays in its layer
+    full = [t.copy() for t in (err, m, p)]
+    _, _, ratios, _, _ = oracle.lamb_compress_step(g, *full[:2], v, full[2], off, lr=1e-3, beta1=0.9,
+                                                   eps=1e-8)
+    assert np.isnan(ratios[0]) and np.all(np.isnan(full[2][:int(off[1])]))
+    assert ratios[1] == 1.0 and ratios[3] == 1.0
+    assert np.array_equal(full[2][int(off[3]):], p[int(off[3]):])      # zero direction: p unchanged
+    for c in range(1, off.size - 1):
+        lo, hi = int(off[c]), int(off[c + 1])
+        part = [t[lo:hi].copy() for t in (err, m, p)]
+        _, _, rc, _, _ = oracle.lamb_compress_step(g[lo:hi].copy(), part[0], part[1], v[lo:hi].copy(),
+                                                   part[2], np.asarray([0, hi - lo], np.int64), lr=1e-3,
+                                                   beta1=0.9, eps=1e-8)
+        assert rc[0] == ratios[c] or (np.isnan(rc[0]) and np.isnan(ratios[c]))
+        for x, y in zip(part, full):
+            assert np.array_equal(x, y[lo:hi], equal_nan=True)

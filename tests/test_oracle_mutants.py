@@ -32,8 +32,8 @@ MUTANTS = {
                         "m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)x[i]);"),
     "momentum_coeffs_swapped": ("m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)gh);",
                                 "m[i] = (float)((1.0 - b1) * (double)m[i] + b1 * (double)gh);"),
-    "update_sign": ("p[i] = (float)((double)p[i] -\n                           (double)lr",
-                    "p[i] = (float)((double)p[i] +\n                           (double)lr"),
+    "update_sign": ("p[i] = (float)((double)p[i] -\n                               (double)lr",
+                    "p[i] = (float)((double)p[i] +\n                               (double)lr"),
     "update_drops_eps": ("(sqrt((double)v[i]) + (double)eps)));\n            if (signs",
                          "(sqrt((double)v[i]))));\n            if (signs"),
     "update_no_sqrt": ("((double)m[i] / (sqrt((double)v[i]) + (double)eps)",
@@ -73,6 +73,17 @@ MUTANTS = {
     "server_divisor": ("float avg = (float)(a / (double)W);", "float avg = (float)(a / (double)(W + 1));"),
     "server_error_uses_avg": ("server_err[i] = (float)((double)x[i] - (double)gh);",
                               "server_err[i] = (float)((double)x[i] - (double)gh + (double)server_err[i]);"),
+    "lamb_ratio_inverted": ("(float)(sqrt(sw) / sqrt(su))", "(float)(sqrt(su) / sqrt(sw))"),
+    "lamb_ratio_squared": ("(float)(sqrt(sw) / sqrt(su))", "(float)(sw / su)"),
+    "lamb_degenerate_zero": ("(sw == 0.0 || su == 0.0) ? 1.0f :", "(sw == 0.0 || su == 0.0) ? 0.0f :"),
+    "lamb_u_drops_eps": ("(sqrt((double)v[i] / bc2) + (double)eps)", "(sqrt((double)v[i] / bc2))", 2),
+    "lamb_update_without_ratio": ("(double)lr * ((double)r * u)", "(double)lr * u"),
+    "lamb_dense_no_bias_correction": ("lamb_update(K, off, m, v, p, ratios, lr, eps, bc1, bc2);",
+                                      "lamb_update(K, off, m, v, p, ratios, lr, eps, 1.0, 1.0);"),
+    "lamb_weight_norm_of_m": ("sw += (double)p[i] * (double)p[i];", "sw += (double)m[i] * (double)m[i];"),
+    "lamb_compress_also_adam": ("nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 0);",
+                                "nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 1);"),
+    "lamb_dense_also_adam": ("bias_correction, step, 0);", "bias_correction, step, 1);"),
     "unpack_polarity": ("out[i] = word_bit(words, i) ? scales[c] : -scales[c];",
                         "out[i] = word_bit(words, i) ? -scales[c] : scales[c];"),
 }
