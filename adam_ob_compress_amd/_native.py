@@ -18,11 +18,11 @@ OB_OK, OB_ERR_ARG, OB_ERR_ALIGN, OB_ERR_DTYPE, OB_ERR_HIP, OB_ERR_OOM = range(6)
 OB_F32, OB_BF16, OB_F16 = 0, 1, 2
 OB_EF_PLAIN, OB_EF_EMA = 0, 1
 (OB_KERNEL_CHUNK_SUMSQ, OB_KERNEL_COMPRESS, OB_KERNEL_DENSE, OB_KERNEL_SERVER_SUMSQ,
- OB_KERNEL_SERVER_APPLY, OB_KERNEL_UNPACK) = range(6)
+ OB_KERNEL_SERVER_APPLY, OB_KERNEL_UNPACK, OB_KERNEL_TRUST_RATIO, OB_KERNEL_LAMB_APPLY) = range(8)
 KERNEL_NAMES = {
     OB_KERNEL_CHUNK_SUMSQ: "chunk_sumsq", OB_KERNEL_COMPRESS: "compress", OB_KERNEL_DENSE: "dense",
     OB_KERNEL_SERVER_SUMSQ: "server_sumsq", OB_KERNEL_SERVER_APPLY: "server_apply",
-    OB_KERNEL_UNPACK: "unpack",
+    OB_KERNEL_UNPACK: "unpack", OB_KERNEL_TRUST_RATIO: "trust_ratio", OB_KERNEL_LAMB_APPLY: "lamb_apply",
 }
 
 
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         "ob_plan_block_elems": (I64, [P]),
         "ob_adam_warmup_step": (I32, [P, P, I32, P, P, P, HP, P]),
         "ob_adam_compress_step": (I32, [P, P, I32, P, I32, P, P, P, P, P, P, P, HP, P]),
+        "ob_lamb_compress_step": (I32, [P, P, I32, P, I32, P, P, P, P, P, P, P, P, HP, P]),
+        "ob_lamb_warmup_step": (I32, [P, P, I32, P, P, P, P, HP, P]),
         "ob_server_reduce": (I32, [P, I32, P, P, P, P, P, P]),
         "ob_pack": (I32, [P, I32, I64, P, P]),
         "ob_unpack": (I32, [P, P, I64, P, P, P]),
@@ -205,6 +207,36 @@ def ob_adam_compress_step(plan: Plan, g, err, m, v, p, words_out, scales_out, hp
         _dev(p, "p"),
         _dev(words_out, "words_out"), _dev(scales_out, "scales_out"), _dev(signs_out, "signs_out"),
         _dev(nonfinite_out, "nonfinite_out"), ctypes.byref(hp), _stream(stream)), "ob_adam_compress_step")
+
+
+def ob_lamb_compress_step(plan: Plan, g, err, m, v, p, words_out, scales_out, ratios_out, hp: ob_hparams,
+                          signs_out=None, nonfinite_out=None, stream=None):
+    n = plan.n
+    _want(g, "g", g.dtype, n)
+    _want(err, "err", err.dtype, n)
+    for name, t in (("m", m), ("v", v), ("p", p)):
+        _want(t, name, torch.float32, n)
+    _want(words_out, "words_out", torch.int32, (n + 31) // 32)
+    _want(scales_out, "scales_out", torch.float32, plan.num_chunks)
+    _want(ratios_out, "ratios_out", torch.float32, plan.num_chunks)
+    _want(signs_out, "signs_out", torch.int8, n)
+    _want(nonfinite_out, "nonfinite_out", torch.int64, 1)
+    _check(lib().ob_lamb_compress_step(
+        plan.handle, _dev(g, "g"), _gdtype(g), _dev(err, "err"), _errdtype(err), _dev(m, "m"), _dev(v, "v"),
+        _dev(p, "p"), _dev(words_out, "words_out"), _dev(scales_out, "scales_out"),
+        _dev(ratios_out, "ratios_out"), _dev(signs_out, "signs_out"), _dev(nonfinite_out, "nonfinite_out"),
+        ctypes.byref(hp), _stream(stream)), "ob_lamb_compress_step")
+
+
+def ob_lamb_warmup_step(plan: Plan, g, m, v, p, ratios_out, hp: ob_hparams, stream=None):
+    n = plan.n
+    _want(g, "g", g.dtype, n)
+    for name, t in (("m", m), ("v", v), ("p", p)):
+        _want(t, name, torch.float32, n)
+    _want(ratios_out, "ratios_out", torch.float32, plan.num_chunks)
+    _check(lib().ob_lamb_warmup_step(plan.handle, _dev(g, "g"), _gdtype(g), _dev(m, "m"), _dev(v, "v"),
+                                     _dev(p, "p"), _dev(ratios_out, "ratios_out"), ctypes.byref(hp),
+                                     _stream(stream)), "ob_lamb_warmup_step")
 
 
 def ob_server_reduce(plan: Plan, worker_words, worker_scales, server_err, words_out, scales_out,

@@ -19,6 +19,8 @@ struct ob_plan_s {
     int32_t K = 0;
     int64_t* d_chunk_off = nullptr;
     double* d_partials = nullptr;  // one per pass-1 block
+    double* d_partials_w = nullptr;  // LAMB: one per pass-1 or dense block (the larger)
+    double* d_partials_u = nullptr;  // LAMB: one per compressed-pass-2 or dense block (the larger)
 
     // block tables, one per kernel kind (kTables)
     struct Table {
@@ -47,6 +49,10 @@ struct ob_plan_s {
         pd.p1_first = t[0].d_first;
         pd.chunk_off = d_chunk_off;
         pd.partials = d_partials;
+        pd.partials_w = d_partials_w;
+        pd.w_first = nullptr;
+        pd.partials_u = d_partials_u;
+        pd.u_first = nullptr;
         pd.n = n;
         pd.n_items = t[table].n_items;
         pd.K = K;
@@ -123,6 +129,8 @@ void free_plan(ob_plan p)
     }
     if (p->d_chunk_off) (void)hipFree(p->d_chunk_off);
     if (p->d_partials) (void)hipFree(p->d_partials);
+    if (p->d_partials_w) (void)hipFree(p->d_partials_w);
+    if (p->d_partials_u) (void)hipFree(p->d_partials_u);
     delete p;
 }
 
@@ -180,6 +188,25 @@ ob_status drain_timing(ob_plan p)
 
 // gradient / packed-input types
 bool valid_dtype(int d) { return d == OB_F32 || d == OB_BF16; }
+
+ob::DenseParams dense_params(const ob_hparams* hp)
+{
+    ob::DenseParams dp;
+    dp.lr = hp->lr;
+    dp.beta1 = hp->beta1;
+    dp.one_m_beta1 = 1.0 - static_cast<double>(hp->beta1);
+    dp.beta2 = hp->beta2;
+    dp.one_m_beta2 = 1.0 - static_cast<double>(hp->beta2);
+    dp.eps = hp->eps;
+    dp.bias_correction = hp->bias_correction ? 1 : 0;
+    dp.bc1 = 1.0;
+    dp.bc2 = 1.0;
+    if (hp->bias_correction) {
+        dp.bc1 = 1.0 - std::pow(static_cast<double>(hp->beta1), static_cast<double>(hp->step));
+        dp.bc2 = 1.0 - std::pow(static_cast<double>(hp->beta2), static_cast<double>(hp->step));
+    }
+    return dp;
+}
 // error-buffer storage formats
 bool valid_err_dtype(int d) { return d == OB_F32 || d == OB_BF16 || d == OB_F16; }
 
@@ -292,6 +319,10 @@ ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_off
                 return fail(e);
         }
         if ((e = hipMalloc(&p->d_partials, items[0].size() * sizeof(double))) != hipSuccess) return fail(e);
+        const size_t nw = std::max(items[T_PASS1].size(), items[T_DENSE].size());
+        const size_t nu = std::max(items[T_COMPRESS].size(), items[T_DENSE].size());
+        if ((e = hipMalloc(&p->d_partials_w, nw * sizeof(double))) != hipSuccess) return fail(e);
+        if ((e = hipMalloc(&p->d_partials_u, nu * sizeof(double))) != hipSuccess) return fail(e);
         if ((e = hipMalloc(&p->d_chunk_off, off.size() * sizeof(int64_t))) != hipSuccess) return fail(e);
         if ((e = hipMemcpy(p->d_chunk_off, off.data(), off.size() * sizeof(int64_t), hipMemcpyHostToDevice)) !=
             hipSuccess)
@@ -325,31 +356,25 @@ ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, flo
     if (!aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16)) return OB_ERR_ALIGN;
     if (hp->bias_correction && hp->step < 1) return OB_ERR_ARG;
 
-    ob::DenseParams dp;
-    dp.lr = hp->lr;
-    dp.beta1 = hp->beta1;
-    dp.one_m_beta1 = 1.0 - static_cast<double>(hp->beta1);
-    dp.beta2 = hp->beta2;
-    dp.one_m_beta2 = 1.0 - static_cast<double>(hp->beta2);
-    dp.eps = hp->eps;
-    dp.bias_correction = hp->bias_correction ? 1 : 0;
-    dp.bc1 = 1.0;
-    dp.bc2 = 1.0;
-    if (hp->bias_correction) {
-        dp.bc1 = 1.0 - std::pow(static_cast<double>(hp->beta1), static_cast<double>(hp->step));
-        dp.bc2 = 1.0 - std::pow(static_cast<double>(hp->beta2), static_cast<double>(hp->step));
-    }
+    const ob::DenseParams dp = dense_params(hp);
     DeviceGuard guard(plan->device);
     if (!guard.ok) return OB_ERR_HIP;
     const ob::PlanDev pd = plan->dev(T_DENSE);
     const int bf = g_dtype == OB_BF16;
-    return timed(plan, OB_KERNEL_DENSE, stream, [&] { return ob::launch_dense(pd, g, bf, m, v, p, dp, stream); });
+    return timed(plan, OB_KERNEL_DENSE, stream,
+                 [&] { return ob::launch_dense(pd, g, bf, m, v, p, 0, dp, stream); });
 }
 
-ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
-                                float* m, const float* v, float* p, uint32_t* words_out, float* scales_out,
-                                int8_t* signs_out, uint64_t* nonfinite_out, const ob_hparams* hp,
-                                hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// Validation and passes 1-2 of the compressed step.  lamb != 0: passes 1-2 of the 1-bit LAMB step
+// (sums of p^2 and u^2 instead of the update); the caller then runs the trust ratio and the update.
+ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
+                          float* m, const float* v, float* p, uint32_t* words_out, float* scales_out,
+                          int8_t* signs_out, uint64_t* nonfinite_out, const ob_hparams* hp, int lamb,
+                          hipStream_t stream)
 {
     if (!plan || !hp) return OB_ERR_ARG;
     if (!valid_dtype(g_dtype) || !valid_err_dtype(err_dtype)) return OB_ERR_DTYPE;
@@ -378,11 +403,12 @@ ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, v
     const int bf = g_dtype == OB_BF16;
     const int ema = hp->ef_mode == OB_EF_EMA;
     auto nf = reinterpret_cast<unsigned long long*>(nonfinite_out);
+    const float* lamb_p = lamb ? p : nullptr;
     ob_status st = timed(plan, OB_KERNEL_CHUNK_SUMSQ, stream, [&] {
         switch (err_dtype) {
-        case OB_BF16: return ob::launch_chunk_sumsq<OB_BF16>(pd1, g, bf, err, cp.clip, stream);
-        case OB_F16: return ob::launch_chunk_sumsq<OB_F16>(pd1, g, bf, err, cp.clip, stream);
-        default: return ob::launch_chunk_sumsq<OB_F32>(pd1, g, bf, err, cp.clip, stream);
+        case OB_BF16: return ob::launch_chunk_sumsq<OB_BF16>(pd1, g, bf, err, cp.clip, lamb_p, stream);
+        case OB_F16: return ob::launch_chunk_sumsq<OB_F16>(pd1, g, bf, err, cp.clip, lamb_p, stream);
+        default: return ob::launch_chunk_sumsq<OB_F32>(pd1, g, bf, err, cp.clip, lamb_p, stream);
         }
     });
     if (st != OB_OK) return st;
@@ -390,15 +416,92 @@ ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, v
         switch (err_dtype) {
         case OB_BF16:
             return ob::launch_compress<OB_BF16>(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf,
-                                                ema, cp, stream);
+                                                ema, lamb, cp, stream);
         case OB_F16:
             return ob::launch_compress<OB_F16>(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf,
-                                               ema, cp, stream);
+                                               ema, lamb, cp, stream);
         default:
             return ob::launch_compress<OB_F32>(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf,
-                                               ema, cp, stream);
+                                               ema, lamb, cp, stream);
         }
     });
+}
+
+ob::LambParams lamb_params(const ob_hparams* hp, double bc1, double bc2)
+{
+    ob::LambParams lp;
+    lp.lr = hp->lr;
+    lp.eps = hp->eps;
+    lp.bc1 = bc1;
+    lp.bc2 = bc2;
+    return lp;
+}
+
+// Trust ratios of every layer from the per-block sums (tables w_table / u_table), then the update on
+// the dense block table.
+ob_status lamb_finish(ob_plan plan, int w_table, int u_table, const float* m, const float* v, float* p,
+                      float* ratios_out, int bias_correction, const ob::LambParams& lp, hipStream_t stream)
+{
+    ob::PlanDev pr = plan->dev(T_DENSE);
+    pr.w_first = plan->t[w_table].d_first;
+    pr.u_first = plan->t[u_table].d_first;
+    ob_status st = timed(plan, OB_KERNEL_TRUST_RATIO, stream,
+                         [&] { return ob::launch_trust_ratio(pr, ratios_out, stream); });
+    if (st != OB_OK) return st;
+    const ob::PlanDev pa = plan->dev(T_DENSE);
+    return timed(plan, OB_KERNEL_LAMB_APPLY, stream, [&] {
+        return ob::launch_lamb_apply(pa, m, v, p, ratios_out, bias_correction, lp, stream);
+    });
+}
+
+}  // namespace
+
+extern "C" {
+
+ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
+                                float* m, const float* v, float* p, uint32_t* words_out, float* scales_out,
+                                int8_t* signs_out, uint64_t* nonfinite_out, const ob_hparams* hp,
+                                hipStream_t stream)
+{
+    return compress_passes(plan, g, g_dtype, err, err_dtype, m, v, p, words_out, scales_out, signs_out,
+                           nonfinite_out, hp, 0, stream);
+}
+
+ob_status ob_lamb_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
+                                float* m, const float* v, float* p, uint32_t* words_out, float* scales_out,
+                                float* ratios_out, int8_t* signs_out, uint64_t* nonfinite_out,
+                                const ob_hparams* hp, hipStream_t stream)
+{
+    if (!plan || !hp) return OB_ERR_ARG;
+    if (plan->n > 0 && (!ratios_out || !aligned(ratios_out, 4))) return ratios_out ? OB_ERR_ALIGN : OB_ERR_ARG;
+    ob_status st = compress_passes(plan, g, g_dtype, err, err_dtype, m, v, p, words_out, scales_out, signs_out,
+                                   nonfinite_out, hp, 1, stream);
+    if (st != OB_OK || plan->n == 0) return st;
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return OB_ERR_HIP;
+    return lamb_finish(plan, T_PASS1, T_COMPRESS, m, v, p, ratios_out, 0, lamb_params(hp, 1.0, 1.0), stream);
+}
+
+ob_status ob_lamb_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* m, float* v, float* p,
+                              float* ratios_out, const ob_hparams* hp, hipStream_t stream)
+{
+    if (!plan || !hp) return OB_ERR_ARG;
+    if (!valid_dtype(g_dtype)) return OB_ERR_DTYPE;
+    if (plan->n == 0) return OB_OK;
+    if (ob_status st = check_grad(g, g_dtype)) return st;
+    if (!m || !v || !p || !ratios_out) return OB_ERR_ARG;
+    if (!aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16) || !aligned(ratios_out, 4)) return OB_ERR_ALIGN;
+    if (hp->bias_correction && hp->step < 1) return OB_ERR_ARG;
+    const ob::DenseParams dp = dense_params(hp);
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return OB_ERR_HIP;
+    const ob::PlanDev pd = plan->dev(T_DENSE);
+    const int bf = g_dtype == OB_BF16;
+    ob_status st = timed(plan, OB_KERNEL_DENSE, stream,
+                         [&] { return ob::launch_dense(pd, g, bf, m, v, p, 1, dp, stream); });
+    if (st != OB_OK) return st;
+    return lamb_finish(plan, T_DENSE, T_DENSE, m, v, p, ratios_out, dp.bias_correction,
+                       lamb_params(hp, dp.bc1, dp.bc2), stream);
 }
 
 ob_status ob_server_reduce(ob_plan plan, int32_t W, const uint32_t* worker_words, const float* worker_scales,

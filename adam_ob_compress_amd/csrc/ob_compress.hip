@@ -8,6 +8,8 @@
 //        (clip before quantizing, NaN check, int8 signs).
 //   [P2] "DeepSpeed Communication Compression and Hiding": "1-bit Adam: warmup, frozen variance,
 //        error feedback" (compressed branch of the two-phase step, dequantize).
+//        "1-bit LAMB: also protect the layer-wise trust ratio" (the LAMB variant: the layer's
+//        norms are taken on the reconstructed direction; the update itself is in ob_kernels.hip).
 //   [P3] gradient-compression survey (bmjup.com post 14450): Q&A on the memory cost of error
 //        feedback (a 16-bit error term).
 //
@@ -35,25 +37,28 @@ namespace {
 
 // ------------------------------------------------------------------------------------------------
 // compressed step, pass 1: per-block sum of squares of x = clip(g) + err
+// (LAMB: and of the parameters, for the layer's ||w||)
 // ------------------------------------------------------------------------------------------------
 
-template <class G, class E, bool CLIP>
+template <class G, class E, bool CLIP, bool LAMB>
 __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typename G::T* __restrict__ g,
-                                                        const typename E::T* __restrict__ err, float clip)
+                                                        const typename E::T* __restrict__ err, float clip,
+                                                        const float* __restrict__ p)
 {
     __shared__ double lds[kBlock / 64];
     const Item it = pd.items[blockIdx.x];
     const int tid = threadIdx.x;
-    double acc = 0.0;
+    double acc = 0.0, accw = 0.0;
     constexpr int U = OB_P1_UNROLL;
     int base = 0;
     for (; base + U * kTile <= it.len; base += U * kTile) {
-        f4 gv[U], ev[U];
+        f4 gv[U], ev[U], pv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = it.start + base + u * kTile + kVec * tid;
             gv[u] = G::template load4<OB_NT_P1>(g, i);
             ev[u] = E::template load4<OB_NT_P1>(err, i);
+            if (LAMB) pv[u] = ld4<OB_NT_P1>(p, i);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -61,6 +66,7 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
             for (int k = 0; k < kVec; ++k) {
                 const double x = compensate<CLIP>(gv[u][k], ev[u][k], clip);
                 acc = fma(x, x, acc);
+                if (LAMB) accw = fma(static_cast<double>(pv[u][k]), static_cast<double>(pv[u][k]), accw);
             }
         }
     }
@@ -69,10 +75,13 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
         const int64_t i = it.start + base + kVec * tid;
         if (cnt >= kVec) {
             const f4 gv = G::load4(g, i), ev = E::load4(err, i);
+            f4 pv = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (LAMB) pv = ld4(p, i);
 #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 const double x = compensate<CLIP>(gv[k], ev[k], clip);
                 acc = fma(x, x, acc);
+                if (LAMB) accw = fma(static_cast<double>(pv[k]), static_cast<double>(pv[k]), accw);
             }
         } else {
             #pragma unroll
@@ -80,18 +89,24 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
                 if (k >= cnt) continue;
                 const double x = compensate<CLIP>(G::load1(g, i + k), E::load1(err, i + k), clip);
                 acc = fma(x, x, acc);
+                if (LAMB) accw = fma(static_cast<double>(p[i + k]), static_cast<double>(p[i + k]), accw);
             }
         }
     }
     const double s = block_sum(acc, lds);
     if (tid == 0) pd.partials[blockIdx.x] = s;
+    if (LAMB) {
+        const double sw = block_sum(accw, lds);
+        if (tid == 0) pd.partials_w[blockIdx.x] = sw;
+    }
 }
 
 // ------------------------------------------------------------------------------------------------
 // compressed step, pass 2: scale, sign bits, error, m, p in one streaming pass
+// (LAMB: no update of p; the block's sum of u^2 for the layer's ||u|| instead)
 // ------------------------------------------------------------------------------------------------
 
-template <class G, class E, bool CLIP, bool EMA, bool SIGNS, bool NONFIN>
+template <class G, class E, bool CLIP, bool EMA, bool SIGNS, bool NONFIN, bool LAMB>
 __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename G::T* __restrict__ g,
                                                      typename E::T* __restrict__ err, float* __restrict__ m,
                                                      const float* __restrict__ v, float* __restrict__ p,
@@ -107,6 +122,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
     if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
 
     uint32_t nf = 0;
+    double usq = 0.0;
     constexpr int U = OB_P2_UNROLL;
     int base = 0;
     for (; base + U * kTile <= it.len; base += U * kTile) {
@@ -118,7 +134,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
             ev[u] = E::template load4<OB_NT_P2>(err, i);
             mv[u] = ld4<OB_NT_P2>(m, i);
             vv[u] = ld4<OB_NT_P2>(v, i);
-            pv[u] = ld4<OB_NT_P2>(p, i);
+            if (!LAMB) pv[u] = ld4<OB_NT_P2>(p, i);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -127,17 +143,17 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
 #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 const float x = compensate<CLIP>(gv[u][k], ev[u][k], cp.clip);
-                float e = ev[u][k], mm = mv[u][k], pp = pv[u][k];
-                nib |= compress_elem<EMA>(x, e, mm, vv[u][k], pp, scale, cp) << k;
+                float e = ev[u][k], mm = mv[u][k], pp = LAMB ? 0.0f : pv[u][k];
+                nib |= compress_elem<EMA, LAMB>(x, e, mm, vv[u][k], pp, usq, scale, cp) << k;
                 e = E::rounded(e);
                 ev[u][k] = e;
                 mv[u][k] = mm;
-                pv[u][k] = pp;
+                if (!LAMB) pv[u][k] = pp;
                 if (NONFIN) nf += __builtin_isfinite(e) ? 0u : 1u;
             }
             E::template store4<OB_NT_ST>(err, i, ev[u]);
             st4<OB_NT_ST>(m, i, mv[u]);
-            st4<OB_NT_ST>(p, i, pv[u]);
+            if (!LAMB) st4<OB_NT_ST>(p, i, pv[u]);
             if (SIGNS) {
                 uint32_t* sp = reinterpret_cast<uint32_t*>(signs + i);
                 if (OB_NT_BITS)
@@ -155,12 +171,13 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
         uint32_t nib = 0;
         if (cnt >= kVec) {
             const f4 gv = G::load4(g, i), vv = ld4(v, i);
-            f4 ev = E::load4(err, i), mv = ld4(m, i), pv = ld4(p, i);
+            f4 ev = E::load4(err, i), mv = ld4(m, i), pv = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (!LAMB) pv = ld4(p, i);
 #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 const float x = compensate<CLIP>(gv[k], ev[k], cp.clip);
                 float e = ev[k], mm = mv[k], pp = pv[k];
-                nib |= compress_elem<EMA>(x, e, mm, vv[k], pp, scale, cp) << k;
+                nib |= compress_elem<EMA, LAMB>(x, e, mm, vv[k], pp, usq, scale, cp) << k;
                 e = E::rounded(e);
                 ev[k] = e;
                 mv[k] = mm;
@@ -169,20 +186,20 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
             }
             E::store4(err, i, ev);
             st4(m, i, mv);
-            st4(p, i, pv);
+            if (!LAMB) st4(p, i, pv);
             if (SIGNS) *reinterpret_cast<uint32_t*>(signs + i) = signs4(nib);
         } else if (cnt > 0) {
             #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 if (k >= cnt) continue;
-                float e = E::load1(err, i + k), mm = m[i + k], pp = p[i + k];
+                float e = E::load1(err, i + k), mm = m[i + k], pp = LAMB ? 0.0f : p[i + k];
                 const float x = compensate<CLIP>(G::load1(g, i + k), e, cp.clip);
-                const uint32_t b = compress_elem<EMA>(x, e, mm, v[i + k], pp, scale, cp);
+                const uint32_t b = compress_elem<EMA, LAMB>(x, e, mm, v[i + k], pp, usq, scale, cp);
                 nib |= b << k;
                 e = E::rounded(e);
                 E::store1(err, i + k, e);
                 m[i + k] = mm;
-                p[i + k] = pp;
+                if (!LAMB) p[i + k] = pp;
                 if (SIGNS) signs[i + k] = b ? int8_t(1) : int8_t(-1);
                 if (NONFIN) nf += __builtin_isfinite(e) ? 0u : 1u;
             }
@@ -194,6 +211,10 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
         const uint32_t t = block_sum_u32(nf, ldsu);
         if (tid == 0 && t) atomicAdd(nonfinite, static_cast<unsigned long long>(t));
     }
+    if (LAMB) {
+        const double su = block_sum(usq, lds);
+        if (tid == 0) pd.partials_u[blockIdx.x] = su;
+    }
 }
 
 }  // namespace
@@ -202,32 +223,37 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
 // launchers
 // ------------------------------------------------------------------------------------------------
 
+namespace {
+template <class G, class E>
+void sumsq_dispatch(int sel, dim3 grid, dim3 block, hipStream_t s, const PlanDev& pd, const typename G::T* g,
+                    const typename E::T* err, float clip, const float* p)
+{
+    switch (sel) {
+    case 0: hipLaunchKernelGGL((k_chunk_sumsq<G, E, false, false>), grid, block, 0, s, pd, g, err, clip, p); break;
+    case 1: hipLaunchKernelGGL((k_chunk_sumsq<G, E, true, false>), grid, block, 0, s, pd, g, err, clip, p); break;
+    case 2: hipLaunchKernelGGL((k_chunk_sumsq<G, E, false, true>), grid, block, 0, s, pd, g, err, clip, p); break;
+    default: hipLaunchKernelGGL((k_chunk_sumsq<G, E, true, true>), grid, block, 0, s, pd, g, err, clip, p); break;
+    }
+}
+}  // namespace
+
 template <int EF>
 hipError_t launch_chunk_sumsq(const PlanDev& pd, const void* g, int g_bf16, const void* err_v, float clip,
-                              hipStream_t s)
+                              const float* lamb_p, hipStream_t s)
 {
     using E = typename ErrOf<EF>::type;
     auto err = static_cast<const typename E::T*>(err_v);
     const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
-    const bool cl = clip > 0.0f;
-    if (g_bf16) {
-        auto gp = static_cast<const uint16_t*>(g);
-        if (cl)
-            hipLaunchKernelGGL((k_chunk_sumsq<GradBF16, E, true>), grid, block, 0, s, pd, gp, err, clip);
-        else
-            hipLaunchKernelGGL((k_chunk_sumsq<GradBF16, E, false>), grid, block, 0, s, pd, gp, err, clip);
-    } else {
-        auto gp = static_cast<const float*>(g);
-        if (cl)
-            hipLaunchKernelGGL((k_chunk_sumsq<GradF32, E, true>), grid, block, 0, s, pd, gp, err, clip);
-        else
-            hipLaunchKernelGGL((k_chunk_sumsq<GradF32, E, false>), grid, block, 0, s, pd, gp, err, clip);
-    }
+    const int sel = (clip > 0.0f ? 1 : 0) | (lamb_p ? 2 : 0);
+    if (g_bf16)
+        sumsq_dispatch<GradBF16, E>(sel, grid, block, s, pd, static_cast<const uint16_t*>(g), err, clip, lamb_p);
+    else
+        sumsq_dispatch<GradF32, E>(sel, grid, block, s, pd, static_cast<const float*>(g), err, clip, lamb_p);
     return hipGetLastError();
 }
 
 namespace {
-template <class G, class E, bool CLIP, bool EMA>
+template <class G, class E, bool CLIP, bool EMA, bool LAMB>
 void compress_dispatch(const PlanDev& pd, const typename G::T* g, typename E::T* err, float* m, const float* v,
                        float* p, uint32_t* words, float* scales, int8_t* signs,
                        unsigned long long* nonfinite, const CompressParams& cp, hipStream_t s)
@@ -236,20 +262,20 @@ void compress_dispatch(const PlanDev& pd, const typename G::T* g, typename E::T*
     const int sel = (signs ? 1 : 0) | (nonfinite ? 2 : 0);
     switch (sel) {
     case 0:
-        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, false, false>), grid, block, 0, s, pd, g, err, m, v,
-                           p, words, scales, signs, nonfinite, cp);
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, false, false, LAMB>), grid, block, 0, s, pd, g, err, m,
+                           v, p, words, scales, signs, nonfinite, cp);
         break;
     case 1:
-        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, true, false>), grid, block, 0, s, pd, g, err, m, v,
-                           p, words, scales, signs, nonfinite, cp);
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, true, false, LAMB>), grid, block, 0, s, pd, g, err, m,
+                           v, p, words, scales, signs, nonfinite, cp);
         break;
     case 2:
-        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, false, true>), grid, block, 0, s, pd, g, err, m, v,
-                           p, words, scales, signs, nonfinite, cp);
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, false, true, LAMB>), grid, block, 0, s, pd, g, err, m,
+                           v, p, words, scales, signs, nonfinite, cp);
         break;
     default:
-        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, true, true>), grid, block, 0, s, pd, g, err, m, v,
-                           p, words, scales, signs, nonfinite, cp);
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, true, true, LAMB>), grid, block, 0, s, pd, g, err, m,
+                           v, p, words, scales, signs, nonfinite, cp);
         break;
     }
 }
@@ -257,41 +283,50 @@ void compress_dispatch(const PlanDev& pd, const typename G::T* g, typename E::T*
 template <class G, class E>
 void compress_dispatch_g(const PlanDev& pd, const typename G::T* g, typename E::T* err, float* m, const float* v,
                          float* p, uint32_t* words, float* scales, int8_t* signs,
-                         unsigned long long* nonfinite, int ema, const CompressParams& cp, hipStream_t s)
+                         unsigned long long* nonfinite, int ema, int lamb, const CompressParams& cp,
+                         hipStream_t s)
 {
-    const bool cl = cp.clip > 0.0f;
-    if (cl && ema)
-        compress_dispatch<G, E, true, true>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
-    else if (cl)
-        compress_dispatch<G, E, true, false>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
-    else if (ema)
-        compress_dispatch<G, E, false, true>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
-    else
-        compress_dispatch<G, E, false, false>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s);
+    const int sel = (cp.clip > 0.0f ? 1 : 0) | (ema ? 2 : 0) | (lamb ? 4 : 0);
+#define OB_CASE(k, CL, EM, LA)                                                                              \
+    case k:                                                                                                  \
+        compress_dispatch<G, E, CL, EM, LA>(pd, g, err, m, v, p, words, scales, signs, nonfinite, cp, s); \
+        break;
+    switch (sel) {
+        OB_CASE(0, false, false, false)
+        OB_CASE(1, true, false, false)
+        OB_CASE(2, false, true, false)
+        OB_CASE(3, true, true, false)
+        OB_CASE(4, false, false, true)
+        OB_CASE(5, true, false, true)
+        OB_CASE(6, false, true, true)
+        OB_CASE(7, true, true, true)
+    }
+#undef OB_CASE
 }
 }  // namespace
 
 template <int EF>
 hipError_t launch_compress(const PlanDev& pd, const void* g, int g_bf16, void* err_v, float* m, const float* v,
                            float* p, uint32_t* words, float* scales, int8_t* signs,
-                           unsigned long long* nonfinite, int ema, const CompressParams& cp, hipStream_t s)
+                           unsigned long long* nonfinite, int ema, int lamb, const CompressParams& cp,
+                           hipStream_t s)
 {
     using E = typename ErrOf<EF>::type;
     auto err = static_cast<typename E::T*>(err_v);
     if (g_bf16)
         compress_dispatch_g<GradBF16, E>(pd, static_cast<const uint16_t*>(g), err, m, v, p, words, scales,
-                                      signs, nonfinite, ema, cp, s);
+                                         signs, nonfinite, ema, lamb, cp, s);
     else
-        compress_dispatch_g<GradF32, E>(pd, static_cast<const float*>(g), err, m, v, p, words, scales,
-                                     signs, nonfinite, ema, cp, s);
+        compress_dispatch_g<GradF32, E>(pd, static_cast<const float*>(g), err, m, v, p, words, scales, signs,
+                                        nonfinite, ema, lamb, cp, s);
     return hipGetLastError();
 }
 
 // this build's format
 template hipError_t launch_chunk_sumsq<OB_ERR_FMT>(const PlanDev&, const void*, int, const void*, float,
-                                                   hipStream_t);
+                                                   const float*, hipStream_t);
 template hipError_t launch_compress<OB_ERR_FMT>(const PlanDev&, const void*, int, void*, float*, const float*,
                                                 float*, uint32_t*, float*, int8_t*, unsigned long long*, int,
-                                                const CompressParams&, hipStream_t);
+                                                int, const CompressParams&, hipStream_t);
 
 }  // namespace ob

@@ -317,8 +317,10 @@ __device__ __forceinline__ float compensate(float g, float e, float clip)
 // One element of the compressed step; returns the sign bit (1 <=> +1).
 // x, g_hat and delta are single fp32 operations; the error (EMA), m and p lines are evaluated in
 // double and rounded once, so a large update that nearly cancels p keeps full fp32 accuracy.
-template <bool EMA>
-__device__ __forceinline__ uint32_t compress_elem(float x, float& e, float& mm, float vv, float& pp,
+// LAMB: p is left alone; u = m / (sqrt(v) + eps) (double, not stored) adds u^2 to usq for the layer's
+// trust ratio.
+template <bool EMA, bool LAMB>
+__device__ __forceinline__ uint32_t compress_elem(float x, float& e, float& mm, float vv, float& pp, double& usq,
                                                   float scale, const CompressParams& cp)
 {
     const bool b = x >= 0.0f;
@@ -331,7 +333,12 @@ __device__ __forceinline__ uint32_t compress_elem(float x, float& e, float& mm, 
     // m on g_hat ([P1] sec. 2.2; [P2]), then the frozen-v update with the stored (new) m ([P2])
     mm = static_cast<float>(cp.beta1 * static_cast<double>(mm) + cp.one_m_beta1 * static_cast<double>(gh));
     const double den = sqrt(static_cast<double>(vv)) + cp.eps;
-    pp = static_cast<float>(static_cast<double>(pp) - cp.lr * (static_cast<double>(mm) / den));
+    if (LAMB) {
+        const double u = static_cast<double>(mm) / den;
+        usq = fma(u, u, usq);
+    } else {
+        pp = static_cast<float>(static_cast<double>(pp) - cp.lr * (static_cast<double>(mm) / den));
+    }
     return b ? 1u : 0u;
 }
 

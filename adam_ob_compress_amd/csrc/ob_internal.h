@@ -31,6 +31,12 @@ struct PlanDev {
     const int32_t* p1_first;    // [K + 1]: the same for the pass-1 table (indexes `partials`)
     const int64_t* chunk_off;   // [K + 1]: element offsets
     double* partials;           // [pass-1 blocks]: per-block sum of squares (workspace)
+    // LAMB (layer = chunk): per-block sums of p^2 and of u^2, and the chunk_first arrays of the tables
+    // whose blocks wrote them
+    double* partials_w;
+    const int32_t* w_first;
+    double* partials_u;
+    const int32_t* u_first;
     int64_t n;
     int64_t n_items;
     int32_t K;
@@ -46,17 +52,30 @@ struct DenseParams {
     int bias_correction;
 };
 
+// LAMB update: p -= lr * r_c * (m / bc1) / (sqrt(v / bc2) + eps)
+struct LambParams {
+    double lr, eps, bc1, bc2;
+};
+
 // Compressed-step launchers for error-buffer format EF (0 fp32, 1 bf16, 2 fp16); ob_compress.hip,
 // built once per format, instantiates each.
+// lamb_p != nullptr: also the per-block sum of p^2 (LAMB), into pd.partials_w.
 template <int EF>
 hipError_t launch_chunk_sumsq(const PlanDev& pd, const void* g, int g_bf16, const void* err, float clip,
-                              hipStream_t s);
+                              const float* lamb_p, hipStream_t s);
+// lamb != 0: no parameter update; the per-block sum of u^2 goes to pd.partials_u (p is not touched).
 template <int EF>
 hipError_t launch_compress(const PlanDev& pd, const void* g, int g_bf16, void* err, float* m, const float* v,
                            float* p, uint32_t* words, float* scales, int8_t* signs,
-                           unsigned long long* nonfinite, int ema, const CompressParams& cp, hipStream_t s);
+                           unsigned long long* nonfinite, int ema, int lamb, const CompressParams& cp,
+                           hipStream_t s);
+// lamb != 0: moments only, plus per-block sums of p^2 and u^2 into pd.partials_w / partials_u.
 hipError_t launch_dense(const PlanDev& pd, const void* g, int g_bf16, float* m, float* v, float* p,
-                        const DenseParams& dp, hipStream_t s);
+                        int lamb, const DenseParams& dp, hipStream_t s);
+// One block per chunk: r_c from the chunk's partials_w / partials_u.
+hipError_t launch_trust_ratio(const PlanDev& pd, float* ratios, hipStream_t s);
+hipError_t launch_lamb_apply(const PlanDev& pd, const float* m, const float* v, float* p, const float* ratios,
+                             int bias_correction, const LambParams& lp, hipStream_t s);
 hipError_t launch_server_sumsq(const PlanDev& pd, int W, const uint32_t* ww, const float* ws,
                                const float* e, hipStream_t s);
 hipError_t launch_server_apply(const PlanDev& pd, int W, const uint32_t* ww, const float* ws,

@@ -5,7 +5,8 @@
 // Pages cited (title and section):
 //   [P2] "DeepSpeed Communication Compression and Hiding": "baseline" section (Adam moments),
 //        "1-bit Adam: warmup, frozen variance, error feedback" (dequantize, compressed_allreduce),
-//        "0/1 Adam" (refresh step = dense step).
+//        "0/1 Adam" (refresh step = dense step), "1-bit LAMB: also protect the layer-wise trust
+//        ratio" (r = ||w|| / ||u|| per layer, w -= lr * r * u).
 //
 // Design (memory bound, no dense contraction, so no MFMA): every per-element kernel walks work
 // blocks ("items") of one chunk each; a block of 256 threads = four wave64s; each lane owns 4
@@ -22,8 +23,11 @@ namespace {
 // ------------------------------------------------------------------------------------------------
 
 // Each line in double from fp32 operands, rounded once when stored; p uses the stored m and v.
-template <bool BC>
-__device__ __forceinline__ void dense_elem(float g, float& mm, float& vv, float& pp, const DenseParams& dp)
+// LAMB: p is left alone; the direction u = mh / (sqrt(vh) + eps) (double, not stored) adds u^2 to usq
+// and p^2 goes to wsq, for the layer's trust ratio.
+template <bool BC, bool LAMB>
+__device__ __forceinline__ void dense_elem(float g, float& mm, float& vv, float& pp, double& wsq, double& usq,
+                                           const DenseParams& dp)
 {
     const double gd = static_cast<double>(g);
     mm = static_cast<float>(dp.beta1 * static_cast<double>(mm) + dp.one_m_beta1 * gd);
@@ -33,16 +37,23 @@ __device__ __forceinline__ void dense_elem(float g, float& mm, float& vv, float&
         mh = mh / dp.bc1;
         vh = vh / dp.bc2;
     }
-    pp = static_cast<float>(static_cast<double>(pp) - dp.lr * (mh / (sqrt(vh) + dp.eps)));
+    const double u = mh / (sqrt(vh) + dp.eps);
+    if (LAMB) {
+        wsq = fma(static_cast<double>(pp), static_cast<double>(pp), wsq);
+        usq = fma(u, u, usq);
+    } else {
+        pp = static_cast<float>(static_cast<double>(pp) - dp.lr * u);
+    }
 }
 
-template <class G, bool BC>
+template <class G, bool BC, bool LAMB>
 __global__ __launch_bounds__(kBlock) void k_dense(PlanDev pd, const typename G::T* __restrict__ g,
                                                   float* __restrict__ m, float* __restrict__ v,
                                                   float* __restrict__ p, DenseParams dp)
 {
     const Item it = pd.items[blockIdx.x];
     const int tid = threadIdx.x;
+    double wsq = 0.0, usq = 0.0;
     constexpr int U = 2;
     int base = 0;
     for (; base + U * kTile <= it.len; base += U * kTile) {
@@ -61,14 +72,14 @@ __global__ __launch_bounds__(kBlock) void k_dense(PlanDev pd, const typename G::
 #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 float mm = mv[u][k], vq = vv[u][k], pp = pv[u][k];
-                dense_elem<BC>(gv[u][k], mm, vq, pp, dp);
+                dense_elem<BC, LAMB>(gv[u][k], mm, vq, pp, wsq, usq, dp);
                 mv[u][k] = mm;
                 vv[u][k] = vq;
                 pv[u][k] = pp;
             }
             st4<OB_NT_DENSE>(m, i, mv[u]);
             st4<OB_NT_DENSE>(v, i, vv[u]);
-            st4<OB_NT_DENSE>(p, i, pv[u]);
+            if (!LAMB) st4<OB_NT_DENSE>(p, i, pv[u]);
         }
     }
     for (; base < it.len; base += kTile) {
@@ -80,23 +91,110 @@ __global__ __launch_bounds__(kBlock) void k_dense(PlanDev pd, const typename G::
 #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 float mm = mv[k], vq = vv[k], pp = pv[k];
-                dense_elem<BC>(gv[k], mm, vq, pp, dp);
+                dense_elem<BC, LAMB>(gv[k], mm, vq, pp, wsq, usq, dp);
                 mv[k] = mm;
                 vv[k] = vq;
                 pv[k] = pp;
             }
             st4(m, i, mv);
             st4(v, i, vv);
-            st4(p, i, pv);
+            if (!LAMB) st4(p, i, pv);
         } else {
             #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 if (k >= cnt) continue;
                 float mm = m[i + k], vq = v[i + k], pp = p[i + k];
-                dense_elem<BC>(G::load1(g, i + k), mm, vq, pp, dp);
+                dense_elem<BC, LAMB>(G::load1(g, i + k), mm, vq, pp, wsq, usq, dp);
                 m[i + k] = mm;
                 v[i + k] = vq;
-                p[i + k] = pp;
+                if (!LAMB) p[i + k] = pp;
+            }
+        }
+    }
+    if (LAMB) {
+        __shared__ double lds[kBlock / 64];
+        const double sw = block_sum(wsq, lds);
+        const double su = block_sum(usq, lds);
+        if (tid == 0) {
+            pd.partials_w[blockIdx.x] = sw;
+            pd.partials_u[blockIdx.x] = su;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// LAMB ([P2] "1-bit LAMB"): the layer's trust ratio from the per-block sums, then the update
+// ------------------------------------------------------------------------------------------------
+
+// One block per layer (chunk): r = ||w|| / ||u||, the chunk's partial sums added in a fixed order;
+// r = 1 when either sum is 0 (the ratio is undefined there; NaN and Inf propagate).
+__global__ __launch_bounds__(kBlock) void k_trust_ratio(PlanDev pd, float* __restrict__ ratios)
+{
+    __shared__ double lds[kBlock / 64];
+    const int c = blockIdx.x;
+    const int tid = threadIdx.x;
+    double sw = 0.0, su = 0.0;
+    for (int i = pd.w_first[c] + tid; i < pd.w_first[c + 1]; i += kBlock) sw += pd.partials_w[i];
+    for (int i = pd.u_first[c] + tid; i < pd.u_first[c + 1]; i += kBlock) su += pd.partials_u[i];
+    sw = block_sum(sw, lds);
+    su = block_sum(su, lds);
+    if (tid == 0) ratios[c] = (sw == 0.0 || su == 0.0) ? 1.0f : static_cast<float>(sqrt(sw) / sqrt(su));
+}
+
+// p -= lr * (r * u), u = mh / (sqrt(vh) + eps) from the stored m and v, in double, rounded once.
+template <bool BC>
+__device__ __forceinline__ float lamb_elem(float mm, float vv, float pp, double r, const LambParams& lp)
+{
+    double mh = static_cast<double>(mm), vh = static_cast<double>(vv);
+    if (BC) {
+        mh = mh / lp.bc1;
+        vh = vh / lp.bc2;
+    }
+    const double u = mh / (sqrt(vh) + lp.eps);
+    return static_cast<float>(static_cast<double>(pp) - lp.lr * (r * u));
+}
+
+template <bool BC>
+__global__ __launch_bounds__(kBlock) void k_lamb_apply(PlanDev pd, const float* __restrict__ m,
+                                                       const float* __restrict__ v, float* __restrict__ p,
+                                                       const float* __restrict__ ratios, LambParams lp)
+{
+    const Item it = pd.items[blockIdx.x];
+    const int tid = threadIdx.x;
+    const double r = static_cast<double>(ratios[it.chunk]);
+    constexpr int U = 2;
+    int base = 0;
+    for (; base + U * kTile <= it.len; base += U * kTile) {
+        f4 mv[U], vv[U], pv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            mv[u] = ld4<OB_NT_DENSE>(m, i);
+            vv[u] = ld4<OB_NT_DENSE>(v, i);
+            pv[u] = ld4<OB_NT_DENSE>(p, i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) pv[u][k] = lamb_elem<BC>(mv[u][k], vv[u][k], pv[u][k], r, lp);
+            st4<OB_NT_DENSE>(p, i, pv[u]);
+        }
+    }
+    for (; base < it.len; base += kTile) {
+        const int cnt = it.len - base - kVec * tid;
+        const int64_t i = it.start + base + kVec * tid;
+        if (cnt >= kVec) {
+            const f4 mv = ld4(m, i), vv = ld4(v, i);
+            f4 pv = ld4(p, i);
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) pv[k] = lamb_elem<BC>(mv[k], vv[k], pv[k], r, lp);
+            st4(p, i, pv);
+        } else {
+            #pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                if (k >= cnt) continue;
+                p[i + k] = lamb_elem<BC>(m[i + k], v[i + k], p[i + k], r, lp);
             }
         }
     }
@@ -350,22 +448,42 @@ __global__ __launch_bounds__(kBlock) void k_pack(const typename G::T* __restrict
 // ------------------------------------------------------------------------------------------------
 
 hipError_t launch_dense(const PlanDev& pd, const void* g, int g_bf16, float* m, float* v, float* p,
-                        const DenseParams& dp, hipStream_t s)
+                        int lamb, const DenseParams& dp, hipStream_t s)
 {
     const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
-    if (g_bf16) {
-        auto gp = static_cast<const uint16_t*>(g);
-        if (dp.bias_correction)
-            hipLaunchKernelGGL((k_dense<GradBF16, true>), grid, block, 0, s, pd, gp, m, v, p, dp);
-        else
-            hipLaunchKernelGGL((k_dense<GradBF16, false>), grid, block, 0, s, pd, gp, m, v, p, dp);
-    } else {
-        auto gp = static_cast<const float*>(g);
-        if (dp.bias_correction)
-            hipLaunchKernelGGL((k_dense<GradF32, true>), grid, block, 0, s, pd, gp, m, v, p, dp);
-        else
-            hipLaunchKernelGGL((k_dense<GradF32, false>), grid, block, 0, s, pd, gp, m, v, p, dp);
+    const int sel = (dp.bias_correction ? 1 : 0) | (lamb ? 2 : 0);
+#define OB_DENSE(G, T)                                                                                   \
+    {                                                                                                    \
+        auto gp = static_cast<const T*>(g);                                                              \
+        switch (sel) {                                                                                   \
+        case 0: hipLaunchKernelGGL((k_dense<G, false, false>), grid, block, 0, s, pd, gp, m, v, p, dp); break; \
+        case 1: hipLaunchKernelGGL((k_dense<G, true, false>), grid, block, 0, s, pd, gp, m, v, p, dp); break;  \
+        case 2: hipLaunchKernelGGL((k_dense<G, false, true>), grid, block, 0, s, pd, gp, m, v, p, dp); break;  \
+        default: hipLaunchKernelGGL((k_dense<G, true, true>), grid, block, 0, s, pd, gp, m, v, p, dp); break;  \
+        }                                                                                                \
     }
+    if (g_bf16)
+        OB_DENSE(GradBF16, uint16_t)
+    else
+        OB_DENSE(GradF32, float)
+#undef OB_DENSE
+    return hipGetLastError();
+}
+
+hipError_t launch_trust_ratio(const PlanDev& pd, float* ratios, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_trust_ratio, dim3(static_cast<unsigned>(pd.K)), dim3(kBlock), 0, s, pd, ratios);
+    return hipGetLastError();
+}
+
+hipError_t launch_lamb_apply(const PlanDev& pd, const float* m, const float* v, float* p, const float* ratios,
+                             int bias_correction, const LambParams& lp, hipStream_t s)
+{
+    const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
+    if (bias_correction)
+        hipLaunchKernelGGL((k_lamb_apply<true>), grid, block, 0, s, pd, m, v, p, ratios, lp);
+    else
+        hipLaunchKernelGGL((k_lamb_apply<false>), grid, block, 0, s, pd, m, v, p, ratios, lp);
     return hipGetLastError();
 }
 

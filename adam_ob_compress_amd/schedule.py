@@ -4,7 +4,9 @@
   * section "1-bit Adam: warmup, frozen variance, error feedback": dense Adam while
     step < freeze_step (step counted from 0), the compressed step afterwards;
   * section "0/1 Adam": a full-precision variance refresh on chosen steps, 1-bit steps otherwise; the
-    refresh here is every period-th step with steps counted from 1.
+    refresh here is every period-th step with steps counted from 1;
+  * section "1-bit LAMB": the same warmup / compressed schedule with LAMB's layer-wise trust ratio
+    (OneBitLamb; the plan's chunks are the layers).
 """
 from __future__ import annotations
 
@@ -57,9 +59,31 @@ class OneBitAdam:
             self.dense_steps += 1
             self.hp.bias_correction = 1 if self.bias_correction else 0
             self.hp.step = self.dense_steps
-            nat.ob_adam_warmup_step(self.plan, g, self.m, self.v, self.p, self.hp, stream)
+            self._dense(g, stream)
         else:
-            nat.ob_adam_compress_step(self.plan, g, self.err, self.m, self.v, self.p, self.words,
-                                      self.scales, self.hp, self.signs, self.nonfinite, stream)
+            self._compressed(g, stream)
         self.step_index += 1
         return kind
+
+    def _dense(self, g, stream):
+        nat.ob_adam_warmup_step(self.plan, g, self.m, self.v, self.p, self.hp, stream)
+
+    def _compressed(self, g, stream):
+        nat.ob_adam_compress_step(self.plan, g, self.err, self.m, self.v, self.p, self.words, self.scales,
+                                  self.hp, self.signs, self.nonfinite, stream)
+
+
+class OneBitLamb(OneBitAdam):
+    """1-bit LAMB: OneBitAdam's state and schedule, with the layer-wise trust ratio in both step kinds.
+    ``self.ratios`` holds each layer's (chunk's) ratio from the last step."""
+
+    def __init__(self, plan: nat.Plan, err, m, v, p, **kw):
+        super().__init__(plan, err, m, v, p, **kw)
+        self.ratios = torch.zeros(plan.num_chunks, dtype=torch.float32, device=p.device)
+
+    def _dense(self, g, stream):
+        nat.ob_lamb_warmup_step(self.plan, g, self.m, self.v, self.p, self.ratios, self.hp, stream)
+
+    def _compressed(self, g, stream):
+        nat.ob_lamb_compress_step(self.plan, g, self.err, self.m, self.v, self.p, self.words, self.scales,
+                                  self.ratios, self.hp, self.signs, self.nonfinite, stream)

@@ -51,6 +51,7 @@ class Workload:
     steps: int = 10
     workers: int = 0           # > 0: server-stage workload
     err_dtype: str = "f32"     # storage of the error buffer: "f32" | "bf16" | "f16"
+    optimizer: str = "adam"    # "adam" | "lamb" (1-bit LAMB: the chunks are the layers)
 
     @property
     def n_chunks(self) -> int:
@@ -79,6 +80,18 @@ def bert_base_tensor_sizes() -> list[int]:
     return sizes
 
 
+def llama2_7b_tensor_sizes() -> list[int]:
+    """Element counts of Llama-2-7B's 291 tensors, in model order."""
+    h, ff, vocab, layers = 4096, 11008, 32000, 32
+    sizes = [vocab * h]                                     # token embedding
+    for _ in range(layers):
+        sizes += [h * h] * 4                                # q, k, v, o projections
+        sizes += [ff * h, ff * h, h * ff]                   # gate, up, down projections
+        sizes += [h, h]                                     # the two RMSNorm weights
+    sizes += [h, vocab * h]                                 # final norm, output head
+    return sizes
+
+
 def _offsets_from_sizes(sizes) -> tuple:
     off = [0]
     for s in sizes:
@@ -96,7 +109,14 @@ LLAMA2_7B = Workload("llama2-7B-bf16-ema", 6_738_415_616, None, 1 << 24, "bf16",
                      outlier_frac=0.01, clip=5.0, ef_mode=1, ef_beta=0.9, int8_signs=True,
                      refresh_period=16, steps=48)
 
-WORKLOADS = {w.name: w for w in (SINGLE_1M, BERT_BASE, SERVER_W8, GPT2_XL, LLAMA2_7B)}
+# 1-bit LAMB: the layers are the model's tensors (one chunk each)
+BERT_BASE_LAMB = dataclasses.replace(BERT_BASE, name="bert-base-110M-fp32-lamb", optimizer="lamb")
+LLAMA2_7B_LAMB = Workload("llama2-7B-bf16-lamb", 6_738_415_616, _offsets_from_sizes(llama2_7b_tensor_sizes()),
+                          0, "bf16", 1e-3, outlier_frac=0.01, clip=5.0, ef_mode=1, ef_beta=0.9,
+                          int8_signs=True, freeze_step=2, steps=10, optimizer="lamb")
+
+WORKLOADS = {w.name: w for w in (SINGLE_1M, BERT_BASE, SERVER_W8, GPT2_XL, LLAMA2_7B, BERT_BASE_LAMB,
+                                 LLAMA2_7B_LAMB)}
 # the same optimizer workloads with the error buffer stored in 16 bits ("<name>-err-bf16", "-err-f16")
 WORKLOADS.update({f"{w.name}-err-{e}": dataclasses.replace(w, name=f"{w.name}-err-{e}", err_dtype=e)
                   for w in (BERT_BASE, GPT2_XL, LLAMA2_7B) for e in ("bf16", "f16")})

@@ -49,12 +49,20 @@ def bytes_per_elem(w, kernel: str) -> float:
     """Algorithmic (compulsory) HBM bytes per element of one launch of `kernel` on workload w."""
     gb = 2.0 if w.grad_dtype == "bf16" else 4.0
     eb = 4.0 if w.err_dtype == "f32" else 2.0
+    sb = 1.0 if w.int8_signs else 0.0
+    lamb = w.optimizer == "lamb"
     if kernel == "compress":          # read g err m v p, write err m p + 1 bit (+ int8 sign)
-        return gb + eb + 12.0 + eb + 8.0 + 0.125 + (1.0 if w.int8_signs else 0.0)
-    if kernel == "chunk_sumsq":       # read g err
-        return gb + eb
-    if kernel == "dense":             # read g m v p, write m v p
-        return gb + 12.0 + 12.0
+        if lamb:                      # LAMB pass 2: no p; read g err m v, write err m + bits
+            return gb + eb + 8.0 + eb + 4.0 + 0.125 + sb
+        return gb + eb + 12.0 + eb + 8.0 + 0.125 + sb
+    if kernel == "chunk_sumsq":       # read g err (LAMB: and p)
+        return gb + eb + (4.0 if lamb else 0.0)
+    if kernel == "dense":             # read g m v p, write m v p (LAMB: m v only)
+        return gb + 12.0 + (8.0 if lamb else 12.0)
+    if kernel == "lamb_apply":        # read m v p, write p
+        return 16.0
+    if kernel == "trust_ratio":       # per-block partial sums only
+        return 0.0
     if kernel == "server_sumsq":      # read W sign bits and the server error
         return w.workers / 8.0 + 4.0
     if kernel == "server_apply":      # read W bits + error, write error + 1 bit
@@ -65,12 +73,15 @@ def bytes_per_elem(w, kernel: str) -> float:
 
 
 def step_compulsory_bytes(w, kind: str) -> float:
-    """Bytes per element the method must move once per step (the two-pass re-read not counted)."""
+    """Bytes per element the method must move once per step: every array read and written once (the
+    re-reads that the per-chunk scale and LAMB's per-layer ratio force are not counted)."""
+    import dataclasses
+    adam = dataclasses.replace(w, optimizer="adam")   # LAMB touches the same arrays once each
     if kind == "dense":
-        return bytes_per_elem(w, "dense")
+        return bytes_per_elem(adam, "dense")
     if w.workers:
         return w.workers / 8.0 + 4.0 + 4.0 + 0.125 + bytes_per_elem(w, "unpack")
-    return bytes_per_elem(w, "compress")
+    return bytes_per_elem(adam, "compress")
 
 
 def load_traffic(kernel: str, workload: str):
@@ -116,8 +127,9 @@ def cpu_baseline(w, seconds: float):
         t0 = time.perf_counter()
         if w.workers:
             raise NotImplementedError
-        oracle.compress_step(g, err, m, v, p, offs, lr=w.lr, beta1=w.beta1, eps=w.eps, clip=w.clip,
-                             ef_mode=w.ef_mode, ef_beta=w.ef_beta, want_signs=w.int8_signs)
+        step = oracle.lamb_compress_step if w.optimizer == "lamb" else oracle.compress_step
+        step(g, err, m, v, p, offs, lr=w.lr, beta1=w.beta1, eps=w.eps, clip=w.clip, ef_mode=w.ef_mode,
+             ef_beta=w.ef_beta, want_signs=w.int8_signs)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     return {"value": n_s / t, "unit": "elements/s", "cores": 1, "kind": "oracle",
@@ -144,7 +156,8 @@ def run(args):
     err, m, v, p = synth.draw_state(w, dev)
     ring = 1 if w.n > (1 << 31) else min(4, max(1, args.steps))
     grads = [synth.draw_grad(w, s, dev) for s in range(ring)]
-    opt = schedule.OneBitAdam(plan, err, m, v, p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+    cls = schedule.OneBitLamb if w.optimizer == "lamb" else schedule.OneBitAdam
+    opt = cls(plan, err, m, v, p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                               clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta, int8_signs=w.int8_signs,
                               freeze_step=w.freeze_step, refresh_period=w.refresh_period)
     stream = torch.cuda.current_stream()
@@ -201,7 +214,8 @@ def run(args):
         kern["torch_copy_probe"] = {"bytes_per_launch": 2 * nb, "GBps": copy_gbps}
         del src, dst
 
-    dom = "compress"
+    # the dominant kernel of the timed steps: the longest per launch (the fused pass 2 for 1-bit Adam)
+    dom = max((k for k in ("compress", "lamb_apply") if k in kern), key=lambda k: kern[k]["avg_ms"])
     avg = kern[dom]["avg_ms"]
     bpe = bytes_per_elem(w, dom)
     achieved = bpe * w.n / (avg * 1e-3) / 1e9
@@ -223,6 +237,7 @@ def run(args):
                   + ("" if w.err_dtype == "f32" else f", {w.err_dtype} error buffer")),
         "data": "synthetic (seeded; ring of pre-drawn gradients)",
         "config": {"workload": w.name, "elements": w.n, "chunks": plan.num_chunks,
+                   "optimizer": "1-bit " + ("LAMB" if w.optimizer == "lamb" else "Adam"),
                    "grad_dtype": w.grad_dtype, "err_dtype": w.err_dtype, "clip": w.clip,
                    "error_feedback": "ema" if w.ef_mode else "plain", "int8_signs": w.int8_signs,
                    "freeze_step": w.freeze_step, "refresh_period": w.refresh_period,

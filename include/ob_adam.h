@@ -11,7 +11,8 @@
  *        sec. 3.2 compress routine (clip, NaN check, int8 signs), sec. 4.2 packing into one buffer.
  *   [P2] "DeepSpeed Communication Compression and Hiding": section "baseline: why Adam is hard to
  *        compress" (Adam moments), section "1-bit Adam: warmup, frozen variance, error feedback"
- *        (the two-phase step and compressed_allreduce), section "0/1 Adam" (variance refresh).
+ *        (the two-phase step and compressed_allreduce), section "0/1 Adam" (variance refresh),
+ *        section "1-bit LAMB: also protect the layer-wise trust ratio".
  *   [P3] gradient-compression survey (bmjup.com post 14450): Q&A on the memory cost of error
  *        feedback (the error term kept in a 16-bit format such as FP16).
  *
@@ -129,6 +130,31 @@ ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, v
                                 int8_t* signs_out, uint64_t* nonfinite_out, const ob_hparams* hp,
                                 hipStream_t stream);
 
+/* ---- 1-bit LAMB ([P2] section "1-bit LAMB: also protect the layer-wise trust ratio") ----
+ * LAMB scales the Adam direction of each layer by the trust ratio r = ||w|| / ||u|| and updates
+ * w -= lr * r * u; in 1-bit LAMB the direction is built from the reconstructed (compressed) gradient.
+ * Here a layer is a chunk of the plan (create the plan with one chunk per parameter tensor):
+ *   u_i = mh_i / (sqrt(vh_i) + eps)      (double, not stored; mh = m, vh = v unless bias-corrected)
+ *   r_c = ||p_c|| / ||u_c||               (p before the update; sums of squares in double, rounded
+ *                                         once to fp32; r_c = 1 when either norm is 0, NaN/Inf propagate)
+ *   p_i -= lr * r_c * u_i                 (double, rounded once)
+ * No weight decay and no clamp of r.  ratios_out: fp32[K], the ratio each layer used.
+ * Each call runs 4 kernels (compressed) or 3 (dense): the passes below, one block per layer for the
+ * ratios, and the update. */
+
+/* Compressed 1-bit LAMB step: exactly ob_adam_compress_step's compensate / quantize / pack / error /
+ * momentum (same arguments and outputs), then the trust ratio on the new m and the frozen v, and the
+ * update of p. */
+ob_status ob_lamb_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
+                                float* m, const float* v, float* p, uint32_t* words_out, float* scales_out,
+                                float* ratios_out, int8_t* signs_out, uint64_t* nonfinite_out,
+                                const ob_hparams* hp, hipStream_t stream);
+
+/* Dense LAMB step (the warmup of 1-bit LAMB): m and v as in ob_adam_warmup_step (bias correction by
+ * hp->bias_correction / hp->step), then the trust ratio and the update of p. */
+ob_status ob_lamb_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* m, float* v, float* p,
+                              float* ratios_out, const ob_hparams* hp, hipStream_t stream);
+
 /* Server half of compressed_allreduce ([P2] 1-bit Adam) on this GPU's share of n elements:
  *   avg_i = (sum_{w<W} (bit_w(i) ? s_{w,c} : -s_{w,c})) / W, summed in double in ascending w and
  *           rounded once to fp32;
@@ -157,13 +183,15 @@ const char* ob_status_str(ob_status s);
  * launches, on the call's stream.  ob_plan_read_timing waits for the recorded events and returns the
  * summed milliseconds and launch count of one kernel kind since timing was switched on. */
 typedef enum {
-    OB_KERNEL_CHUNK_SUMSQ = 0,     /* compressed step, pass 1 */
-    OB_KERNEL_COMPRESS = 1,        /* compressed step, pass 2 (fused streaming pass) */
-    OB_KERNEL_DENSE = 2,           /* dense Adam step */
+    OB_KERNEL_CHUNK_SUMSQ = 0,     /* compressed step (Adam or LAMB), pass 1 */
+    OB_KERNEL_COMPRESS = 1,        /* compressed step (Adam or LAMB), pass 2 (fused streaming pass) */
+    OB_KERNEL_DENSE = 2,           /* dense step (Adam, or the moments pass of dense LAMB) */
     OB_KERNEL_SERVER_SUMSQ = 3,    /* server reduce, pass 1 */
     OB_KERNEL_SERVER_APPLY = 4,    /* server reduce, pass 2 */
     OB_KERNEL_UNPACK = 5,
-    OB_KERNEL_COUNT = 6
+    OB_KERNEL_TRUST_RATIO = 6,     /* LAMB: per-layer ratios */
+    OB_KERNEL_LAMB_APPLY = 7,      /* LAMB: parameter update */
+    OB_KERNEL_COUNT = 8
 } ob_kernel;
 
 ob_status ob_plan_set_timing(ob_plan plan, int32_t enable);

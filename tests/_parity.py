@@ -18,7 +18,9 @@ Tolerances:
     mismatches are counted and returned;
   * fp32 state: |gpu - ref| <= 2e-6*|ref| + 1e-9 (+ the exact propagation of a scale difference:
     err moves by |dscale| (EMA: (1-ef_beta)|dscale|), m by (1-beta1)|dscale|, p by
-    lr*(1-beta1)|dscale|/(sqrt(v)+eps)); NaN must match NaN and +-Inf must match exactly.
+    lr*(1-beta1)|dscale|/(sqrt(v)+eps)); NaN must match NaN and +-Inf must match exactly;
+  * 1-bit LAMB: the layer's trust ratio equal or 1 ulp apart (2 after a scale difference: the sums of
+    squares are reduced in a different order); p then also moves by lr*|dr|*|u|.
 """
 from __future__ import annotations
 
@@ -126,17 +128,25 @@ def upload(refs, err, m, v, p):
 
 
 def _oracle_compress(r, g, w):
-    words, scales, signs, nf = oracle.compress_step(
-        g, r.err, r.m, r.v, r.p, np.asarray([0, r.b - r.a], np.int64), lr=w.lr, beta1=w.beta1,
-        eps=w.eps, clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta, want_signs=w.int8_signs,
-        count_nonfinite=True)
-    r.out = dict(words=words, scale=scales[0], signs=signs, nf=nf)
+    off = np.asarray([0, r.b - r.a], np.int64)
+    hp = dict(lr=w.lr, beta1=w.beta1, eps=w.eps, clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta,
+              want_signs=w.int8_signs, count_nonfinite=True)
+    if w.optimizer == "lamb":
+        words, scales, ratios, signs, nf = oracle.lamb_compress_step(g, r.err, r.m, r.v, r.p, off, **hp)
+        r.out = dict(words=words, scale=scales[0], signs=signs, nf=nf, ratio=ratios[0])
+    else:
+        words, scales, signs, nf = oracle.compress_step(g, r.err, r.m, r.v, r.p, off, **hp)
+        r.out = dict(words=words, scale=scales[0], signs=signs, nf=nf)
 
 
 def _oracle_dense(r, g, w, bias_correction, t):
-    oracle.warmup_step(g, r.m, r.v, r.p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
-                       bias_correction=bias_correction, step=t)
-    r.out = {}
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, bias_correction=bias_correction, step=t)
+    if w.optimizer == "lamb":
+        ratios = oracle.lamb_warmup_step(g, r.m, r.v, r.p, np.asarray([0, r.b - r.a], np.int64), **hp)
+        r.out = dict(ratio=ratios[0])
+    else:
+        oracle.warmup_step(g, r.m, r.v, r.p, **hp)
+        r.out = {}
 
 
 def oracle_step(refs, g_dev, w, kind, bias_correction=False, t=0):
@@ -149,7 +159,7 @@ def oracle_step(refs, g_dev, w, kind, bias_correction=False, t=0):
         f.result()
 
 
-def compare_chunks(refs, w, kind, err, m, v, p, words=None, scales=None, signs=None):
+def compare_chunks(refs, w, kind, err, m, v, p, words=None, scales=None, signs=None, ratios=None):
     """Compare the GPU buffers on the checked chunks with the oracle; returns scale-ulp mismatches."""
     mism = 0
     b1 = np.float64(np.float32(w.beta1))
@@ -177,7 +187,16 @@ def compare_chunks(refs, w, kind, err, m, v, p, words=None, scales=None, signs=N
             assert_f32_close(gv, r.v, f"{tag}: v")
         err_slack = ds * ((1 - eb) if w.ef_mode == 1 else 1.0)
         m_slack = ds * (1 - b1)
-        p_slack = lr * m_slack / (np.sqrt(r.v.astype(np.float64)) + eps) if ds else 0.0
+        den = np.sqrt(r.v.astype(np.float64)) + eps
+        p_slack = lr * m_slack / den if ds else 0.0
+        if w.optimizer == "lamb":
+            rg, rr = np.float32(ratios[r.c].item()), np.float32(r.out["ratio"])
+            dr_ulp = int(ulp_diff(rg, rr))
+            assert dr_ulp <= (2 if ds else 1) or (np.isnan(rg) and np.isnan(rr)), \
+                f"{tag}: trust ratio {rg!r} vs {rr!r} ({dr_ulp} ulp)"
+            dr = abs(float(rg) - float(rr)) if np.isfinite(rr) else 0.0
+            u = np.abs(r.m.astype(np.float64)) / den     # run_workload's steps have no bias correction
+            p_slack = float(abs(rr)) * p_slack + lr * dr * u
         assert_err_close(ge, r.err, f"{tag}: err", err_slack)
         assert_f32_close(gm, r.m, f"{tag}: m", m_slack)
         assert_f32_close(gp, r.p, f"{tag}: p", p_slack)
@@ -194,7 +213,8 @@ def run_workload(w, chunks=None, steps=None, device="cuda:0", log=print):
     plan = ob.ob_plan_create(w.n, chunk_size=w.chunk if w.offsets is None else 0,
                              chunk_offsets=w.offsets)
     err, m, v, p = synth.draw_state(w, device)
-    opt = schedule.OneBitAdam(plan, err, m, v, p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+    cls = schedule.OneBitLamb if w.optimizer == "lamb" else schedule.OneBitAdam
+    opt = cls(plan, err, m, v, p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                               clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta,
                               int8_signs=w.int8_signs, count_nonfinite=True,
                               freeze_step=w.freeze_step, refresh_period=w.refresh_period)
@@ -211,7 +231,8 @@ def run_workload(w, chunks=None, steps=None, device="cuda:0", log=print):
         oracle_step(refs, g, w, kind, t=opt.dense_steps)
         counts[kind] += 1
         counts["scale_ulp_mismatch"] += compare_chunks(refs, w, kind, err, m, v, p, opt.words,
-                                                       opt.scales, opt.signs)
+                                                       opt.scales, opt.signs,
+                                                       getattr(opt, "ratios", None))
         if kind == "compressed":
             nf_ref += sum(r.out["nf"] for r in refs)
         log(f"{w.name} step {s} {kind}: {len(refs)} chunks match")

@@ -246,6 +246,129 @@ def test_server_bruteforce_small():
 
 
 # ------------------------------------------------------------------------------------------------
+# 1-bit LAMB: compressed and dense steps with the layer-wise trust ratio
+# ------------------------------------------------------------------------------------------------
+
+def _gpu_vs_oracle_lamb(n, chunk, var, seed, kind="compressed", steps=1, lr=1e-4, bias_correction=False,
+                        mutate=None):
+    gnp, err, m, v, p = _small_state(n, seed, wide=var["clip"] > 0)
+    if mutate is not None:
+        mutate(gnp, err, m, v, p)
+    err = _as_err_format(err, var.get("edt", "f32"))
+    if var["gdt"] == "bf16":
+        gnp = _bf16_bits(gnp)
+    off = oracle.uniform_offsets(n, chunk)
+    K = off.size - 1
+    plan = ob.ob_plan_create(n, chunk_size=chunk)
+    hp = ob.hparams(lr=lr, beta1=0.9, beta2=0.999, eps=1e-8, clip=var["clip"], ef_mode=var["ef_mode"],
+                    ef_beta=0.9, bias_correction=bias_correction, step=3)
+    for st in range(steps):
+        d = [_t(a) for a in (gnp, err, m, v, p)]
+        ratios = torch.full((K,), -7.0, dtype=torch.float32, device=DEV)
+        tag = f"lamb {kind} n={n} chunk={chunk} {var} step {st}"
+        if kind == "compressed":
+            words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+            scales = torch.zeros(K, dtype=torch.float32, device=DEV)
+            signs = torch.zeros(n, dtype=torch.int8, device=DEV) if var["signs"] else None
+            nf = torch.zeros(1, dtype=torch.int64, device=DEV)
+            ob.ob_lamb_compress_step(plan, d[0], d[1], d[2], d[3], d[4], words, scales, ratios, hp, signs, nf)
+            rw, rs, rr, rsg, rnf = oracle.lamb_compress_step(
+                gnp, err, m, v, p, off, lr=lr, beta1=0.9, eps=1e-8, clip=var["clip"], ef_mode=var["ef_mode"],
+                ef_beta=0.9, want_signs=var["signs"], count_nonfinite=True)
+            assert np.array_equal(synth.host(words), rw), f"{tag}: words"
+            if signs is not None:
+                assert np.array_equal(synth.host(signs), rsg), f"{tag}: signs"
+            gs = synth.host(scales)
+            assert np.all(P.ulp_diff(gs, rs) <= 1), f"{tag}: scales"
+            assert int(nf.item()) == rnf, f"{tag}: non-finite count"
+            assert np.array_equal(synth.host(d[3]), v), f"{tag}: v changed"
+            ds = np.abs(gs.astype(np.float64) - rs.astype(np.float64))
+        else:
+            ob.ob_lamb_warmup_step(plan, d[0], d[2], d[3], d[4], ratios, hp)
+            rr = oracle.lamb_warmup_step(gnp, m, v, p, off, lr=lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                                         bias_correction=bias_correction, step=3)
+            P.assert_f32_close(synth.host(d[3]), v, f"{tag}: v")
+            ds = np.zeros(K)
+        gr = synth.host(ratios)
+        both_nan = np.isnan(gr) & np.isnan(rr)
+        dr_ulp = np.where(both_nan, 0, P.ulp_diff(gr, rr))
+        assert np.all(dr_ulp <= np.where(ds > 0, 2, 1)), f"{tag}: ratios {gr} vs {rr}"
+        cidx = np.repeat(np.arange(K), np.diff(off))
+        ds_e = np.where(np.isfinite(ds), ds, 0.0)[cidx]
+        dr = np.where(both_nan, 0.0, np.abs(gr.astype(np.float64) - rr.astype(np.float64)))[cidx]
+        dr = np.where(np.isfinite(dr), dr, 0.0)
+        den = np.sqrt(v.astype(np.float64)) + 1e-8
+        if bias_correction and kind == "dense":
+            den = np.sqrt(v.astype(np.float64) / (1 - 0.999 ** 3)) + 1e-8
+        u = np.abs(m.astype(np.float64)) / den
+        rabs = np.where(np.isfinite(rr), np.abs(rr.astype(np.float64)), 0.0)[cidx]
+        if kind == "compressed":
+            P.assert_err_close(synth.host(d[1]), err, f"{tag}: err", ds_e * (0.1 if var["ef_mode"] else 1.0))
+        P.assert_f32_close(synth.host(d[2]), m, f"{tag}: m", 0.1 * ds_e)
+        P.assert_f32_close(synth.host(d[4]), p, f"{tag}: p", lr * (rabs * 0.1 * ds_e / den + dr * u))
+        gnp = _small_state(n, seed + 1000 + st, wide=var["clip"] > 0)[0]
+        if var["gdt"] == "bf16":
+            gnp = _bf16_bits(gnp)
+    return rr
+
+
+LAMB_VARIANTS = ("fp32_plain", "bf16_ema_clip_int8_f16err")
+
+
+@pytest.mark.parametrize("vname", LAMB_VARIANTS)
+def test_lamb_compress_bruteforce_small(vname):
+    for n in range(1, 131):
+        for chunk in sorted({64, 128, n}):
+            _gpu_vs_oracle_lamb(n, chunk, VARIANTS[vname], seed=n * 5 + chunk)
+
+
+@pytest.mark.parametrize("bias_correction", [False, True])
+def test_lamb_dense_bruteforce_small(bias_correction):
+    for n in range(1, 131, 3):
+        for chunk in sorted({64, n}):
+            _gpu_vs_oracle_lamb(n, chunk, VARIANTS["fp32_plain"], seed=n, kind="dense",
+                                bias_correction=bias_correction)
+
+
+@pytest.mark.parametrize("vname", LAMB_VARIANTS + ("bf16_plain_bf16err",))
+@pytest.mark.parametrize("n,chunk", [(1 << 20, 1 << 20), (1_000_003, 1 << 16), (5_000_000, 5_000_000 - 64 * 7)])
+def test_lamb_compress_multi_tile(vname, n, chunk):
+    _gpu_vs_oracle_lamb(n, chunk, VARIANTS[vname], seed=n, steps=3)
+
+
+@pytest.mark.parametrize("n,chunk", [(1_000_003, 1 << 16), (3_000_017, 1 << 20)])
+def test_lamb_dense_multi_tile(n, chunk):
+    for bc in (False, True):
+        _gpu_vs_oracle_lamb(n, chunk, VARIANTS["bf16_plain"], seed=n, kind="dense", steps=2, bias_correction=bc)
+
+
+def test_lamb_degenerate_layers():
+    """A zero layer (r = 1), a zero direction (r = 1, p unchanged) and a NaN parameter (its layer's
+    ratio and update are NaN, the other layers are not touched by it)."""
+    n, chunk = 4 * 4096 + 100, 4096
+
+    def mutate(g, err, m, v, p):
+        p[4096:8192] = 0.0
+        g[8192:12288] = 0.0
+        err[8192:12288] = 0.0
+        m[8192:12288] = 0.0
+        p[5] = np.nan
+
+    for kind in ("compressed", "dense"):
+        rr = _gpu_vs_oracle_lamb(n, chunk, VARIANTS["fp32_plain"], seed=4, kind=kind, mutate=mutate)
+        assert np.isnan(rr[0]) and rr[1] == 1.0
+        if kind == "compressed":
+            assert rr[2] == 1.0
+
+
+def test_workload_bert_base_lamb():
+    """1-bit LAMB on BERT-base's 197 tensors (one layer each): 5 dense LAMB steps, then 20 compressed;
+    every layer checked every step, ratios included."""
+    counts = P.run_workload(synth.BERT_BASE_LAMB, log=lambda *_: None)
+    assert counts["dense"] == 5 and counts["compressed"] == 20
+
+
+# ------------------------------------------------------------------------------------------------
 # edge cases of the boundary
 # ------------------------------------------------------------------------------------------------
 
@@ -437,3 +560,13 @@ def test_workload_llama2_7b_bf16_error():
     w = dataclasses.replace(synth.WORKLOADS[f"{synth.LLAMA2_7B.name}-err-bf16"], steps=20)
     counts = P.run_workload(w, chunks=[0, 200, w.n_chunks - 1], log=lambda *_: None)
     assert counts["dense"] == 1 and counts["compressed"] == 19
+
+
+@pytest.mark.slow
+def test_workload_llama2_7b_lamb():
+    """1-bit LAMB on Llama-2-7B's 291 tensors (6,738,415,616 bf16-gradient elements), clip, EMA error,
+    int8 signs, 2 dense steps then 8 compressed: the embedding (layer 0), a mid-network projection
+    (145) and the output head (290) checked every step."""
+    w = synth.LLAMA2_7B_LAMB
+    counts = P.run_workload(w, chunks=[0, 145, w.n_chunks - 1], log=lambda *_: None)
+    assert counts["dense"] == 2 and counts["compressed"] == 8
