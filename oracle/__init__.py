@@ -63,6 +63,7 @@ def _load():
     lib.or_lamb_compress_step.argtypes = [I64, I64, P, P, I, P, I, P, P, P, P, P, P, P, P,
                                           F, F, F, F, I, F]
     lib.or_lamb_warmup_step.argtypes = [I64, I64, P, P, I, P, P, P, P, F, F, F, F, I, I64]
+    lib.or_diagnostics.argtypes = [I64, I64, P, P, I, P, P, P]
     lib.or_to_format.argtypes = [P, I64, I, P]
     lib.or_from_format.argtypes = [P, I64, I, P]
     lib.or_warmup_step.argtypes = [I64, P, I, P, P, P, F, F, F, F, I, I64]
@@ -74,7 +75,7 @@ def _load():
     lib.or_chunk_scale.restype = ctypes.c_float
     for name in ("or_pack", "or_unpack", "or_compress_step", "or_warmup_step",
                  "or_server_reduce", "or_server_average", "or_to_format", "or_from_format",
-                 "or_lamb_compress_step", "or_lamb_warmup_step"):
+                 "or_lamb_compress_step", "or_lamb_warmup_step", "or_diagnostics"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -211,6 +212,19 @@ def warmup_step(g, m, v, p, *, lr, beta1, beta2, eps, bias_correction=False, ste
     rc = _load().or_warmup_step(n, _ptr(g), bf, _ptr(m), _ptr(v), _ptr(p), lr, beta1, beta2, eps,
                                 1 if bias_correction else 0, step)
     _check(rc, "warmup_step")
+
+
+def diagnostics(err_before, words, offsets):
+    """Per-chunk diagnostics of a compressed step (reading R17): (sum of squares of the error buffer
+    the step read, float64[K]; number of +1 signs in the step's words, int64[K])."""
+    err_before, efmt = _err(np.ascontiguousarray(err_before))
+    k = offsets.size - 1
+    ss = np.zeros(max(k, 0), dtype=np.float64)
+    plus = np.zeros(max(k, 0), dtype=np.int64)
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    _check(_load().or_diagnostics(err_before.size, k, _ptr(offsets), _ptr(err_before), efmt, _ptr(words),
+                                  _ptr(ss), _ptr(plus)), "diagnostics")
+    return ss, plus
 
 
 def lamb_compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef_mode=0, ef_beta=0.9,

@@ -56,6 +56,11 @@
  *      S_u == 0 (the ratio is undefined there, and a zero-initialised layer must still move);
  *      p_i = fl32(p_i - lr * (r * u_i)) in double.  No weight decay and no clamp of r: the pages
  *      give neither.
+ *   R17 diagnostics ([P1] sec. 6.2: the L2 norm of each parameter's error buffer, warned about below
+ *      1e-6; [P1] sec. 8: monitor that norm and the quantization rate): per chunk, the sum of squares
+ *      of the stored error buffer as the step reads it (double, ascending index; its square root is
+ *      the norm) and the number of elements whose sign bit is +1 in the step's packed words (the
+ *      bit balance; the ideal share for a zero-mean gradient is one half).
  */
 #include <math.h>
 #include <stdint.h>
@@ -340,6 +345,27 @@ int or_compress_step(int64_t n, int64_t K, const int64_t* off,
 {
     return compress_core(n, K, off, g, g_is_bf16, err_store, err_fmt, m, v, p, words, scales, signs,
                          nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 1);
+}
+
+/* ---------- R17: per-chunk diagnostics of a compressed step ([P1] sec. 6.2 and 8) ----------
+ * err_store: the error buffer as the step read it (before the step); words: the step's packed signs. */
+int or_diagnostics(int64_t n, int64_t K, const int64_t* off, const void* err_store, int err_fmt,
+                   const uint32_t* words, double* err_sumsq, int64_t* plus_count)
+{
+    if (!check_offsets(n, K, off)) return OR_ERR_ARG;
+    if (err_fmt != OR_FMT_F32 && err_fmt != OR_FMT_BF16 && err_fmt != OR_FMT_F16) return OR_ERR_ARG;
+    for (int64_t c = 0; c < K; ++c) {
+        double s = 0.0;
+        int64_t plus = 0;
+        for (int64_t i = off[c]; i < off[c + 1]; ++i) {
+            double e = (double)load_err(err_store, err_fmt, i);
+            s += e * e;
+            plus += word_bit(words, i);
+        }
+        err_sumsq[c] = s;
+        plus_count[c] = plus;
+    }
+    return OR_OK;
 }
 
 /* ---------- dense Adam step (warmup before freeze_step, and the 0/1 Adam refresh) ----------

@@ -18,7 +18,9 @@ Pins used (none retypes the oracle's formula):
   * 1-bit LAMB (R16): hand-derived two-layer examples (compressed and dense, with a zero layer and a
     zero direction), the reduction of each layer's update to the already pinned Adam steps with
     lr * r (exact when lr is a power of two), the ratio against math.fsum norms, exact scale
-    invariances (p x 2, v x 4, and g, err, m x 2), and layer independence.
+    invariances (p x 2, v x 4, and g, err, m x 2), and layer independence;
+  * diagnostics (R17): the error norm against math.fsum, the +1 count against numpy.unpackbits, and
+    the worked example's values.
 """
 import math
 from fractions import Fraction
@@ -805,3 +807,40 @@ def test_lamb_degenerate_layers_and_independence():
         assert rc[0] == ratios[c] or (np.isnan(rc[0]) and np.isnan(ratios[c]))
         for x, y in zip(part, full):
             assert np.array_equal(x, y[lo:hi], equal_nan=True)
+
+
+# ------------------------------------------------------------------------------------------------
+# R17: diagnostics
+# ------------------------------------------------------------------------------------------------
+
+def test_diagnostics_worked_example(golden):
+    case = golden["compress_plain_one_chunk"]
+    err0 = _arr([1.0, -2.0, 0.5, 0.0])                # any buffer: the norm is of what the step reads
+    ss, plus = oracle.diagnostics(err0, np.asarray(case["expect_words"], np.uint32),
+                                  np.asarray(case["offsets"], np.int64))
+    assert ss.tolist() == [5.25] and plus.tolist() == [3]     # 1 + 4 + 0.25; bits [1,0,1,1]
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "f16"])
+def test_diagnostics_vs_fsum_and_unpackbits(fmt):
+    n = 5000 + 13
+    off = np.asarray([0, 64, 1000, 4096, n], np.int64)
+    rng = np.random.default_rng(31)
+    e32 = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    e32[77] = -0.0
+    if fmt == "f16":
+        e = e32.astype(np.float16)
+        ew = e.astype(np.float64)
+    elif fmt == "bf16":
+        e = _lib_narrow(e32, "bf16")
+        ew = _lib_widen(e, "bf16").astype(np.float64)
+    else:
+        e, ew = e32, e32.astype(np.float64)
+    words = rng.integers(0, 1 << 32, size=(n + 31) // 32, dtype=np.uint64).astype(np.uint32)
+    ss, plus = oracle.diagnostics(e, words, off)
+    bits = np.unpackbits(words.view(np.uint8), bitorder="little")[:n]
+    for c in range(off.size - 1):
+        lo, hi = int(off[c]), int(off[c + 1])
+        ref = math.fsum(ew[lo:hi] * ew[lo:hi])
+        assert abs(ss[c] - ref) <= 1e-13 * ref
+        assert plus[c] == int(bits[lo:hi].sum())

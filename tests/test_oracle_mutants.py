@@ -84,6 +84,8 @@ MUTANTS = {
     "lamb_compress_also_adam": ("nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 0);",
                                 "nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 1);"),
     "lamb_dense_also_adam": ("bias_correction, step, 0);", "bias_correction, step, 1);"),
+    "diag_norm_not_squared": ("            s += e * e;", "            s += fabs(e);"),
+    "diag_counts_minus": ("plus += word_bit(words, i);", "plus += 1 - word_bit(words, i);"),
     "unpack_polarity": ("out[i] = word_bit(words, i) ? scales[c] : -scales[c];",
                         "out[i] = word_bit(words, i) ? -scales[c] : scales[c];"),
 }
