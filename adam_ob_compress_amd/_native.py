@@ -18,11 +18,13 @@ OB_OK, OB_ERR_ARG, OB_ERR_ALIGN, OB_ERR_DTYPE, OB_ERR_HIP, OB_ERR_OOM = range(6)
 OB_F32, OB_BF16, OB_F16 = 0, 1, 2
 OB_EF_PLAIN, OB_EF_EMA = 0, 1
 (OB_KERNEL_CHUNK_SUMSQ, OB_KERNEL_COMPRESS, OB_KERNEL_DENSE, OB_KERNEL_SERVER_SUMSQ,
- OB_KERNEL_SERVER_APPLY, OB_KERNEL_UNPACK, OB_KERNEL_TRUST_RATIO, OB_KERNEL_LAMB_APPLY) = range(8)
+ OB_KERNEL_SERVER_APPLY, OB_KERNEL_UNPACK, OB_KERNEL_TRUST_RATIO, OB_KERNEL_LAMB_APPLY,
+ OB_KERNEL_DIAG) = range(9)
 KERNEL_NAMES = {
     OB_KERNEL_CHUNK_SUMSQ: "chunk_sumsq", OB_KERNEL_COMPRESS: "compress", OB_KERNEL_DENSE: "dense",
     OB_KERNEL_SERVER_SUMSQ: "server_sumsq", OB_KERNEL_SERVER_APPLY: "server_apply",
     OB_KERNEL_UNPACK: "unpack", OB_KERNEL_TRUST_RATIO: "trust_ratio", OB_KERNEL_LAMB_APPLY: "lamb_apply",
+    OB_KERNEL_DIAG: "diag",
 }
 
 
@@ -74,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "ob_unpack": (I32, [P, P, I64, P, P, P]),
         "ob_status_str": (ctypes.c_char_p, [I32]),
         "ob_plan_set_timing": (I32, [P, I32]),
+        "ob_plan_set_diagnostics": (I32, [P, P, P]),
         "ob_plan_read_timing": (I32, [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I64)]),
     }
     for name, (res, args) in sig.items():
@@ -270,6 +273,15 @@ def ob_unpack(plan: Plan | None, words, n: int, out, scales=None, stream=None):
         _want(scales, "scales", torch.float32, plan.num_chunks)
     _check(lib().ob_unpack(plan.handle if plan is not None else None, _dev(words, "words"), n,
                            _dev(scales, "scales"), _dev(out, "out"), _stream(stream)), "ob_unpack")
+
+
+def ob_plan_set_diagnostics(plan: Plan, err_sumsq=None, plus_count=None):
+    """Per-chunk diagnostics of later compressed steps into err_sumsq (float64[K]) and plus_count
+    (int64[K]); both None switches them off."""
+    _want(err_sumsq, "err_sumsq", torch.float64, plan.num_chunks)
+    _want(plus_count, "plus_count", torch.int64, plan.num_chunks)
+    _check(lib().ob_plan_set_diagnostics(plan.handle, _dev(err_sumsq, "err_sumsq"),
+                                         _dev(plus_count, "plus_count")), "ob_plan_set_diagnostics")
 
 
 def ob_plan_set_timing(plan: Plan, enable: bool):

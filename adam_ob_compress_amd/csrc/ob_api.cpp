@@ -22,6 +22,12 @@ struct ob_plan_s {
     double* d_partials_w = nullptr;  // LAMB: one per pass-1 or dense block (the larger)
     double* d_partials_u = nullptr;  // LAMB: one per compressed-pass-2 or dense block (the larger)
 
+    // diagnostics (off until ob_plan_set_diagnostics): workspaces and the caller's output arrays
+    double* d_partials_e = nullptr;    // one per pass-1 block
+    uint32_t* d_partials_b = nullptr;  // one per compressed-pass-2 block
+    double* diag_err_sumsq = nullptr;
+    unsigned long long* diag_plus = nullptr;
+
     // block tables, one per kernel kind (kTables)
     struct Table {
         int64_t block_elems = 0;
@@ -53,6 +59,9 @@ struct ob_plan_s {
         pd.w_first = nullptr;
         pd.partials_u = d_partials_u;
         pd.u_first = nullptr;
+        const bool diag = diag_err_sumsq != nullptr;
+        pd.partials_e = diag ? d_partials_e : nullptr;
+        pd.partials_b = diag ? d_partials_b : nullptr;
         pd.n = n;
         pd.n_items = t[table].n_items;
         pd.K = K;
@@ -131,6 +140,8 @@ void free_plan(ob_plan p)
     if (p->d_partials) (void)hipFree(p->d_partials);
     if (p->d_partials_w) (void)hipFree(p->d_partials_w);
     if (p->d_partials_u) (void)hipFree(p->d_partials_u);
+    if (p->d_partials_e) (void)hipFree(p->d_partials_e);
+    if (p->d_partials_b) (void)hipFree(p->d_partials_b);
     delete p;
 }
 
@@ -412,7 +423,7 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
         }
     });
     if (st != OB_OK) return st;
-    return timed(plan, OB_KERNEL_COMPRESS, stream, [&] {
+    st = timed(plan, OB_KERNEL_COMPRESS, stream, [&] {
         switch (err_dtype) {
         case OB_BF16:
             return ob::launch_compress<OB_BF16>(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf,
@@ -424,6 +435,10 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
             return ob::launch_compress<OB_F32>(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf,
                                                ema, lamb, cp, stream);
         }
+    });
+    if (st != OB_OK || !plan->diag_err_sumsq) return st;
+    return timed(plan, OB_KERNEL_DIAG, stream, [&] {
+        return ob::launch_diag_reduce(pd, plan->diag_err_sumsq, plan->diag_plus, stream);
     });
 }
 
@@ -556,6 +571,29 @@ ob_status ob_unpack(ob_plan plan, const uint32_t* words, int64_t n, const float*
     }
     (void)hipGetLastError();
     return ob::launch_unpack(nullptr, words, n, nullptr, out, stream) == hipSuccess ? OB_OK : OB_ERR_HIP;
+}
+
+ob_status ob_plan_set_diagnostics(ob_plan plan, double* err_sumsq_out, uint64_t* plus_count_out)
+{
+    if (!plan) return OB_ERR_ARG;
+    if ((err_sumsq_out == nullptr) != (plus_count_out == nullptr)) return OB_ERR_ARG;
+    if (err_sumsq_out && (!aligned(err_sumsq_out, 8) || !aligned(plus_count_out, 8))) return OB_ERR_ALIGN;
+    if (err_sumsq_out && plan->n > 0 && !plan->d_partials_e) {
+        DeviceGuard guard(plan->device);
+        if (!guard.ok) return OB_ERR_HIP;
+        hipError_t e = hipMalloc(&plan->d_partials_e, plan->t[T_PASS1].n_items * sizeof(double));
+        if (e == hipSuccess)
+            e = hipMalloc(&plan->d_partials_b, plan->t[T_COMPRESS].n_items * sizeof(uint32_t));
+        if (e != hipSuccess) {
+            if (plan->d_partials_e) (void)hipFree(plan->d_partials_e);
+            plan->d_partials_e = nullptr;
+            plan->d_partials_b = nullptr;
+            return e == hipErrorOutOfMemory ? OB_ERR_OOM : OB_ERR_HIP;
+        }
+    }
+    plan->diag_err_sumsq = err_sumsq_out;
+    plan->diag_plus = reinterpret_cast<unsigned long long*>(plus_count_out);
+    return OB_OK;
 }
 
 ob_status ob_plan_set_timing(ob_plan plan, int32_t enable)

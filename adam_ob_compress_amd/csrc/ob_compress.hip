@@ -37,10 +37,10 @@ namespace {
 
 // ------------------------------------------------------------------------------------------------
 // compressed step, pass 1: per-block sum of squares of x = clip(g) + err
-// (LAMB: and of the parameters, for the layer's ||w||)
+// (LAMB: and of the parameters, for the layer's ||w||; DIAG: and of the error buffer read)
 // ------------------------------------------------------------------------------------------------
 
-template <class G, class E, bool CLIP, bool LAMB>
+template <class G, class E, bool CLIP, bool LAMB, bool DIAG>
 __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typename G::T* __restrict__ g,
                                                         const typename E::T* __restrict__ err, float clip,
                                                         const float* __restrict__ p)
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
     __shared__ double lds[kBlock / 64];
     const Item it = pd.items[blockIdx.x];
     const int tid = threadIdx.x;
-    double acc = 0.0, accw = 0.0;
+    double acc = 0.0, accw = 0.0, acce = 0.0;
     constexpr int U = OB_P1_UNROLL;
     int base = 0;
     for (; base + U * kTile <= it.len; base += U * kTile) {
@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
                 const double x = compensate<CLIP>(gv[u][k], ev[u][k], clip);
                 acc = fma(x, x, acc);
                 if (LAMB) accw = fma(static_cast<double>(pv[u][k]), static_cast<double>(pv[u][k]), accw);
+                if (DIAG) acce = fma(static_cast<double>(ev[u][k]), static_cast<double>(ev[u][k]), acce);
             }
         }
     }
@@ -82,14 +83,17 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
                 const double x = compensate<CLIP>(gv[k], ev[k], clip);
                 acc = fma(x, x, acc);
                 if (LAMB) accw = fma(static_cast<double>(pv[k]), static_cast<double>(pv[k]), accw);
+                if (DIAG) acce = fma(static_cast<double>(ev[k]), static_cast<double>(ev[k]), acce);
             }
         } else {
             #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 if (k >= cnt) continue;
-                const double x = compensate<CLIP>(G::load1(g, i + k), E::load1(err, i + k), clip);
+                const float e = E::load1(err, i + k);
+                const double x = compensate<CLIP>(G::load1(g, i + k), e, clip);
                 acc = fma(x, x, acc);
                 if (LAMB) accw = fma(static_cast<double>(p[i + k]), static_cast<double>(p[i + k]), accw);
+                if (DIAG) acce = fma(static_cast<double>(e), static_cast<double>(e), acce);
             }
         }
     }
@@ -98,6 +102,10 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
     if (LAMB) {
         const double sw = block_sum(accw, lds);
         if (tid == 0) pd.partials_w[blockIdx.x] = sw;
+    }
+    if (DIAG) {
+        const double se = block_sum(acce, lds);
+        if (tid == 0) pd.partials_e[blockIdx.x] = se;
     }
 }
 
@@ -121,7 +129,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
     const float scale = chunk_scale(pd, it.chunk, lds);
     if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
 
-    uint32_t nf = 0;
+    uint32_t nf = 0, plus = 0;
     double usq = 0.0;
     constexpr int U = OB_P2_UNROLL;
     int base = 0;
@@ -162,6 +170,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
                     *sp = signs4(nib);
             }
             store_word(words, i, nib, true);
+            plus += __builtin_popcount(nib);
         }
     }
     for (; base < it.len; base += kTile) {
@@ -205,6 +214,12 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
             }
         }
         store_word(words, i, nib, 32 * (tid >> 3) < rem);
+        plus += __builtin_popcount(nib);
+    }
+    if (pd.partials_b != nullptr) {   // diagnostics: +1 signs of the block (nib holds valid elements only)
+        __shared__ uint32_t ldsb[kBlock / 64];
+        const uint32_t t = block_sum_u32(plus, ldsb);
+        if (tid == 0) pd.partials_b[blockIdx.x] = t;
     }
     if (NONFIN) {
         __shared__ uint32_t ldsu[kBlock / 64];
@@ -228,12 +243,21 @@ template <class G, class E>
 void sumsq_dispatch(int sel, dim3 grid, dim3 block, hipStream_t s, const PlanDev& pd, const typename G::T* g,
                     const typename E::T* err, float clip, const float* p)
 {
+#define OB_CASE(k, CL, LA, DG)                                                                        \
+    case k:                                                                                            \
+        hipLaunchKernelGGL((k_chunk_sumsq<G, E, CL, LA, DG>), grid, block, 0, s, pd, g, err, clip, p); \
+        break;
     switch (sel) {
-    case 0: hipLaunchKernelGGL((k_chunk_sumsq<G, E, false, false>), grid, block, 0, s, pd, g, err, clip, p); break;
-    case 1: hipLaunchKernelGGL((k_chunk_sumsq<G, E, true, false>), grid, block, 0, s, pd, g, err, clip, p); break;
-    case 2: hipLaunchKernelGGL((k_chunk_sumsq<G, E, false, true>), grid, block, 0, s, pd, g, err, clip, p); break;
-    default: hipLaunchKernelGGL((k_chunk_sumsq<G, E, true, true>), grid, block, 0, s, pd, g, err, clip, p); break;
+        OB_CASE(0, false, false, false)
+        OB_CASE(1, true, false, false)
+        OB_CASE(2, false, true, false)
+        OB_CASE(3, true, true, false)
+        OB_CASE(4, false, false, true)
+        OB_CASE(5, true, false, true)
+        OB_CASE(6, false, true, true)
+        OB_CASE(7, true, true, true)
     }
+#undef OB_CASE
 }
 }  // namespace
 
@@ -244,7 +268,7 @@ hipError_t launch_chunk_sumsq(const PlanDev& pd, const void* g, int g_bf16, cons
     using E = typename ErrOf<EF>::type;
     auto err = static_cast<const typename E::T*>(err_v);
     const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
-    const int sel = (clip > 0.0f ? 1 : 0) | (lamb_p ? 2 : 0);
+    const int sel = (clip > 0.0f ? 1 : 0) | (lamb_p ? 2 : 0) | (pd.partials_e ? 4 : 0);
     if (g_bf16)
         sumsq_dispatch<GradBF16, E>(sel, grid, block, s, pd, static_cast<const uint16_t*>(g), err, clip, lamb_p);
     else

@@ -37,6 +37,10 @@ struct PlanDev {
     const int32_t* w_first;
     double* partials_u;
     const int32_t* u_first;
+    // diagnostics (nullptr = off): per pass-1 block, the sum of squares of the error buffer read;
+    // per pass-2 block, the number of +1 signs
+    double* partials_e;
+    uint32_t* partials_b;
     int64_t n;
     int64_t n_items;
     int32_t K;
@@ -72,6 +76,10 @@ hipError_t launch_compress(const PlanDev& pd, const void* g, int g_bf16, void* e
 // lamb != 0: moments only, plus per-block sums of p^2 and u^2 into pd.partials_w / partials_u.
 hipError_t launch_dense(const PlanDev& pd, const void* g, int g_bf16, float* m, float* v, float* p,
                         int lamb, const DenseParams& dp, hipStream_t s);
+// One block per chunk: the diagnostics of the chunk from partials_e (pass-1 table, p1_first) and
+// partials_b (this launch's pass-2 table, chunk_first).
+hipError_t launch_diag_reduce(const PlanDev& pd, double* err_sumsq, unsigned long long* plus_count,
+                              hipStream_t s);
 // One block per chunk: r_c from the chunk's partials_w / partials_u.
 hipError_t launch_trust_ratio(const PlanDev& pd, float* ratios, hipStream_t s);
 hipError_t launch_lamb_apply(const PlanDev& pd, const float* m, const float* v, float* p, const float* ratios,

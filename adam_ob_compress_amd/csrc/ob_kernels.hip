@@ -141,6 +141,30 @@ __global__ __launch_bounds__(kBlock) void k_trust_ratio(PlanDev pd, float* __res
     if (tid == 0) ratios[c] = (sw == 0.0 || su == 0.0) ? 1.0f : static_cast<float>(sqrt(sw) / sqrt(su));
 }
 
+// ------------------------------------------------------------------------------------------------
+// diagnostics ([P1] sec. 6.2 and 8): one block per chunk adds its blocks' partial results in a fixed
+// order: the sum of squares of the error buffer the step read, and the number of +1 signs
+// ------------------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void k_diag_reduce(PlanDev pd, double* __restrict__ err_sumsq,
+                                                        unsigned long long* __restrict__ plus_count)
+{
+    __shared__ double lds[kBlock / 64];
+    const int c = blockIdx.x;
+    const int tid = threadIdx.x;
+    double se = 0.0;
+    unsigned long long pc = 0;
+    for (int i = pd.p1_first[c] + tid; i < pd.p1_first[c + 1]; i += kBlock) se += pd.partials_e[i];
+    for (int i = pd.chunk_first[c] + tid; i < pd.chunk_first[c + 1]; i += kBlock) pc += pd.partials_b[i];
+    se = block_sum(se, lds);
+    // the counts are integers below 2^53, exact in double whatever the order
+    const double pcs = block_sum(static_cast<double>(pc), lds);
+    if (tid == 0) {
+        err_sumsq[c] = se;
+        plus_count[c] = static_cast<unsigned long long>(pcs);
+    }
+}
+
 // p -= lr * (r * u), u = mh / (sqrt(vh) + eps) from the stored m and v, in double, rounded once.
 template <bool BC>
 __device__ __forceinline__ float lamb_elem(float mm, float vv, float pp, double r, const LambParams& lp)
@@ -467,6 +491,14 @@ hipError_t launch_dense(const PlanDev& pd, const void* g, int g_bf16, float* m, 
     else
         OB_DENSE(GradF32, float)
 #undef OB_DENSE
+    return hipGetLastError();
+}
+
+hipError_t launch_diag_reduce(const PlanDev& pd, double* err_sumsq, unsigned long long* plus_count,
+                              hipStream_t s)
+{
+    hipLaunchKernelGGL(k_diag_reduce, dim3(static_cast<unsigned>(pd.K)), dim3(kBlock), 0, s, pd, err_sumsq,
+                       plus_count);
     return hipGetLastError();
 }
 

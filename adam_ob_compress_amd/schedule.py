@@ -30,11 +30,16 @@ class OneBitAdam:
     ``step(g)`` enqueues one dense or compressed step on the current stream and returns its kind.
     The compressed step's outputs (packed words, per-chunk scales, optional int8 signs and the
     non-finite counter) stay in ``self.words`` etc. for the caller to send or inspect.
+
+    With ``diagnostics=True`` every compressed step also leaves, per chunk, the squared L2 norm of the
+    error buffer it read and its number of +1 signs ([P1] sec. 6.2 and 8); see ``error_norms``,
+    ``small_error_chunks`` and ``plus_share``.
     """
 
     def __init__(self, plan: nat.Plan, err, m, v, p, *, lr, beta1=0.9, beta2=0.999, eps=1e-8,
                  clip=0.0, ef_mode=nat.OB_EF_PLAIN, ef_beta=0.9, int8_signs=False,
-                 count_nonfinite=False, freeze_step=0, refresh_period=0, bias_correction=False):
+                 count_nonfinite=False, freeze_step=0, refresh_period=0, bias_correction=False,
+                 diagnostics=False):
         self.plan = plan
         self.err, self.m, self.v, self.p = err, m, v, p
         self.freeze_step, self.refresh_period = freeze_step, refresh_period
@@ -49,6 +54,11 @@ class OneBitAdam:
         self.nonfinite = torch.zeros(1, dtype=torch.int64, device=dev) if count_nonfinite else None
         self.step_index = 0
         self.dense_steps = 0
+        self.err_sumsq = self.plus_count = None
+        if diagnostics:
+            self.err_sumsq = torch.zeros(plan.num_chunks, dtype=torch.float64, device=dev)
+            self.plus_count = torch.zeros(plan.num_chunks, dtype=torch.int64, device=dev)
+            nat.ob_plan_set_diagnostics(plan, self.err_sumsq, self.plus_count)
 
     def kind(self) -> str:
         return step_kind(self.step_index, self.freeze_step, self.refresh_period)
@@ -64,6 +74,18 @@ class OneBitAdam:
             self._compressed(g, stream)
         self.step_index += 1
         return kind
+
+    def error_norms(self) -> torch.Tensor:
+        """Per-chunk L2 norm of the error buffer read by the last compressed step."""
+        return torch.sqrt(self.err_sumsq)
+
+    def small_error_chunks(self, threshold: float = 1e-6) -> list[int]:
+        """Chunks whose error-buffer norm was below `threshold` ([P1] sec. 6.2's warning)."""
+        return torch.nonzero(self.error_norms() < threshold).flatten().tolist()
+
+    def plus_share(self, chunk_sizes: torch.Tensor) -> torch.Tensor:
+        """Per-chunk share of +1 signs in the last compressed step (about 0.5 for zero-mean data)."""
+        return self.plus_count.double() / chunk_sizes.double()
 
     def _dense(self, g, stream):
         nat.ob_adam_warmup_step(self.plan, g, self.m, self.v, self.p, self.hp, stream)

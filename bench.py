@@ -61,7 +61,7 @@ def bytes_per_elem(w, kernel: str) -> float:
         return gb + 12.0 + (8.0 if lamb else 12.0)
     if kernel == "lamb_apply":        # read m v p, write p
         return 16.0
-    if kernel == "trust_ratio":       # per-block partial sums only
+    if kernel in ("trust_ratio", "diag"):   # one block per chunk over the per-block partial sums
         return 0.0
     if kernel == "server_sumsq":      # read W sign bits and the server error
         return w.workers / 8.0 + 4.0
@@ -159,7 +159,8 @@ def run(args):
     cls = schedule.OneBitLamb if w.optimizer == "lamb" else schedule.OneBitAdam
     opt = cls(plan, err, m, v, p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                               clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta, int8_signs=w.int8_signs,
-                              freeze_step=w.freeze_step, refresh_period=w.refresh_period)
+                              freeze_step=w.freeze_step, refresh_period=w.refresh_period,
+                              diagnostics=args.diagnostics)
     stream = torch.cuda.current_stream()
     print(f"# {w.name}: n={w.n} chunks={plan.num_chunks} blocks={plan.num_blocks} "
           f"block_elems={plan.block_elems}", file=sys.stderr, flush=True)
@@ -241,7 +242,8 @@ def run(args):
                    "grad_dtype": w.grad_dtype, "err_dtype": w.err_dtype, "clip": w.clip,
                    "error_feedback": "ema" if w.ef_mode else "plain", "int8_signs": w.int8_signs,
                    "freeze_step": w.freeze_step, "refresh_period": w.refresh_period,
-                   "block_elems": plan.block_elems, "work_blocks": plan.num_blocks},
+                   "block_elems": plan.block_elems, "work_blocks": plan.num_blocks,
+                   "diagnostics": bool(args.diagnostics)},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "bytes_per_elem": bpe, "traffic": traffic},
@@ -266,6 +268,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain torch copy of this many MiB (counter calibration)")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="also compute the per-chunk error norm and +1 count in every compressed step")
     ap.add_argument("--rocprof-summary", metavar="DIR")
     ap.add_argument("--traffic-profile", metavar="DIR")
     ap.add_argument("--kernel", default="compress")

@@ -191,11 +191,24 @@ typedef enum {
     OB_KERNEL_UNPACK = 5,
     OB_KERNEL_TRUST_RATIO = 6,     /* LAMB: per-layer ratios */
     OB_KERNEL_LAMB_APPLY = 7,      /* LAMB: parameter update */
-    OB_KERNEL_COUNT = 8
+    OB_KERNEL_DIAG = 8,            /* diagnostics: per-chunk totals */
+    OB_KERNEL_COUNT = 9
 } ob_kernel;
 
 ob_status ob_plan_set_timing(ob_plan plan, int32_t enable);
 ob_status ob_plan_read_timing(ob_plan plan, int32_t kernel, double* total_ms, int64_t* launches);
+
+/* ---- diagnostics ([P1] sec. 6.2: warn when a parameter's error-buffer L2 norm is below 1e-6;
+ * [P1] sec. 8: monitor that norm and the quantization rate) ----
+ * With both pointers set (device arrays of K elements, 8-byte aligned), every later compressed step
+ * with this plan (ob_adam_compress_step or ob_lamb_compress_step) also writes, per chunk c:
+ *   err_sumsq_out[c]  = sum of squares (double) of the error buffer as that step read it, i.e. the
+ *                       error left by the previous step; sqrt gives the L2 norm;
+ *   plus_count_out[c] = number of elements of the chunk whose sign bit is +1 (the bit balance).
+ * The first pass accumulates the first, the fused pass the second, and a one-block-per-chunk kernel
+ * writes both.  The first call that enables them allocates two workspaces for the plan.  Both NULL
+ * switches them off; exactly one NULL is OB_ERR_ARG. */
+ob_status ob_plan_set_diagnostics(ob_plan plan, double* err_sumsq_out, uint64_t* plus_count_out);
 
 #ifdef __cplusplus
 }

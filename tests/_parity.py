@@ -151,6 +151,8 @@ def _oracle_dense(r, g, w, bias_correction, t):
 
 def oracle_step(refs, g_dev, w, kind, bias_correction=False, t=0):
     gs = [synth.host(g_dev[r.a:r.b]) for r in refs]
+    for r in refs:
+        r.err_before = r.err.copy()
     if kind == "compressed":
         futs = [_POOL.submit(_oracle_compress, r, g, w) for r, g in zip(refs, gs)]
     else:
@@ -159,8 +161,10 @@ def oracle_step(refs, g_dev, w, kind, bias_correction=False, t=0):
         f.result()
 
 
-def compare_chunks(refs, w, kind, err, m, v, p, words=None, scales=None, signs=None, ratios=None):
-    """Compare the GPU buffers on the checked chunks with the oracle; returns scale-ulp mismatches."""
+def compare_chunks(refs, w, kind, err, m, v, p, words=None, scales=None, signs=None, ratios=None,
+                   diag=None):
+    """Compare the GPU buffers on the checked chunks with the oracle; returns scale-ulp mismatches.
+    diag: (err_sumsq, plus_count) device arrays of a compressed step's diagnostics, or None."""
     mism = 0
     b1 = np.float64(np.float32(w.beta1))
     eb = np.float64(np.float32(w.ef_beta))
@@ -182,6 +186,11 @@ def compare_chunks(refs, w, kind, err, m, v, p, words=None, scales=None, signs=N
                 ds = abs(float(sc) - float(r.out["scale"]))
             if signs is not None:
                 assert np.array_equal(synth.host(signs[r.a:r.b]), r.out["signs"]), f"{tag}: int8 signs differ"
+            if diag is not None:
+                rss, rpc = oracle.diagnostics(r.err_before, r.out["words"], np.asarray([0, r.b - r.a], np.int64))
+                gss = float(diag[0][r.c].item())
+                assert abs(gss - rss[0]) <= 1e-10 * rss[0], f"{tag}: error norm^2 {gss} vs {rss[0]}"
+                assert int(diag[1][r.c].item()) == int(rpc[0]), f"{tag}: +1 count"
             assert np.array_equal(gv, r.v), f"{tag}: v changed in the compressed step"
         else:
             assert_f32_close(gv, r.v, f"{tag}: v")
@@ -203,7 +212,7 @@ def compare_chunks(refs, w, kind, err, m, v, p, words=None, scales=None, signs=N
     return mism
 
 
-def run_workload(w, chunks=None, steps=None, device="cuda:0", log=print):
+def run_workload(w, chunks=None, steps=None, device="cuda:0", log=print, diagnostics=False):
     """Run w's schedule on the GPU and check the given chunks (all if None) every step.
 
     Returns a dict of counts (steps by kind, scale mismatches)."""
@@ -217,7 +226,8 @@ def run_workload(w, chunks=None, steps=None, device="cuda:0", log=print):
     opt = cls(plan, err, m, v, p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                               clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta,
                               int8_signs=w.int8_signs, count_nonfinite=True,
-                              freeze_step=w.freeze_step, refresh_period=w.refresh_period)
+                              freeze_step=w.freeze_step, refresh_period=w.refresh_period,
+                              diagnostics=diagnostics)
     refs = host_chunks(w, chunks, err, m, v, p)
     g = None
     counts = {"dense": 0, "compressed": 0, "scale_ulp_mismatch": 0}
@@ -232,7 +242,9 @@ def run_workload(w, chunks=None, steps=None, device="cuda:0", log=print):
         counts[kind] += 1
         counts["scale_ulp_mismatch"] += compare_chunks(refs, w, kind, err, m, v, p, opt.words,
                                                        opt.scales, opt.signs,
-                                                       getattr(opt, "ratios", None))
+                                                       getattr(opt, "ratios", None),
+                                                       (opt.err_sumsq, opt.plus_count)
+                                                       if diagnostics and kind == "compressed" else None)
         if kind == "compressed":
             nf_ref += sum(r.out["nf"] for r in refs)
         log(f"{w.name} step {s} {kind}: {len(refs)} chunks match")

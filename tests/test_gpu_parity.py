@@ -369,6 +369,46 @@ def test_workload_bert_base_lamb():
 
 
 # ------------------------------------------------------------------------------------------------
+# diagnostics: per-chunk error-buffer norm and +1 count
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("vname", ["fp32_plain", "bf16_ema_clip_int8_f16err", "fp32_ema_bf16err"])
+@pytest.mark.parametrize("lamb", [False, True])
+def test_diagnostics(vname, lamb):
+    var = VARIANTS[vname]
+    for n, chunk in ((1, 64), (130, 64), (5000, 1024), (1_000_003, 1 << 16), (3_000_017, 3_000_017)):
+        gnp, err, m, v, p = _small_state(n, n + 3, wide=var["clip"] > 0)
+        err = _as_err_format(err, var.get("edt", "f32"))
+        if var["gdt"] == "bf16":
+            gnp = _bf16_bits(gnp)
+        off = oracle.uniform_offsets(n, chunk)
+        K = off.size - 1
+        plan = ob.ob_plan_create(n, chunk_size=chunk)
+        ss = torch.full((K,), -1.0, dtype=torch.float64, device=DEV)
+        pc = torch.full((K,), -1, dtype=torch.int64, device=DEV)
+        ob.ob_plan_set_diagnostics(plan, ss, pc)
+        d = [_t(a) for a in (gnp, err, m, v, p)]
+        words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+        scales = torch.zeros(K, dtype=torch.float32, device=DEV)
+        hp = ob.hparams(lr=1e-4, clip=var["clip"], ef_mode=var["ef_mode"], ef_beta=0.9)
+        if lamb:
+            ob.ob_lamb_compress_step(plan, *d, words, scales, torch.zeros(K, device=DEV), hp)
+        else:
+            ob.ob_adam_compress_step(plan, *d, words, scales, hp)
+        rss, rpc = oracle.diagnostics(err, synth.host(words), off)
+        tag = f"diagnostics n={n} chunk={chunk} {vname} lamb={lamb}"
+        gss = synth.host(ss)
+        assert np.all(np.abs(gss - rss) <= 1e-10 * rss), f"{tag}: {gss} vs {rss}"
+        assert np.array_equal(synth.host(pc), rpc), tag
+        # switched off: the next step leaves the arrays alone
+        ob.ob_plan_set_diagnostics(plan, None, None)
+        ss.fill_(-1.0)
+        ob.ob_adam_compress_step(plan, *d, words, scales, hp)
+        torch.cuda.synchronize()
+        assert bool((ss == -1.0).all()), tag
+
+
+# ------------------------------------------------------------------------------------------------
 # edge cases of the boundary
 # ------------------------------------------------------------------------------------------------
 
@@ -482,8 +522,8 @@ def test_workload_single_1m():
 
 def test_workload_bert_base():
     """197 per-tensor chunks (108,891,648 fp32 elements): 5 dense steps, then 20 compressed; every
-    chunk checked every step."""
-    counts = P.run_workload(synth.BERT_BASE, log=lambda *_: None)
+    chunk checked every step, diagnostics (error norm, +1 count) included."""
+    counts = P.run_workload(synth.BERT_BASE, log=lambda *_: None, diagnostics=True)
     assert counts["dense"] == 5 and counts["compressed"] == 20
 
 
