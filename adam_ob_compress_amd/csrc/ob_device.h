@@ -46,6 +46,13 @@ constexpr int kPlainItem = 16 * kTile;  // elements per block for the plan-less 
 #ifndef OB_NT_DENSE
 #define OB_NT_DENSE 1
 #endif
+//   OB_SRV_UNROLL / OB_UNPACK_UNROLL  tiles in flight per loop trip in the server passes / unpack
+#ifndef OB_SRV_UNROLL
+#define OB_SRV_UNROLL 4
+#endif
+#ifndef OB_UNPACK_UNROLL
+#define OB_UNPACK_UNROLL 4
+#endif
 //   OB_NT_SRV2                    nontemporal loads and stores in server pass 2
 //   OB_NT_BITS                    nontemporal stores of packed words and int8 signs
 #ifndef OB_NT_SRV2

@@ -280,19 +280,36 @@ __device__ __forceinline__ f4 server_avg4(int W, const uint32_t* __restrict__ ww
 }
 
 // Sign patterns of the 4 elements of a lane, one byte each: byte k holds bit k of worker w's nibble
-// at bit w.  The 8 nibbles are packed as bits 4w+k and the 32-bit index is rotated right by two
-// index bits (4w+k -> 8k+w) with four delta swaps.
+// at bit w.  Input: the 8 workers' nibbles of the lane packed as bits 4w+k; the 32-bit index is
+// rotated right by two index bits (4w+k -> 8k+w) with four delta swaps.
 __device__ __forceinline__ uint32_t delta_swap(uint32_t x, int d, uint32_t mask)
 {
     const uint32_t t = ((x >> d) ^ x) & mask;
     return x ^ t ^ (t << d);
 }
 
-__device__ __forceinline__ uint32_t patterns4(const uint32_t (&nib)[kWorkerBatch])
+// 8x8 transpose of nibbles across each group of 8 lanes: on entry lane j holds the 8 nibbles
+// M[j][0..7] (nibble q at bits 4q..4q+3), on exit M[0..7][j] (M[w][j] at bits 4w..4w+3).  Three
+// butterfly stages; the stage of distance d swaps lane-index bit d with nibble-index bit d: the
+// lane with that bit clear keeps its low nibbles and takes its partner's low nibbles as its high
+// ones, the other lane the reverse.  DPP moves, no LDS; all lanes must be active.
+__device__ __forceinline__ uint32_t nib_transpose8(uint32_t x)
 {
-    uint32_t x = 0;
-#pragma unroll
-    for (int w = 0; w < kWorkerBatch; ++w) x |= (nib[w] & 0xFu) << (4 * w);
+    const int j = threadIdx.x & 7;
+    uint32_t y;
+    y = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0xB1, 0xF, 0xF, false));  // lane j^1
+    x = (j & 1) ? ((x & 0xF0F0F0F0u) | ((y & 0xF0F0F0F0u) >> 4)) : ((x & 0x0F0F0F0Fu) | ((y & 0x0F0F0F0Fu) << 4));
+    y = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x4E, 0xF, 0xF, false));  // lane j^2
+    x = (j & 2) ? ((x & 0xFF00FF00u) | ((y & 0xFF00FF00u) >> 8)) : ((x & 0x00FF00FFu) | ((y & 0x00FF00FFu) << 8));
+    // lane j^4: row_shl:4 (lane l reads lane l+4) for j < 4, row_shr:4 (lane l-4) for j >= 4
+    const uint32_t up = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x104, 0xF, 0xF, false));
+    const uint32_t dn = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xF, 0xF, false));
+    x = (j & 4) ? ((x & 0xFFFF0000u) | (dn >> 16)) : ((x & 0x0000FFFFu) | (up << 16));
+    return x;
+}
+
+__device__ __forceinline__ uint32_t patterns_of(uint32_t x)
+{
     x = delta_swap(x, 3, 0x0A0A0A0Au);   // index bits 0 <-> 2
     x = delta_swap(x, 6, 0x00CC00CCu);   // index bits 1 <-> 3
     x = delta_swap(x, 12, 0x0000F0F0u);  // index bits 2 <-> 4
@@ -333,67 +350,97 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
         scale = chunk_scale(pd, c, lds);
         if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[c]) scales[c] = scale;
     }
+    constexpr bool NTS = (!APPLY && OB_NT_SRV) || (APPLY && OB_NT_SRV2);
     double acc = 0.0;
-    for (int base = 0; base < it.len; base += kTile) {
-        const int rem = it.len - base;
-        const int cnt = rem - kVec * tid;
-        const int64_t i = it.start + base + kVec * tid;
+    // One tile's worth: given the error and (W <= 8) the lane's worker word, form x = avg + e, then
+    // the sum of squares (pass 1) or the new error and sign nibble (pass 2).
+    auto tile = [&](int64_t i, int cnt, f4 ev, uint32_t wd) -> uint32_t {
+        uint32_t pats = 0;
+        if (tabulate) {
+            // the transpose hands every lane its own nibble of all workers' words
+            wd = nib_transpose8(wd);
+            if (W < kWorkerBatch) wd &= (1u << (4 * W)) - 1u;
+            pats = patterns_of(wd);
+        }
         uint32_t nib = 0;
-        if (cnt > 0) {
-            // the error and worker loads are all issued before any of them is used
-            f4 ev = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (cnt >= kVec) ev = ld4 < (!APPLY && OB_NT_SRV) || (APPLY && OB_NT_SRV2) > (e, i);
-            f4 avg;
-            if (tabulate) {
-                uint32_t nb[kWorkerBatch];
-                const int64_t wi = i >> 5;
-                const int sh = static_cast<int>(i & 31);
-                // unconditional loads (clamped worker index) so that all are issued before the first use
+        if (cnt <= 0) return nib;
+        f4 avg;
+        if (tabulate) {
 #pragma unroll
-                for (int w = 0; w < kWorkerBatch; ++w) {
-                    const int wc = w < W ? w : W - 1;
-                    const uint32_t* wp = ww + static_cast<int64_t>(wc) * nw + wi;
-                    const uint32_t word = ((!APPLY && OB_NT_SRV) || (APPLY && OB_NT_SRV2)) ? __builtin_nontemporal_load(wp) : *wp;
-                    nb[w] = (word >> sh) & (w < W ? 0xFu : 0u);
-                }
-                const uint32_t pats = patterns4(nb);
+            for (int k = 0; k < kVec; ++k) avg[k] = table[(pats >> (8 * k)) & 0xFFu];
+        } else {
+            avg = server_avg4(W, ww, nw, ws, pd.K, c, i);
+        }
+        if (cnt >= kVec) {
+            f4 x;
 #pragma unroll
-                for (int k = 0; k < kVec; ++k) avg[k] = table[(pats >> (8 * k)) & 0xFFu];
-            } else {
-                avg = server_avg4(W, ww, nw, ws, pd.K, c, i);
-            }
-            if (cnt >= kVec) {
-                f4 x;
-#pragma unroll
-                for (int k = 0; k < kVec; ++k) x[k] = avg[k] + ev[k];
-                if (APPLY) {
-#pragma unroll
-                    for (int k = 0; k < kVec; ++k) {
-                        const bool b = x[k] >= 0.0f;
-                        ev[k] = x[k] - (b ? scale : -scale);
-                        nib |= (b ? 1u : 0u) << k;
-                    }
-                    st4<OB_NT_SRV2>(e, i, ev);
-                } else {
-#pragma unroll
-                    for (int k = 0; k < kVec; ++k) acc = fma(static_cast<double>(x[k]), static_cast<double>(x[k]), acc);
-                }
-            } else {
+            for (int k = 0; k < kVec; ++k) x[k] = avg[k] + ev[k];
+            if (APPLY) {
 #pragma unroll
                 for (int k = 0; k < kVec; ++k) {
-                    if (k >= cnt) continue;
-                    const float x = avg[k] + e[i + k];
-                    if (APPLY) {
-                        const bool b = x >= 0.0f;
-                        e[i + k] = x - (b ? scale : -scale);
-                        nib |= (b ? 1u : 0u) << k;
-                    } else {
-                        acc = fma(static_cast<double>(x), static_cast<double>(x), acc);
-                    }
+                    const bool b = x[k] >= 0.0f;
+                    ev[k] = x[k] - (b ? scale : -scale);
+                    nib |= (b ? 1u : 0u) << k;
+                }
+                st4<OB_NT_SRV2>(e, i, ev);
+            } else {
+#pragma unroll
+                for (int k = 0; k < kVec; ++k) acc = fma(static_cast<double>(x[k]), static_cast<double>(x[k]), acc);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                if (k >= cnt) continue;
+                const float x = avg[k] + e[i + k];
+                if (APPLY) {
+                    const bool b = x >= 0.0f;
+                    e[i + k] = x - (b ? scale : -scale);
+                    nib |= (b ? 1u : 0u) << k;
+                } else {
+                    acc = fma(static_cast<double>(x), static_cast<double>(x), acc);
                 }
             }
         }
-        if (APPLY) store_word(words, i, nib, 32 * (tid >> 3) < rem);
+        return nib;
+    };
+    // lane j of each 8-lane group loads worker j's word of the group's 32 elements (worker index
+    // clamped to W-1; the surplus nibbles are masked off after the transpose)
+    const int wc = (tid & 7) < W ? (tid & 7) : W - 1;
+    const uint32_t* __restrict__ wrow = ww + static_cast<int64_t>(wc) * nw;
+    auto load_word = [&](int64_t i) -> uint32_t {
+        const uint32_t* wp = wrow + (i >> 5);
+        return NTS ? __builtin_nontemporal_load(wp) : *wp;
+    };
+    // whole tiles, OB_SRV_UNROLL in flight: all their loads are issued before any is used
+    constexpr int U = OB_SRV_UNROLL;
+    int base = 0;
+    for (; base + U * kTile <= it.len; base += U * kTile) {
+        f4 ev[U];
+        uint32_t wd[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            ev[u] = ld4<NTS>(e, i);
+            wd[u] = tabulate ? load_word(i) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            const uint32_t nib = tile(i, kVec, ev[u], wd[u]);
+            if (APPLY) store_word(words, i, nib, true);
+        }
+    }
+    // the rest, one (possibly ragged) tile at a time
+    for (; base < it.len; base += kTile) {
+        const int rem = it.len - base;
+        const int cnt = rem - kVec * tid;
+        const int64_t i = it.start + base + kVec * tid;
+        const bool group_valid = 32 * (tid >> 3) < rem;   // the word of this lane's 8-lane group exists
+        f4 ev = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (cnt >= kVec) ev = ld4<NTS>(e, i);
+        const uint32_t wd = (tabulate && group_valid) ? load_word(i) : 0u;
+        const uint32_t nib = tile(i, cnt, ev, wd);
+        if (APPLY) store_word(words, i, nib, group_valid);
     }
     if (!APPLY) {
         const double s = block_sum(acc, lds);
@@ -422,14 +469,33 @@ __global__ __launch_bounds__(kBlock) void k_unpack(const Item* __restrict__ item
         len = static_cast<int>(min(static_cast<int64_t>(kPlainItem), n - start));
     }
     const int tid = threadIdx.x;
-    for (int base = 0; base < len; base += kTile) {
-        const int cnt = len - base - kVec * tid;
-        const int64_t i = start + base + kVec * tid;
-        if (cnt <= 0) continue;
-        const uint32_t bits = words[i >> 5] >> (i & 31);
+    auto values = [&](uint32_t bits) {
         f4 r;
 #pragma unroll
         for (int k = 0; k < kVec; ++k) r[k] = ((bits >> k) & 1u) ? s : -s;
+        return r;
+    };
+    // whole tiles, OB_UNPACK_UNROLL in flight: the word loads are issued before the stores
+    constexpr int U = OB_UNPACK_UNROLL;
+    int base = 0;
+    for (; base + U * kTile <= len; base += U * kTile) {
+        uint32_t bits[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = start + base + u * kTile + kVec * tid;
+            bits[u] = words[i >> 5] >> (i & 31);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = start + base + u * kTile + kVec * tid;
+            st4<OB_NT_UNPACK>(out, i, values(bits[u]));
+        }
+    }
+    for (; base < len; base += kTile) {
+        const int cnt = len - base - kVec * tid;
+        const int64_t i = start + base + kVec * tid;
+        if (cnt <= 0) continue;
+        const f4 r = values(words[i >> 5] >> (i & 31));
         if (cnt >= kVec) {
             st4<OB_NT_UNPACK>(out, i, r);
         } else {
