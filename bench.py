@@ -299,7 +299,8 @@ def main():
 # ------------------------------------------------------------------------------------------------
 
 def _short(name: str) -> str:
-    for key in ("k_chunk_sumsq", "k_compress", "k_dense", "k_server", "k_unpack", "k_pack"):
+    for key in ("k_chunk_sumsq", "k_compress", "k_dense", "k_server", "k_unpack", "k_pack", "k_lamb_apply",
+                "k_trust_ratio", "k_diag_reduce"):
         if key in name:
             tmpl = name.split(key, 1)[1]
             return key + (tmpl[:60] if tmpl else "")
@@ -307,7 +308,8 @@ def _short(name: str) -> str:
 
 
 KERNEL_SYMBOL = {"compress": "k_compress<", "chunk_sumsq": "k_chunk_sumsq<", "dense": "k_dense<",
-                 "server_sumsq": "k_server<false>", "server_apply": "k_server<true>", "unpack": "k_unpack"}
+                 "server_sumsq": "k_server<false>", "server_apply": "k_server<true>", "unpack": "k_unpack",
+                 "lamb_apply": "k_lamb_apply<", "trust_ratio": "k_trust_ratio", "diag": "k_diag_reduce"}
 
 
 def _counter_rows(d: str, counter: str):
