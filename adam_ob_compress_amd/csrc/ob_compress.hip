@@ -371,7 +371,7 @@ hipError_t launch_compress(const PlanDev& pd, const void* g, int g_bf16, void* e
     return hipGetLastError();
 }
 
-// this build's format
+// the error format this translation unit is compiled for
 template hipError_t launch_chunk_sumsq<OB_ERR_FMT>(const PlanDev&, const void*, int, const void*, float,
                                                    const float*, hipStream_t);
 template hipError_t launch_compress<OB_ERR_FMT>(const PlanDev&, const void*, int, void*, float*, const float*,

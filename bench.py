@@ -284,7 +284,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): the "
-              "compressed step is one GPU's share; the multi-GPU exchange is not part of this build.",
+              "compressed step is one GPU's share; the multi-GPU exchange is not implemented here.",
               file=sys.stderr)
         return 2
     w, res = run(args)
@@ -349,9 +349,9 @@ Kernel source sha (ob_compress.hip, ob_kernels.hip, ob_device.h, ob_internal.h):
 
 Commands (each its own run on one MI355X, from the repository root, `export TMPDIR=/tmp`):
 
-    rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o run --output-format csv -- python bench.py --workload {w.name} --steps 5 --warmup 2 --no-cpu --copy-probe-mib 1024
-    rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o run --output-format csv -- python bench.py --workload {w.name} --steps 5 --warmup 2 --no-cpu --copy-probe-mib 1024
-    python bench.py --traffic-profile gpurun_out --kernel {kernel} --workload {w.name}
+    rocprofv3 --pmc FETCH_SIZE -d rocprof_out/fetch -o run --output-format csv -- python bench.py --workload {w.name} --steps 5 --warmup 2 --no-cpu --copy-probe-mib 1024
+    rocprofv3 --pmc WRITE_SIZE -d rocprof_out/write -o run --output-format csv -- python bench.py --workload {w.name} --steps 5 --warmup 2 --no-cpu --copy-probe-mib 1024
+    python bench.py --traffic-profile rocprof_out --kernel {kernel} --workload {w.name}
 
 Calibration: the run also copies 1 GiB with torch (`__amd_rocclr_copyBuffer`, grid 131072), which
 reads and writes 1,048,576 KiB.  The counters read {ff * probe_kib:,.1f} KiB (FETCH_SIZE) and
