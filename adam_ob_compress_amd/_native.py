@@ -19,12 +19,12 @@ OB_F32, OB_BF16, OB_F16 = 0, 1, 2
 OB_EF_PLAIN, OB_EF_EMA = 0, 1
 (OB_KERNEL_CHUNK_SUMSQ, OB_KERNEL_COMPRESS, OB_KERNEL_DENSE, OB_KERNEL_SERVER_SUMSQ,
  OB_KERNEL_SERVER_APPLY, OB_KERNEL_UNPACK, OB_KERNEL_TRUST_RATIO, OB_KERNEL_LAMB_APPLY,
- OB_KERNEL_DIAG) = range(9)
+ OB_KERNEL_DIAG, OB_KERNEL_SCALE) = range(10)
 KERNEL_NAMES = {
     OB_KERNEL_CHUNK_SUMSQ: "chunk_sumsq", OB_KERNEL_COMPRESS: "compress", OB_KERNEL_DENSE: "dense",
     OB_KERNEL_SERVER_SUMSQ: "server_sumsq", OB_KERNEL_SERVER_APPLY: "server_apply",
     OB_KERNEL_UNPACK: "unpack", OB_KERNEL_TRUST_RATIO: "trust_ratio", OB_KERNEL_LAMB_APPLY: "lamb_apply",
-    OB_KERNEL_DIAG: "diag",
+    OB_KERNEL_DIAG: "diag", OB_KERNEL_SCALE: "scale",
 }
 
 

@@ -19,6 +19,10 @@ struct ob_plan_s {
     int32_t K = 0;
     int64_t* d_chunk_off = nullptr;
     double* d_partials = nullptr;  // one per pass-1 block
+    int64_t p1_max = 0;            // most pass-1 blocks in one chunk
+    // plans with more than kFinalizeAt pass-1 blocks in a chunk: per-chunk sums and the identity table
+    double* d_chunk_sums = nullptr;  // [K]
+    int32_t* d_ident = nullptr;      // [K + 1]: 0, 1, ..., K
     double* d_partials_w = nullptr;  // LAMB: one per pass-1 or dense block (the larger)
     double* d_partials_u = nullptr;  // LAMB: one per compressed-pass-2 or dense block (the larger)
 
@@ -72,6 +76,12 @@ struct ob_plan_s {
 namespace {
 
 constexpr int64_t kMaxBlockElems = int64_t(1) << 20;
+
+// Chunks with more pass-1 partials than this get one sum per chunk (a one-block-per-chunk kernel)
+// before pass 2; below it every pass-2 block adds its chunk's partials itself, with no extra launch.
+// Measured: at 1,761 partials (BERT-base's embedding) the in-block reduction is still the faster; the
+// extra launch is for chunks so large that every block re-adding their partials would dominate.
+constexpr int64_t kFinalizeAt = 16 * ob::kBlock;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -141,6 +151,8 @@ void free_plan(ob_plan p)
     if (p->d_partials_w) (void)hipFree(p->d_partials_w);
     if (p->d_partials_u) (void)hipFree(p->d_partials_u);
     if (p->d_partials_e) (void)hipFree(p->d_partials_e);
+    if (p->d_chunk_sums) (void)hipFree(p->d_chunk_sums);
+    if (p->d_ident) (void)hipFree(p->d_ident);
     if (p->d_partials_b) (void)hipFree(p->d_partials_b);
     delete p;
 }
@@ -307,6 +319,8 @@ ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_off
         first[pass][K] = static_cast<int32_t>(items[pass].size());
         t.n_items = static_cast<int64_t>(items[pass].size());
     }
+    for (int64_t c = 0; c < K; ++c)
+        p->p1_max = std::max<int64_t>(p->p1_max, first[T_PASS1][c + 1] - first[T_PASS1][c]);
 
     if (hipGetDevice(&p->device) != hipSuccess) {
         delete p;
@@ -330,6 +344,15 @@ ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_off
                 return fail(e);
         }
         if ((e = hipMalloc(&p->d_partials, items[0].size() * sizeof(double))) != hipSuccess) return fail(e);
+        if (p->p1_max > kFinalizeAt) {
+            std::vector<int32_t> ident(static_cast<size_t>(K) + 1);
+            for (int64_t c = 0; c <= K; ++c) ident[c] = static_cast<int32_t>(c);
+            if ((e = hipMalloc(&p->d_chunk_sums, static_cast<size_t>(K) * sizeof(double))) != hipSuccess) return fail(e);
+            if ((e = hipMalloc(&p->d_ident, ident.size() * sizeof(int32_t))) != hipSuccess) return fail(e);
+            if ((e = hipMemcpy(p->d_ident, ident.data(), ident.size() * sizeof(int32_t), hipMemcpyHostToDevice)) !=
+                hipSuccess)
+                return fail(e);
+        }
         const size_t nw = std::max(items[T_PASS1].size(), items[T_DENSE].size());
         const size_t nu = std::max(items[T_COMPRESS].size(), items[T_DENSE].size());
         if ((e = hipMalloc(&p->d_partials_w, nw * sizeof(double))) != hipSuccess) return fail(e);
@@ -380,6 +403,21 @@ ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, flo
 
 namespace {
 
+// Pass-2 view of the plan.  With many partials per chunk, the chunk sums are formed first (one block
+// per chunk) and the view's pass-1 table becomes the identity over them, so that each pass-2 block
+// forms its scale from one partial instead of all of them.
+ob_status pass2_view(ob_plan plan, int table, hipStream_t stream, ob::PlanDev* out)
+{
+    *out = plan->dev(table);
+    if (plan->p1_max <= kFinalizeAt) return OB_OK;
+    const ob::PlanDev pd1 = plan->dev(T_PASS1);
+    const ob_status st = timed(plan, OB_KERNEL_SCALE, stream,
+                               [&] { return ob::launch_chunk_sums(pd1, plan->d_chunk_sums, stream); });
+    out->p1_first = plan->d_ident;
+    out->partials = plan->d_chunk_sums;
+    return st;
+}
+
 // Validation and passes 1-2 of the compressed step.  lamb != 0: passes 1-2 of the 1-bit LAMB step
 // (sums of p^2 and u^2 instead of the update); the caller then runs the trust ratio and the update.
 ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
@@ -410,7 +448,8 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
 
     DeviceGuard guard(plan->device);
     if (!guard.ok) return OB_ERR_HIP;
-    const ob::PlanDev pd1 = plan->dev(T_PASS1), pd = plan->dev(T_COMPRESS);
+    const ob::PlanDev pd1 = plan->dev(T_PASS1);
+    ob::PlanDev pd;
     const int bf = g_dtype == OB_BF16;
     const int ema = hp->ef_mode == OB_EF_EMA;
     auto nf = reinterpret_cast<unsigned long long*>(nonfinite_out);
@@ -423,6 +462,7 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
         }
     });
     if (st != OB_OK) return st;
+    if ((st = pass2_view(plan, T_COMPRESS, stream, &pd)) != OB_OK) return st;
     st = timed(plan, OB_KERNEL_COMPRESS, stream, [&] {
         switch (err_dtype) {
         case OB_BF16:
@@ -437,8 +477,9 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
         }
     });
     if (st != OB_OK || !plan->diag_err_sumsq) return st;
+    const ob::PlanDev pdd = plan->dev(T_COMPRESS);   // the pass-1 table the error sums were written by
     return timed(plan, OB_KERNEL_DIAG, stream, [&] {
-        return ob::launch_diag_reduce(pd, plan->diag_err_sumsq, plan->diag_plus, stream);
+        return ob::launch_diag_reduce(pdd, plan->diag_err_sumsq, plan->diag_plus, stream);
     });
 }
 
@@ -531,11 +572,13 @@ ob_status ob_server_reduce(ob_plan plan, int32_t W, const uint32_t* worker_words
         return OB_ERR_ALIGN;
     DeviceGuard guard(plan->device);
     if (!guard.ok) return OB_ERR_HIP;
-    const ob::PlanDev pd1 = plan->dev(T_PASS1), pd = plan->dev(T_SERVER);
+    const ob::PlanDev pd1 = plan->dev(T_PASS1);
     ob_status st = timed(plan, OB_KERNEL_SERVER_SUMSQ, stream, [&] {
         return ob::launch_server_sumsq(pd1, W, worker_words, worker_scales, server_err, stream);
     });
     if (st != OB_OK) return st;
+    ob::PlanDev pd;
+    if ((st = pass2_view(plan, T_SERVER, stream, &pd)) != OB_OK) return st;
     return timed(plan, OB_KERNEL_SERVER_APPLY, stream, [&] {
         return ob::launch_server_apply(pd, W, worker_words, worker_scales, server_err, words_out, scales_out,
                                        stream);

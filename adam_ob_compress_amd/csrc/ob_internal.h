@@ -80,6 +80,10 @@ hipError_t launch_dense(const PlanDev& pd, const void* g, int g_bf16, float* m, 
 // partials_b (this launch's pass-2 table, chunk_first).
 hipError_t launch_diag_reduce(const PlanDev& pd, double* err_sumsq, unsigned long long* plus_count,
                               hipStream_t s);
+// One block per chunk: the chunk's pass-1 partials (p1_first ranges) added in a fixed order into
+// sums[c].  A pass-2 view whose p1_first is the identity 0..K and whose partials are `sums` then forms
+// the same scale from one partial per chunk.
+hipError_t launch_chunk_sums(const PlanDev& pd, double* sums, hipStream_t s);
 // One block per chunk: r_c from the chunk's partials_w / partials_u.
 hipError_t launch_trust_ratio(const PlanDev& pd, float* ratios, hipStream_t s);
 hipError_t launch_lamb_apply(const PlanDev& pd, const float* m, const float* v, float* p, const float* ratios,

@@ -126,6 +126,20 @@ __global__ __launch_bounds__(kBlock) void k_dense(PlanDev pd, const typename G::
 // LAMB ([P2] "1-bit LAMB"): the layer's trust ratio from the per-block sums, then the update
 // ------------------------------------------------------------------------------------------------
 
+// One block per chunk: S_c = the chunk's pass-1 partials added in the fixed order chunk_scale uses
+// (for plans whose chunks have so many partials that every pass-2 block adding them all would cost
+// more than this launch).
+__global__ __launch_bounds__(kBlock) void k_chunk_sums(PlanDev pd, double* __restrict__ sums)
+{
+    __shared__ double lds[kBlock / 64];
+    const int c = blockIdx.x;
+    double s = 0.0;
+    for (int i = pd.p1_first[c] + static_cast<int>(threadIdx.x); i < pd.p1_first[c + 1]; i += kBlock)
+        s += pd.partials[i];
+    s = block_sum(s, lds);
+    if (threadIdx.x == 0) sums[c] = s;
+}
+
 // One block per layer (chunk): r = ||w|| / ||u||, the chunk's partial sums added in a fixed order;
 // r = 1 when either sum is 0 (the ratio is undefined there; NaN and Inf propagate).
 __global__ __launch_bounds__(kBlock) void k_trust_ratio(PlanDev pd, float* __restrict__ ratios)
@@ -565,6 +579,12 @@ hipError_t launch_diag_reduce(const PlanDev& pd, double* err_sumsq, unsigned lon
 {
     hipLaunchKernelGGL(k_diag_reduce, dim3(static_cast<unsigned>(pd.K)), dim3(kBlock), 0, s, pd, err_sumsq,
                        plus_count);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_sums(const PlanDev& pd, double* sums, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_chunk_sums, dim3(static_cast<unsigned>(pd.K)), dim3(kBlock), 0, s, pd, sums);
     return hipGetLastError();
 }
 

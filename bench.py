@@ -61,7 +61,7 @@ def bytes_per_elem(w, kernel: str) -> float:
         return gb + 12.0 + (8.0 if lamb else 12.0)
     if kernel == "lamb_apply":        # read m v p, write p
         return 16.0
-    if kernel in ("trust_ratio", "diag"):   # one block per chunk over the per-block partial sums
+    if kernel in ("trust_ratio", "diag", "scale"):   # one block per chunk over the per-block partial sums
         return 0.0
     if kernel == "server_sumsq":      # read W sign bits and the server error
         return w.workers / 8.0 + 4.0
@@ -300,7 +300,7 @@ def main():
 
 def _short(name: str) -> str:
     for key in ("k_chunk_sumsq", "k_compress", "k_dense", "k_server", "k_unpack", "k_pack", "k_lamb_apply",
-                "k_trust_ratio", "k_diag_reduce"):
+                "k_trust_ratio", "k_diag_reduce", "k_scale_finalize"):
         if key in name:
             tmpl = name.split(key, 1)[1]
             return key + (tmpl[:60] if tmpl else "")
@@ -309,7 +309,8 @@ def _short(name: str) -> str:
 
 KERNEL_SYMBOL = {"compress": "k_compress<", "chunk_sumsq": "k_chunk_sumsq<", "dense": "k_dense<",
                  "server_sumsq": "k_server<false>", "server_apply": "k_server<true>", "unpack": "k_unpack",
-                 "lamb_apply": "k_lamb_apply<", "trust_ratio": "k_trust_ratio", "diag": "k_diag_reduce"}
+                 "lamb_apply": "k_lamb_apply<", "trust_ratio": "k_trust_ratio", "diag": "k_diag_reduce",
+                 "scale": "k_scale_finalize"}
 
 
 def _counter_rows(d: str, counter: str):

@@ -192,7 +192,9 @@ typedef enum {
     OB_KERNEL_TRUST_RATIO = 6,     /* LAMB: per-layer ratios */
     OB_KERNEL_LAMB_APPLY = 7,      /* LAMB: parameter update */
     OB_KERNEL_DIAG = 8,            /* diagnostics: per-chunk totals */
-    OB_KERNEL_COUNT = 9
+    OB_KERNEL_SCALE = 9,           /* per-chunk sums of squares formed before pass 2 (plans with a
+                                      chunk of more than 4096 pass-1 blocks) */
+    OB_KERNEL_COUNT = 10
 } ob_kernel;
 
 ob_status ob_plan_set_timing(ob_plan plan, int32_t enable);

@@ -174,6 +174,17 @@ def test_compress_multi_tile(vname, n, chunk):
     _gpu_vs_oracle_compress(n, chunk, VARIANTS[vname], seed=n, steps=3)
 
 
+@pytest.mark.parametrize("vname", ["fp32_plain", "bf16_ema_clip_int8_f16err"])
+def test_compress_single_huge_chunk(vname):
+    """One chunk of 17,000,003 elements: more than 4096 pass-1 blocks, so the scale is formed by its own
+    kernel before pass 2 (the other tests take the in-block reduction)."""
+    n = 17_000_003
+    plan = ob.ob_plan_create(n, chunk_size=n)
+    assert plan.num_chunks == 1
+    _gpu_vs_oracle_compress(n, n, VARIANTS[vname], seed=5, steps=2)
+    _gpu_vs_oracle_lamb(n, n, VARIANTS[vname], seed=6)
+
+
 def test_compress_edge_values():
     """Negative denormals, both zeros, NaN and Inf in g and in the error buffer."""
     n = 4096 + 17
@@ -219,6 +230,27 @@ def test_dense_step(gdt, bias_correction):
                            bias_correction=bias_correction, step=3)
         for name, dev_t, ref in (("m", d[1], m), ("v", d[2], v), ("p", d[3], p)):
             P.assert_f32_close(synth.host(dev_t), ref, f"dense n={n} {gdt} bc={bias_correction}: {name}")
+
+
+@pytest.mark.parametrize("W", [2, 8, 9])
+def test_server_single_huge_chunk(W):
+    """One 17,000,003-element chunk (scale formed by its own kernel before pass 2), one round."""
+    n = 17_000_003
+    off = oracle.uniform_offsets(n, n)
+    rng = np.random.default_rng([W, 17])
+    ww = rng.integers(0, 1 << 32, size=(W, (n + 31) // 32), dtype=np.uint64).astype(np.uint32)
+    ws = rng.uniform(1e-4, 1e-2, size=(W, 1)).astype(np.float32)
+    e = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+    plan = ob.ob_plan_create(n, chunk_size=n)
+    de = _t(e)
+    words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+    scales = torch.zeros(1, dtype=torch.float32, device=DEV)
+    ob.ob_server_reduce(plan, _t(ww).view(W, -1), _t(ws), de, words, scales)
+    rw, rs = oracle.server_reduce(ww, ws, e, off)
+    assert np.array_equal(synth.host(words), rw)
+    gs = synth.host(scales)
+    assert np.all(P.ulp_diff(gs, rs) <= 1)
+    P.assert_f32_close(synth.host(de), e, f"server W={W} huge chunk: err", abs(float(gs[0]) - float(rs[0])))
 
 
 def test_server_bruteforce_small():
