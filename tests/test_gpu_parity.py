@@ -199,6 +199,51 @@ def test_compress_edge_values():
                                     state=tuple(a.copy() for a in state))
 
 
+def test_compress_and_dense_divide_by_zero():
+    """v = 0 with eps = 0: the update divides by zero (m/0 = +-Inf, 0/0 = NaN) on both sides, per IEEE;
+    a few v are also negative denormals and +Inf."""
+    n = 4096 + 5
+    rng = np.random.default_rng(21)
+    for vname in ("fp32_plain", "bf16_ema_clip_int8"):
+        var = VARIANTS[vname]
+        gnp = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        gnp[::7] = 0.0
+        v = np.zeros(n, np.float32)
+        v[1::11] = np.float32(-1e-45)
+        v[2::13] = np.inf
+        m = np.where(rng.random(n) < 0.5, np.float32(0.0), (rng.standard_normal(n) * 1e-4).astype(np.float32))
+        state = (np.zeros(n, np.float32), m.astype(np.float32), v, (rng.standard_normal(n) * 0.02).astype(np.float32))
+        _gpu_vs_oracle_compress_eps0(n, var, gnp, state)
+
+
+def _gpu_vs_oracle_compress_eps0(n, var, gnp, state):
+    err, m, v, p = (a.copy() for a in state)
+    err = _as_err_format(err, var.get("edt", "f32"))
+    gin = _bf16_bits(gnp) if var["gdt"] == "bf16" else gnp
+    off = oracle.uniform_offsets(n, 1024)
+    plan = ob.ob_plan_create(n, chunk_size=1024)
+    hp = ob.hparams(lr=1e-3, beta1=0.9, beta2=0.999, eps=0.0, clip=var["clip"], ef_mode=var["ef_mode"],
+                    ef_beta=0.9)
+    d = [_t(a) for a in (gin, err, m, v, p)]
+    words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+    scales = torch.zeros(off.size - 1, dtype=torch.float32, device=DEV)
+    ob.ob_adam_compress_step(plan, d[0], d[1], d[2], d[3], d[4], words, scales, hp)
+    rw, rs, _, _ = oracle.compress_step(gin, err, m, v, p, off, lr=1e-3, beta1=0.9, eps=0.0, clip=var["clip"],
+                                        ef_mode=var["ef_mode"], ef_beta=0.9)
+    tag = f"eps=0 v=0 {var}"
+    assert np.array_equal(synth.host(words), rw), tag
+    assert np.all(P.ulp_diff(synth.host(scales), rs) <= 1), tag
+    P.assert_f32_close(synth.host(d[4]), p, tag + ": p")
+    assert np.isinf(p).any() and np.isnan(p).any(), "the case must reach +-Inf and NaN"
+    # the dense step from the same state: v grows from 0, and where g = 0 too, 0/0
+    m2, v2, p2 = (a.copy() for a in state[1:])
+    dd = [_t(a) for a in (gin, m2, v2, p2)]
+    ob.ob_adam_warmup_step(plan, dd[0], dd[1], dd[2], dd[3], hp)
+    oracle.warmup_step(gin, m2, v2, p2, lr=1e-3, beta1=0.9, beta2=0.999, eps=0.0)
+    for name, t, ref in (("m", dd[1], m2), ("v", dd[2], v2), ("p", dd[3], p2)):
+        P.assert_f32_close(synth.host(t), ref, tag + ": dense " + name)
+
+
 def test_compress_f16_error_overflow_is_counted():
     """New errors beyond fp16's range are stored as +-Inf and counted as non-finite."""
     n = 10_000 + 3
