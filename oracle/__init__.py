@@ -64,6 +64,12 @@ def _load():
                                           F, F, F, F, I, F]
     lib.or_lamb_warmup_step.argtypes = [I64, I64, P, P, I, P, P, P, P, F, F, F, F, I, I64]
     lib.or_diagnostics.argtypes = [I64, I64, P, P, I, P, P, P]
+    U64 = ctypes.c_uint64
+    lib.or_philox4x64.argtypes = [P, P, P]
+    lib.or_philox4x64.restype = None
+    lib.or_to_format_sr.argtypes = [P, I64, I, U64, U64, I64, P]
+    lib.or_compress_step_sr.argtypes = [I64, I64, P, P, I, P, I, P, P, P, P, P, P, P,
+                                        F, F, F, F, I, F, I, P, U64, U64]
     lib.or_to_format.argtypes = [P, I64, I, P]
     lib.or_from_format.argtypes = [P, I64, I, P]
     lib.or_warmup_step.argtypes = [I64, P, I, P, P, P, F, F, F, F, I, I64]
@@ -75,7 +81,8 @@ def _load():
     lib.or_chunk_scale.restype = ctypes.c_float
     for name in ("or_pack", "or_unpack", "or_compress_step", "or_warmup_step",
                  "or_server_reduce", "or_server_average", "or_to_format", "or_from_format",
-                 "or_lamb_compress_step", "or_lamb_warmup_step", "or_diagnostics"):
+                 "or_lamb_compress_step", "or_lamb_warmup_step", "or_diagnostics", "or_to_format_sr",
+                 "or_compress_step_sr"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -123,6 +130,25 @@ def to_format(x: np.ndarray, fmt: str) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     bits = np.zeros(x.size, dtype=np.uint16)
     _check(_load().or_to_format(_ptr(x), x.size, ERR_FORMATS[fmt], _ptr(bits)), "to_format")
+    return bits.view(np.float16) if fmt == "f16" else bits
+
+
+def philox4x64(counter, key) -> np.ndarray:
+    """Philox4x64-10 of a 4 x uint64 counter under a 2 x uint64 key (reading R18)."""
+    c = np.ascontiguousarray(counter, dtype=np.uint64)
+    k = np.ascontiguousarray(key, dtype=np.uint64)
+    out = np.zeros(4, dtype=np.uint64)
+    _load().or_philox4x64(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def to_format_sr(x: np.ndarray, fmt: str, seed: int, step: int, index0: int = 0) -> np.ndarray:
+    """Stochastic rounding (R18) of fp32 values stored as flat elements index0.. of a "bf16" (uint16 bits)
+    or "f16" (float16) error buffer, with the random bits of (seed, step)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = np.zeros(x.size, dtype=np.uint16)
+    _check(_load().or_to_format_sr(_ptr(x), x.size, ERR_FORMATS[fmt], seed, step, index0, _ptr(bits)),
+           "to_format_sr")
     return bits.view(np.float16) if fmt == "f16" else bits
 
 
@@ -179,7 +205,7 @@ def chunk_scale(x: np.ndarray, begin: int, end: int) -> float:
 
 
 def compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef_mode=0, ef_beta=0.9,
-                  want_signs=False, count_nonfinite=False):
+                  want_signs=False, count_nonfinite=False, stochastic=False, sr_seed=0, sr_step=0):
     """One compressed step.  err, m, p are updated in place; v is read only.  m, v, p are fp32; the
     error buffer is fp32, fp16 (numpy float16) or bf16 (uint16 bits), see R15.
 
@@ -196,9 +222,15 @@ def compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef_mode
     scales = np.zeros(max(k, 0), dtype=np.float32)
     signs = np.zeros(n, dtype=np.int8) if want_signs else None
     nf = np.zeros(1, dtype=np.int64) if count_nonfinite else None
-    rc = _load().or_compress_step(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m), _ptr(v),
-                                  _ptr(p), _ptr(words), _ptr(scales), _ptr(signs), _ptr(nf),
-                                  lr, beta1, eps, clip, ef_mode, ef_beta)
+    if stochastic:      # R18: stochastic rounding of a 16-bit error buffer
+        rc = _load().or_compress_step_sr(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m),
+                                         _ptr(v), _ptr(p), _ptr(words), _ptr(scales), _ptr(signs),
+                                         _ptr(nf), lr, beta1, eps, clip, ef_mode, ef_beta, 0, None,
+                                         sr_seed, sr_step)
+    else:
+        rc = _load().or_compress_step(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m), _ptr(v),
+                                      _ptr(p), _ptr(words), _ptr(scales), _ptr(signs), _ptr(nf),
+                                      lr, beta1, eps, clip, ef_mode, ef_beta)
     _check(rc, "compress_step")
     return words, scales, signs, (int(nf[0]) if nf is not None else None)
 
@@ -228,7 +260,7 @@ def diagnostics(err_before, words, offsets):
 
 
 def lamb_compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef_mode=0, ef_beta=0.9,
-                       want_signs=False, count_nonfinite=False):
+                       want_signs=False, count_nonfinite=False, stochastic=False, sr_seed=0, sr_step=0):
     """One compressed 1-bit LAMB step (reading R16): as compress_step up to the momentum, then the
     per-chunk (layer) trust ratio and update.  err, m, p in place; v read only.
 
@@ -245,9 +277,15 @@ def lamb_compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef
     ratios = np.zeros(max(k, 0), dtype=np.float32)
     signs = np.zeros(n, dtype=np.int8) if want_signs else None
     nf = np.zeros(1, dtype=np.int64) if count_nonfinite else None
-    rc = _load().or_lamb_compress_step(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m),
-                                       _ptr(v), _ptr(p), _ptr(words), _ptr(scales), _ptr(ratios),
-                                       _ptr(signs), _ptr(nf), lr, beta1, eps, clip, ef_mode, ef_beta)
+    if stochastic:
+        rc = _load().or_compress_step_sr(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m),
+                                         _ptr(v), _ptr(p), _ptr(words), _ptr(scales), _ptr(signs),
+                                         _ptr(nf), lr, beta1, eps, clip, ef_mode, ef_beta, 1, _ptr(ratios),
+                                         sr_seed, sr_step)
+    else:
+        rc = _load().or_lamb_compress_step(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m),
+                                           _ptr(v), _ptr(p), _ptr(words), _ptr(scales), _ptr(ratios),
+                                           _ptr(signs), _ptr(nf), lr, beta1, eps, clip, ef_mode, ef_beta)
     _check(rc, "lamb_compress_step")
     return words, scales, ratios, signs, (int(nf[0]) if nf is not None else None)
 

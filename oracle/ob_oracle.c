@@ -47,6 +47,15 @@
  *      in R4/R6 and then rounded to the storage format to nearest, ties to even (IEEE 754's default
  *      rounding), overflowing to +-Inf.  The R8 check counts non-finite STORED values, so an fp16
  *      overflow is reported.
+ *   R18 stochastic rounding of a 16-bit error buffer (optional; the nearest-even store of R15 is the
+ *      default): the new fp32 error e is stored as lo or hi, the two format values around |e| (lo
+ *      toward zero, hi = lo + one quantum q), choosing hi iff r * q < (|e| - lo) * 65536, where r is a
+ *      16-bit random integer; so hi comes with probability (|e| - lo)/q (to 1/65536).  Values of the
+ *      format, +-0, NaN and +-Inf are stored unchanged; a hi beyond the largest finite value is Inf.
+ *      r for flat element i: output word (i >> 2) & 3, bits 16*(i & 3) .. +15, of Philox4x64-10
+ *      (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011) at counter
+ *      (i >> 4, 0, 0, 0) with key (seed, step): a counter-based generator, so every element's bits are
+ *      a function of (seed, step, i) alone.
  *   R16 1-bit LAMB ([P2] section "1-bit LAMB: also protect the layer-wise trust ratio"): a layer is a
  *      chunk (one chunk per parameter tensor).  The direction is u_i = m_i / (sqrt(v_i) + eps) with
  *      the new m (compressed step: v frozen, m driven by g_hat as in R5/R6; dense step: the new m and
@@ -112,6 +121,65 @@ static double round_to_format(double x, int prec, int emin, double maxf)
     return copysign(r, x);
 }
 
+/* R18: the format value next to |x| toward zero, and its quantum (x an fp32 value, finite). */
+static double truncate_to_format(double a, int prec, int emin, double* quantum)
+{
+    int e;
+    frexp(a, &e);
+    int E = e - 1;
+    if (a == 0.0 || E < emin) E = emin;
+    double q = ldexp(1.0, E - (prec - 1));
+    *quantum = q;
+    return floor(a / q) * q;
+}
+
+/* R18: stochastic rounding of x to the format with the 16-bit random integer r. */
+static double stochastic_round(double x, int prec, int emin, double maxf, uint32_t r)
+{
+    if (isnan(x) || isinf(x)) return x;
+    double a = fabs(x), q;
+    double lo = truncate_to_format(a, prec, emin, &q);
+    double v = lo;
+    if (lo != a && (double)r * q < (a - lo) * 65536.0) v = lo + q;
+    if (v > maxf) v = INFINITY;
+    return copysign(v, x);
+}
+
+/* Philox4x64-10: ten rounds of the Philox S-box on a 4 x 64-bit counter with a 2 x 64-bit key, the
+ * key bumped by the Weyl constants between rounds (SC 2011 paper cited with R18). */
+void or_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4])
+{
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+    uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        unsigned __int128 p0 = (unsigned __int128)M0 * c0, p1 = (unsigned __int128)M1 * c2;
+        uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        uint64_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* R18: the 16 random bits of flat element i. */
+static uint32_t sr_bits(uint64_t seed, uint64_t step, int64_t i)
+{
+    uint64_t ctr[4] = {(uint64_t)i >> 4, 0, 0, 0}, key[2] = {seed, step}, out[4];
+    or_philox4x64(ctr, key, out);
+    return (uint32_t)((out[(i >> 2) & 3] >> (16 * (i & 3))) & 0xFFFFu);
+}
+
 #define BF16_MAXF ((2.0 - ldexp(1.0, -7)) * ldexp(1.0, 127))
 #define F16_MAXF 65504.0
 
@@ -166,6 +234,19 @@ static float load_err(const void* buf, int fmt, int64_t i)
     return ((const float*)buf)[i];
 }
 
+/* R18: store e (fp32) as element i of a 16-bit error buffer, stochastically rounded with r. */
+static float store_err_sr(void* buf, int fmt, int64_t i, float e, uint32_t r)
+{
+    if (fmt == OR_FMT_BF16) {
+        uint16_t b = bf16_bits_of(stochastic_round(e, 8, -126, BF16_MAXF, r));
+        ((uint16_t*)buf)[i] = b;
+        return bf16_bits_to_float(b);
+    }
+    uint16_t h = f16_bits_of(stochastic_round(e, 11, -14, F16_MAXF, r));
+    ((uint16_t*)buf)[i] = h;
+    return f16_bits_to_float(h);
+}
+
 /* Store e (fp32) as element i of an error buffer in format fmt; returns the stored value, widened. */
 static float store_err(void* buf, int fmt, int64_t i, float e)
 {
@@ -189,6 +270,19 @@ int or_to_format(const float* x, int64_t n, int fmt, uint16_t* bits)
 {
     if (n < 0 || (fmt != OR_FMT_BF16 && fmt != OR_FMT_F16)) return 1;
     for (int64_t i = 0; i < n; ++i) store_err(bits, fmt, i, x[i]);
+    return 0;
+}
+
+/* R18 on its own: x[k] stored as flat element index0 + k of a 16-bit buffer with (seed, step). */
+int or_to_format_sr(const float* x, int64_t n, int fmt, uint64_t seed, uint64_t step, int64_t index0,
+                    uint16_t* bits)
+{
+    if (n < 0 || (fmt != OR_FMT_BF16 && fmt != OR_FMT_F16)) return 1;
+    for (int64_t k = 0; k < n; ++k) {
+        uint16_t tmp[1];
+        store_err_sr(tmp, fmt, 0, x[k], sr_bits(seed, step, index0 + k));
+        bits[k] = tmp[0];
+    }
     return 0;
 }
 
@@ -268,8 +362,9 @@ static int compress_core(int64_t n, int64_t K, const int64_t* off,
                          void* err_store, int err_fmt, float* m, const float* v, float* p,
                          uint32_t* words, float* scales, int8_t* signs, int64_t* nonfinite,
                          float lr, float beta1, float eps, float clip, int ef_mode, float ef_beta,
-                         int adam_update)
+                         int adam_update, int stochastic, uint64_t sr_seed, uint64_t sr_step)
 {
+    if (stochastic && err_fmt == OR_FMT_F32) return OR_ERR_ARG;
     if (!check_offsets(n, K, off)) return OR_ERR_ARG;
     if (err_fmt != OR_FMT_F32 && err_fmt != OR_FMT_BF16 && err_fmt != OR_FMT_F16) return OR_ERR_ARG;
     if (n == 0) return OR_OK;
@@ -327,9 +422,10 @@ static int compress_core(int64_t n, int64_t K, const int64_t* off,
             if (signs != NULL) signs[i] = (int8_t)(b ? 1 : -1);
         }
     }
-    /* R15: store the new error in its format; R8: count non-finite stored values. */
+    /* R15 (R18 when stochastic): store the new error in its format; R8: count non-finite stored values. */
     for (int64_t i = 0; i < n; ++i) {
-        float stored = store_err(err_store, err_fmt, i, err[i]);
+        float stored = stochastic ? store_err_sr(err_store, err_fmt, i, err[i], sr_bits(sr_seed, sr_step, i))
+                                  : store_err(err_store, err_fmt, i, err[i]);
         if (nonfinite != NULL && !isfinite(stored)) *nonfinite += 1;
     }
     free(x);
@@ -344,8 +440,9 @@ int or_compress_step(int64_t n, int64_t K, const int64_t* off,
                      float lr, float beta1, float eps, float clip, int ef_mode, float ef_beta)
 {
     return compress_core(n, K, off, g, g_is_bf16, err_store, err_fmt, m, v, p, words, scales, signs,
-                         nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 1);
+                         nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 1, 0, 0, 0);
 }
+
 
 /* ---------- R17: per-chunk diagnostics of a compressed step ([P1] sec. 6.2 and 8) ----------
  * err_store: the error buffer as the step read it (before the step); words: the step's packed signs. */
@@ -440,7 +537,7 @@ int or_lamb_compress_step(int64_t n, int64_t K, const int64_t* off,
 {
     if (n > 0 && ratios == NULL) return OR_ERR_ARG;
     int rc = compress_core(n, K, off, g, g_is_bf16, err_store, err_fmt, m, v, p, words, scales, signs,
-                           nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 0);
+                           nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 0, 0, 0, 0);
     if (rc != OR_OK || n == 0) return rc;
     lamb_update(K, off, m, v, p, ratios, lr, eps, 1.0, 1.0);
     return OR_OK;
@@ -461,6 +558,22 @@ int or_lamb_warmup_step(int64_t n, int64_t K, const int64_t* off, const void* g,
         bc2 = 1.0 - pow((double)beta2, (double)step);
     }
     lamb_update(K, off, m, v, p, ratios, lr, eps, bc1, bc2);
+    return OR_OK;
+}
+
+/* The compressed step with the new error stochastically rounded into a 16-bit buffer (R18). */
+int or_compress_step_sr(int64_t n, int64_t K, const int64_t* off,
+                        const void* g, int g_is_bf16,
+                        void* err_store, int err_fmt, float* m, const float* v, float* p,
+                        uint32_t* words, float* scales, int8_t* signs, int64_t* nonfinite,
+                        float lr, float beta1, float eps, float clip, int ef_mode, float ef_beta,
+                        int lamb, float* ratios, uint64_t sr_seed, uint64_t sr_step)
+{
+    if (lamb && n > 0 && ratios == NULL) return OR_ERR_ARG;
+    int rc = compress_core(n, K, off, g, g_is_bf16, err_store, err_fmt, m, v, p, words, scales, signs,
+                           nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, !lamb, 1, sr_seed, sr_step);
+    if (rc != OR_OK || n == 0 || !lamb) return rc;
+    lamb_update(K, off, m, v, p, ratios, lr, eps, 1.0, 1.0);
     return OR_OK;
 }
 

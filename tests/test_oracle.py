@@ -844,3 +844,125 @@ def test_diagnostics_vs_fsum_and_unpackbits(fmt):
         ref = math.fsum(ew[lo:hi] * ew[lo:hi])
         assert abs(ss[c] - ref) <= 1e-13 * ref
         assert plus[c] == int(bits[lo:hi].sum())
+
+
+# ------------------------------------------------------------------------------------------------
+# R18: stochastic rounding of a 16-bit error buffer (Philox4x64-10 random bits)
+# ------------------------------------------------------------------------------------------------
+
+M64 = (1 << 64) - 1
+
+
+def _np_philox(counter, key):
+    """numpy's Philox4x64-10 output at `counter` (numpy bumps its 256-bit counter before each block)."""
+    c = sum(int(w) << (64 * k) for k, w in enumerate(counter))
+    c = (c - 1) % (1 << 256)
+    prev = np.asarray([(c >> (64 * k)) & M64 for k in range(4)], dtype=np.uint64)
+    bg = np.random.Philox(counter=prev, key=np.asarray(key, dtype=np.uint64))
+    return bg.random_raw(4)
+
+
+@pytest.mark.parametrize("counter,key", [
+    ([0, 0, 0, 0], [0, 0]),
+    ([1, 0, 0, 0], [0x0123456789ABCDEF, 0xFEDCBA9876543210]),
+    ([M64, 0, 0, 0], [5, 7]),                        # numpy's predecessor borrows across words
+    ([12345, 678, M64, 9], [M64, M64]),
+    ([0xDEADBEEF, 0, 0, 0], [2 ** 63, 1]),
+])
+def test_philox_matches_numpy(counter, key):
+    assert np.array_equal(oracle.philox4x64(counter, key), _np_philox(counter, key))
+
+
+def _np_sr_bits(seed, step, idx):
+    out = {}
+    r = np.zeros(idx.size, dtype=np.uint32)
+    for k, i in enumerate(idx.tolist()):
+        c = i >> 4
+        if c not in out:
+            out[c] = _np_philox([c, 0, 0, 0], [seed, step])
+        r[k] = (int(out[c][(i >> 2) & 3]) >> (16 * (i & 3))) & 0xFFFF
+    return r
+
+
+def test_sr_bf16_is_the_bit_rule():
+    """bf16 = the high half of the fp32 bits: round the magnitude up iff r < its low 16 bits."""
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal(4096) * 10.0 ** rng.uniform(-30, 30, 4096)).astype(np.float32)
+    x[:64] = (rng.standard_normal(64) * 1e-40).astype(np.float32)      # fp32 subnormals
+    seed, step, i0 = 0x5EED, 12, 1000
+    got = oracle.to_format_sr(x, "bf16", seed, step, i0)
+    r = _np_sr_bits(seed, step, np.arange(i0, i0 + x.size))
+    u = x.view(np.uint32)
+    mag = (u & 0x7FFFFFFF).astype(np.uint64)
+    up = (r.astype(np.uint64) < (mag & 0xFFFF)).astype(np.uint64)
+    want = ((mag >> 16) + up).astype(np.uint32) | ((u >> 16) & 0x8000)
+    assert np.array_equal(got.astype(np.uint32), want.astype(np.uint32))
+
+
+def test_sr_f16_exact_rule():
+    """fp16: the neighbours of |x| and the decision r*q < (|x| - lo)*65536 in exact rationals."""
+    rng = np.random.default_rng(42)
+    x = np.concatenate([(rng.standard_normal(600) * 10.0 ** rng.uniform(-9, 4.8, 600)),
+                        rng.uniform(65000, 65600, 40), rng.uniform(0, 2 ** -24, 40)]).astype(np.float32)
+    seed, step, i0 = 99, 3, 7
+    got = oracle.to_format_sr(x, "f16", seed, step, i0).astype(np.float64)
+    r = _np_sr_bits(seed, step, np.arange(i0, i0 + x.size))
+    for k, xv in enumerate(x.astype(np.float64)):
+        a = Fraction(abs(xv))
+        with np.errstate(over="ignore"):
+            near = np.float16(abs(xv))                           # nearest; step back if above a
+        lo = Fraction(float(near)) if np.isfinite(near) and Fraction(float(near)) <= a else None
+        if lo is None:
+            lo = Fraction(float(np.nextafter(near, np.float16(0)))) if np.isfinite(near) else Fraction(65504)
+        e = math.frexp(float(lo))[1] - 1 if lo > 0 else -14
+        q = Fraction(2) ** (max(e, -14) - 10)
+        if lo + q <= a:                                          # near rounded down by a full step
+            lo += q
+        v = lo if lo == a or not (int(r[k]) * q < (a - lo) * 65536) else lo + q
+        want = math.copysign(float(v) if v <= 65504 else math.inf, xv)
+        assert got[k] == want, (k, xv, got[k], want, int(r[k]))
+
+
+def test_sr_is_unbiased_and_keeps_exact_values():
+    n = 40000
+    for fmt, x0, q in (("bf16", 1.0 + 2 ** -9 + 2 ** -11, 2 ** -7), ("f16", 1000.0 + 0.3, 0.5)):
+        x = np.full(n, x0, np.float32)
+        w = oracle.from_format(oracle.to_format_sr(x, fmt, 2024, 1).view(np.uint16), fmt).astype(np.float64)
+        lo = np.min(w)
+        assert set(np.unique(w).tolist()) <= {lo, lo + q}
+        p = (float(np.float32(x0)) - lo) / q
+        sigma = q * math.sqrt(p * (1 - p) / n)
+        assert abs(w.mean() - float(np.float32(x0))) < 5 * sigma, (fmt, w.mean(), x0)
+    for fmt, big in (("bf16", 65280.0), ("f16", 65504.0)):      # values of both formats, and each one's
+        exact = np.asarray([0.0, -0.0, 1.0, -2.5, big, 2.0 ** -24, np.inf, -np.inf], np.float32)   # large
+        w = oracle.from_format(oracle.to_format_sr(exact, fmt, 1, 1).view(np.uint16), fmt)
+        assert np.array_equal(w.view(np.uint32), exact.view(np.uint32)), fmt
+        nan = oracle.from_format(oracle.to_format_sr(np.asarray([np.nan], np.float32), fmt, 1, 1).view(np.uint16), fmt)
+        assert np.isnan(nan[0])
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("lamb", [False, True])
+def test_compress_sr_is_fp32_step_then_stochastic_rounding(fmt, lamb):
+    """R18 as a relation: the step on a 16-bit error buffer with stochastic rounding equals the fp32
+    step on its widening with the new error stochastically rounded (same seed, step, indices)."""
+    n = 2 * 1024 + 333
+    off = oracle.uniform_offsets(n, 1024)
+    g, err32, m, v, p = _random_state(n, 43, sigma=1.0)
+    err32 *= 0.1
+    bits = _lib_narrow(err32, fmt)
+    err16 = bits.view(np.float16).copy() if fmt == "f16" else bits.copy()
+    e_ref = _lib_widen(bits, fmt)
+    m2, p2 = m.copy(), p.copy()
+    hp = dict(HP, ef_mode=1, ef_beta=0.9, want_signs=True, count_nonfinite=True)
+    step = oracle.lamb_compress_step if lamb else oracle.compress_step
+    a = step(g, err16, m, v, p, off, stochastic=True, sr_seed=77, sr_step=5, **hp)
+    b = step(g, e_ref, m2, v, p2, off, **hp)
+    assert np.array_equal(m, m2) and np.array_equal(p, p2, equal_nan=True)
+    for x, y in zip(a[:-1], b[:-1]):
+        if x is not None:
+            assert np.array_equal(x, y)
+    want = oracle.to_format_sr(e_ref, fmt, 77, 5, 0)
+    assert np.array_equal(err16.view(np.uint16), want.view(np.uint16))
+    with pytest.raises(ValueError):                      # fp32 buffers have nothing to round
+        step(g, e_ref.copy(), m.copy(), v, p.copy(), off, stochastic=True, sr_seed=1, sr_step=1, **hp)
