@@ -69,7 +69,7 @@ def _load():
     lib.or_philox4x64.restype = None
     lib.or_to_format_sr.argtypes = [P, I64, I, U64, U64, I64, P]
     lib.or_compress_step_sr.argtypes = [I64, I64, P, P, I, P, I, P, P, P, P, P, P, P,
-                                        F, F, F, F, I, F, I, P, U64, U64]
+                                        F, F, F, F, I, F, I, P, U64, U64, I64]
     lib.or_to_format.argtypes = [P, I64, I, P]
     lib.or_from_format.argtypes = [P, I64, I, P]
     lib.or_warmup_step.argtypes = [I64, P, I, P, P, P, F, F, F, F, I, I64]
@@ -205,7 +205,8 @@ def chunk_scale(x: np.ndarray, begin: int, end: int) -> float:
 
 
 def compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef_mode=0, ef_beta=0.9,
-                  want_signs=False, count_nonfinite=False, stochastic=False, sr_seed=0, sr_step=0):
+                  want_signs=False, count_nonfinite=False, stochastic=False, sr_seed=0, sr_step=0,
+                  sr_index0=0):
     """One compressed step.  err, m, p are updated in place; v is read only.  m, v, p are fp32; the
     error buffer is fp32, fp16 (numpy float16) or bf16 (uint16 bits), see R15.
 
@@ -226,7 +227,7 @@ def compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef_mode
         rc = _load().or_compress_step_sr(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m),
                                          _ptr(v), _ptr(p), _ptr(words), _ptr(scales), _ptr(signs),
                                          _ptr(nf), lr, beta1, eps, clip, ef_mode, ef_beta, 0, None,
-                                         sr_seed, sr_step)
+                                         sr_seed, sr_step, sr_index0)
     else:
         rc = _load().or_compress_step(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m), _ptr(v),
                                       _ptr(p), _ptr(words), _ptr(scales), _ptr(signs), _ptr(nf),
@@ -260,7 +261,8 @@ def diagnostics(err_before, words, offsets):
 
 
 def lamb_compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef_mode=0, ef_beta=0.9,
-                       want_signs=False, count_nonfinite=False, stochastic=False, sr_seed=0, sr_step=0):
+                       want_signs=False, count_nonfinite=False, stochastic=False, sr_seed=0, sr_step=0,
+                       sr_index0=0):
     """One compressed 1-bit LAMB step (reading R16): as compress_step up to the momentum, then the
     per-chunk (layer) trust ratio and update.  err, m, p in place; v read only.
 
@@ -281,7 +283,7 @@ def lamb_compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef
         rc = _load().or_compress_step_sr(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m),
                                          _ptr(v), _ptr(p), _ptr(words), _ptr(scales), _ptr(signs),
                                          _ptr(nf), lr, beta1, eps, clip, ef_mode, ef_beta, 1, _ptr(ratios),
-                                         sr_seed, sr_step)
+                                         sr_seed, sr_step, sr_index0)
     else:
         rc = _load().or_lamb_compress_step(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(m),
                                            _ptr(v), _ptr(p), _ptr(words), _ptr(scales), _ptr(ratios),

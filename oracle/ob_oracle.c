@@ -362,7 +362,8 @@ static int compress_core(int64_t n, int64_t K, const int64_t* off,
                          void* err_store, int err_fmt, float* m, const float* v, float* p,
                          uint32_t* words, float* scales, int8_t* signs, int64_t* nonfinite,
                          float lr, float beta1, float eps, float clip, int ef_mode, float ef_beta,
-                         int adam_update, int stochastic, uint64_t sr_seed, uint64_t sr_step)
+                         int adam_update, int stochastic, uint64_t sr_seed, uint64_t sr_step,
+                         int64_t sr_index0)
 {
     if (stochastic && err_fmt == OR_FMT_F32) return OR_ERR_ARG;
     if (!check_offsets(n, K, off)) return OR_ERR_ARG;
@@ -424,7 +425,8 @@ static int compress_core(int64_t n, int64_t K, const int64_t* off,
     }
     /* R15 (R18 when stochastic): store the new error in its format; R8: count non-finite stored values. */
     for (int64_t i = 0; i < n; ++i) {
-        float stored = stochastic ? store_err_sr(err_store, err_fmt, i, err[i], sr_bits(sr_seed, sr_step, i))
+        float stored = stochastic ? store_err_sr(err_store, err_fmt, i, err[i],
+                                                 sr_bits(sr_seed, sr_step, sr_index0 + i))
                                   : store_err(err_store, err_fmt, i, err[i]);
         if (nonfinite != NULL && !isfinite(stored)) *nonfinite += 1;
     }
@@ -440,7 +442,7 @@ int or_compress_step(int64_t n, int64_t K, const int64_t* off,
                      float lr, float beta1, float eps, float clip, int ef_mode, float ef_beta)
 {
     return compress_core(n, K, off, g, g_is_bf16, err_store, err_fmt, m, v, p, words, scales, signs,
-                         nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 1, 0, 0, 0);
+                         nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 1, 0, 0, 0, 0);
 }
 
 
@@ -537,7 +539,7 @@ int or_lamb_compress_step(int64_t n, int64_t K, const int64_t* off,
 {
     if (n > 0 && ratios == NULL) return OR_ERR_ARG;
     int rc = compress_core(n, K, off, g, g_is_bf16, err_store, err_fmt, m, v, p, words, scales, signs,
-                           nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 0, 0, 0, 0);
+                           nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 0, 0, 0, 0, 0);
     if (rc != OR_OK || n == 0) return rc;
     lamb_update(K, off, m, v, p, ratios, lr, eps, 1.0, 1.0);
     return OR_OK;
@@ -561,17 +563,20 @@ int or_lamb_warmup_step(int64_t n, int64_t K, const int64_t* off, const void* g,
     return OR_OK;
 }
 
-/* The compressed step with the new error stochastically rounded into a 16-bit buffer (R18). */
+/* The compressed step with the new error stochastically rounded into a 16-bit buffer (R18).  The arrays
+ * hold flat elements sr_index0 .. sr_index0 + n - 1 of the buffer (the random bits follow the flat
+ * index). */
 int or_compress_step_sr(int64_t n, int64_t K, const int64_t* off,
                         const void* g, int g_is_bf16,
                         void* err_store, int err_fmt, float* m, const float* v, float* p,
                         uint32_t* words, float* scales, int8_t* signs, int64_t* nonfinite,
                         float lr, float beta1, float eps, float clip, int ef_mode, float ef_beta,
-                        int lamb, float* ratios, uint64_t sr_seed, uint64_t sr_step)
+                        int lamb, float* ratios, uint64_t sr_seed, uint64_t sr_step, int64_t sr_index0)
 {
     if (lamb && n > 0 && ratios == NULL) return OR_ERR_ARG;
     int rc = compress_core(n, K, off, g, g_is_bf16, err_store, err_fmt, m, v, p, words, scales, signs,
-                           nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, !lamb, 1, sr_seed, sr_step);
+                           nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, !lamb, 1, sr_seed, sr_step,
+                           sr_index0);
     if (rc != OR_OK || n == 0 || !lamb) return rc;
     lamb_update(K, off, m, v, p, ratios, lr, eps, 1.0, 1.0);
     return OR_OK;

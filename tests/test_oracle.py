@@ -964,5 +964,12 @@ def test_compress_sr_is_fp32_step_then_stochastic_rounding(fmt, lamb):
             assert np.array_equal(x, y)
     want = oracle.to_format_sr(e_ref, fmt, 77, 5, 0)
     assert np.array_equal(err16.view(np.uint16), want.view(np.uint16))
+    # a chunk run on its own with its flat start index draws the same bits as inside the whole buffer
+    lo, hi = int(off[1]), int(off[2])
+    part = bits[lo:hi].view(np.float16).copy() if fmt == "f16" else bits[lo:hi].copy()
+    mm, pp = m2.copy(), p2.copy()   # any state: only the error's rounding is compared
+    step(g[lo:hi].copy(), part, mm[lo:hi].copy(), v[lo:hi].copy(), pp[lo:hi].copy(),
+         np.asarray([0, hi - lo], np.int64), stochastic=True, sr_seed=77, sr_step=5, sr_index0=lo, **hp)
+    assert np.array_equal(part.view(np.uint16), want[lo:hi].view(np.uint16))
     with pytest.raises(ValueError):                      # fp32 buffers have nothing to round
         step(g, e_ref.copy(), m.copy(), v, p.copy(), off, stochastic=True, sr_seed=1, sr_step=1, **hp)

@@ -81,8 +81,8 @@ MUTANTS = {
     "lamb_dense_no_bias_correction": ("lamb_update(K, off, m, v, p, ratios, lr, eps, bc1, bc2);",
                                       "lamb_update(K, off, m, v, p, ratios, lr, eps, 1.0, 1.0);"),
     "lamb_weight_norm_of_m": ("sw += (double)p[i] * (double)p[i];", "sw += (double)m[i] * (double)m[i];"),
-    "lamb_compress_also_adam": ("nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 0, 0, 0, 0);",
-                                "nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 1, 0, 0, 0);"),
+    "lamb_compress_also_adam": ("nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 0, 0, 0, 0, 0);",
+                                "nonfinite, lr, beta1, eps, clip, ef_mode, ef_beta, 1, 0, 0, 0, 0);"),
     "lamb_dense_also_adam": ("bias_correction, step, 0);", "bias_correction, step, 1);"),
     "diag_norm_not_squared": ("            s += e * e;", "            s += fabs(e);"),
     "diag_counts_minus": ("plus += word_bit(words, i);", "plus += 1 - word_bit(words, i);"),
@@ -92,8 +92,8 @@ MUTANTS = {
     "sr_decision_inverted": ("(double)r * q < (a - lo) * 65536.0", "(double)r * q > (a - lo) * 65536.0"),
     "sr_overflow_saturates": ("    if (v > maxf) v = INFINITY;\n    return copysign(v, x);",
                               "    if (v > maxf) v = maxf;\n    return copysign(v, x);"),
-    "sr_falls_back_to_nearest": ("float stored = stochastic ? store_err_sr(err_store, err_fmt, i, err[i], sr_bits(sr_seed, sr_step, i))",
-                                 "float stored = 0 ? store_err_sr(err_store, err_fmt, i, err[i], sr_bits(sr_seed, sr_step, i))"),
+    "sr_falls_back_to_nearest": ("float stored = stochastic ? store_err_sr(", "float stored = 0 ? store_err_sr("),
+    "sr_ignores_index0": ("sr_bits(sr_seed, sr_step, sr_index0 + i))", "sr_bits(sr_seed, sr_step, i))"),
     "philox_no_key_bump": ("            k0 += W0;\n            k1 += W1;", "            k0 += 0;\n            k1 += W1;"),
     "philox_lanes_swapped": ("uint64_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;",
                              "uint64_t n0 = hi0 ^ c1 ^ k0, n1 = lo0, n2 = hi1 ^ c3 ^ k1, n3 = lo1;"),
