@@ -6,7 +6,8 @@ synthetic workloads (``synth``).  Importing the package does not load the librar
 and raises if it has not been built (there is no CPU fallback).
 """
 from ._native import (  # noqa: F401
-    KERNEL_NAMES, OB_BF16, OB_EF_EMA, OB_EF_PLAIN, OB_F16, OB_F32, OB_KERNEL_CHUNK_SUMSQ,
+    KERNEL_NAMES, OB_BF16, OB_EF_EMA, OB_EF_PLAIN, OB_F16, OB_F32, OB_ROUND_NEAREST, OB_ROUND_STOCHASTIC,
+    OB_KERNEL_CHUNK_SUMSQ,
     OB_KERNEL_COMPRESS, OB_KERNEL_DENSE, OB_KERNEL_DIAG, OB_KERNEL_LAMB_APPLY, OB_KERNEL_SERVER_APPLY,
     OB_KERNEL_SERVER_SUMSQ, OB_KERNEL_TRUST_RATIO, OB_KERNEL_UNPACK, LIB_PATH, ObError, Plan, hparams,
     lib, ob_adam_compress_step, ob_adam_warmup_step, ob_hparams, ob_lamb_compress_step,

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libobadam.so")
 OB_OK, OB_ERR_ARG, OB_ERR_ALIGN, OB_ERR_DTYPE, OB_ERR_HIP, OB_ERR_OOM = range(6)
 OB_F32, OB_BF16, OB_F16 = 0, 1, 2
 OB_EF_PLAIN, OB_EF_EMA = 0, 1
+OB_ROUND_NEAREST, OB_ROUND_STOCHASTIC = 0, 1
 (OB_KERNEL_CHUNK_SUMSQ, OB_KERNEL_COMPRESS, OB_KERNEL_DENSE, OB_KERNEL_SERVER_SUMSQ,
  OB_KERNEL_SERVER_APPLY, OB_KERNEL_UNPACK, OB_KERNEL_TRUST_RATIO, OB_KERNEL_LAMB_APPLY,
  OB_KERNEL_DIAG, OB_KERNEL_SCALE) = range(10)
@@ -38,12 +39,14 @@ class ob_hparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("clip", ctypes.c_float), ("ef_mode", ctypes.c_int32),
                 ("ef_beta", ctypes.c_float), ("bias_correction", ctypes.c_int32),
-                ("step", ctypes.c_int64)]
+                ("step", ctypes.c_int64), ("err_rounding", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("sr_seed", ctypes.c_uint64)]
 
 
 def hparams(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, clip=0.0, ef_mode=OB_EF_PLAIN, ef_beta=0.9,
-            bias_correction=False, step=0) -> ob_hparams:
-    return ob_hparams(lr, beta1, beta2, eps, clip, ef_mode, ef_beta, 1 if bias_correction else 0, step)
+            bias_correction=False, step=0, err_rounding=OB_ROUND_NEAREST, sr_seed=0) -> ob_hparams:
+    return ob_hparams(lr, beta1, beta2, eps, clip, ef_mode, ef_beta, 1 if bias_correction else 0, step,
+                      err_rounding, 0, sr_seed)
 
 
 _lib = None

@@ -436,6 +436,8 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
     if (signs_out && !aligned(signs_out, 4)) return OB_ERR_ALIGN;
     if (nonfinite_out && !aligned(nonfinite_out, 8)) return OB_ERR_ALIGN;
     if (hp->ef_mode != OB_EF_PLAIN && hp->ef_mode != OB_EF_EMA) return OB_ERR_ARG;
+    if (hp->err_rounding != OB_ROUND_NEAREST && hp->err_rounding != OB_ROUND_STOCHASTIC) return OB_ERR_ARG;
+    if (hp->err_rounding == OB_ROUND_STOCHASTIC && err_dtype == OB_F32) return OB_ERR_ARG;
 
     ob::CompressParams cp;
     cp.lr = hp->lr;
@@ -445,6 +447,9 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
     cp.clip = hp->clip > 0.0f ? hp->clip : 0.0f;
     cp.ef_beta = hp->ef_beta;
     cp.one_m_ef_beta = 1.0 - static_cast<double>(hp->ef_beta);
+    cp.stochastic = hp->err_rounding == OB_ROUND_STOCHASTIC;
+    cp.sr_seed = hp->sr_seed;
+    cp.sr_step = static_cast<uint64_t>(hp->step);
 
     DeviceGuard guard(plan->device);
     if (!guard.ok) return OB_ERR_HIP;

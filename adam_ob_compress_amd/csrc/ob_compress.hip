@@ -28,6 +28,8 @@
 //     sign -1).
 #include "ob_device.h"
 
+#include <type_traits>
+
 #ifndef OB_ERR_FMT
 #error "build with -DOB_ERR_FMT=0 (fp32), 1 (bf16) or 2 (fp16)"
 #endif
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
 // (LAMB: no update of p; the block's sum of u^2 for the layer's ||u|| instead)
 // ------------------------------------------------------------------------------------------------
 
-template <class G, class E, bool CLIP, bool EMA, bool SIGNS, bool NONFIN, bool LAMB>
+template <class G, class E, bool CLIP, bool EMA, bool SIGNS, bool NONFIN, bool LAMB, bool SR>
 __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename G::T* __restrict__ g,
                                                      typename E::T* __restrict__ err, float* __restrict__ m,
                                                      const float* __restrict__ v, float* __restrict__ p,
@@ -172,13 +174,14 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = it.start + base + u * kTile + kVec * tid;
+            const u4 rw = SR ? philox_block(cp.sr_seed, cp.sr_step, i) : u4{};
             uint32_t nib = 0;
 #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 const float x = compensate<CLIP>(gv[u][k], ev[u][k], cp.clip);
                 float e = ev[u][k], mm = mv[u][k], pp = LAMB ? 0.0f : pv[u][k];
                 nib |= compress_elem<EMA, LAMB>(x, e, mm, vv[u][k], pp, usq, scale, cp) << k;
-                e = E::rounded(e);
+                e = SR ? E::rounded_sr(e, rw.x[k] >> 16) : E::rounded(e);
                 ev[u][k] = e;
                 mv[u][k] = mm;
                 if (!LAMB) pv[u][k] = pp;
@@ -202,6 +205,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
         const int rem = it.len - base;
         const int cnt = rem - kVec * tid;
         const int64_t i = it.start + base + kVec * tid;
+        const u4 rw = (SR && cnt > 0) ? philox_block(cp.sr_seed, cp.sr_step, i) : u4{};
         uint32_t nib = 0;
         if (cnt >= kVec) {
             const f4 gv = G::load4(g, i), vv = ld4(v, i);
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
                 const float x = compensate<CLIP>(gv[k], ev[k], cp.clip);
                 float e = ev[k], mm = mv[k], pp = pv[k];
                 nib |= compress_elem<EMA, LAMB>(x, e, mm, vv[k], pp, usq, scale, cp) << k;
-                e = E::rounded(e);
+                e = SR ? E::rounded_sr(e, rw.x[k] >> 16) : E::rounded(e);
                 ev[k] = e;
                 mv[k] = mm;
                 pv[k] = pp;
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
                 const float x = compensate<CLIP>(G::load1(g, i + k), e, cp.clip);
                 const uint32_t b = compress_elem<EMA, LAMB>(x, e, mm, v[i + k], pp, usq, scale, cp);
                 nib |= b << k;
-                e = E::rounded(e);
+                e = SR ? E::rounded_sr(e, rw.x[k] >> 16) : E::rounded(e);
                 E::store1(err, i + k, e);
                 m[i + k] = mm;
                 if (!LAMB) p[i + k] = pp;
@@ -302,31 +306,48 @@ hipError_t launch_chunk_sumsq(const PlanDev& pd, const void* g, int g_bf16, cons
 }
 
 namespace {
-template <class G, class E, bool CLIP, bool EMA, bool LAMB>
-void compress_dispatch(const PlanDev& pd, const typename G::T* g, typename E::T* err, float* m, const float* v,
-                       float* p, uint32_t* words, float* scales, int8_t* signs,
-                       unsigned long long* nonfinite, const CompressParams& cp, hipStream_t s)
+template <class G, class E, bool CLIP, bool EMA, bool LAMB, bool SR>
+void compress_dispatch_sr(const PlanDev& pd, const typename G::T* g, typename E::T* err, float* m,
+                          const float* v, float* p, uint32_t* words, float* scales, int8_t* signs,
+                          unsigned long long* nonfinite, const CompressParams& cp, hipStream_t s)
 {
     const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
     const int sel = (signs ? 1 : 0) | (nonfinite ? 2 : 0);
     switch (sel) {
     case 0:
-        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, false, false, LAMB>), grid, block, 0, s, pd, g, err, m,
-                           v, p, words, scales, signs, nonfinite, cp);
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, false, false, LAMB, SR>), grid, block, 0, s, pd, g, err,
+                           m, v, p, words, scales, signs, nonfinite, cp);
         break;
     case 1:
-        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, true, false, LAMB>), grid, block, 0, s, pd, g, err, m,
-                           v, p, words, scales, signs, nonfinite, cp);
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, true, false, LAMB, SR>), grid, block, 0, s, pd, g, err,
+                           m, v, p, words, scales, signs, nonfinite, cp);
         break;
     case 2:
-        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, false, true, LAMB>), grid, block, 0, s, pd, g, err, m,
-                           v, p, words, scales, signs, nonfinite, cp);
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, false, true, LAMB, SR>), grid, block, 0, s, pd, g, err,
+                           m, v, p, words, scales, signs, nonfinite, cp);
         break;
     default:
-        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, true, true, LAMB>), grid, block, 0, s, pd, g, err, m,
-                           v, p, words, scales, signs, nonfinite, cp);
+        hipLaunchKernelGGL((k_compress<G, E, CLIP, EMA, true, true, LAMB, SR>), grid, block, 0, s, pd, g, err,
+                           m, v, p, words, scales, signs, nonfinite, cp);
         break;
     }
+}
+
+// stochastic rounding exists for the 16-bit formats only (the host rejects it for fp32 buffers)
+template <class G, class E, bool CLIP, bool EMA, bool LAMB>
+void compress_dispatch(const PlanDev& pd, const typename G::T* g, typename E::T* err, float* m, const float* v,
+                       float* p, uint32_t* words, float* scales, int8_t* signs,
+                       unsigned long long* nonfinite, const CompressParams& cp, hipStream_t s)
+{
+    if constexpr (!std::is_same<E, ErrF32>::value) {
+        if (cp.stochastic) {
+            compress_dispatch_sr<G, E, CLIP, EMA, LAMB, true>(pd, g, err, m, v, p, words, scales, signs,
+                                                              nonfinite, cp, s);
+            return;
+        }
+    }
+    compress_dispatch_sr<G, E, CLIP, EMA, LAMB, false>(pd, g, err, m, v, p, words, scales, signs, nonfinite,
+                                                       cp, s);
 }
 
 template <class G, class E>

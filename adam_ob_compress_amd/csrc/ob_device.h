@@ -122,6 +122,7 @@ struct ErrF32 {
     template <class I>
     static __device__ __forceinline__ float load1(const float* __restrict__ p, I i) { return p[i]; }
     static __device__ __forceinline__ float rounded(float e) { return e; }
+    static __device__ __forceinline__ float rounded_sr(float e, uint32_t) { return e; }
     template <bool NT = false, class I>
     static __device__ __forceinline__ void store4(float* __restrict__ p, I i, f4 v)
     {
@@ -153,6 +154,16 @@ struct ErrBF16 {
         const uint32_t u = __float_as_uint(e);
         if ((u & 0x7fffffffu) > 0x7f800000u) return __uint_as_float((u & 0x80000000u) | 0x7fc00000u);
         return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+    }
+    // stochastic: the magnitude's low 16 bits are the distance to the lower neighbour in units of
+    // 2^-16 quanta, so it rounds up iff r < them (a carry moves to the next binade, or to Inf)
+    static __device__ __forceinline__ float rounded_sr(float e, uint32_t r)
+    {
+        const uint32_t u = __float_as_uint(e), mag = u & 0x7fffffffu;
+        if (mag > 0x7f800000u) return __uint_as_float((u & 0x80000000u) | 0x7fc00000u);
+        if (mag == 0x7f800000u) return e;
+        const uint32_t res = (mag & 0xffff0000u) + (r < (mag & 0xffffu) ? 0x10000u : 0u);
+        return __uint_as_float(res | (u & 0x80000000u));
     }
     template <bool NT = false, class I>
     static __device__ __forceinline__ void store4(uint16_t* __restrict__ p, I i, f4 v)
@@ -197,6 +208,32 @@ struct ErrF16 {
     template <class I>
     static __device__ __forceinline__ float load1(const uint16_t* __restrict__ p, I i) { return widen(p[i]); }
     static __device__ __forceinline__ float rounded(float e) { return static_cast<float>(static_cast<_Float16>(e)); }
+    // stochastic: lo = |e| truncated to fp16, q its quantum; hi = lo + q iff r*q < (|e| - lo)*65536,
+    // taken on the fp32 bits.  |e| >= 2^-14 (fp16 normal): q is 2^13 fp32 quanta, so the fraction is
+    // the low 13 significand bits f and the test is r < 8f; the carry of lo + q moves into the next
+    // binade, and above 65504 (0x477fe000) is Inf.  Below: q = 2^-24; with the 24-bit significand S
+    // and |e| = S * 2^-(24 + s), lo = (S >> s) q and the test is r * 2^s < frac * 2^16 (s >= 14; past
+    // s = 47 only r = 0 rounds up, as r * 2^s > frac * 2^16 for r >= 1).
+    static __device__ __forceinline__ float rounded_sr(float e, uint32_t r)
+    {
+        const uint32_t u = __float_as_uint(e), mag = u & 0x7fffffffu;
+        if (mag >= 0x7f800000u) return e;
+        uint32_t res;
+        if (mag >= 0x38800000u) {
+            res = (mag & ~0x1fffu) + (r < ((mag & 0x1fffu) << 3) ? 0x2000u : 0u);
+            if (res > 0x477fe000u) res = 0x7f800000u;
+        } else {
+            const uint32_t ex = mag >> 23;
+            const uint32_t S = ex ? ((mag & 0x7fffffu) | 0x800000u) : mag;
+            const uint32_t s = ex ? 126u - ex : 125u;
+            const uint32_t k = s < 32u ? (S >> s) : 0u;
+            const uint64_t frac = s < 32u ? (S & ((1u << s) - 1u)) : S;
+            const uint32_t sc = s < 47u ? s : 47u;
+            const uint32_t up = (static_cast<uint64_t>(r) << sc) < (frac << 16) ? 1u : 0u;
+            res = __float_as_uint(static_cast<float>(k + up) * 5.9604644775390625e-8f);
+        }
+        return __uint_as_float(res | (u & 0x80000000u));
+    }
     template <bool NT = false, class I>
     static __device__ __forceinline__ void store4(uint16_t* __restrict__ p, I i, f4 v)
     {
@@ -214,6 +251,42 @@ struct ErrF16 {
         p[i] = static_cast<uint16_t>(bits(e));
     }
 };
+
+// ------------------------------------------------------------------------------------------------
+// stochastic rounding of the error buffer: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011), a counter-based generator, gives element i the high 16 bits
+// of output word i & 3 at the 128-bit counter (i >> 2, step) under the 64-bit key seed (each split
+// into 32-bit words, low word first).  One block serves the 4 elements of a lane (i a multiple of 4);
+// its multiplies are native 32 x 32 -> 64-bit products.
+// ------------------------------------------------------------------------------------------------
+
+struct u4 {
+    uint32_t x[4];
+};
+
+__device__ __forceinline__ u4 philox_block(uint64_t seed, uint64_t step, int64_t i)
+{
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u, W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    const uint64_t blk = static_cast<uint64_t>(i) >> 2;
+    uint32_t c0 = static_cast<uint32_t>(blk), c1 = static_cast<uint32_t>(blk >> 32);
+    uint32_t c2 = static_cast<uint32_t>(step), c3 = static_cast<uint32_t>(step >> 32);
+    uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const uint64_t p0 = static_cast<uint64_t>(M0) * c0, p1 = static_cast<uint64_t>(M1) * c2;
+        const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+        c1 = static_cast<uint32_t>(p1);
+        c3 = static_cast<uint32_t>(p0);
+        c0 = n0;
+        c2 = n2;
+    }
+    return u4{{c0, c1, c2, c3}};
+}
 
 // ob_dtype code of the error buffer -> its format
 template <int EF> struct ErrOf;

@@ -49,6 +49,8 @@ struct PlanDev {
 struct CompressParams {
     double lr, beta1, one_m_beta1, eps, ef_beta, one_m_ef_beta;
     float clip;
+    int stochastic;          // 16-bit error buffers: stochastic rounding with (sr_seed, sr_step)
+    uint64_t sr_seed, sr_step;
 };
 
 struct DenseParams {

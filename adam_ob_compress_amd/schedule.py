@@ -31,6 +31,9 @@ class OneBitAdam:
     The compressed step's outputs (packed words, per-chunk scales, optional int8 signs and the
     non-finite counter) stay in ``self.words`` etc. for the caller to send or inspect.
 
+    ``err_rounding="stochastic"`` (16-bit error buffers) rounds each new error stochastically, with
+    random bits from (``sr_seed``, the step index).
+
     With ``diagnostics=True`` every compressed step also leaves, per chunk, the squared L2 norm of the
     error buffer it read and its number of +1 signs ([P1] sec. 6.2 and 8); see ``error_norms``,
     ``small_error_chunks`` and ``plus_share``.
@@ -39,13 +42,15 @@ class OneBitAdam:
     def __init__(self, plan: nat.Plan, err, m, v, p, *, lr, beta1=0.9, beta2=0.999, eps=1e-8,
                  clip=0.0, ef_mode=nat.OB_EF_PLAIN, ef_beta=0.9, int8_signs=False,
                  count_nonfinite=False, freeze_step=0, refresh_period=0, bias_correction=False,
-                 diagnostics=False):
+                 diagnostics=False, err_rounding="nearest", sr_seed=0):
         self.plan = plan
         self.err, self.m, self.v, self.p = err, m, v, p
         self.freeze_step, self.refresh_period = freeze_step, refresh_period
         self.bias_correction = bias_correction
         self.hp = nat.hparams(lr=lr, beta1=beta1, beta2=beta2, eps=eps, clip=clip, ef_mode=ef_mode,
-                              ef_beta=ef_beta)
+                              ef_beta=ef_beta, sr_seed=sr_seed,
+                              err_rounding={"nearest": nat.OB_ROUND_NEAREST,
+                                            "stochastic": nat.OB_ROUND_STOCHASTIC}[err_rounding])
         dev = p.device
         n = plan.n
         self.words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=dev)
@@ -71,6 +76,7 @@ class OneBitAdam:
             self.hp.step = self.dense_steps
             self._dense(g, stream)
         else:
+            self.hp.step = self.step_index      # the stochastic-rounding stream of this step
             self._compressed(g, stream)
         self.step_index += 1
         return kind

@@ -52,6 +52,7 @@ class Workload:
     workers: int = 0           # > 0: server-stage workload
     err_dtype: str = "f32"     # storage of the error buffer: "f32" | "bf16" | "f16"
     optimizer: str = "adam"    # "adam" | "lamb" (1-bit LAMB: the chunks are the layers)
+    err_rounding: str = "nearest"  # 16-bit error buffers: "nearest" | "stochastic"
 
     @property
     def n_chunks(self) -> int:
@@ -120,6 +121,11 @@ WORKLOADS = {w.name: w for w in (SINGLE_1M, BERT_BASE, SERVER_W8, GPT2_XL, LLAMA
 # the same optimizer workloads with the error buffer stored in 16 bits ("<name>-err-bf16", "-err-f16")
 WORKLOADS.update({f"{w.name}-err-{e}": dataclasses.replace(w, name=f"{w.name}-err-{e}", err_dtype=e)
                   for w in (BERT_BASE, GPT2_XL, LLAMA2_7B) for e in ("bf16", "f16")})
+# ... and stored with stochastic rounding ("<name>-err-bf16-sr", "<name>-err-f16-sr")
+WORKLOADS.update({f"{w.name}-err-{e}-sr": dataclasses.replace(w, name=f"{w.name}-err-{e}-sr", err_dtype=e,
+                                                              err_rounding="stochastic")
+                  for w in (BERT_BASE, GPT2_XL, LLAMA2_7B) for e in ("bf16", "f16")})
+SR_SEED = 0x0B1AD  # the stochastic-rounding key of every workload
 
 
 def scaled(w: Workload, n: int, chunk: int | None = None) -> Workload:

@@ -128,8 +128,10 @@ def cpu_baseline(w, seconds: float):
         if w.workers:
             raise NotImplementedError
         step = oracle.lamb_compress_step if w.optimizer == "lamb" else oracle.compress_step
+        sr = (dict(stochastic=True, sr_seed=synth.SR_SEED, sr_step=len(times))
+              if w.err_rounding == "stochastic" else {})
         step(g, err, m, v, p, offs, lr=w.lr, beta1=w.beta1, eps=w.eps, clip=w.clip, ef_mode=w.ef_mode,
-             ef_beta=w.ef_beta, want_signs=w.int8_signs)
+             ef_beta=w.ef_beta, want_signs=w.int8_signs, **sr)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     return {"value": n_s / t, "unit": "elements/s", "cores": 1, "kind": "oracle",
@@ -160,7 +162,8 @@ def run(args):
     opt = cls(plan, err, m, v, p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                               clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta, int8_signs=w.int8_signs,
                               freeze_step=w.freeze_step, refresh_period=w.refresh_period,
-                              diagnostics=args.diagnostics)
+                              diagnostics=args.diagnostics, err_rounding=w.err_rounding,
+                              sr_seed=synth.SR_SEED)
     stream = torch.cuda.current_stream()
     print(f"# {w.name}: n={w.n} chunks={plan.num_chunks} blocks={plan.num_blocks} "
           f"block_elems={plan.block_elems}", file=sys.stderr, flush=True)
@@ -235,11 +238,13 @@ def run(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": (("bf16 grads + f32 state" if w.grad_dtype == "bf16" else "f32")
-                  + ("" if w.err_dtype == "f32" else f", {w.err_dtype} error buffer")),
+                  + ("" if w.err_dtype == "f32" else f", {w.err_dtype} error buffer")
+                  + (" (stochastic rounding)" if w.err_rounding == "stochastic" else "")),
         "data": "synthetic (seeded; ring of pre-drawn gradients)",
         "config": {"workload": w.name, "elements": w.n, "chunks": plan.num_chunks,
                    "optimizer": "1-bit " + ("LAMB" if w.optimizer == "lamb" else "Adam"),
-                   "grad_dtype": w.grad_dtype, "err_dtype": w.err_dtype, "clip": w.clip,
+                   "grad_dtype": w.grad_dtype, "err_dtype": w.err_dtype, "err_rounding": w.err_rounding,
+                   "clip": w.clip,
                    "error_feedback": "ema" if w.ef_mode else "plain", "int8_signs": w.int8_signs,
                    "freeze_step": w.freeze_step, "refresh_period": w.refresh_period,
                    "block_elems": plan.block_elems, "work_blocks": plan.num_blocks,

@@ -69,6 +69,11 @@ typedef enum { OB_F32 = 0, OB_BF16 = 1, OB_F16 = 2 } ob_dtype;
  * EMA keeps ef_beta*err + (1-ef_beta)*(x - g_hat) ([P1] sec. 2.1). */
 typedef enum { OB_EF_PLAIN = 0, OB_EF_EMA = 1 } ob_ef_mode;
 
+/* How a new error is stored in a 16-bit error buffer: to nearest, ties to even, or stochastically
+ * (round up with probability equal to the fraction of the quantum; 16 random bits per element from
+ * Philox4x32-10 at counter (i >> 2, step) with key sr_seed; see ob_adam_compress_step). */
+typedef enum { OB_ROUND_NEAREST = 0, OB_ROUND_STOCHASTIC = 1 } ob_rounding;
+
 /* Hyperparameters, fp32 as in the per-parameter state of [P1] sec. 3.1. */
 typedef struct {
     float lr;
@@ -81,7 +86,11 @@ typedef struct {
     float ef_beta;          /* EMA coefficient ([P1] sec. 2.1 uses beta1 = 0.9) */
     int32_t bias_correction;/* dense step only: divide m, v by 1 - beta^step (textbook Adam);
                                the pages' step has none, so 0 is the default */
-    int64_t step;           /* dense step with bias_correction: t >= 1 */
+    int64_t step;           /* dense step with bias_correction: t >= 1; compressed step with
+                               stochastic rounding: the random stream (use a new value every step) */
+    int32_t err_rounding;   /* ob_rounding; compressed steps with a 16-bit error buffer only */
+    int32_t reserved;       /* 0 */
+    uint64_t sr_seed;       /* stochastic rounding: the generator's key, with step */
 } ob_hparams;
 
 typedef struct ob_plan_s* ob_plan;
@@ -119,7 +128,12 @@ ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, flo
  * v: fp32[n] read only; words_out: uint32[ceil(n/32)]; scales_out: fp32[K];
  * err_dtype ([P3] Q&A on error-feedback memory): OB_F32, or OB_BF16 / OB_F16 -- the stored error is
  *   widened exactly when read, and the new error, computed in fp32 as above, is rounded to the format
- *   (nearest, ties to even; beyond the largest finite value, +-Inf) when stored;
+ *   (nearest, ties to even; beyond the largest finite value, +-Inf) when stored.  With
+ *   hp->err_rounding = OB_ROUND_STOCHASTIC it is stored as lo or hi = lo + q (lo its truncation toward
+ *   zero, q the format's quantum there), hi iff r*q < (|e| - lo)*65536 with r the element's 16
+ *   random bits: the high half of output word i & 3 of Philox4x32-10 (Salmon et al., SC 2011) at the
+ *   128-bit counter (i >> 2, hp->step) under the 64-bit key hp->sr_seed (32-bit words, low first).
+ *   OB_ERR_ARG for an fp32 error buffer;
  * signs_out (optional, NULL = off): int8[n] of +1/-1 ([P1] sec. 3.2);
  * nonfinite_out (optional, NULL = off): device uint64 counter to which the number of non-finite
  * STORED new error elements is added ([P1] sec. 3.2 NaN check; the caller zeroes it), so an fp16

@@ -65,8 +65,8 @@ def _load():
     lib.or_lamb_warmup_step.argtypes = [I64, I64, P, P, I, P, P, P, P, F, F, F, F, I, I64]
     lib.or_diagnostics.argtypes = [I64, I64, P, P, I, P, P, P]
     U64 = ctypes.c_uint64
-    lib.or_philox4x64.argtypes = [P, P, P]
-    lib.or_philox4x64.restype = None
+    lib.or_philox4x32.argtypes = [P, P, P]
+    lib.or_philox4x32.restype = None
     lib.or_to_format_sr.argtypes = [P, I64, I, U64, U64, I64, P]
     lib.or_compress_step_sr.argtypes = [I64, I64, P, P, I, P, I, P, P, P, P, P, P, P,
                                         F, F, F, F, I, F, I, P, U64, U64, I64]
@@ -133,12 +133,12 @@ def to_format(x: np.ndarray, fmt: str) -> np.ndarray:
     return bits.view(np.float16) if fmt == "f16" else bits
 
 
-def philox4x64(counter, key) -> np.ndarray:
-    """Philox4x64-10 of a 4 x uint64 counter under a 2 x uint64 key (reading R18)."""
-    c = np.ascontiguousarray(counter, dtype=np.uint64)
-    k = np.ascontiguousarray(key, dtype=np.uint64)
-    out = np.zeros(4, dtype=np.uint64)
-    _load().or_philox4x64(_ptr(c), _ptr(k), _ptr(out))
+def philox4x32(counter, key) -> np.ndarray:
+    """Philox4x32-10 of a 4 x uint32 counter under a 2 x uint32 key (reading R18)."""
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    _load().or_philox4x32(_ptr(c), _ptr(k), _ptr(out))
     return out
 
 

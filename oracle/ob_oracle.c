@@ -52,10 +52,11 @@
  *      toward zero, hi = lo + one quantum q), choosing hi iff r * q < (|e| - lo) * 65536, where r is a
  *      16-bit random integer; so hi comes with probability (|e| - lo)/q (to 1/65536).  Values of the
  *      format, +-0, NaN and +-Inf are stored unchanged; a hi beyond the largest finite value is Inf.
- *      r for flat element i: output word (i >> 2) & 3, bits 16*(i & 3) .. +15, of Philox4x64-10
- *      (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011) at counter
- *      (i >> 4, 0, 0, 0) with key (seed, step): a counter-based generator, so every element's bits are
- *      a function of (seed, step, i) alone.
+ *      r for flat element i: the high 16 bits of output word i & 3 of Philox4x32-10 (Salmon, Moraes,
+ *      Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011) at the 128-bit counter
+ *      (i >> 2, step) -- 32-bit words lo(i >> 2), hi(i >> 2), lo(step), hi(step) -- under the 64-bit
+ *      key seed -- words lo(seed), hi(seed): a counter-based generator, so every element's bits are
+ *      a function of (seed, step, i) alone, and four consecutive elements share one output block.
  *   R16 1-bit LAMB ([P2] section "1-bit LAMB: also protect the layer-wise trust ratio"): a layer is a
  *      chunk (one chunk per parameter tensor).  The direction is u_i = m_i / (sqrt(v_i) + eps) with
  *      the new m (compressed step: v frozen, m driven by g_hat as in R5/R6; dense step: the new m and
@@ -145,22 +146,22 @@ static double stochastic_round(double x, int prec, int emin, double maxf, uint32
     return copysign(v, x);
 }
 
-/* Philox4x64-10: ten rounds of the Philox S-box on a 4 x 64-bit counter with a 2 x 64-bit key, the
+/* Philox4x32-10: ten rounds of the Philox S-box on a 4 x 32-bit counter with a 2 x 32-bit key, the
  * key bumped by the Weyl constants between rounds (SC 2011 paper cited with R18). */
-void or_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4])
+void or_philox4x32(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
 {
-    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-    uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+    const uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
     for (int round = 0; round < 10; ++round) {
         if (round > 0) {
             k0 += W0;
             k1 += W1;
         }
-        unsigned __int128 p0 = (unsigned __int128)M0 * c0, p1 = (unsigned __int128)M1 * c2;
-        uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
-        uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
-        uint64_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;
+        uint64_t p0 = (uint64_t)M0 * c0, p1 = (uint64_t)M1 * c2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;
         c0 = n0;
         c1 = n1;
         c2 = n2;
@@ -175,9 +176,11 @@ void or_philox4x64(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]
 /* R18: the 16 random bits of flat element i. */
 static uint32_t sr_bits(uint64_t seed, uint64_t step, int64_t i)
 {
-    uint64_t ctr[4] = {(uint64_t)i >> 4, 0, 0, 0}, key[2] = {seed, step}, out[4];
-    or_philox4x64(ctr, key, out);
-    return (uint32_t)((out[(i >> 2) & 3] >> (16 * (i & 3))) & 0xFFFFu);
+    uint64_t blk = (uint64_t)i >> 2;
+    uint32_t ctr[4] = {(uint32_t)blk, (uint32_t)(blk >> 32), (uint32_t)step, (uint32_t)(step >> 32)};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)}, out[4];
+    or_philox4x32(ctr, key, out);
+    return out[i & 3] >> 16;
 }
 
 #define BF16_MAXF ((2.0 - ldexp(1.0, -7)) * ldexp(1.0, 127))

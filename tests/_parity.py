@@ -127,10 +127,12 @@ def upload(refs, err, m, v, p):
                 d.copy_(torch.from_numpy(src), non_blocking=False)
 
 
-def _oracle_compress(r, g, w):
+def _oracle_compress(r, g, w, s):
     off = np.asarray([0, r.b - r.a], np.int64)
     hp = dict(lr=w.lr, beta1=w.beta1, eps=w.eps, clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta,
               want_signs=w.int8_signs, count_nonfinite=True)
+    if w.err_rounding == "stochastic":
+        hp.update(stochastic=True, sr_seed=synth.SR_SEED, sr_step=s, sr_index0=r.a)
     if w.optimizer == "lamb":
         words, scales, ratios, signs, nf = oracle.lamb_compress_step(g, r.err, r.m, r.v, r.p, off, **hp)
         r.out = dict(words=words, scale=scales[0], signs=signs, nf=nf, ratio=ratios[0])
@@ -149,12 +151,12 @@ def _oracle_dense(r, g, w, bias_correction, t):
         r.out = {}
 
 
-def oracle_step(refs, g_dev, w, kind, bias_correction=False, t=0):
+def oracle_step(refs, g_dev, w, kind, bias_correction=False, t=0, s=0):
     gs = [synth.host(g_dev[r.a:r.b]) for r in refs]
     for r in refs:
         r.err_before = r.err.copy()
     if kind == "compressed":
-        futs = [_POOL.submit(_oracle_compress, r, g, w) for r, g in zip(refs, gs)]
+        futs = [_POOL.submit(_oracle_compress, r, g, w, s) for r, g in zip(refs, gs)]
     else:
         futs = [_POOL.submit(_oracle_dense, r, g, w, bias_correction, t) for r, g in zip(refs, gs)]
     for f in futs:
@@ -192,6 +194,10 @@ def compare_chunks(refs, w, kind, err, m, v, p, words=None, scales=None, signs=N
                 assert abs(gss - rss[0]) <= 1e-10 * rss[0], f"{tag}: error norm^2 {gss} vs {rss[0]}"
                 assert int(diag[1][r.c].item()) == int(rpc[0]), f"{tag}: +1 count"
             assert np.array_equal(gv, r.v), f"{tag}: v changed in the compressed step"
+            if w.err_rounding == "stochastic" and d == 0:
+                # same scale -> the same fp32 new error and the same random bits on both sides
+                assert np.array_equal(ge.view(np.uint16), r.err.view(np.uint16)), \
+                    f"{tag}: stochastically rounded error differs"
         else:
             assert_f32_close(gv, r.v, f"{tag}: v")
         err_slack = ds * ((1 - eb) if w.ef_mode == 1 else 1.0)
@@ -227,7 +233,7 @@ def run_workload(w, chunks=None, steps=None, device="cuda:0", log=print, diagnos
                               clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta,
                               int8_signs=w.int8_signs, count_nonfinite=True,
                               freeze_step=w.freeze_step, refresh_period=w.refresh_period,
-                              diagnostics=diagnostics)
+                              diagnostics=diagnostics, err_rounding=w.err_rounding, sr_seed=synth.SR_SEED)
     refs = host_chunks(w, chunks, err, m, v, p)
     g = None
     counts = {"dense": 0, "compressed": 0, "scale_ulp_mismatch": 0}
@@ -238,7 +244,7 @@ def run_workload(w, chunks=None, steps=None, device="cuda:0", log=print, diagnos
         torch.cuda.synchronize()
         kind = opt.step(g)
         torch.cuda.synchronize()
-        oracle_step(refs, g, w, kind, t=opt.dense_steps)
+        oracle_step(refs, g, w, kind, t=opt.dense_steps, s=s)
         counts[kind] += 1
         counts["scale_ulp_mismatch"] += compare_chunks(refs, w, kind, err, m, v, p, opt.words,
                                                        opt.scales, opt.signs,

@@ -39,9 +39,11 @@ def test_status_strings(lib):
 
 
 def test_hparams_layout_matches_header():
-    # five floats, int32, float, int32, then an 8-byte aligned int64
-    assert ctypes.sizeof(ob.ob_hparams) == 40
+    # five floats, int32, float, int32, an 8-byte aligned int64, int32 + reserved int32, uint64
+    assert ctypes.sizeof(ob.ob_hparams) == 56
     assert ob.ob_hparams.step.offset == 32
+    assert ob.ob_hparams.err_rounding.offset == 40
+    assert ob.ob_hparams.sr_seed.offset == 48
 
 
 P = ctypes.c_void_p

@@ -88,7 +88,27 @@ VARIANTS = {
     "fp32_ema_bf16err": dict(gdt="f32", clip=0.0, ef_mode=1, signs=True, edt="bf16"),
     "bf16_ema_clip_int8_f16err": dict(gdt="bf16", clip=5.0, ef_mode=1, signs=True, edt="f16"),
     "bf16_plain_bf16err": dict(gdt="bf16", clip=0.0, ef_mode=0, signs=False, edt="bf16"),
+    # ... stored with stochastic rounding
+    "fp32_ema_bf16err_sr": dict(gdt="f32", clip=0.0, ef_mode=1, signs=True, edt="bf16", sr=True),
+    "bf16_plain_f16err_sr": dict(gdt="bf16", clip=0.0, ef_mode=0, signs=False, edt="f16", sr=True),
 }
+SR_SEED = 0x5EED0B17
+
+
+def _sr_hp(var, step):
+    """hparams fields and oracle keywords of a variant's error rounding at one step."""
+    if not var.get("sr"):
+        return {}, {}
+    return (dict(err_rounding=ob.OB_ROUND_STOCHASTIC, sr_seed=SR_SEED, step=step),
+            dict(stochastic=True, sr_seed=SR_SEED, sr_step=step))
+
+
+def _assert_sr_mostly_exact(gpu, ref, what):
+    """Stochastic rounding takes the same decision on both sides unless the new error before rounding
+    differs (an ulp of a chunk's scale); all but a small fraction of the stored words agree exactly."""
+    g16, r16 = np.asarray(gpu).view(np.uint16), np.asarray(ref).view(np.uint16)
+    same = np.count_nonzero(g16 == r16)
+    assert same >= g16.size - max(2, g16.size // 500), f"{what}: {g16.size - same} of {g16.size} differ"
 
 
 def _as_err_format(err32, edt):
@@ -123,8 +143,10 @@ def _gpu_vs_oracle_compress(n, chunk, var, seed, g=None, state=None, steps=1, lr
         gnp = _bf16_bits(gnp)
     off = oracle.uniform_offsets(n, chunk)
     plan = ob.ob_plan_create(n, chunk_size=chunk)
-    hp = ob.hparams(lr=lr, beta1=0.9, eps=1e-8, clip=var["clip"], ef_mode=var["ef_mode"], ef_beta=0.9)
     for _ in range(steps):
+        sr_h, sr_o = _sr_hp(var, 7 + _)
+        hp = ob.hparams(lr=lr, beta1=0.9, eps=1e-8, clip=var["clip"], ef_mode=var["ef_mode"], ef_beta=0.9,
+                        **sr_h)
         d = [_t(a) for a in (gnp, err, m, v, p)]
         words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
         scales = torch.zeros(off.size - 1, dtype=torch.float32, device=DEV)
@@ -133,8 +155,10 @@ def _gpu_vs_oracle_compress(n, chunk, var, seed, g=None, state=None, steps=1, lr
         ob.ob_adam_compress_step(plan, d[0], d[1], d[2], d[3], d[4], words, scales, hp, signs, nf)
         rw, rs, rsg, rnf = oracle.compress_step(gnp, err, m, v, p, off, lr=lr, beta1=0.9, eps=1e-8,
                                                 clip=var["clip"], ef_mode=var["ef_mode"], ef_beta=0.9,
-                                                want_signs=var["signs"], count_nonfinite=True)
+                                                want_signs=var["signs"], count_nonfinite=True, **sr_o)
         tag = f"n={n} chunk={chunk} {var}"
+        if sr_o:
+            _assert_sr_mostly_exact(synth.host(d[1]), err, f"{tag}: err (stochastic)")
         assert np.array_equal(synth.host(words), rw), f"{tag}: words"
         if signs is not None:
             assert np.array_equal(synth.host(signs), rsg), f"{tag}: signs"
@@ -348,10 +372,15 @@ def _gpu_vs_oracle_lamb(n, chunk, var, seed, kind="compressed", steps=1, lr=1e-4
             scales = torch.zeros(K, dtype=torch.float32, device=DEV)
             signs = torch.zeros(n, dtype=torch.int8, device=DEV) if var["signs"] else None
             nf = torch.zeros(1, dtype=torch.int64, device=DEV)
+            sr_h, sr_o = _sr_hp(var, 3 + st)
+            for k, val in sr_h.items():
+                setattr(hp, k, val)
             ob.ob_lamb_compress_step(plan, d[0], d[1], d[2], d[3], d[4], words, scales, ratios, hp, signs, nf)
             rw, rs, rr, rsg, rnf = oracle.lamb_compress_step(
                 gnp, err, m, v, p, off, lr=lr, beta1=0.9, eps=1e-8, clip=var["clip"], ef_mode=var["ef_mode"],
-                ef_beta=0.9, want_signs=var["signs"], count_nonfinite=True)
+                ef_beta=0.9, want_signs=var["signs"], count_nonfinite=True, **sr_o)
+            if sr_o:
+                _assert_sr_mostly_exact(synth.host(d[1]), err, f"{tag}: err (stochastic)")
             assert np.array_equal(synth.host(words), rw), f"{tag}: words"
             if signs is not None:
                 assert np.array_equal(synth.host(signs), rsg), f"{tag}: signs"
@@ -389,7 +418,7 @@ def _gpu_vs_oracle_lamb(n, chunk, var, seed, kind="compressed", steps=1, lr=1e-4
     return rr
 
 
-LAMB_VARIANTS = ("fp32_plain", "bf16_ema_clip_int8_f16err")
+LAMB_VARIANTS = ("fp32_plain", "bf16_ema_clip_int8_f16err", "fp32_ema_bf16err_sr")
 
 
 @pytest.mark.parametrize("vname", LAMB_VARIANTS)
@@ -549,6 +578,13 @@ def test_misaligned_and_invalid_arguments():
                                      ctypes.c_void_p(words.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
                                      None, None, ctypes.byref(hp), None)
         assert st == 3, (gdt, edt, st)
+    # stochastic rounding of an fp32 error buffer, or an unknown rounding mode, is OB_ERR_ARG
+    for edt, rounding in ((0, ob.OB_ROUND_STOCHASTIC), (1, 2), (2, -1)):
+        bad = ob.hparams(err_rounding=rounding)
+        st = L.ob_adam_compress_step(plan.handle, ptrs[0], 0, ptrs[1], edt, ptrs[2], ptrs[3], ptrs[4],
+                                     ctypes.c_void_p(words.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                                     None, None, ctypes.byref(bad), None)
+        assert st == 1, (edt, rounding, st)
 
 
 def test_deterministic():
@@ -604,9 +640,10 @@ def test_workload_bert_base():
     assert counts["dense"] == 5 and counts["compressed"] == 20
 
 
-@pytest.mark.parametrize("edt", ["bf16", "f16"])
+@pytest.mark.parametrize("edt", ["bf16", "f16", "bf16-sr"])
 def test_workload_bert_base_16bit_error(edt):
-    """The BERT-base workload with its error buffer stored in bf16 / fp16; every chunk every step."""
+    """The BERT-base workload with its error buffer stored in bf16 / fp16 (bf16-sr: stochastically
+    rounded, a new random stream every step); every chunk every step."""
     w = synth.WORKLOADS[f"{synth.BERT_BASE.name}-err-{edt}"]
     counts = P.run_workload(w, log=lambda *_: None)
     assert counts["dense"] == 5 and counts["compressed"] == 20

@@ -20,7 +20,11 @@ Pins used (none retypes the oracle's formula):
     lr * r (exact when lr is a power of two), the ratio against math.fsum norms, exact scale
     invariances (p x 2, v x 4, and g, err, m x 2), and layer independence;
   * diagnostics (R17): the error norm against math.fsum, the +1 count against numpy.unpackbits, and
-    the worked example's values.
+    the worked example's values;
+  * stochastic rounding (R18): the generator against Random123's published Philox4x32-10
+    known-answer vectors (tests/golden/philox4x32_kat.json), the bf16 rule against the fp32 bit
+    pattern, the fp16 rule in exact rationals (fractions.Fraction), unbiasedness within 5 sigma,
+    and the reduction of a step with stochastic rounding to the fp32 step followed by the rounding.
 """
 import math
 from fractions import Fraction
@@ -847,40 +851,30 @@ def test_diagnostics_vs_fsum_and_unpackbits(fmt):
 
 
 # ------------------------------------------------------------------------------------------------
-# R18: stochastic rounding of a 16-bit error buffer (Philox4x64-10 random bits)
+# R18: stochastic rounding of a 16-bit error buffer (Philox4x32-10 random bits)
 # ------------------------------------------------------------------------------------------------
 
-M64 = (1 << 64) - 1
+def test_philox4x32_known_answers():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "philox4x32_kat.json")) as f:
+        kat = json.load(f)
+    for vec in kat["vectors"]:
+        c, k, want = ([int(w, 16) for w in vec[key]] for key in ("counter", "key", "out"))
+        assert oracle.philox4x32(c, k).tolist() == want, vec
 
 
-def _np_philox(counter, key):
-    """numpy's Philox4x64-10 output at `counter` (numpy bumps its 256-bit counter before each block)."""
-    c = sum(int(w) << (64 * k) for k, w in enumerate(counter))
-    c = (c - 1) % (1 << 256)
-    prev = np.asarray([(c >> (64 * k)) & M64 for k in range(4)], dtype=np.uint64)
-    bg = np.random.Philox(counter=prev, key=np.asarray(key, dtype=np.uint64))
-    return bg.random_raw(4)
-
-
-@pytest.mark.parametrize("counter,key", [
-    ([0, 0, 0, 0], [0, 0]),
-    ([1, 0, 0, 0], [0x0123456789ABCDEF, 0xFEDCBA9876543210]),
-    ([M64, 0, 0, 0], [5, 7]),                        # numpy's predecessor borrows across words
-    ([12345, 678, M64, 9], [M64, M64]),
-    ([0xDEADBEEF, 0, 0, 0], [2 ** 63, 1]),
-])
-def test_philox_matches_numpy(counter, key):
-    assert np.array_equal(oracle.philox4x64(counter, key), _np_philox(counter, key))
-
-
-def _np_sr_bits(seed, step, idx):
-    out = {}
+def _sr_bits(seed, step, idx):
+    """r of each flat index: the high 16 bits of word i & 3 of Philox4x32-10 (the oracle's, pinned by
+    the known answers above) at counter (i >> 2, step) under key seed, each split into 32-bit words."""
+    M32 = 0xFFFFFFFF
+    blocks = {}
     r = np.zeros(idx.size, dtype=np.uint32)
     for k, i in enumerate(idx.tolist()):
-        c = i >> 4
-        if c not in out:
-            out[c] = _np_philox([c, 0, 0, 0], [seed, step])
-        r[k] = (int(out[c][(i >> 2) & 3]) >> (16 * (i & 3))) & 0xFFFF
+        b = i >> 2
+        if b not in blocks:
+            blocks[b] = oracle.philox4x32([b & M32, b >> 32, step & M32, step >> 32], [seed & M32, seed >> 32])
+        r[k] = int(blocks[b][i & 3]) >> 16
     return r
 
 
@@ -889,9 +883,9 @@ def test_sr_bf16_is_the_bit_rule():
     rng = np.random.default_rng(41)
     x = (rng.standard_normal(4096) * 10.0 ** rng.uniform(-30, 30, 4096)).astype(np.float32)
     x[:64] = (rng.standard_normal(64) * 1e-40).astype(np.float32)      # fp32 subnormals
-    seed, step, i0 = 0x5EED, 12, 1000
+    seed, step, i0 = 0x0123456789ABCDEF, (1 << 40) + 12, (1 << 34) + 1000     # every 32-bit word in use
     got = oracle.to_format_sr(x, "bf16", seed, step, i0)
-    r = _np_sr_bits(seed, step, np.arange(i0, i0 + x.size))
+    r = _sr_bits(seed, step, np.arange(i0, i0 + x.size))
     u = x.view(np.uint32)
     mag = (u & 0x7FFFFFFF).astype(np.uint64)
     up = (r.astype(np.uint64) < (mag & 0xFFFF)).astype(np.uint64)
@@ -906,7 +900,7 @@ def test_sr_f16_exact_rule():
                         rng.uniform(65000, 65600, 40), rng.uniform(0, 2 ** -24, 40)]).astype(np.float32)
     seed, step, i0 = 99, 3, 7
     got = oracle.to_format_sr(x, "f16", seed, step, i0).astype(np.float64)
-    r = _np_sr_bits(seed, step, np.arange(i0, i0 + x.size))
+    r = _sr_bits(seed, step, np.arange(i0, i0 + x.size))
     for k, xv in enumerate(x.astype(np.float64)):
         a = Fraction(abs(xv))
         with np.errstate(over="ignore"):

@@ -86,17 +86,20 @@ MUTANTS = {
     "lamb_dense_also_adam": ("bias_correction, step, 0);", "bias_correction, step, 1);"),
     "diag_norm_not_squared": ("            s += e * e;", "            s += fabs(e);"),
     "diag_counts_minus": ("plus += word_bit(words, i);", "plus += 1 - word_bit(words, i);"),
-    "sr_counter_shift": ("uint64_t ctr[4] = {(uint64_t)i >> 4, 0, 0, 0}", "uint64_t ctr[4] = {(uint64_t)i >> 2, 0, 0, 0}"),
-    "sr_slice": ("(out[(i >> 2) & 3] >> (16 * (i & 3)))", "(out[i & 3] >> (16 * ((i >> 2) & 3)))"),
-    "sr_key_without_step": ("key[2] = {seed, step}", "key[2] = {seed, 0}"),
+    "sr_counter_shift": ("uint64_t blk = (uint64_t)i >> 2;", "uint64_t blk = (uint64_t)i >> 4;"),
     "sr_decision_inverted": ("(double)r * q < (a - lo) * 65536.0", "(double)r * q > (a - lo) * 65536.0"),
     "sr_overflow_saturates": ("    if (v > maxf) v = INFINITY;\n    return copysign(v, x);",
                               "    if (v > maxf) v = maxf;\n    return copysign(v, x);"),
     "sr_falls_back_to_nearest": ("float stored = stochastic ? store_err_sr(", "float stored = 0 ? store_err_sr("),
     "sr_ignores_index0": ("sr_bits(sr_seed, sr_step, sr_index0 + i))", "sr_bits(sr_seed, sr_step, i))"),
     "philox_no_key_bump": ("            k0 += W0;\n            k1 += W1;", "            k0 += 0;\n            k1 += W1;"),
-    "philox_lanes_swapped": ("uint64_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;",
-                             "uint64_t n0 = hi0 ^ c1 ^ k0, n1 = lo0, n2 = hi1 ^ c3 ^ k1, n3 = lo1;"),
+    "philox_lanes_swapped": ("uint32_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;",
+                             "uint32_t n0 = hi0 ^ c1 ^ k0, n1 = lo0, n2 = hi1 ^ c3 ^ k1, n3 = lo1;"),
+    "sr_wrong_word": ("return out[i & 3] >> 16;", "return out[(i >> 1) & 3] >> 16;"),
+    "sr_low_half": ("return out[i & 3] >> 16;", "return out[i & 3] & 0xFFFFu;"),
+    "sr_step_dropped": ("(uint32_t)step, (uint32_t)(step >> 32)};", "0, 0};"),
+    "sr_seed_high_dropped": ("uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)}, out[4];",
+                             "uint32_t key[2] = {(uint32_t)seed, 0}, out[4];"),
     "unpack_polarity": ("out[i] = word_bit(words, i) ? scales[c] : -scales[c];",
                         "out[i] = word_bit(words, i) ? -scales[c] : scales[c];"),
 }
