@@ -68,6 +68,8 @@ def _load():
     lib.or_philox4x32.argtypes = [P, P, P]
     lib.or_philox4x32.restype = None
     lib.or_to_format_sr.argtypes = [P, I64, I, U64, U64, I64, P]
+    lib.or_worker_compress.argtypes = [I64, I64, P, P, I, P, I, P, P, P, P, F, I, F, I, U64, U64, I64]
+    lib.or_worker_update.argtypes = [I64, I64, P, P, P, P, P, P, F, F, F]
     lib.or_compress_step_sr.argtypes = [I64, I64, P, P, I, P, I, P, P, P, P, P, P, P,
                                         F, F, F, F, I, F, I, P, U64, U64, I64]
     lib.or_to_format.argtypes = [P, I64, I, P]
@@ -234,6 +236,38 @@ def compress_step(g, err, m, v, p, offsets, *, lr, beta1, eps, clip=0.0, ef_mode
                                       lr, beta1, eps, clip, ef_mode, ef_beta)
     _check(rc, "compress_step")
     return words, scales, signs, (int(nf[0]) if nf is not None else None)
+
+
+def worker_compress(g, err, offsets, *, clip=0.0, ef_mode=0, ef_beta=0.9, want_signs=False,
+                    count_nonfinite=False, stochastic=False, sr_seed=0, sr_step=0, sr_index0=0):
+    """The worker's half before the exchange (reading R19 (a)): err updated in place with the worker's
+    own g_hat.  Returns (words, scales, signs or None, nonfinite or None)."""
+    g, bf = _grad(np.ascontiguousarray(g))
+    n = g.size
+    err, efmt = _err(err)
+    assert err.size == n and err.flags["C_CONTIGUOUS"]
+    k = offsets.size - 1
+    words = np.zeros(n_words(n), dtype=np.uint32)
+    scales = np.zeros(max(k, 0), dtype=np.float32)
+    signs = np.zeros(n, dtype=np.int8) if want_signs else None
+    nf = np.zeros(1, dtype=np.int64) if count_nonfinite else None
+    _check(_load().or_worker_compress(n, k, _ptr(offsets), _ptr(g), bf, _ptr(err), efmt, _ptr(words),
+                                      _ptr(scales), _ptr(signs), _ptr(nf), clip, ef_mode, ef_beta,
+                                      1 if stochastic else 0, sr_seed, sr_step, sr_index0), "worker_compress")
+    return words, scales, signs, (int(nf[0]) if nf is not None else None)
+
+
+def worker_update(words, scales, m, v, p, offsets, *, lr, beta1, eps):
+    """The worker's half after the exchange (reading R19 (b)): g_hat from the exchanged words and scales,
+    then m and p in place (v read only)."""
+    n = m.size
+    for a in (m, v, p):
+        assert a.dtype == np.float32 and a.size == n and a.flags["C_CONTIGUOUS"]
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    assert words.size == n_words(n) and scales.size == offsets.size - 1
+    _check(_load().or_worker_update(n, offsets.size - 1, _ptr(offsets), _ptr(words), _ptr(scales), _ptr(m),
+                                    _ptr(v), _ptr(p), lr, beta1, eps), "worker_update")
 
 
 def warmup_step(g, m, v, p, *, lr, beta1, beta2, eps, bias_correction=False, step=0):

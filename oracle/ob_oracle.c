@@ -71,6 +71,13 @@
  *      of the stored error buffer as the step reads it (double, ascending index; its square root is
  *      the norm) and the number of elements whose sign bit is +1 in the step's packed words (the
  *      bit balance; the ideal share for a zero-mean gradient is one half).
+ *   R19 the worker's compressed step split at the exchange ([P2] compressed branch: the quantize
+ *      line runs before compressed_allreduce, the dequantize, momentum and update lines after it).
+ *      (a) worker compress: compensate, per-chunk scale, pack, and the new error from the worker's
+ *      OWN g_hat (R10), stored as in R15/R18; m and p are not touched.  (b) worker update: g_hat
+ *      from the words and scales the exchange returns (the server's), then m and the frozen-v
+ *      update exactly as in the fused step.  With one worker and a zero server error the exchange
+ *      returns the worker's own words and scales, and (a) then (b) is the fused step.
  */
 #include <math.h>
 #include <stdint.h>
@@ -582,6 +589,82 @@ int or_compress_step_sr(int64_t n, int64_t K, const int64_t* off,
                            sr_index0);
     if (rc != OR_OK || n == 0 || !lamb) return rc;
     lamb_update(K, off, m, v, p, ratios, lr, eps, 1.0, 1.0);
+    return OR_OK;
+}
+
+/* ---------- R19: the worker's step split at the exchange ---------- */
+
+/* (a) compensate, scale, pack, error with the worker's own g_hat; m, v, p are not part of it. */
+int or_worker_compress(int64_t n, int64_t K, const int64_t* off, const void* g, int g_is_bf16,
+                       void* err_store, int err_fmt, uint32_t* words, float* scales, int8_t* signs,
+                       int64_t* nonfinite, float clip, int ef_mode, float ef_beta,
+                       int stochastic, uint64_t sr_seed, uint64_t sr_step, int64_t sr_index0)
+{
+    if (stochastic && err_fmt == OR_FMT_F32) return OR_ERR_ARG;
+    if (!check_offsets(n, K, off)) return OR_ERR_ARG;
+    if (err_fmt != OR_FMT_F32 && err_fmt != OR_FMT_BF16 && err_fmt != OR_FMT_F16) return OR_ERR_ARG;
+    if (n == 0) return OR_OK;
+    if (!g || !err_store || !words || !scales) return OR_ERR_ARG;
+    float* x = (float*)calloc((size_t)n, sizeof(float));
+    float* err = (float*)calloc((size_t)n, sizeof(float));
+    if (x == NULL || err == NULL) {
+        free(x);
+        free(err);
+        return OR_ERR_OOM;
+    }
+    for (int64_t i = 0; i < n; ++i) err[i] = load_err(err_store, err_fmt, i);
+    /* compensated = grad (+clip, R7) + error */
+    for (int64_t i = 0; i < n; ++i) {
+        double gi = (double)load_grad(g, g_is_bf16, i);
+        if (clip > 0.0f) {
+            double c = (double)clip;
+            if (gi > c)
+                gi = c;
+            else if (gi < -c)
+                gi = -c;
+        }
+        x[i] = (float)(gi + (double)err[i]);
+    }
+    /* q, scale = one_bit_quantize(compensated) */
+    for (int64_t c = 0; c < K; ++c) scales[c] = or_chunk_scale(x, off[c], off[c + 1]);
+    or_pack(x, 0, n, words);
+    /* error = compensated - g_hat with the worker's own g_hat (plain), or its EMA */
+    const double eb = (double)ef_beta;
+    for (int64_t c = 0; c < K; ++c) {
+        for (int64_t i = off[c]; i < off[c + 1]; ++i) {
+            int b = sign_bit(x[i]);
+            float gh = b ? scales[c] : -scales[c];
+            float delta = (float)((double)x[i] - (double)gh);
+            err[i] = ef_mode == 1 ? (float)(eb * (double)err[i] + (1.0 - eb) * (double)delta) : delta;
+            if (signs != NULL) signs[i] = (int8_t)(b ? 1 : -1);
+        }
+    }
+    for (int64_t i = 0; i < n; ++i) {
+        float stored = stochastic ? store_err_sr(err_store, err_fmt, i, err[i],
+                                                 sr_bits(sr_seed, sr_step, sr_index0 + i))
+                                  : store_err(err_store, err_fmt, i, err[i]);
+        if (nonfinite != NULL && !isfinite(stored)) *nonfinite += 1;
+    }
+    free(x);
+    free(err);
+    return OR_OK;
+}
+
+/* (b) g_hat = dequantize(the exchanged words and scales), then m and the frozen-v update. */
+int or_worker_update(int64_t n, int64_t K, const int64_t* off, const uint32_t* words, const float* scales,
+                     float* m, const float* v, float* p, float lr, float beta1, float eps)
+{
+    if (!check_offsets(n, K, off)) return OR_ERR_ARG;
+    if (n == 0) return OR_OK;
+    if (!words || !scales || !m || !v || !p) return OR_ERR_ARG;
+    const double b1 = (double)beta1;
+    for (int64_t c = 0; c < K; ++c) {
+        for (int64_t i = off[c]; i < off[c + 1]; ++i) {
+            float ghat = word_bit(words, i) ? scales[c] : -scales[c];
+            m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)ghat);
+            p[i] = (float)((double)p[i] - (double)lr * ((double)m[i] / (sqrt((double)v[i]) + (double)eps)));
+        }
+    }
     return OR_OK;
 }
 

@@ -967,3 +967,76 @@ def test_compress_sr_is_fp32_step_then_stochastic_rounding(fmt, lamb):
     assert np.array_equal(part.view(np.uint16), want[lo:hi].view(np.uint16))
     with pytest.raises(ValueError):                      # fp32 buffers have nothing to round
         step(g, e_ref.copy(), m.copy(), v, p.copy(), off, stochastic=True, sr_seed=1, sr_step=1, **hp)
+
+
+# ------------------------------------------------------------------------------------------------
+# R19: the worker's step split at the exchange
+# ------------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gdt", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("ef_mode,clip", [(0, 0.0), (1, 0.0), (1, 0.5)])
+def test_worker_split_is_the_fused_step_at_one_worker(gdt, fmt, ef_mode, clip):
+    """With one worker the exchange returns the worker's own words and scales, so compress-then-update
+    equals the fused compressed step bit for bit (err, m, p, words, scales, signs, non-finite count)."""
+    n = 3 * 1000 + 77
+    off = np.asarray([0, 1000, 2000, n], np.int64)
+    g, err32, m, v, p = _random_state(n, 61, sigma=0.3)
+    err32 *= 0.1
+    if gdt == "bf16":
+        g = _lib_narrow(g, "bf16")
+    stochastic = fmt != "f32"
+    for sr in ([False, True] if stochastic else [False]):
+        if fmt == "f32":
+            e_a, e_b = err32.copy(), err32.copy()
+        else:
+            bits = _lib_narrow(err32, fmt)
+            e_a = bits.view(np.float16).copy() if fmt == "f16" else bits.copy()
+            e_b = e_a.copy()
+        m_a, p_a, m_b, p_b = m.copy(), p.copy(), m.copy(), p.copy()
+        srk = dict(stochastic=True, sr_seed=5, sr_step=9, sr_index0=0) if sr else {}
+        wa, sa, ga, na = oracle.compress_step(g, e_a, m_a, v, p_a, off, **HP, clip=clip, ef_mode=ef_mode,
+                                              ef_beta=0.9, want_signs=True, count_nonfinite=True, **srk)
+        wb, sb, gb, nb = oracle.worker_compress(g, e_b, off, clip=clip, ef_mode=ef_mode, ef_beta=0.9,
+                                                want_signs=True, count_nonfinite=True, **srk)
+        oracle.worker_update(wb, sb, m_b, v, p_b, off, **HP)
+        for a, b in ((wa, wb), (sa, sb), (ga, gb), (e_a, e_b), (m_a, m_b), (p_a, p_b)):
+            assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
+        assert na == nb
+
+
+def test_worker_update_exact_values():
+    """Dyadic values: beta1 = 1/2, lr = 1/4, eps = 0, v = 1, so m' = (m + g_hat)/2 and p' = p - m'/4."""
+    n = 64 + 30
+    off = np.asarray([0, 64, n], np.int64)
+    scales = np.asarray([2.0, 0.5], np.float32)
+    bits = np.arange(n) % 3 == 0                       # +1 at every third element
+    words = np.packbits(bits.astype(np.uint8), bitorder="little")
+    words = np.concatenate([words, np.zeros((-words.size) % 4, np.uint8)]).view(np.uint32)
+    m = np.full(n, 1.0, np.float32)
+    v = np.ones(n, np.float32)
+    p = np.full(n, 3.0, np.float32)
+    oracle.worker_update(words, scales, m, v, p, off, lr=0.25, beta1=0.5, eps=0.0)
+    s = np.where(np.arange(n) < 64, 2.0, 0.5)
+    ghat = np.where(bits, s, -s)
+    want_m = (1.0 + ghat) / 2
+    assert np.array_equal(m, want_m.astype(np.float32))
+    assert np.array_equal(p, (3.0 - want_m / 4).astype(np.float32))
+    assert np.array_equal(v, np.ones(n, np.float32))
+
+
+def test_worker_update_follows_the_exchanged_signs():
+    """The update uses the words it is given, not the worker's own: with every exchanged sign flipped,
+    m moves by (1 - beta1) * 2 * scale in the other direction."""
+    n = 2048 + 5
+    off = oracle.uniform_offsets(n, 1024)
+    g, err, m, v, p = _random_state(n, 62)
+    words, scales, _, _ = oracle.worker_compress(g, err, off)
+    flipped = ~words
+    flipped[-1] &= np.uint32((1 << (n % 32)) - 1)
+    m_a, p_a, m_b, p_b = m.copy(), p.copy(), m.copy(), p.copy()
+    oracle.worker_update(words, scales, m_a, v, p_a, off, lr=0.0, beta1=0.5, eps=1e-8)
+    oracle.worker_update(flipped, scales, m_b, v, p_b, off, lr=0.0, beta1=0.5, eps=1e-8)
+    s = np.repeat(scales, np.diff(off)).astype(np.float64)
+    assert np.allclose(np.abs(m_a.astype(np.float64) - m_b.astype(np.float64)), s, rtol=1e-6, atol=0)
+    assert np.array_equal(p_a, p) and np.array_equal(p_b, p)     # lr = 0

@@ -27,7 +27,7 @@ MUTANTS = {
     "scale_no_sqrt": ("return (float)sqrt(s / (double)(end - begin));",
                       "return (float)(s / (double)(end - begin));"),
     "error_sign": ("float delta = (float)((double)x[i] - (double)gh);",
-                   "float delta = (float)((double)gh - (double)x[i]);"),
+                   "float delta = (float)((double)gh - (double)x[i]);", 2),
     "momentum_uses_x": ("m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)gh);",
                         "m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)x[i]);"),
     "momentum_coeffs_swapped": ("m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)gh);",
@@ -37,16 +37,16 @@ MUTANTS = {
     "update_drops_eps": ("(sqrt((double)v[i]) + (double)eps)));\n            if (signs",
                          "(sqrt((double)v[i]))));\n            if (signs"),
     "update_no_sqrt": ("((double)m[i] / (sqrt((double)v[i]) + (double)eps)",
-                       "((double)m[i] / ((double)v[i] + (double)eps)"),
+                       "((double)m[i] / ((double)v[i] + (double)eps)", 2),
     "ema_coeffs_swapped": ("e_new = (float)(eb * (double)err[i] + (1.0 - eb) * (double)delta);",
                            "e_new = (float)((1.0 - eb) * (double)err[i] + eb * (double)delta);"),
     "ema_unscaled_sign": ("float delta = (float)((double)x[i] - (double)gh);",
-                          "float delta = (float)((double)x[i] - (b ? 1.0 : -1.0));"),
-    "clip_lower_bound": ("gi = -c;", "gi = c;"),
+                          "float delta = (float)((double)x[i] - (b ? 1.0 : -1.0));", 2),
+    "clip_lower_bound": ("gi = -c;", "gi = c;", 2),
     "gh_wrong_chunk": ("float gh = b ? scales[c] : -scales[c];",
-                       "float gh = b ? scales[0] : -scales[0];"),
-    "nonfinite_nan_only": ("!isfinite(stored)", "isnan(stored)"),
-    "nonfinite_counts_unrounded": ("!isfinite(stored)", "!isfinite(err[i])"),
+                       "float gh = b ? scales[0] : -scales[0];", 2),
+    "nonfinite_nan_only": ("!isfinite(stored)", "isnan(stored)", 2),
+    "nonfinite_counts_unrounded": ("!isfinite(stored)", "!isfinite(err[i])", 2),
     "format_ties_away": ("nearbyint(a / q)", "round(a / q)"),
     "format_truncates": ("nearbyint(a / q)", "trunc(a / q)"),
     "overflow_saturates": ("if (r > maxf) r = INFINITY;", "if (r > maxf) r = maxf;"),
@@ -56,10 +56,10 @@ MUTANTS = {
     "f16_decode_bias": ("v = ldexp((double)(mant + 1024), ex - 25);", "v = ldexp((double)(mant + 1024), ex - 24);"),
     "f16_subnormal_decode": ("v = ldexp((double)mant, -24);", "v = ldexp((double)mant, -25);"),
     "error_not_widened": ("for (int64_t i = 0; i < n; ++i) err[i] = load_err(err_store, err_fmt, i);",
-                          "for (int64_t i = 0; i < n; ++i) err[i] = 0.0f;"),
+                          "for (int64_t i = 0; i < n; ++i) err[i] = 0.0f;", 2),
     "error_stored_unrounded_bf16": ("uint16_t b = bf16_bits_of(round_to_format(e, 8, -126, BF16_MAXF));",
                                     "uint16_t b = bf16_bits_of((double)(float)((double)e));"),
-    "int8_zero_for_plus": ("signs[i] = (int8_t)(b ? 1 : -1);", "signs[i] = (int8_t)(b ? 0 : -1);"),
+    "int8_zero_for_plus": ("signs[i] = (int8_t)(b ? 1 : -1);", "signs[i] = (int8_t)(b ? 0 : -1);", 2),
     "dense_v_not_squared": ("(1.0 - b2) * (gi * gi)", "(1.0 - b2) * gi"),
     "dense_v_uses_beta1": ("v[i] = (float)(b2 * (double)v[i]", "v[i] = (float)(b1 * (double)v[i]"),
     "dense_bias_corr_power": ("bc2 = 1.0 - pow(b2, (double)step);", "bc2 = 1.0 - pow(b1, (double)step);"),
@@ -90,8 +90,8 @@ MUTANTS = {
     "sr_decision_inverted": ("(double)r * q < (a - lo) * 65536.0", "(double)r * q > (a - lo) * 65536.0"),
     "sr_overflow_saturates": ("    if (v > maxf) v = INFINITY;\n    return copysign(v, x);",
                               "    if (v > maxf) v = maxf;\n    return copysign(v, x);"),
-    "sr_falls_back_to_nearest": ("float stored = stochastic ? store_err_sr(", "float stored = 0 ? store_err_sr("),
-    "sr_ignores_index0": ("sr_bits(sr_seed, sr_step, sr_index0 + i))", "sr_bits(sr_seed, sr_step, i))"),
+    "sr_falls_back_to_nearest": ("float stored = stochastic ? store_err_sr(", "float stored = 0 ? store_err_sr(", 2),
+    "sr_ignores_index0": ("sr_bits(sr_seed, sr_step, sr_index0 + i))", "sr_bits(sr_seed, sr_step, i))", 2),
     "philox_no_key_bump": ("            k0 += W0;\n            k1 += W1;", "            k0 += 0;\n            k1 += W1;"),
     "philox_lanes_swapped": ("uint32_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;",
                              "uint32_t n0 = hi0 ^ c1 ^ k0, n1 = lo0, n2 = hi1 ^ c3 ^ k1, n3 = lo1;"),
@@ -100,6 +100,14 @@ MUTANTS = {
     "sr_step_dropped": ("(uint32_t)step, (uint32_t)(step >> 32)};", "0, 0};"),
     "sr_seed_high_dropped": ("uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)}, out[4];",
                              "uint32_t key[2] = {(uint32_t)seed, 0}, out[4];"),
+    # R19: the worker's split step
+    "worker_update_polarity": ("float ghat = word_bit(words, i) ? scales[c] : -scales[c];",
+                               "float ghat = word_bit(words, i) ? -scales[c] : scales[c];"),
+    "worker_update_momentum_coeff": ("(1.0 - b1) * (double)ghat);", "(double)ghat);"),
+    "worker_update_skips_p": ("            p[i] = (float)((double)p[i] - (double)lr * ((double)m[i] / (sqrt((double)v[i]) + (double)eps)));\n        }\n    }\n    return OR_OK;",
+                              "        }\n    }\n    return OR_OK;"),
+    "worker_compress_global_error": ("err[i] = ef_mode == 1 ? (float)(eb * (double)err[i] + (1.0 - eb) * (double)delta) : delta;",
+                                     "err[i] = ef_mode == 1 ? (float)(eb * (double)err[i] + (1.0 - eb) * (double)delta) : x[i];"),
     "unpack_polarity": ("out[i] = word_bit(words, i) ? scales[c] : -scales[c];",
                         "out[i] = word_bit(words, i) ? -scales[c] : scales[c];"),
 }
