@@ -20,12 +20,13 @@ OB_EF_PLAIN, OB_EF_EMA = 0, 1
 OB_ROUND_NEAREST, OB_ROUND_STOCHASTIC = 0, 1
 (OB_KERNEL_CHUNK_SUMSQ, OB_KERNEL_COMPRESS, OB_KERNEL_DENSE, OB_KERNEL_SERVER_SUMSQ,
  OB_KERNEL_SERVER_APPLY, OB_KERNEL_UNPACK, OB_KERNEL_TRUST_RATIO, OB_KERNEL_LAMB_APPLY,
- OB_KERNEL_DIAG, OB_KERNEL_SCALE) = range(10)
+ OB_KERNEL_DIAG, OB_KERNEL_SCALE, OB_KERNEL_WORKER_COMPRESS, OB_KERNEL_WORKER_UPDATE) = range(12)
 KERNEL_NAMES = {
     OB_KERNEL_CHUNK_SUMSQ: "chunk_sumsq", OB_KERNEL_COMPRESS: "compress", OB_KERNEL_DENSE: "dense",
     OB_KERNEL_SERVER_SUMSQ: "server_sumsq", OB_KERNEL_SERVER_APPLY: "server_apply",
     OB_KERNEL_UNPACK: "unpack", OB_KERNEL_TRUST_RATIO: "trust_ratio", OB_KERNEL_LAMB_APPLY: "lamb_apply",
-    OB_KERNEL_DIAG: "diag", OB_KERNEL_SCALE: "scale",
+    OB_KERNEL_DIAG: "diag", OB_KERNEL_SCALE: "scale", OB_KERNEL_WORKER_COMPRESS: "worker_compress",
+    OB_KERNEL_WORKER_UPDATE: "worker_update",
 }
 
 
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
         "ob_adam_compress_step": (I32, [P, P, I32, P, I32, P, P, P, P, P, P, P, HP, P]),
         "ob_lamb_compress_step": (I32, [P, P, I32, P, I32, P, P, P, P, P, P, P, P, HP, P]),
         "ob_lamb_warmup_step": (I32, [P, P, I32, P, P, P, P, HP, P]),
+        "ob_adam_worker_compress": (I32, [P, P, I32, P, I32, P, P, P, P, HP, P]),
+        "ob_adam_worker_update": (I32, [P, P, P, P, P, P, HP, P]),
         "ob_server_reduce": (I32, [P, I32, P, P, P, P, P, P]),
         "ob_pack": (I32, [P, I32, I64, P, P]),
         "ob_unpack": (I32, [P, P, I64, P, P, P]),
@@ -213,6 +216,34 @@ def ob_adam_compress_step(plan: Plan, g, err, m, v, p, words_out, scales_out, hp
         _dev(p, "p"),
         _dev(words_out, "words_out"), _dev(scales_out, "scales_out"), _dev(signs_out, "signs_out"),
         _dev(nonfinite_out, "nonfinite_out"), ctypes.byref(hp), _stream(stream)), "ob_adam_compress_step")
+
+
+def ob_adam_worker_compress(plan: Plan, g, err, words_out, scales_out, hp: ob_hparams, signs_out=None,
+                            nonfinite_out=None, stream=None):
+    """The worker's half before the exchange: signs, scales and the error from its own g_hat."""
+    n = plan.n
+    _want(g, "g", g.dtype, n)
+    _want(err, "err", err.dtype, n)
+    _want(words_out, "words_out", torch.int32, (n + 31) // 32)
+    _want(scales_out, "scales_out", torch.float32, plan.num_chunks)
+    _want(signs_out, "signs_out", torch.int8, n)
+    _want(nonfinite_out, "nonfinite_out", torch.int64, 1)
+    _check(lib().ob_adam_worker_compress(
+        plan.handle, _dev(g, "g"), _gdtype(g), _dev(err, "err"), _errdtype(err), _dev(words_out, "words_out"),
+        _dev(scales_out, "scales_out"), _dev(signs_out, "signs_out"), _dev(nonfinite_out, "nonfinite_out"),
+        ctypes.byref(hp), _stream(stream)), "ob_adam_worker_compress")
+
+
+def ob_adam_worker_update(plan: Plan, words, scales, m, v, p, hp: ob_hparams, stream=None):
+    """The worker's half after the exchange: g_hat from the exchanged words and scales, then m and p."""
+    n = plan.n
+    _want(words, "words", torch.int32, (n + 31) // 32)
+    _want(scales, "scales", torch.float32, plan.num_chunks)
+    for name, t in (("m", m), ("v", v), ("p", p)):
+        _want(t, name, torch.float32, n)
+    _check(lib().ob_adam_worker_update(
+        plan.handle, _dev(words, "words"), _dev(scales, "scales"), _dev(m, "m"), _dev(v, "v"), _dev(p, "p"),
+        ctypes.byref(hp), _stream(stream)), "ob_adam_worker_update")
 
 
 def ob_lamb_compress_step(plan: Plan, g, err, m, v, p, words_out, scales_out, ratios_out, hp: ob_hparams,

@@ -418,6 +418,22 @@ ob_status pass2_view(ob_plan plan, int table, hipStream_t stream, ob::PlanDev* o
     return st;
 }
 
+ob::CompressParams compress_params(const ob_hparams* hp)
+{
+    ob::CompressParams cp;
+    cp.lr = hp->lr;
+    cp.beta1 = hp->beta1;
+    cp.one_m_beta1 = 1.0 - static_cast<double>(hp->beta1);
+    cp.eps = hp->eps;
+    cp.clip = hp->clip > 0.0f ? hp->clip : 0.0f;
+    cp.ef_beta = hp->ef_beta;
+    cp.one_m_ef_beta = 1.0 - static_cast<double>(hp->ef_beta);
+    cp.stochastic = hp->err_rounding == OB_ROUND_STOCHASTIC;
+    cp.sr_seed = hp->sr_seed;
+    cp.sr_step = static_cast<uint64_t>(hp->step);
+    return cp;
+}
+
 // Validation and passes 1-2 of the compressed step.  lamb != 0: passes 1-2 of the 1-bit LAMB step
 // (sums of p^2 and u^2 instead of the update); the caller then runs the trust ratio and the update.
 ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
@@ -439,17 +455,7 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
     if (hp->err_rounding != OB_ROUND_NEAREST && hp->err_rounding != OB_ROUND_STOCHASTIC) return OB_ERR_ARG;
     if (hp->err_rounding == OB_ROUND_STOCHASTIC && err_dtype == OB_F32) return OB_ERR_ARG;
 
-    ob::CompressParams cp;
-    cp.lr = hp->lr;
-    cp.beta1 = hp->beta1;
-    cp.one_m_beta1 = 1.0 - static_cast<double>(hp->beta1);
-    cp.eps = hp->eps;
-    cp.clip = hp->clip > 0.0f ? hp->clip : 0.0f;
-    cp.ef_beta = hp->ef_beta;
-    cp.one_m_ef_beta = 1.0 - static_cast<double>(hp->ef_beta);
-    cp.stochastic = hp->err_rounding == OB_ROUND_STOCHASTIC;
-    cp.sr_seed = hp->sr_seed;
-    cp.sr_step = static_cast<uint64_t>(hp->step);
+    const ob::CompressParams cp = compress_params(hp);
 
     DeviceGuard guard(plan->device);
     if (!guard.ok) return OB_ERR_HIP;
@@ -526,6 +532,70 @@ ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, v
 {
     return compress_passes(plan, g, g_dtype, err, err_dtype, m, v, p, words_out, scales_out, signs_out,
                            nonfinite_out, hp, 0, stream);
+}
+
+ob_status ob_adam_worker_compress(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
+                                  uint32_t* words_out, float* scales_out, int8_t* signs_out,
+                                  uint64_t* nonfinite_out, const ob_hparams* hp, hipStream_t stream)
+{
+    if (!plan || !hp) return OB_ERR_ARG;
+    if (!valid_dtype(g_dtype) || !valid_err_dtype(err_dtype)) return OB_ERR_DTYPE;
+    if (plan->n == 0) return OB_OK;
+    if (ob_status st = check_grad(g, g_dtype)) return st;
+    if (!err || !words_out || !scales_out) return OB_ERR_ARG;
+    if (!aligned(err, err_dtype == OB_F32 ? 16 : 8)) return OB_ERR_ALIGN;
+    if (!aligned(words_out, 4) || !aligned(scales_out, 4)) return OB_ERR_ALIGN;
+    if (signs_out && !aligned(signs_out, 4)) return OB_ERR_ALIGN;
+    if (nonfinite_out && !aligned(nonfinite_out, 8)) return OB_ERR_ALIGN;
+    if (hp->ef_mode != OB_EF_PLAIN && hp->ef_mode != OB_EF_EMA) return OB_ERR_ARG;
+    if (hp->err_rounding != OB_ROUND_NEAREST && hp->err_rounding != OB_ROUND_STOCHASTIC) return OB_ERR_ARG;
+    if (hp->err_rounding == OB_ROUND_STOCHASTIC && err_dtype == OB_F32) return OB_ERR_ARG;
+    const ob::CompressParams cp = compress_params(hp);
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return OB_ERR_HIP;
+    const ob::PlanDev pd1 = plan->dev(T_PASS1);
+    const int bf = g_dtype == OB_BF16;
+    const int ema = hp->ef_mode == OB_EF_EMA;
+    auto nf = reinterpret_cast<unsigned long long*>(nonfinite_out);
+    ob_status st = timed(plan, OB_KERNEL_CHUNK_SUMSQ, stream, [&] {
+        switch (err_dtype) {
+        case OB_BF16: return ob::launch_chunk_sumsq<OB_BF16>(pd1, g, bf, err, cp.clip, nullptr, stream);
+        case OB_F16: return ob::launch_chunk_sumsq<OB_F16>(pd1, g, bf, err, cp.clip, nullptr, stream);
+        default: return ob::launch_chunk_sumsq<OB_F32>(pd1, g, bf, err, cp.clip, nullptr, stream);
+        }
+    });
+    if (st != OB_OK) return st;
+    ob::PlanDev pd;
+    if ((st = pass2_view(plan, T_COMPRESS, stream, &pd)) != OB_OK) return st;
+    return timed(plan, OB_KERNEL_WORKER_COMPRESS, stream, [&] {
+        switch (err_dtype) {
+        case OB_BF16:
+            return ob::launch_worker_compress<OB_BF16>(pd, g, bf, err, words_out, scales_out, signs_out, nf, ema, cp,
+                                                       stream);
+        case OB_F16:
+            return ob::launch_worker_compress<OB_F16>(pd, g, bf, err, words_out, scales_out, signs_out, nf, ema, cp,
+                                                      stream);
+        default:
+            return ob::launch_worker_compress<OB_F32>(pd, g, bf, err, words_out, scales_out, signs_out, nf, ema, cp,
+                                                      stream);
+        }
+    });
+}
+
+ob_status ob_adam_worker_update(ob_plan plan, const uint32_t* words, const float* scales, float* m,
+                                const float* v, float* p, const ob_hparams* hp, hipStream_t stream)
+{
+    if (!plan || !hp) return OB_ERR_ARG;
+    if (plan->n == 0) return OB_OK;
+    if (!words || !scales || !m || !v || !p) return OB_ERR_ARG;
+    if (!aligned(words, 4) || !aligned(scales, 4)) return OB_ERR_ALIGN;
+    if (!aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16)) return OB_ERR_ALIGN;
+    const ob::CompressParams cp = compress_params(hp);
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return OB_ERR_HIP;
+    const ob::PlanDev pd = plan->dev(T_COMPRESS);
+    return timed(plan, OB_KERNEL_WORKER_UPDATE, stream,
+                 [&] { return ob::launch_worker_update(pd, words, scales, m, v, p, cp, stream); });
 }
 
 ob_status ob_lamb_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,

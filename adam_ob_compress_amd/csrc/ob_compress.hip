@@ -261,6 +261,81 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
     }
 }
 
+// ------------------------------------------------------------------------------------------------
+// the worker's half of a compressed step before the exchange (more than one worker): pass 2 without
+// m, v and p -- scale, sign bits and the error from the worker's own g_hat
+// ------------------------------------------------------------------------------------------------
+
+template <class G, class E, bool CLIP, bool EMA, bool SR>
+__global__ __launch_bounds__(kBlock) void k_worker_compress(PlanDev pd, const typename G::T* __restrict__ g,
+                                                            typename E::T* __restrict__ err,
+                                                            uint32_t* __restrict__ words, float* __restrict__ scales,
+                                                            int8_t* __restrict__ signs,
+                                                            unsigned long long* __restrict__ nonfinite,
+                                                            CompressParams cp)
+{
+    __shared__ double lds[kBlock / 64];
+    const Item it = pd.items[blockIdx.x];
+    const int tid = threadIdx.x;
+    constexpr int U = OB_P2_UNROLL;
+    const float scale = chunk_scale(pd, it.chunk, lds);
+    if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
+    uint32_t nf = 0;
+    int base = 0;
+    for (; base + U * kTile <= it.len; base += U * kTile) {
+        f4 gv[U], ev[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            gv[u] = G::template load4<OB_NT_P2>(g, i);
+            ev[u] = E::template load4<OB_NT_P2>(err, i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            const u4 rw = SR ? philox_block(cp.sr_seed, cp.sr_step, i) : u4{};
+            uint32_t nib = 0;
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                const float x = compensate<CLIP>(gv[u][k], ev[u][k], cp.clip);
+                float e = ev[u][k];
+                nib |= error_elem<EMA>(x, e, scale, cp) << k;
+                e = SR ? E::rounded_sr(e, rw.x[k] >> 16) : E::rounded(e);
+                ev[u][k] = e;
+                nf += __builtin_isfinite(e) ? 0u : 1u;
+            }
+            E::template store4<OB_NT_ST>(err, i, ev[u]);
+            if (signs) *reinterpret_cast<uint32_t*>(signs + i) = signs4(nib);
+            store_word(words, i, nib, true);
+        }
+    }
+    for (; base < it.len; base += kTile) {
+        const int rem = it.len - base;
+        const int cnt = rem - kVec * tid;
+        const int64_t i = it.start + base + kVec * tid;
+        const u4 rw = (SR && cnt > 0) ? philox_block(cp.sr_seed, cp.sr_step, i) : u4{};
+        uint32_t nib = 0;
+        #pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+            if (k >= cnt) continue;
+            float e = E::load1(err, i + k);
+            const float x = compensate<CLIP>(G::load1(g, i + k), e, cp.clip);
+            const uint32_t b = error_elem<EMA>(x, e, scale, cp);
+            nib |= b << k;
+            e = SR ? E::rounded_sr(e, rw.x[k] >> 16) : E::rounded(e);
+            E::store1(err, i + k, e);
+            if (signs) signs[i + k] = b ? int8_t(1) : int8_t(-1);
+            nf += __builtin_isfinite(e) ? 0u : 1u;
+        }
+        store_word(words, i, nib, 32 * (tid >> 3) < rem);
+    }
+    if (nonfinite) {
+        __shared__ uint32_t ldsu[kBlock / 64];
+        const uint32_t t = block_sum_u32(nf, ldsu);
+        if (tid == 0 && t) atomicAdd(nonfinite, static_cast<unsigned long long>(t));
+    }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------------------
@@ -392,11 +467,63 @@ hipError_t launch_compress(const PlanDev& pd, const void* g, int g_bf16, void* e
     return hipGetLastError();
 }
 
+namespace {
+template <class G, class E, bool CLIP, bool EMA>
+void worker_dispatch(const PlanDev& pd, const typename G::T* g, typename E::T* err, uint32_t* words,
+                     float* scales, int8_t* signs, unsigned long long* nonfinite, const CompressParams& cp,
+                     hipStream_t s)
+{
+    const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
+    if constexpr (!std::is_same<E, ErrF32>::value) {
+        if (cp.stochastic) {
+            hipLaunchKernelGGL((k_worker_compress<G, E, CLIP, EMA, true>), grid, block, 0, s, pd, g, err, words,
+                               scales, signs, nonfinite, cp);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((k_worker_compress<G, E, CLIP, EMA, false>), grid, block, 0, s, pd, g, err, words, scales,
+                       signs, nonfinite, cp);
+}
+
+template <class G, class E>
+void worker_dispatch_g(const PlanDev& pd, const typename G::T* g, typename E::T* err, uint32_t* words,
+                       float* scales, int8_t* signs, unsigned long long* nonfinite, int ema,
+                       const CompressParams& cp, hipStream_t s)
+{
+    const int sel = (cp.clip > 0.0f ? 1 : 0) | (ema ? 2 : 0);
+    switch (sel) {
+    case 0: worker_dispatch<G, E, false, false>(pd, g, err, words, scales, signs, nonfinite, cp, s); break;
+    case 1: worker_dispatch<G, E, true, false>(pd, g, err, words, scales, signs, nonfinite, cp, s); break;
+    case 2: worker_dispatch<G, E, false, true>(pd, g, err, words, scales, signs, nonfinite, cp, s); break;
+    default: worker_dispatch<G, E, true, true>(pd, g, err, words, scales, signs, nonfinite, cp, s); break;
+    }
+}
+}  // namespace
+
+template <int EF>
+hipError_t launch_worker_compress(const PlanDev& pd, const void* g, int g_bf16, void* err_v, uint32_t* words,
+                                  float* scales, int8_t* signs, unsigned long long* nonfinite, int ema,
+                                  const CompressParams& cp, hipStream_t s)
+{
+    using E = typename ErrOf<EF>::type;
+    auto err = static_cast<typename E::T*>(err_v);
+    if (g_bf16)
+        worker_dispatch_g<GradBF16, E>(pd, static_cast<const uint16_t*>(g), err, words, scales, signs, nonfinite,
+                                       ema, cp, s);
+    else
+        worker_dispatch_g<GradF32, E>(pd, static_cast<const float*>(g), err, words, scales, signs, nonfinite, ema,
+                                      cp, s);
+    return hipGetLastError();
+}
+
 // the error format this translation unit is compiled for
 template hipError_t launch_chunk_sumsq<OB_ERR_FMT>(const PlanDev&, const void*, int, const void*, float,
                                                    const float*, hipStream_t);
 template hipError_t launch_compress<OB_ERR_FMT>(const PlanDev&, const void*, int, void*, float*, const float*,
                                                 float*, uint32_t*, float*, int8_t*, unsigned long long*, int,
                                                 int, const CompressParams&, hipStream_t);
+template hipError_t launch_worker_compress<OB_ERR_FMT>(const PlanDev&, const void*, int, void*, uint32_t*, float*,
+                                                       int8_t*, unsigned long long*, int, const CompressParams&,
+                                                       hipStream_t);
 
 }  // namespace ob

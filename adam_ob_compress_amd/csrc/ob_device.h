@@ -394,14 +394,10 @@ __device__ __forceinline__ float compensate(float g, float e, float clip)
     return g + e;
 }
 
-// One element of the compressed step; returns the sign bit (1 <=> +1).
-// x, g_hat and delta are single fp32 operations; the error (EMA), m and p lines are evaluated in
-// double and rounded once, so a large update that nearly cancels p keeps full fp32 accuracy.
-// LAMB: p is left alone; u = m / (sqrt(v) + eps) (double, not stored) adds u^2 to usq for the layer's
-// trust ratio.
-template <bool EMA, bool LAMB>
-__device__ __forceinline__ uint32_t compress_elem(float x, float& e, float& mm, float vv, float& pp, double& usq,
-                                                  float scale, const CompressParams& cp)
+// The sign bit of one element (1 <=> +1) and its new error from g_hat = +-scale: x, g_hat and delta
+// are single fp32 operations, the EMA line is evaluated in double and rounded once.
+template <bool EMA>
+__device__ __forceinline__ uint32_t error_elem(float x, float& e, float scale, const CompressParams& cp)
 {
     const bool b = x >= 0.0f;
     const float gh = b ? scale : -scale;              // g_hat = dequantize(q)
@@ -410,16 +406,36 @@ __device__ __forceinline__ uint32_t compress_elem(float x, float& e, float& mm, 
         e = static_cast<float>(cp.ef_beta * static_cast<double>(e) + cp.one_m_ef_beta * static_cast<double>(delta));
     else
         e = delta;
-    // m on g_hat ([P1] sec. 2.2; [P2]), then the frozen-v update with the stored (new) m ([P2])
+    return b ? 1u : 0u;
+}
+
+// m on g_hat ([P1] sec. 2.2; [P2]) and the frozen-v update with the stored (new) m ([P2]); both lines in
+// double, rounded once, so a large update that nearly cancels p keeps full fp32 accuracy.
+__device__ __forceinline__ void update_elem(float gh, float& mm, float vv, float& pp, const CompressParams& cp)
+{
     mm = static_cast<float>(cp.beta1 * static_cast<double>(mm) + cp.one_m_beta1 * static_cast<double>(gh));
     const double den = sqrt(static_cast<double>(vv)) + cp.eps;
-    if (LAMB) {
-        const double u = static_cast<double>(mm) / den;
-        usq = fma(u, u, usq);
-    } else {
-        pp = static_cast<float>(static_cast<double>(pp) - cp.lr * (static_cast<double>(mm) / den));
+    pp = static_cast<float>(static_cast<double>(pp) - cp.lr * (static_cast<double>(mm) / den));
+}
+
+// One element of the compressed step; returns the sign bit (1 <=> +1).
+// LAMB: p is left alone; u = m / (sqrt(v) + eps) (double, not stored) adds u^2 to usq for the layer's
+// trust ratio.
+template <bool EMA, bool LAMB>
+__device__ __forceinline__ uint32_t compress_elem(float x, float& e, float& mm, float vv, float& pp, double& usq,
+                                                  float scale, const CompressParams& cp)
+{
+    const uint32_t b = error_elem<EMA>(x, e, scale, cp);
+    const float gh = b ? scale : -scale;
+    if (!LAMB) {
+        update_elem(gh, mm, vv, pp, cp);
+        return b;
     }
-    return b ? 1u : 0u;
+    mm = static_cast<float>(cp.beta1 * static_cast<double>(mm) + cp.one_m_beta1 * static_cast<double>(gh));
+    const double den = sqrt(static_cast<double>(vv)) + cp.eps;
+    const double u = static_cast<double>(mm) / den;
+    usq = fma(u, u, usq);
+    return b;
 }
 
 // Chunk scale from the chunk's pass-1 partials, reduced in a fixed order (so every pass-2 block of

@@ -587,6 +587,84 @@ hipError_t launch_chunk_sums(const PlanDev& pd, double* sums, hipStream_t s)
     hipLaunchKernelGGL(k_chunk_sums, dim3(static_cast<unsigned>(pd.K)), dim3(kBlock), 0, s, pd, sums);
     return hipGetLastError();
 }
+// ------------------------------------------------------------------------------------------------
+// the worker's half of a compressed step after the exchange (more than one worker): g_hat from the
+// exchanged words and per-chunk scales, then m and the frozen-v update
+// ------------------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kBlock) void k_worker_update(PlanDev pd, const uint32_t* __restrict__ words,
+                                                          const float* __restrict__ scales, float* __restrict__ m,
+                                                          const float* __restrict__ v, float* __restrict__ p,
+                                                          CompressParams cp)
+{
+    const Item it = pd.items[blockIdx.x];
+    const int tid = threadIdx.x;
+    const float s = scales[it.chunk];
+    constexpr int U = OB_P2_UNROLL;
+    int base = 0;
+    for (; base + U * kTile <= it.len; base += U * kTile) {
+        f4 mv[U], vv[U], pv[U];
+        uint32_t wv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            wv[u] = words[i >> 5];
+            mv[u] = ld4<OB_NT_P2>(m, i);
+            vv[u] = ld4<OB_NT_P2>(v, i);
+            pv[u] = ld4<OB_NT_P2>(p, i);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + base + u * kTile + kVec * tid;
+            const uint32_t nib = wv[u] >> (static_cast<uint32_t>(i) & 31u);
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                float mm = mv[u][k], pp = pv[u][k];
+                update_elem((nib >> k) & 1u ? s : -s, mm, vv[u][k], pp, cp);
+                mv[u][k] = mm;
+                pv[u][k] = pp;
+            }
+            st4<OB_NT_ST>(m, i, mv[u]);
+            st4<OB_NT_ST>(p, i, pv[u]);
+        }
+    }
+    for (; base < it.len; base += kTile) {
+        const int cnt = it.len - base - kVec * tid;
+        const int64_t i = it.start + base + kVec * tid;
+        if (cnt <= 0) continue;
+        const uint32_t nib = words[i >> 5] >> (static_cast<uint32_t>(i) & 31u);
+        if (cnt >= kVec) {
+            f4 mv = ld4(m, i), pv = ld4(p, i);
+            const f4 vv = ld4(v, i);
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                float mm = mv[k], pp = pv[k];
+                update_elem((nib >> k) & 1u ? s : -s, mm, vv[k], pp, cp);
+                mv[k] = mm;
+                pv[k] = pp;
+            }
+            st4(m, i, mv);
+            st4(p, i, pv);
+        } else {
+            #pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                if (k >= cnt) continue;
+                float mm = m[i + k], pp = p[i + k];
+                update_elem((nib >> k) & 1u ? s : -s, mm, v[i + k], pp, cp);
+                m[i + k] = mm;
+                p[i + k] = pp;
+            }
+        }
+    }
+}
+
+hipError_t launch_worker_update(const PlanDev& pd, const uint32_t* words, const float* scales, float* m,
+                                const float* v, float* p, const CompressParams& cp, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_worker_update, dim3(static_cast<unsigned>(pd.n_items)), dim3(kBlock), 0, s, pd, words,
+                       scales, m, v, p, cp);
+    return hipGetLastError();
+}
 
 hipError_t launch_trust_ratio(const PlanDev& pd, float* ratios, hipStream_t s)
 {

@@ -181,6 +181,23 @@ ob_status ob_server_reduce(ob_plan plan, int32_t W, const uint32_t* worker_words
                            const float* worker_scales, float* server_err, uint32_t* words_out,
                            float* scales_out, hipStream_t stream);
 
+/* ---- the worker's compressed step split at the exchange (more than one worker; [P2] "1-bit Adam:
+ * warmup, frozen variance, error feedback", compressed branch: the quantize line runs before
+ * compressed_allreduce, the dequantize, momentum and update lines after it) ----
+ * ob_adam_worker_compress: ob_adam_compress_step up to the packed signs, scales and error: the error
+ *   uses the worker's own g_hat; m, v and p are not touched.  Arguments, layout and errors as there.
+ * ob_adam_worker_update: g_hat_i = bit(i) ? scales[c] : -scales[c] from the exchanged words
+ *   (uint32[ceil(n/32)], pad bits ignored) and scales (fp32[K]), e.g. the output of ob_server_reduce
+ *   gathered back; then m = beta1*m + (1-beta1)*g_hat and p -= lr * m / (sqrt(v) + eps), m and p in
+ *   place, v read only (hp: lr, beta1, eps).
+ * With one worker and a zero server error the exchange returns the worker's own words and scales, and
+ * the two calls give bit for bit the results of ob_adam_compress_step. */
+ob_status ob_adam_worker_compress(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
+                                  uint32_t* words_out, float* scales_out, int8_t* signs_out,
+                                  uint64_t* nonfinite_out, const ob_hparams* hp, hipStream_t stream);
+ob_status ob_adam_worker_update(ob_plan plan, const uint32_t* words, const float* scales, float* m,
+                                const float* v, float* p, const ob_hparams* hp, hipStream_t stream);
+
 /* Pack signs of x (OB_F32 or OB_BF16, n elements) into ceil(n/32) words ([P2] one_bit_quantize, sign part). */
 ob_status ob_pack(const void* x, ob_dtype x_dtype, int64_t n, uint32_t* words_out, hipStream_t stream);
 
@@ -208,7 +225,9 @@ typedef enum {
     OB_KERNEL_DIAG = 8,            /* diagnostics: per-chunk totals */
     OB_KERNEL_SCALE = 9,           /* per-chunk sums of squares formed before pass 2 (plans with a
                                       chunk of more than 4096 pass-1 blocks) */
-    OB_KERNEL_COUNT = 10
+    OB_KERNEL_WORKER_COMPRESS = 10,/* worker compress, pass 2 (pass 1 is OB_KERNEL_CHUNK_SUMSQ) */
+    OB_KERNEL_WORKER_UPDATE = 11,  /* worker update */
+    OB_KERNEL_COUNT = 12
 } ob_kernel;
 
 ob_status ob_plan_set_timing(ob_plan plan, int32_t enable);
