@@ -55,6 +55,10 @@ def bytes_per_elem(w, kernel: str) -> float:
         if lamb:                      # LAMB pass 2: no p; read g err m v, write err m + bits
             return gb + eb + 8.0 + eb + 4.0 + 0.125 + sb
         return gb + eb + 12.0 + eb + 8.0 + 0.125 + sb
+    if kernel == "worker_compress":   # read g err, write err + 1 bit (+ int8 sign)
+        return gb + eb + eb + 0.125 + sb
+    if kernel == "worker_update":     # read 1 bit m v p, write m p
+        return 0.125 + 12.0 + 8.0
     if kernel == "chunk_sumsq":       # read g err (LAMB: and p)
         return gb + eb + (4.0 if lamb else 0.0)
     if kernel == "dense":             # read g m v p, write m v p (LAMB: m v only)
@@ -179,8 +183,19 @@ def run(args):
         dense_ms = ms / max(cnt, 1)
         ob.ob_plan_set_timing(plan, False)
 
+    step = opt.step
+    if args.split:
+        if w.optimizer != "adam":
+            raise SystemExit("--split times the 1-bit Adam worker step")
+
+        def step(g, s=None):
+            # the worker's step split at the exchange, with one worker: its own words are the exchange's
+            ob.ob_adam_worker_compress(plan, g, err, opt.words, opt.scales, opt.hp, opt.signs, None, s)
+            ob.ob_adam_worker_update(plan, opt.words, opt.scales, m, v, p, opt.hp, s)
+            return "compressed"
+
     for k in range(args.warmup):
-        opt.step(grads[k % ring])
+        step(grads[k % ring])
     torch.cuda.synchronize()
 
     ob.ob_plan_set_timing(plan, True)
@@ -188,7 +203,7 @@ def run(args):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        kinds[opt.step(grads[k % ring], stream)] += 1
+        kinds[step(grads[k % ring], stream)] += 1
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -219,7 +234,8 @@ def run(args):
         del src, dst
 
     # the dominant kernel of the timed steps: the longest per launch (the fused pass 2 for 1-bit Adam)
-    dom = max((k for k in ("compress", "lamb_apply") if k in kern), key=lambda k: kern[k]["avg_ms"])
+    dom = max((k for k in ("compress", "lamb_apply", "worker_update") if k in kern),
+              key=lambda k: kern[k]["avg_ms"])
     avg = kern[dom]["avg_ms"]
     bpe = bytes_per_elem(w, dom)
     achieved = bpe * w.n / (avg * 1e-3) / 1e9
@@ -248,7 +264,7 @@ def run(args):
                    "error_feedback": "ema" if w.ef_mode else "plain", "int8_signs": w.int8_signs,
                    "freeze_step": w.freeze_step, "refresh_period": w.refresh_period,
                    "block_elems": plan.block_elems, "work_blocks": plan.num_blocks,
-                   "diagnostics": bool(args.diagnostics)},
+                   "diagnostics": bool(args.diagnostics), "split": bool(args.split)},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "bytes_per_elem": bpe, "traffic": traffic},
@@ -273,6 +289,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain torch copy of this many MiB (counter calibration)")
+    ap.add_argument("--split", action="store_true",
+                    help="time the worker step split at the exchange (worker compress + worker update, "
+                         "one worker) instead of the fused compressed step")
     ap.add_argument("--diagnostics", action="store_true",
                     help="also compute the per-chunk error norm and +1 count in every compressed step")
     ap.add_argument("--rocprof-summary", metavar="DIR")
@@ -315,7 +334,8 @@ def _short(name: str) -> str:
 KERNEL_SYMBOL = {"compress": "k_compress<", "chunk_sumsq": "k_chunk_sumsq<", "dense": "k_dense<",
                  "server_sumsq": "k_server<false>", "server_apply": "k_server<true>", "unpack": "k_unpack",
                  "lamb_apply": "k_lamb_apply<", "trust_ratio": "k_trust_ratio", "diag": "k_diag_reduce",
-                 "scale": "k_scale_finalize"}
+                 "scale": "k_scale_finalize", "worker_compress": "k_worker_compress<",
+                 "worker_update": "k_worker_update"}
 
 
 def _counter_rows(d: str, counter: str):
@@ -345,6 +365,7 @@ def traffic_profile(d: str, kernel: str, workload: str) -> str:
     (fk, fn, ff), (wk, wn, wf) = res["FETCH_SIZE"], res["WRITE_SIZE"]
     traffic = (fk / ff + wk / wf) * 1024
     alg = bytes_per_elem(w, kernel) * w.n
+    run_flags = " --split" if kernel.startswith("worker_") else ""   # the split step's kernels
     rec = {"kernel": kernel, "workload": w.name, "kernel_src_sha": kernel_source_sha(),
            "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
            "fetch_factor": round(ff, 5), "write_factor": round(wf, 5), "bytes_per_launch": round(traffic),
@@ -355,8 +376,8 @@ Kernel source sha (ob_compress.hip, ob_kernels.hip, ob_device.h, ob_internal.h):
 
 Commands (each its own run on one MI355X, from the repository root, `export TMPDIR=/tmp`):
 
-    rocprofv3 --pmc FETCH_SIZE -d rocprof_out/fetch -o run --output-format csv -- python bench.py --workload {w.name} --steps 5 --warmup 2 --no-cpu --copy-probe-mib 1024
-    rocprofv3 --pmc WRITE_SIZE -d rocprof_out/write -o run --output-format csv -- python bench.py --workload {w.name} --steps 5 --warmup 2 --no-cpu --copy-probe-mib 1024
+    rocprofv3 --pmc FETCH_SIZE -d rocprof_out/fetch -o run --output-format csv -- python bench.py --workload {w.name}{run_flags} --steps 5 --warmup 2 --no-cpu --copy-probe-mib 1024
+    rocprofv3 --pmc WRITE_SIZE -d rocprof_out/write -o run --output-format csv -- python bench.py --workload {w.name}{run_flags} --steps 5 --warmup 2 --no-cpu --copy-probe-mib 1024
     python bench.py --traffic-profile rocprof_out --kernel {kernel} --workload {w.name}
 
 Calibration: the run also copies 1 GiB with torch (`__amd_rocclr_copyBuffer`, grid 131072), which
