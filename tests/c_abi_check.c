@@ -110,6 +110,28 @@ int main(void)
     const float want_o[N] = {6.5f, -6.5f, 6.5f, 6.5f};
     if (!same("unpack", ho, want_o, N)) return 1;
 
+    /* the same step split at the exchange, with one worker: the same results */
+    CHECK_HIP(hipMemcpy(err, z, sizeof z, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(m, m0, sizeof m0, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemcpy(p, p0, sizeof p0, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemset(words, 0, sizeof(uint32_t)));
+    CHECK_HIP(hipMemset(scales, 0, sizeof(float)));
+    CHECK_OB(ob_adam_worker_compress(plan, g, OB_F32, err, OB_F32, words, scales, signs, NULL, &hp, NULL));
+    CHECK_OB(ob_adam_worker_update(plan, words, scales, m, v, p, &hp, NULL));
+    CHECK_HIP(hipDeviceSynchronize());
+    CHECK_HIP(hipMemcpy(he, err, sizeof he, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(hm, m, sizeof hm, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(hpp, p, sizeof hpp, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(&hs, scales, sizeof hs, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(&hw, words, sizeof hw, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(hsg, signs, sizeof hsg, hipMemcpyDeviceToHost));
+    if (hw != 13u || hs != 6.5f || memcmp(hsg, want_s, N) != 0) {
+        fprintf(stderr, "split: word %u scale %.9g\n", hw, hs);
+        return 1;
+    }
+    if (!same("split err", he, want_e, N) || !same("split m", hm, want_m, N) || !same("split p", hpp, want_p, N))
+        return 1;
+
     /* dense step */
     const float gd[N] = {2, -2, 0.5f, -4}, ones[N] = {1, 1, 1, 1};
     CHECK_HIP(hipMemcpy(g, gd, sizeof gd, hipMemcpyHostToDevice));
