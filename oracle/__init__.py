@@ -70,6 +70,7 @@ def _load():
     lib.or_to_format_sr.argtypes = [P, I64, I, U64, U64, I64, P]
     lib.or_worker_compress.argtypes = [I64, I64, P, P, I, P, I, P, P, P, P, F, I, F, I, U64, U64, I64]
     lib.or_worker_update.argtypes = [I64, I64, P, P, P, P, P, P, F, F, F]
+    lib.or_lamb_worker_update.argtypes = [I64, I64, P, P, P, P, P, P, P, F, F, F]
     lib.or_compress_step_sr.argtypes = [I64, I64, P, P, I, P, I, P, P, P, P, P, P, P,
                                         F, F, F, F, I, F, I, P, U64, U64, I64]
     lib.or_to_format.argtypes = [P, I64, I, P]
@@ -268,6 +269,22 @@ def worker_update(words, scales, m, v, p, offsets, *, lr, beta1, eps):
     assert words.size == n_words(n) and scales.size == offsets.size - 1
     _check(_load().or_worker_update(n, offsets.size - 1, _ptr(offsets), _ptr(words), _ptr(scales), _ptr(m),
                                     _ptr(v), _ptr(p), lr, beta1, eps), "worker_update")
+
+
+def lamb_worker_update(words, scales, m, v, p, offsets, *, lr, beta1, eps):
+    """1-bit LAMB's half after the exchange (readings R16, R19): m on the exchanged g_hat, then the
+    per-layer trust ratio and the update.  m, p in place; returns the ratios fp32[K]."""
+    n = m.size
+    for a in (m, v, p):
+        assert a.dtype == np.float32 and a.size == n and a.flags["C_CONTIGUOUS"]
+    words = np.ascontiguousarray(words, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    k = offsets.size - 1
+    assert words.size == n_words(n) and scales.size == k
+    ratios = np.zeros(max(k, 0), dtype=np.float32)
+    _check(_load().or_lamb_worker_update(n, k, _ptr(offsets), _ptr(words), _ptr(scales), _ptr(m), _ptr(v),
+                                         _ptr(p), _ptr(ratios), lr, beta1, eps), "lamb_worker_update")
+    return ratios
 
 
 def warmup_step(g, m, v, p, *, lr, beta1, beta2, eps, bias_correction=False, step=0):

@@ -668,6 +668,25 @@ int or_worker_update(int64_t n, int64_t K, const int64_t* off, const uint32_t* w
     return OR_OK;
 }
 
+/* (b) for 1-bit LAMB (R16): g_hat from the exchanged words and scales, m on it, then the layer-wise
+ * trust ratio on the reconstructed direction and the update (v frozen). */
+int or_lamb_worker_update(int64_t n, int64_t K, const int64_t* off, const uint32_t* words, const float* scales,
+                          float* m, const float* v, float* p, float* ratios, float lr, float beta1, float eps)
+{
+    if (!check_offsets(n, K, off)) return OR_ERR_ARG;
+    if (n == 0) return OR_OK;
+    if (!words || !scales || !m || !v || !p || !ratios) return OR_ERR_ARG;
+    const double b1 = (double)beta1;
+    for (int64_t c = 0; c < K; ++c) {
+        for (int64_t i = off[c]; i < off[c + 1]; ++i) {
+            float gl = word_bit(words, i) ? scales[c] : -scales[c];
+            m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)gl);
+        }
+    }
+    lamb_update(K, off, m, v, p, ratios, lr, eps, 1.0, 1.0);
+    return OR_OK;
+}
+
 /* ---------- server half of the compressed allreduce on one GPU's share ([P2] compressed_allreduce) ----
  * worker_words: W rows of ceil(n/32) words; worker_scales: W rows of K scales.  R9. */
 int or_server_reduce(int64_t n, int64_t K, const int64_t* off, int W,

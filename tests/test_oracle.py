@@ -1040,3 +1040,47 @@ def test_worker_update_follows_the_exchanged_signs():
     s = np.repeat(scales, np.diff(off)).astype(np.float64)
     assert np.allclose(np.abs(m_a.astype(np.float64) - m_b.astype(np.float64)), s, rtol=1e-6, atol=0)
     assert np.array_equal(p_a, p) and np.array_equal(p_b, p)     # lr = 0
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+@pytest.mark.parametrize("ef_mode", [0, 1])
+def test_lamb_worker_split_is_the_fused_step_at_one_worker(fmt, ef_mode):
+    """1-bit LAMB (R16) split at the exchange: at one worker compress-then-update equals the fused LAMB
+    step bit for bit, ratios included (a zero layer keeps r = 1 on both paths)."""
+    n = 3 * 1000 + 77
+    off = np.asarray([0, 1000, 2000, n], np.int64)
+    g, err32, m, v, p = _random_state(n, 63, sigma=0.3)
+    p[1000:2000] = 0.0                                   # a zero layer
+    e_a = err32.copy() if fmt == "f32" else _lib_narrow(err32, fmt).copy()
+    e_b = e_a.copy()
+    m_a, p_a, m_b, p_b = m.copy(), p.copy(), m.copy(), p.copy()
+    wa, sa, ra, ga, na = oracle.lamb_compress_step(g, e_a, m_a, v, p_a, off, **HP, ef_mode=ef_mode, ef_beta=0.9,
+                                                   want_signs=True, count_nonfinite=True)
+    wb, sb, gb, nb = oracle.worker_compress(g, e_b, off, ef_mode=ef_mode, ef_beta=0.9, want_signs=True,
+                                            count_nonfinite=True)
+    rb = oracle.lamb_worker_update(wb, sb, m_b, v, p_b, off, **HP)
+    for a, b in ((wa, wb), (sa, sb), (ra, rb), (ga, gb), (e_a, e_b), (m_a, m_b), (p_a, p_b)):
+        assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
+    assert na == nb and ra[1] == 1.0
+
+
+def test_lamb_worker_update_follows_the_exchanged_signs():
+    """The LAMB update's direction comes from the words it is given: flipping every exchanged sign
+    changes m by (1 - beta1) * 2 * scale, and the ratio is taken on that direction."""
+    n = 2048 + 5
+    off = oracle.uniform_offsets(n, 1024)
+    g, err, m, v, p = _random_state(n, 64)
+    words, scales, _, _ = oracle.worker_compress(g, err, off)
+    flipped = ~words
+    flipped[-1] &= np.uint32((1 << (n % 32)) - 1)
+    m_a, p_a, m_b, p_b = m.copy(), p.copy(), m.copy(), p.copy()
+    oracle.lamb_worker_update(words, scales, m_a, v, p_a, off, lr=1e-3, beta1=0.5, eps=1e-8)
+    rb = oracle.lamb_worker_update(flipped, scales, m_b, v, p_b, off, lr=1e-3, beta1=0.5, eps=1e-8)
+    s = np.repeat(scales, np.diff(off)).astype(np.float64)
+    assert np.allclose(np.abs(m_a.astype(np.float64) - m_b.astype(np.float64)), s, rtol=1e-6, atol=0)
+    # the ratio on the flipped direction, from math.fsum norms
+    for c in range(off.size - 1):
+        lo, hi = int(off[c]), int(off[c + 1])
+        u = m_b[lo:hi].astype(np.float64) / (np.sqrt(v[lo:hi].astype(np.float64)) + np.float64(np.float32(1e-8)))
+        want = math.sqrt(math.fsum(p[lo:hi].astype(np.float64) ** 2)) / math.sqrt(math.fsum(u * u))
+        assert abs(float(rb[c]) - want) <= 2 * abs(want) * 2.0 ** -23

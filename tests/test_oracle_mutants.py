@@ -108,6 +108,9 @@ MUTANTS = {
                               "        }\n    }\n    return OR_OK;"),
     "worker_compress_global_error": ("err[i] = ef_mode == 1 ? (float)(eb * (double)err[i] + (1.0 - eb) * (double)delta) : delta;",
                                      "err[i] = ef_mode == 1 ? (float)(eb * (double)err[i] + (1.0 - eb) * (double)delta) : x[i];"),
+    "lamb_worker_polarity": ("float gl = word_bit(words, i) ? scales[c] : -scales[c];",
+                             "float gl = word_bit(words, i) ? -scales[c] : scales[c];"),
+    "lamb_worker_momentum_coeff": ("(1.0 - b1) * (double)gl);", "(double)gl);"),
     "unpack_polarity": ("out[i] = word_bit(words, i) ? scales[c] : -scales[c];",
                         "out[i] = word_bit(words, i) ? -scales[c] : scales[c];"),
 }
