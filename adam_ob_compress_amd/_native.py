@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
         "ob_lamb_warmup_step": (I32, [P, P, I32, P, P, P, P, HP, P]),
         "ob_adam_worker_compress": (I32, [P, P, I32, P, I32, P, P, P, P, HP, P]),
         "ob_adam_worker_update": (I32, [P, P, P, P, P, P, HP, P]),
+        "ob_lamb_worker_update": (I32, [P, P, P, P, P, P, P, HP, P]),
         "ob_server_reduce": (I32, [P, I32, P, P, P, P, P, P]),
         "ob_pack": (I32, [P, I32, I64, P, P]),
         "ob_unpack": (I32, [P, P, I64, P, P, P]),
@@ -244,6 +245,19 @@ def ob_adam_worker_update(plan: Plan, words, scales, m, v, p, hp: ob_hparams, st
     _check(lib().ob_adam_worker_update(
         plan.handle, _dev(words, "words"), _dev(scales, "scales"), _dev(m, "m"), _dev(v, "v"), _dev(p, "p"),
         ctypes.byref(hp), _stream(stream)), "ob_adam_worker_update")
+
+
+def ob_lamb_worker_update(plan: Plan, words, scales, m, v, p, ratios_out, hp: ob_hparams, stream=None):
+    """1-bit LAMB's half after the exchange: m on the exchanged g_hat, then trust ratios and the update."""
+    n = plan.n
+    _want(words, "words", torch.int32, (n + 31) // 32)
+    _want(scales, "scales", torch.float32, plan.num_chunks)
+    _want(ratios_out, "ratios_out", torch.float32, plan.num_chunks)
+    for name, t in (("m", m), ("v", v), ("p", p)):
+        _want(t, name, torch.float32, n)
+    _check(lib().ob_lamb_worker_update(
+        plan.handle, _dev(words, "words"), _dev(scales, "scales"), _dev(m, "m"), _dev(v, "v"), _dev(p, "p"),
+        _dev(ratios_out, "ratios_out"), ctypes.byref(hp), _stream(stream)), "ob_lamb_worker_update")
 
 
 def ob_lamb_compress_step(plan: Plan, g, err, m, v, p, words_out, scales_out, ratios_out, hp: ob_hparams,

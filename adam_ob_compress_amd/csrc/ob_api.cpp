@@ -595,7 +595,26 @@ ob_status ob_adam_worker_update(ob_plan plan, const uint32_t* words, const float
     if (!guard.ok) return OB_ERR_HIP;
     const ob::PlanDev pd = plan->dev(T_COMPRESS);
     return timed(plan, OB_KERNEL_WORKER_UPDATE, stream,
-                 [&] { return ob::launch_worker_update(pd, words, scales, m, v, p, cp, stream); });
+                 [&] { return ob::launch_worker_update(pd, words, scales, m, v, p, 0, cp, stream); });
+}
+
+ob_status ob_lamb_worker_update(ob_plan plan, const uint32_t* words, const float* scales, float* m,
+                                const float* v, float* p, float* ratios_out, const ob_hparams* hp,
+                                hipStream_t stream)
+{
+    if (!plan || !hp) return OB_ERR_ARG;
+    if (plan->n == 0) return OB_OK;
+    if (!words || !scales || !m || !v || !p || !ratios_out) return OB_ERR_ARG;
+    if (!aligned(words, 4) || !aligned(scales, 4) || !aligned(ratios_out, 4)) return OB_ERR_ALIGN;
+    if (!aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16)) return OB_ERR_ALIGN;
+    const ob::CompressParams cp = compress_params(hp);
+    DeviceGuard guard(plan->device);
+    if (!guard.ok) return OB_ERR_HIP;
+    const ob::PlanDev pd = plan->dev(T_COMPRESS);
+    ob_status st = timed(plan, OB_KERNEL_WORKER_UPDATE, stream,
+                         [&] { return ob::launch_worker_update(pd, words, scales, m, v, p, 1, cp, stream); });
+    if (st != OB_OK) return st;
+    return lamb_finish(plan, T_COMPRESS, T_COMPRESS, m, v, p, ratios_out, 0, lamb_params(hp, 1.0, 1.0), stream);
 }
 
 ob_status ob_lamb_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,

@@ -81,8 +81,9 @@ template <int EF>
 hipError_t launch_worker_compress(const PlanDev& pd, const void* g, int g_bf16, void* err, uint32_t* words,
                                   float* scales, int8_t* signs, unsigned long long* nonfinite, int ema,
                                   const CompressParams& cp, hipStream_t s);
+// lamb != 0: m only, plus per-block sums of p^2 and u^2 into pd.partials_w / partials_u (this table).
 hipError_t launch_worker_update(const PlanDev& pd, const uint32_t* words, const float* scales, float* m,
-                                const float* v, float* p, const CompressParams& cp, hipStream_t s);
+                                const float* v, float* p, int lamb, const CompressParams& cp, hipStream_t s);
 // lamb != 0: moments only, plus per-block sums of p^2 and u^2 into pd.partials_w / partials_u.
 hipError_t launch_dense(const PlanDev& pd, const void* g, int g_bf16, float* m, float* v, float* p,
                         int lamb, const DenseParams& dp, hipStream_t s);

@@ -589,18 +589,36 @@ hipError_t launch_chunk_sums(const PlanDev& pd, double* sums, hipStream_t s)
 }
 // ------------------------------------------------------------------------------------------------
 // the worker's half of a compressed step after the exchange (more than one worker): g_hat from the
-// exchanged words and per-chunk scales, then m and the frozen-v update
+// exchanged words and per-chunk scales, then m and the frozen-v update (LAMB: m, and the block's sums
+// of p^2 and u^2 for the layer's trust ratio; p is updated after the ratios)
 // ------------------------------------------------------------------------------------------------
 
+template <bool LAMB>
+__device__ __forceinline__ void worker_elem(float gh, float& mm, float vv, float& pp, double& sw, double& su,
+                                            const CompressParams& cp)
+{
+    if (!LAMB) {
+        update_elem(gh, mm, vv, pp, cp);
+        return;
+    }
+    mm = static_cast<float>(cp.beta1 * static_cast<double>(mm) + cp.one_m_beta1 * static_cast<double>(gh));
+    const double u = static_cast<double>(mm) / (sqrt(static_cast<double>(vv)) + cp.eps);
+    su = fma(u, u, su);
+    sw = fma(static_cast<double>(pp), static_cast<double>(pp), sw);
+}
+
+template <bool LAMB>
 __global__ __launch_bounds__(kBlock) void k_worker_update(PlanDev pd, const uint32_t* __restrict__ words,
                                                           const float* __restrict__ scales, float* __restrict__ m,
                                                           const float* __restrict__ v, float* __restrict__ p,
                                                           CompressParams cp)
 {
+    __shared__ double lds[kBlock / 64];
     const Item it = pd.items[blockIdx.x];
     const int tid = threadIdx.x;
     const float s = scales[it.chunk];
     constexpr int U = OB_P2_UNROLL;
+    double sw = 0.0, su = 0.0;
     int base = 0;
     for (; base + U * kTile <= it.len; base += U * kTile) {
         f4 mv[U], vv[U], pv[U];
@@ -620,12 +638,12 @@ __global__ __launch_bounds__(kBlock) void k_worker_update(PlanDev pd, const uint
 #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 float mm = mv[u][k], pp = pv[u][k];
-                update_elem((nib >> k) & 1u ? s : -s, mm, vv[u][k], pp, cp);
+                worker_elem<LAMB>((nib >> k) & 1u ? s : -s, mm, vv[u][k], pp, sw, su, cp);
                 mv[u][k] = mm;
                 pv[u][k] = pp;
             }
             st4<OB_NT_ST>(m, i, mv[u]);
-            st4<OB_NT_ST>(p, i, pv[u]);
+            if (!LAMB) st4<OB_NT_ST>(p, i, pv[u]);
         }
     }
     for (; base < it.len; base += kTile) {
@@ -639,30 +657,41 @@ __global__ __launch_bounds__(kBlock) void k_worker_update(PlanDev pd, const uint
 #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 float mm = mv[k], pp = pv[k];
-                update_elem((nib >> k) & 1u ? s : -s, mm, vv[k], pp, cp);
+                worker_elem<LAMB>((nib >> k) & 1u ? s : -s, mm, vv[k], pp, sw, su, cp);
                 mv[k] = mm;
                 pv[k] = pp;
             }
             st4(m, i, mv);
-            st4(p, i, pv);
+            if (!LAMB) st4(p, i, pv);
         } else {
             #pragma unroll
             for (int k = 0; k < kVec; ++k) {
                 if (k >= cnt) continue;
                 float mm = m[i + k], pp = p[i + k];
-                update_elem((nib >> k) & 1u ? s : -s, mm, v[i + k], pp, cp);
+                worker_elem<LAMB>((nib >> k) & 1u ? s : -s, mm, v[i + k], pp, sw, su, cp);
                 m[i + k] = mm;
-                p[i + k] = pp;
+                if (!LAMB) p[i + k] = pp;
             }
+        }
+    }
+    if (LAMB) {
+        const double tw = block_sum(sw, lds);
+        const double tu = block_sum(su, lds);
+        if (tid == 0) {
+            pd.partials_w[blockIdx.x] = tw;
+            pd.partials_u[blockIdx.x] = tu;
         }
     }
 }
 
 hipError_t launch_worker_update(const PlanDev& pd, const uint32_t* words, const float* scales, float* m,
-                                const float* v, float* p, const CompressParams& cp, hipStream_t s)
+                                const float* v, float* p, int lamb, const CompressParams& cp, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_worker_update, dim3(static_cast<unsigned>(pd.n_items)), dim3(kBlock), 0, s, pd, words,
-                       scales, m, v, p, cp);
+    const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
+    if (lamb)
+        hipLaunchKernelGGL(k_worker_update<true>, grid, block, 0, s, pd, words, scales, m, v, p, cp);
+    else
+        hipLaunchKernelGGL(k_worker_update<false>, grid, block, 0, s, pd, words, scales, m, v, p, cp);
     return hipGetLastError();
 }
 

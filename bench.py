@@ -57,8 +57,8 @@ def bytes_per_elem(w, kernel: str) -> float:
         return gb + eb + 12.0 + eb + 8.0 + 0.125 + sb
     if kernel == "worker_compress":   # read g err, write err + 1 bit (+ int8 sign)
         return gb + eb + eb + 0.125 + sb
-    if kernel == "worker_update":     # read 1 bit m v p, write m p
-        return 0.125 + 12.0 + 8.0
+    if kernel == "worker_update":     # read 1 bit m v p, write m p (LAMB: m only)
+        return 0.125 + 12.0 + (4.0 if lamb else 8.0)
     if kernel == "chunk_sumsq":       # read g err (LAMB: and p)
         return gb + eb + (4.0 if lamb else 0.0)
     if kernel == "dense":             # read g m v p, write m v p (LAMB: m v only)
@@ -185,13 +185,13 @@ def run(args):
 
     step = opt.step
     if args.split:
-        if w.optimizer != "adam":
-            raise SystemExit("--split times the 1-bit Adam worker step")
-
         def step(g, s=None):
             # the worker's step split at the exchange, with one worker: its own words are the exchange's
             ob.ob_adam_worker_compress(plan, g, err, opt.words, opt.scales, opt.hp, opt.signs, None, s)
-            ob.ob_adam_worker_update(plan, opt.words, opt.scales, m, v, p, opt.hp, s)
+            if w.optimizer == "lamb":
+                ob.ob_lamb_worker_update(plan, opt.words, opt.scales, m, v, p, opt.ratios, opt.hp, s)
+            else:
+                ob.ob_adam_worker_update(plan, opt.words, opt.scales, m, v, p, opt.hp, s)
             return "compressed"
 
     for k in range(args.warmup):
@@ -234,7 +234,7 @@ def run(args):
         del src, dst
 
     # the dominant kernel of the timed steps: the longest per launch (the fused pass 2 for 1-bit Adam)
-    dom = max((k for k in ("compress", "lamb_apply", "worker_update") if k in kern),
+    dom = max((k for k in ("compress", "lamb_apply", "worker_compress", "worker_update") if k in kern),
               key=lambda k: kern[k]["avg_ms"])
     avg = kern[dom]["avg_ms"]
     bpe = bytes_per_elem(w, dom)

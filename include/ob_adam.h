@@ -191,12 +191,19 @@ ob_status ob_server_reduce(ob_plan plan, int32_t W, const uint32_t* worker_words
  *   gathered back; then m = beta1*m + (1-beta1)*g_hat and p -= lr * m / (sqrt(v) + eps), m and p in
  *   place, v read only (hp: lr, beta1, eps).
  * With one worker and a zero server error the exchange returns the worker's own words and scales, and
- * the two calls give bit for bit the results of ob_adam_compress_step. */
+ * the two calls give bit for bit the results of ob_adam_compress_step.
+ * ob_lamb_worker_update ([P2] "1-bit LAMB"): the same g_hat and m, then the layer-wise trust ratio on
+ *   the reconstructed direction and the update, as in ob_lamb_compress_step (ratios_out: fp32[K]).
+ *   Its sums of p^2 and u^2 are grouped by other blocks than the fused step's, so a ratio may differ
+ *   from that step's in the last bit. */
 ob_status ob_adam_worker_compress(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
                                   uint32_t* words_out, float* scales_out, int8_t* signs_out,
                                   uint64_t* nonfinite_out, const ob_hparams* hp, hipStream_t stream);
 ob_status ob_adam_worker_update(ob_plan plan, const uint32_t* words, const float* scales, float* m,
                                 const float* v, float* p, const ob_hparams* hp, hipStream_t stream);
+ob_status ob_lamb_worker_update(ob_plan plan, const uint32_t* words, const float* scales, float* m,
+                                const float* v, float* p, float* ratios_out, const ob_hparams* hp,
+                                hipStream_t stream);
 
 /* Pack signs of x (OB_F32 or OB_BF16, n elements) into ceil(n/32) words ([P2] one_bit_quantize, sign part). */
 ob_status ob_pack(const void* x, ob_dtype x_dtype, int64_t n, uint32_t* words_out, hipStream_t stream);

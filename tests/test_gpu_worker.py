@@ -191,3 +191,94 @@ def test_data_parallel_round(W):
             P.assert_f32_close(synth.host(d_m), m, f"{tag}: m", 0.1 * ds)
             P.assert_f32_close(synth.host(d_p), p, f"{tag}: p", 1e-4 * 0.1 * ds / (np.sqrt(v.astype(np.float64)) + 1e-8))
     assert compared >= 1, "every step had a worker scale an ulp apart; nothing past the workers was compared"
+
+
+# ------------------------------------------------------------------------------------------------
+# 1-bit LAMB: the update half after the exchange (trust ratios on the exchanged direction)
+# ------------------------------------------------------------------------------------------------
+
+def _check_lamb_update(d_m, d_p, d_r, m, p, v, rr, off, lr, tag):
+    """m exact; ratios within 2 ulp (sums grouped by other blocks); p within lr * |dr| * |u|."""
+    assert np.array_equal(synth.host(d_m), m), f"{tag}: m"
+    gr = synth.host(d_r)
+    assert np.all(P.ulp_diff(gr, rr) <= 2), f"{tag}: ratios {gr} vs {rr}"
+    dr = np.repeat(np.abs(gr.astype(np.float64) - rr.astype(np.float64)), np.diff(off))
+    u = np.abs(m.astype(np.float64)) / (np.sqrt(v.astype(np.float64)) + np.float64(np.float32(1e-8)))
+    P.assert_f32_close(synth.host(d_p), p, f"{tag}: p", lr * dr * u)
+
+
+@pytest.mark.parametrize("n,chunk", [(130, 64), (4096 + 17, 1024), (1_000_003, 1 << 16), (5_000_000, 5_000_000 - 448)])
+def test_lamb_worker_update(n, chunk):
+    """The LAMB update from the oracle's exchanged words and scales, with a zero layer (r = 1)."""
+    gnp, err, m, v, p = _small_state(n, n + 5)
+    off = oracle.uniform_offsets(n, chunk)
+    p[int(off[0]):int(off[1])] = 0.0
+    plan = ob.ob_plan_create(n, chunk_size=chunk)
+    rw, rs, _, _ = oracle.worker_compress(gnp, err, off)
+    d_m, d_v, d_p = _t(m), _t(v), _t(p)
+    d_r = torch.full((off.size - 1,), -7.0, dtype=torch.float32, device=DEV)
+    ob.ob_lamb_worker_update(plan, _t(rw), _t(rs), d_m, d_v, d_p, d_r, ob.hparams(**HP))
+    rr = oracle.lamb_worker_update(rw, rs, m, v, p, off, **HP)
+    assert rr[0] == 1.0
+    _check_lamb_update(d_m, d_p, d_r, m, p, v, rr, off, HP["lr"], f"lamb worker update n={n}")
+
+
+@pytest.mark.parametrize("W", [1, 4])
+def test_lamb_data_parallel_round(W):
+    """1-bit LAMB with W workers through the server reduce on one GPU, two steps against the oracle."""
+    n, chunk = 1_000_003, 1 << 16
+    off = oracle.uniform_offsets(n, chunk)
+    K = off.size - 1
+    plan = ob.ob_plan_create(n, chunk_size=chunk)
+    rng = np.random.default_rng(100 + W)
+    errs = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for _ in range(W)]
+    _, _, m, v, p = _small_state(n, 92)
+    e_srv = np.zeros(n, np.float32)
+    hp = ob.hparams(**HP)
+    for st in range(2):
+        grads = [(rng.standard_normal(n) * 1e-3).astype(np.float32) for _ in range(W)]
+        ww = np.zeros((W, (n + 31) // 32), np.uint32)
+        ws = np.zeros((W, K), np.float32)
+        for w_ in range(W):
+            ww[w_], ws[w_], _, _ = oracle.worker_compress(grads[w_], errs[w_], off)
+        gw, gs = oracle.server_reduce(ww, ws, e_srv, off)
+        # the GPU update from the oracle's server words (the worker and server kernels are covered above)
+        d_m, d_v, d_p = _t(m), _t(v), _t(p)
+        d_r = torch.zeros(K, dtype=torch.float32, device=DEV)
+        ob.ob_lamb_worker_update(plan, _t(gw), _t(gs), d_m, d_v, d_p, d_r, hp)
+        rr = oracle.lamb_worker_update(gw, gs, m, v, p, off, **HP)
+        _check_lamb_update(d_m, d_p, d_r, m, p, v, rr, off, HP["lr"], f"LAMB W={W} step {st}")
+        # the next step starts from the oracle's state (p within the bound above)
+
+
+def test_one_worker_lamb_split_matches_fused_step():
+    """At one worker the LAMB split gives the fused LAMB step's words, scales, errors and m bit for bit;
+    ratios within 2 ulp and p within the resulting bound (the norms' sums are grouped differently)."""
+    w = synth.BERT_BASE
+    n = w.n
+    plan = ob.ob_plan_create(n, chunk_offsets=w.offsets)
+    off = w.chunk_offsets()
+    err, m, v, p = synth.draw_state(w, DEV)
+    g = synth.draw_grad(w, 0, DEV)
+    hp = ob.hparams(**HP)
+    K = plan.num_chunks
+    res = []
+    for split in (False, True):
+        e, mm, pp = err.clone(), m.clone(), p.clone()
+        words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+        scales = torch.zeros(K, dtype=torch.float32, device=DEV)
+        ratios = torch.zeros(K, dtype=torch.float32, device=DEV)
+        if split:
+            ob.ob_adam_worker_compress(plan, g, e, words, scales, hp)
+            ob.ob_lamb_worker_update(plan, words, scales, mm, v, pp, ratios, hp)
+        else:
+            ob.ob_lamb_compress_step(plan, g, e, mm, v, pp, words, scales, ratios, hp)
+        torch.cuda.synchronize()
+        res.append([synth.host(t) for t in (words, scales, e, mm, pp, ratios)])
+    (w0, s0, e0, m0, p0, r0), (w1, s1, e1, m1, p1, r1) = res
+    for name, a, b in (("words", w0, w1), ("scales", s0, s1), ("err", e0, e1), ("m", m0, m1)):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"{name} differs between split and fused"
+    assert np.all(P.ulp_diff(r1, r0) <= 2), "ratios"
+    dr = np.repeat(np.abs(r1.astype(np.float64) - r0.astype(np.float64)), np.diff(off))
+    u = np.abs(m0.astype(np.float64)) / (np.sqrt(synth.host(v).astype(np.float64)) + np.float64(np.float32(1e-8)))
+    P.assert_f32_close(p1, p0, "p", HP["lr"] * dr * u)
