@@ -324,7 +324,7 @@ def main():
 
 def _short(name: str) -> str:
     for key in ("k_chunk_sumsq", "k_compress", "k_dense", "k_server", "k_unpack", "k_pack", "k_lamb_apply",
-                "k_trust_ratio", "k_diag_reduce", "k_scale_finalize"):
+                "k_trust_ratio", "k_diag_reduce", "k_scale_finalize", "k_worker_compress", "k_worker_update"):
         if key in name:
             tmpl = name.split(key, 1)[1]
             return key + (tmpl[:60] if tmpl else "")

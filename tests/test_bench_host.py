@@ -1,0 +1,65 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU guard, the algorithmic bytes per element, the
+step's compulsory bytes, and the committed rocprofv3 summaries it reads."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from adam_ob_compress_amd import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU only" in r.stderr
+
+
+@pytest.mark.parametrize("name,kernel,want", [
+    ("bert-base-110M-fp32", "compress", 32.125),          # g err m v p in, err m p out, one bit
+    ("gpt2-1.5B-bf16", "compress", 30.125),               # bf16 g
+    ("llama2-7B-bf16-ema", "compress", 31.125),           # bf16 g, + int8 sign
+    ("bert-base-110M-fp32-err-bf16", "compress", 28.125),  # 16-bit error buffer
+    ("bert-base-110M-fp32", "chunk_sumsq", 8.0),
+    ("bert-base-110M-fp32", "dense", 28.0),
+    ("gpt2-1.5B-bf16", "dense", 26.0),
+    ("bert-base-110M-fp32", "worker_compress", 12.125),
+    ("bert-base-110M-fp32", "worker_update", 20.125),
+    ("bert-base-110M-fp32-lamb", "worker_update", 16.125),
+    ("bert-base-110M-fp32-lamb", "compress", 24.125),     # LAMB pass 2: no p
+    ("bert-base-110M-fp32-lamb", "lamb_apply", 16.0),
+])
+def test_bytes_per_element(name, kernel, want):
+    assert bench.bytes_per_elem(synth.WORKLOADS[name], kernel) == want
+
+
+def test_worker_split_moves_one_more_bit_than_the_fused_pass_2():
+    w = synth.WORKLOADS["bert-base-110M-fp32"]
+    split = bench.bytes_per_elem(w, "worker_compress") + bench.bytes_per_elem(w, "worker_update")
+    assert split == bench.bytes_per_elem(w, "compress") + 0.125
+
+
+def test_step_compulsory_bytes():
+    w = synth.WORKLOADS["bert-base-110M-fp32"]
+    assert bench.step_compulsory_bytes(w, "compressed") == 32.125
+    assert bench.step_compulsory_bytes(w, "dense") == 28.0
+
+
+def test_committed_traffic_summaries_parse():
+    """Every profiles/traffic_*.md carries a machine-readable line whose bytes are close to the
+    algorithmic bytes (a large ratio would mean re-reads)."""
+    d = os.path.join(ROOT, "profiles")
+    files = [f for f in os.listdir(d) if f.startswith("traffic_")]
+    assert files
+    for f in files:
+        lines = [ln for ln in open(os.path.join(d, f)) if ln.startswith("traffic-json:")]
+        assert len(lines) == 1, f
+        rec = json.loads(lines[0].split(":", 1)[1])
+        assert 0.99 < rec["traffic_over_algorithmic"] < 1.05, (f, rec)
+        assert f == f"traffic_{rec['kernel']}_{rec['workload']}.md"
