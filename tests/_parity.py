@@ -152,69 +152,75 @@ def _oracle_dense(r, g, w, bias_correction, t):
 
 
 def oracle_step(refs, g_dev, w, kind, bias_correction=False, t=0, s=0):
-    gs = [synth.host(g_dev[r.a:r.b]) for r in refs]
-    for r in refs:
+    def one(r):
+        g = synth.host(g_dev[r.a:r.b])
         r.err_before = r.err.copy()
-    if kind == "compressed":
-        futs = [_POOL.submit(_oracle_compress, r, g, w, s) for r, g in zip(refs, gs)]
-    else:
-        futs = [_POOL.submit(_oracle_dense, r, g, w, bias_correction, t) for r, g in zip(refs, gs)]
-    for f in futs:
+        if kind == "compressed":
+            _oracle_compress(r, g, w, s)
+        else:
+            _oracle_dense(r, g, w, bias_correction, t)
+    for f in [_POOL.submit(one, r) for r in refs]:
         f.result()
 
 
 def compare_chunks(refs, w, kind, err, m, v, p, words=None, scales=None, signs=None, ratios=None,
                    diag=None):
     """Compare the GPU buffers on the checked chunks with the oracle; returns scale-ulp mismatches.
-    diag: (err_sumsq, plus_count) device arrays of a compressed step's diagnostics, or None."""
+    diag: (err_sumsq, plus_count) device arrays of a compressed step's diagnostics, or None.
+    Chunks are compared in parallel threads (numpy and the device-to-host copies release the GIL)."""
+    futs = [_POOL.submit(_compare_one, r, w, kind, err, m, v, p, words, scales, signs, ratios, diag)
+            for r in refs]
+    return sum(f.result() for f in futs)
+
+
+def _compare_one(r, w, kind, err, m, v, p, words, scales, signs, ratios, diag):
     mism = 0
     b1 = np.float64(np.float32(w.beta1))
     eb = np.float64(np.float32(w.ef_beta))
     lr = np.float64(np.float32(w.lr))
     eps = np.float64(np.float32(w.eps))
-    for r in refs:
-        tag = f"{w.name} chunk {r.c} [{r.a},{r.b}) {kind}"
-        ge, gm, gv, gp = (synth.host(t[r.a:r.b]) for t in (err, m, v, p))
-        ds = 0.0
-        if kind == "compressed":
-            ws = synth.host(words[r.a // 32:(r.b + 31) // 32])
-            assert np.array_equal(ws, r.out["words"]), f"{tag}: packed words differ"
-            sc = np.float32(scales[r.c].item())
-            d = int(ulp_diff(sc, r.out["scale"]))
-            assert d <= 1 or (np.isnan(sc) and np.isnan(r.out["scale"])), \
-                f"{tag}: scale {sc!r} vs {r.out['scale']!r} ({d} ulp)"
-            if d == 1:
-                mism += 1
-                ds = abs(float(sc) - float(r.out["scale"]))
-            if signs is not None:
-                assert np.array_equal(synth.host(signs[r.a:r.b]), r.out["signs"]), f"{tag}: int8 signs differ"
-            if diag is not None:
-                rss, rpc = oracle.diagnostics(r.err_before, r.out["words"], np.asarray([0, r.b - r.a], np.int64))
-                gss = float(diag[0][r.c].item())
-                assert abs(gss - rss[0]) <= 1e-10 * rss[0], f"{tag}: error norm^2 {gss} vs {rss[0]}"
-                assert int(diag[1][r.c].item()) == int(rpc[0]), f"{tag}: +1 count"
-            assert np.array_equal(gv, r.v), f"{tag}: v changed in the compressed step"
-            if w.err_rounding == "stochastic" and d == 0:
-                # same scale -> the same fp32 new error and the same random bits on both sides
-                assert np.array_equal(ge.view(np.uint16), r.err.view(np.uint16)), \
-                    f"{tag}: stochastically rounded error differs"
-        else:
-            assert_f32_close(gv, r.v, f"{tag}: v")
-        err_slack = ds * ((1 - eb) if w.ef_mode == 1 else 1.0)
-        m_slack = ds * (1 - b1)
-        den = np.sqrt(r.v.astype(np.float64)) + eps
-        p_slack = lr * m_slack / den if ds else 0.0
-        if w.optimizer == "lamb":
-            rg, rr = np.float32(ratios[r.c].item()), np.float32(r.out["ratio"])
-            dr_ulp = int(ulp_diff(rg, rr))
-            assert dr_ulp <= (2 if ds else 1) or (np.isnan(rg) and np.isnan(rr)), \
-                f"{tag}: trust ratio {rg!r} vs {rr!r} ({dr_ulp} ulp)"
-            dr = abs(float(rg) - float(rr)) if np.isfinite(rr) else 0.0
-            u = np.abs(r.m.astype(np.float64)) / den     # run_workload's steps have no bias correction
-            p_slack = float(abs(rr)) * p_slack + lr * dr * u
-        assert_err_close(ge, r.err, f"{tag}: err", err_slack)
-        assert_f32_close(gm, r.m, f"{tag}: m", m_slack)
-        assert_f32_close(gp, r.p, f"{tag}: p", p_slack)
+    tag = f"{w.name} chunk {r.c} [{r.a},{r.b}) {kind}"
+    ge, gm, gv, gp = (synth.host(t[r.a:r.b]) for t in (err, m, v, p))
+    ds = 0.0
+    if kind == "compressed":
+        ws = synth.host(words[r.a // 32:(r.b + 31) // 32])
+        assert np.array_equal(ws, r.out["words"]), f"{tag}: packed words differ"
+        sc = np.float32(scales[r.c].item())
+        d = int(ulp_diff(sc, r.out["scale"]))
+        assert d <= 1 or (np.isnan(sc) and np.isnan(r.out["scale"])), \
+            f"{tag}: scale {sc!r} vs {r.out['scale']!r} ({d} ulp)"
+        if d == 1:
+            mism += 1
+            ds = abs(float(sc) - float(r.out["scale"]))
+        if signs is not None:
+            assert np.array_equal(synth.host(signs[r.a:r.b]), r.out["signs"]), f"{tag}: int8 signs differ"
+        if diag is not None:
+            rss, rpc = oracle.diagnostics(r.err_before, r.out["words"], np.asarray([0, r.b - r.a], np.int64))
+            gss = float(diag[0][r.c].item())
+            assert abs(gss - rss[0]) <= 1e-10 * rss[0], f"{tag}: error norm^2 {gss} vs {rss[0]}"
+            assert int(diag[1][r.c].item()) == int(rpc[0]), f"{tag}: +1 count"
+        assert np.array_equal(gv, r.v), f"{tag}: v changed in the compressed step"
+        if w.err_rounding == "stochastic" and d == 0:
+            # same scale -> the same fp32 new error and the same random bits on both sides
+            assert np.array_equal(ge.view(np.uint16), r.err.view(np.uint16)), \
+                f"{tag}: stochastically rounded error differs"
+    else:
+        assert_f32_close(gv, r.v, f"{tag}: v")
+    err_slack = ds * ((1 - eb) if w.ef_mode == 1 else 1.0)
+    m_slack = ds * (1 - b1)
+    den = np.sqrt(r.v.astype(np.float64)) + eps
+    p_slack = lr * m_slack / den if ds else 0.0
+    if w.optimizer == "lamb":
+        rg, rr = np.float32(ratios[r.c].item()), np.float32(r.out["ratio"])
+        dr_ulp = int(ulp_diff(rg, rr))
+        assert dr_ulp <= (2 if ds else 1) or (np.isnan(rg) and np.isnan(rr)), \
+            f"{tag}: trust ratio {rg!r} vs {rr!r} ({dr_ulp} ulp)"
+        dr = abs(float(rg) - float(rr)) if np.isfinite(rr) else 0.0
+        u = np.abs(r.m.astype(np.float64)) / den     # run_workload's steps have no bias correction
+        p_slack = float(abs(rr)) * p_slack + lr * dr * u
+    assert_err_close(ge, r.err, f"{tag}: err", err_slack)
+    assert_f32_close(gm, r.m, f"{tag}: m", m_slack)
+    assert_f32_close(gp, r.p, f"{tag}: p", p_slack)
     return mism
 
 
