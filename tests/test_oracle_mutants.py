@@ -5,6 +5,7 @@ term, a wrong sign or index, a transposed operand, a wrong constant), builds it 
 flags and runs tests/test_oracle.py against that copy in a subprocess.  The real oracle is never
 modified.  CPU only.
 """
+import concurrent.futures as cf
 import os
 import subprocess
 import sys
@@ -116,26 +117,41 @@ MUTANTS = {
 }
 
 
-@pytest.fixture(scope="module")
-def workdir():
-    with tempfile.TemporaryDirectory(prefix="ob_mutants_") as d:
-        yield d
-
-
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_planted_mistake_is_caught(name, workdir):
+def _run_mutant(name, workdir):
+    """Build the oracle with the planted mistake and run the pin suite against it; returns the
+    pytest subprocess's exit code and the end of its output."""
     old, new, *count = MUTANTS[name]
     count = count[0] if count else 1
     src = open(SRC).read()
-    assert src.count(old) == count, f"mutation anchor for {name} does not match {count} time(s)"
+    if src.count(old) != count:
+        return None, f"mutation anchor for {name} does not match {count} time(s)"
     csrc = os.path.join(workdir, f"{name}.c")
     lib = os.path.join(workdir, f"lib_{name}.so")
     with open(csrc, "w") as f:
         f.write(src.replace(old, new))
     subprocess.run(["gcc", *oracle.CFLAGS, "-o", lib, csrc, "-lm"], check=True,
                    stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
-    env = dict(os.environ, OB_ORACLE_LIB=lib)
+    env = dict(os.environ, OB_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle.py")],
                        cwd=ROOT, env=env, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    assert r.returncode != 0, f"planted mistake '{name}' passed every pin:\n{r.stdout[-2000:]}"
+    return r.returncode, r.stdout[-2000:]
+
+
+@pytest.fixture(scope="module")
+def mutant_runs():
+    """Every mutant's run, started on first use and run several at a time (each is an independent
+    subprocess); a test waits only for its own mutant."""
+    with tempfile.TemporaryDirectory(prefix="ob_mutants_") as d, \
+            cf.ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1))) as pool:
+        futs = {name: pool.submit(_run_mutant, name, d) for name in sorted(MUTANTS)}
+        yield futs
+        for f in futs.values():
+            f.cancel()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, mutant_runs):
+    rc, out = mutant_runs[name].result()
+    assert rc is not None, out
+    assert rc != 0, f"planted mistake '{name}' passed every pin:\n{out}"
