@@ -46,9 +46,17 @@ constexpr int kPlainItem = 16 * kTile;  // elements per block for the plan-less 
 #ifndef OB_NT_DENSE
 #define OB_NT_DENSE 1
 #endif
-//   OB_SRV_UNROLL / OB_UNPACK_UNROLL  tiles in flight per loop trip in the server passes / unpack
+//   OB_SRV_UNROLL / OB_SRV2_UNROLL / OB_UNPACK_UNROLL  tiles in flight per loop trip in server
+//                                 pass 1 / server pass 2 / unpack
+//   OB_NT_SRV_WORDS               nontemporal loads of the worker words in server pass 1
 #ifndef OB_SRV_UNROLL
-#define OB_SRV_UNROLL 4
+#define OB_SRV_UNROLL 8
+#endif
+#ifndef OB_SRV2_UNROLL
+#define OB_SRV2_UNROLL 4
+#endif
+#ifndef OB_NT_SRV_WORDS
+#define OB_NT_SRV_WORDS OB_NT_SRV
 #endif
 #ifndef OB_UNPACK_UNROLL
 #define OB_UNPACK_UNROLL 4

@@ -347,24 +347,64 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
     const int tid = threadIdx.x;
     const int c = it.chunk;
     const bool tabulate = W <= kWorkerBatch;
+    constexpr bool NTS = (!APPLY && OB_NT_SRV) || (APPLY && OB_NT_SRV2);
+    constexpr bool NTW = (!APPLY && OB_NT_SRV_WORDS) || (APPLY && OB_NT_SRV2);
+    constexpr int U = APPLY ? OB_SRV2_UNROLL : OB_SRV_UNROLL;
+    // lane j of each 8-lane group loads worker j's word of the group's 32 elements (worker index
+    // clamped to W-1; the surplus nibbles are masked off after the transpose)
+    const int wc = (tid & 7) < W ? (tid & 7) : W - 1;
+    const uint32_t* __restrict__ wrow = ww + static_cast<int64_t>(wc) * nw;
+    auto load_word = [&](int64_t i) -> uint32_t {
+        const uint32_t* wp = wrow + (i >> 5);
+        return NTW ? __builtin_nontemporal_load(wp) : *wp;
+    };
+    f4 grp_e[U];
+    uint32_t grp_w[U];
+    auto load_group = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + b + u * kTile + kVec * tid;
+            grp_e[u] = ld4<NTS>(e, i);
+            grp_w[u] = tabulate ? load_word(i) : 0u;
+        }
+    };
+    // Prologue, ordered so that its latency overlaps the first tiles' loads: the chunk's worker scales
+    // (pass 2: and the chunk's pass-1 partials) are loaded first, then the block's first group of
+    // tiles; the table of averages (pass 2: and the scale) is formed while the tiles are in flight.
+    // The table adds +-s_w in ascending w and the scale adds the chunk's partials in chunk_scale's
+    // order, so every block of a chunk forms the same bits.
+    float sc[kWorkerBatch];
+#pragma unroll
+    for (int w = 0; w < kWorkerBatch; ++w) sc[w] = (tabulate && w < W) ? ws[static_cast<int64_t>(w) * pd.K + c] : 0.0f;
+    double part = 0.0;
+    if (APPLY) {
+        const int f0 = pd.p1_first[c], f1 = pd.p1_first[c + 1];
+        for (int j = f0 + tid; j < f1; j += kBlock) part += pd.partials[j];
+    }
+    if (U * kTile <= it.len) load_group(0);
     if (tabulate) {
         const bool pow2 = (W & (W - 1)) == 0;
         for (int pat = tid; pat < (1 << W); pat += kBlock) {
             double a = 0.0;
-            for (int w = 0; w < W; ++w) {
-                const double s = static_cast<double>(ws[static_cast<int64_t>(w) * pd.K + c]);
+#pragma unroll
+            for (int w = 0; w < kWorkerBatch; ++w) {
+                if (w >= W) break;
+                const double s = static_cast<double>(sc[w]);
                 a += ((pat >> w) & 1) ? s : -s;
             }
             table[pat] = static_cast<float>(pow2 ? a * (1.0 / static_cast<double>(W)) : a / static_cast<double>(W));
         }
-        __syncthreads();
     }
     float scale = 0.0f;
     if (APPLY) {
-        scale = chunk_scale(pd, c, lds);
+        // block_sum's barriers also publish the table
+        const double s = block_sum(part, lds);
+        const int64_t nc = pd.chunk_off[c + 1] - pd.chunk_off[c];
+        scale = static_cast<float>(sqrt(s / static_cast<double>(nc)));
         if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[c]) scales[c] = scale;
+    } else if (tabulate) {
+        __syncthreads();
     }
-    constexpr bool NTS = (!APPLY && OB_NT_SRV) || (APPLY && OB_NT_SRV2);
     double acc = 0.0;
     // One tile's worth: given the error and (W <= 8) the lane's worker word, form x = avg + e, then
     // the sum of squares (pass 1) or the new error and sign nibble (pass 2).
@@ -417,30 +457,15 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
         }
         return nib;
     };
-    // lane j of each 8-lane group loads worker j's word of the group's 32 elements (worker index
-    // clamped to W-1; the surplus nibbles are masked off after the transpose)
-    const int wc = (tid & 7) < W ? (tid & 7) : W - 1;
-    const uint32_t* __restrict__ wrow = ww + static_cast<int64_t>(wc) * nw;
-    auto load_word = [&](int64_t i) -> uint32_t {
-        const uint32_t* wp = wrow + (i >> 5);
-        return NTS ? __builtin_nontemporal_load(wp) : *wp;
-    };
-    // whole tiles, OB_SRV_UNROLL in flight: all their loads are issued before any is used
-    constexpr int U = OB_SRV_UNROLL;
+    // whole tiles, U in flight: all their loads are issued before any is used (the first
+    // group's in the prologue)
     int base = 0;
     for (; base + U * kTile <= it.len; base += U * kTile) {
-        f4 ev[U];
-        uint32_t wd[U];
+        if (base > 0) load_group(base);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = it.start + base + u * kTile + kVec * tid;
-            ev[u] = ld4<NTS>(e, i);
-            wd[u] = tabulate ? load_word(i) : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = it.start + base + u * kTile + kVec * tid;
-            const uint32_t nib = tile(i, kVec, ev[u], wd[u]);
+            const uint32_t nib = tile(i, kVec, grp_e[u], grp_w[u]);
             if (APPLY) store_word(words, i, nib, true);
         }
     }
