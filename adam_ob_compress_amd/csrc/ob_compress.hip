@@ -141,29 +141,8 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
             if (!LAMB) pv[u] = ld4<OB_NT_P2>(p, i);
         }
     };
-    // The chunk's scale: the chunk's pass-1 partials are loaded, then the block's first group of
-    // tiles, and only then are the partials reduced, so that the reduction overlaps the tile loads
-    // (the partial loads all precede the tile loads: the in-order load counter then lets the
-    // reduction wait for the partials alone).  The sum order, and so every block's scale bits, are
-    // those of chunk_scale.
-    float scale;
-    {
-        const int c = it.chunk;
-        const int f0 = pd.p1_first[c], f1 = pd.p1_first[c + 1];
-        double s = f0 + tid < f1 ? pd.partials[f0 + tid] : 0.0;
-        if (f1 - f0 > kBlock)
-            for (int j = f0 + tid + kBlock; j < f1; j += kBlock) s += pd.partials[j];
-        const int64_t nc = pd.chunk_off[c + 1] - pd.chunk_off[c];
-        auto reduce = [&]() { return static_cast<float>(sqrt(block_sum(s, lds) / static_cast<double>(nc))); };
-        // (two copies of the reduction, so that the load counter's wait on the path with the tile
-        // loads in flight covers the partials alone)
-        if (U * kTile <= it.len) {
-            load_group(0);
-            scale = reduce();
-        } else {
-            scale = reduce();
-        }
-    }
+    // the chunk's scale, reduced while the block's first group of tiles is in flight
+    const float scale = chunk_scale_overlapped(pd, it.chunk, lds, U * kTile <= it.len, [&] { load_group(0); });
     if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
 
     uint32_t nf = 0, plus = 0;
@@ -278,18 +257,22 @@ __global__ __launch_bounds__(kBlock) void k_worker_compress(PlanDev pd, const ty
     const Item it = pd.items[blockIdx.x];
     const int tid = threadIdx.x;
     constexpr int U = OB_P2_UNROLL;
-    const float scale = chunk_scale(pd, it.chunk, lds);
+    f4 gv[U], ev[U];
+    auto load_group = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = it.start + b + u * kTile + kVec * tid;
+            gv[u] = G::template load4<OB_NT_P2>(g, i);
+            ev[u] = E::template load4<OB_NT_P2>(err, i);
+        }
+    };
+    // the chunk's scale, reduced while the block's first group of tiles is in flight
+    const float scale = chunk_scale_overlapped(pd, it.chunk, lds, U * kTile <= it.len, [&] { load_group(0); });
     if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
     uint32_t nf = 0;
     int base = 0;
     for (; base + U * kTile <= it.len; base += U * kTile) {
-        f4 gv[U], ev[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t i = it.start + base + u * kTile + kVec * tid;
-            gv[u] = G::template load4<OB_NT_P2>(g, i);
-            ev[u] = E::template load4<OB_NT_P2>(err, i);
-        }
+        if (base > 0) load_group(base);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = it.start + base + u * kTile + kVec * tid;

@@ -458,5 +458,29 @@ __device__ __forceinline__ float chunk_scale(const PlanDev& pd, int c, double* l
     return static_cast<float>(sqrt(s / static_cast<double>(nc)));
 }
 
+// chunk_scale with the first group of tile loads overlapped: the chunk's partials are loaded, then
+// `load_first()` issues the block's first tile loads (only when the block has a whole group), and
+// only then are the partials reduced.  The partial loads precede the tile loads, so the in-order load
+// counter lets the reduction wait for the partials alone.  The sum order, and so every block's scale
+// bits, are those of chunk_scale.
+template <class F>
+__device__ __forceinline__ float chunk_scale_overlapped(const PlanDev& pd, int c, double* lds, bool whole_group,
+                                                        F&& load_first)
+{
+    const int f0 = pd.p1_first[c], f1 = pd.p1_first[c + 1];
+    double s = f0 + static_cast<int>(threadIdx.x) < f1 ? pd.partials[f0 + threadIdx.x] : 0.0;
+    if (f1 - f0 > kBlock)
+        for (int j = f0 + static_cast<int>(threadIdx.x) + kBlock; j < f1; j += kBlock) s += pd.partials[j];
+    const int64_t nc = pd.chunk_off[c + 1] - pd.chunk_off[c];
+    auto reduce = [&]() { return static_cast<float>(sqrt(block_sum(s, lds) / static_cast<double>(nc))); };
+    // (two copies of the reduction, so that the load counter's wait on the path with the tile loads in
+    // flight covers the partials alone)
+    if (whole_group) {
+        load_first();
+        return reduce();
+    }
+    return reduce();
+}
+
 }  // namespace
 }  // namespace ob
