@@ -219,7 +219,8 @@ const char* ob_status_str(ob_status s);
 /* ---- kernel timing (measurement support) ----
  * With timing on, every call made with this plan records a hipEvent pair around each kernel it
  * launches, on the call's stream.  ob_plan_read_timing waits for the recorded events and returns the
- * summed milliseconds and launch count of one kernel kind since timing was switched on. */
+ * summed milliseconds and launch count of one kernel kind since timing was switched on.  The events
+ * are created with hipEventDisableSystemFence: they measure time only and order no memory. */
 typedef enum {
     OB_KERNEL_CHUNK_SUMSQ = 0,     /* compressed step (Adam or LAMB), pass 1 */
     OB_KERNEL_COMPRESS = 1,        /* compressed step (Adam or LAMB), pass 2 (fused streaming pass) */
