@@ -113,24 +113,26 @@ def cpu_baseline(w, seconds: float):
     from adam_ob_compress_amd import synth
 
     off = w.chunk_offsets()
-    # whole chunks from the start until ~2^27 elements (all of BERT-base)
+    # whole chunks from the start until ~2^27 elements (all of BERT-base); 2^25 for the server round,
+    # whose oracle runs ~8x slower per element (W workers' bits per element)
+    limit = (1 << 25) if w.workers else (1 << 27)
     K = 1
-    while K < w.n_chunks and off[K] < (1 << 27):
+    while K < w.n_chunks and off[K] < limit:
         K += 1
     n_s = int(off[K])
     sub = synth.scaled(w, n_s, w.chunk) if w.offsets is None else None
     if sub is None:
         import dataclasses
         sub = dataclasses.replace(w, n=n_s, offsets=tuple(int(o) for o in off[:K + 1]))
+    offs = sub.chunk_offsets()
+    if w.workers:
+        return _cpu_baseline_server(w, sub, K, offs, seconds)
     err, m, v, p = (synth.host(t) for t in synth.draw_state(sub, "cpu"))
     g = synth.host(synth.draw_grad(sub, 0, "cpu"))
-    offs = sub.chunk_offsets()
     times = []
     t_end = time.perf_counter() + seconds
     while len(times) < 2 or (time.perf_counter() < t_end and len(times) < 20):
         t0 = time.perf_counter()
-        if w.workers:
-            raise NotImplementedError
         step = oracle.lamb_compress_step if w.optimizer == "lamb" else oracle.compress_step
         sr = (dict(stochastic=True, sr_seed=synth.SR_SEED, sr_step=len(times))
               if w.err_rounding == "stochastic" else {})
@@ -141,6 +143,28 @@ def cpu_baseline(w, seconds: float):
     return {"value": n_s / t, "unit": "elements/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(times)} compressed steps of the oracle on the first {K} chunks "
                       f"({n_s} elements) of {w.name}, single thread, median step {t:.3f} s"}
+
+
+def _cpu_baseline_server(w, sub, K, offs, seconds):
+    import numpy as np
+
+    import oracle
+    from adam_ob_compress_amd import synth
+
+    ww = synth.host(synth.draw_worker_words(sub, 0, "cpu"))
+    ws = synth.host(synth.draw_worker_scales(sub, 0, "cpu"))
+    err = np.zeros(sub.n, np.float32)
+    times = []
+    t_end = time.perf_counter() + seconds
+    while len(times) < 2 or (time.perf_counter() < t_end and len(times) < 20):
+        t0 = time.perf_counter()
+        rw, rs = oracle.server_reduce(ww, ws, err, offs)
+        oracle.unpack(rw, sub.n, offs, rs)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": sub.n / t, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(times)} server rounds (reduce + unpack) of the oracle on the first {K} chunks "
+                      f"({sub.n} elements) of {w.name}, single thread, median round {t:.3f} s"}
 
 
 # ------------------------------------------------------------------------------------------------
@@ -154,10 +178,10 @@ def run(args):
     from adam_ob_compress_amd import schedule, synth
 
     w = synth.WORKLOADS[args.workload]
-    if w.workers:
-        raise SystemExit("bench.py times the optimizer step; the server workload is a parity case")
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if w.workers:
+        return w, run_server(args, w)
     plan = ob.ob_plan_create(w.n, chunk_size=w.chunk if w.offsets is None else 0, chunk_offsets=w.offsets)
     err, m, v, p = synth.draw_state(w, dev)
     ring = 1 if w.n > (1 << 31) else min(4, max(1, args.steps))
@@ -217,21 +241,7 @@ def run(args):
     ob.ob_plan_set_timing(plan, False)
 
     if args.copy_probe_mib:
-        nb = args.copy_probe_mib << 20
-        src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        for _ in range(5):
-            dst.copy_(src)
-        ev1.record()
-        torch.cuda.synchronize()
-        copy_gbps = 2 * nb / (ev0.elapsed_time(ev1) / 5 * 1e-3) / 1e9
-        kern["torch_copy_probe"] = {"bytes_per_launch": 2 * nb, "GBps": copy_gbps}
-        del src, dst
+        kern["torch_copy_probe"] = copy_probe(args.copy_probe_mib, dev)
 
     # the dominant kernel of the timed steps: the longest per launch (the fused pass 2 for 1-bit Adam)
     dom = max((k for k in ("compress", "lamb_apply", "worker_compress", "worker_update") if k in kern),
@@ -277,6 +287,104 @@ def run(args):
         "cpu_baseline": None,
     }
     return w, res
+
+
+def copy_probe(mib: int, dev: str) -> dict:
+    """A plain torch copy of `mib` MiB (3 untimed + 5 timed): the counters' calibration run, and a
+    practical bandwidth reference."""
+    import torch
+
+    nb = mib << 20
+    src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    return {"bytes_per_launch": 2 * nb, "GBps": 2 * nb / (ev0.elapsed_time(ev1) / 5 * 1e-3) / 1e9}
+
+
+def run_server(args, w):
+    """One "step" is a server round on one GPU's share: ob_server_reduce over W workers' packed signs
+    and scales (pass 1 + pass 2), then ob_unpack of the re-packed result.  W rows of words and scales
+    are pre-drawn for two rounds and alternated; the server error carries across rounds."""
+    import torch
+
+    import adam_ob_compress_amd as ob
+    from adam_ob_compress_amd import synth
+
+    dev = "cuda:0"
+    plan = ob.ob_plan_create(w.n, chunk_size=w.chunk)
+    K = plan.num_chunks
+    ww = [synth.draw_worker_words(w, r, dev) for r in range(2)]
+    ws = [synth.draw_worker_scales(w, r, dev) for r in range(2)]
+    err = torch.zeros(w.n, dtype=torch.float32, device=dev)
+    words = torch.empty((w.n + 31) // 32, dtype=torch.int32, device=dev)
+    scales = torch.empty(K, dtype=torch.float32, device=dev)
+    out = torch.empty(w.n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    print(f"# {w.name}: n={w.n} W={w.workers} chunks={K}", file=sys.stderr, flush=True)
+
+    def rnd(r):
+        ob.ob_server_reduce(plan, ww[r % 2], ws[r % 2], err, words, scales, stream)
+        ob.ob_unpack(plan, words, w.n, out, scales, stream)
+
+    for r in range(args.warmup):
+        rnd(r)
+    torch.cuda.synchronize()
+    ob.ob_plan_set_timing(plan, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(args.steps):
+        rnd(r)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern = {}
+    for kid, name in ob.KERNEL_NAMES.items():
+        ms, cnt = ob.ob_plan_read_timing(plan, kid)
+        if cnt:
+            kern[name] = {"avg_ms": ms / cnt, "launches": cnt,
+                          "GBps": bytes_per_elem(w, name) * w.n / (ms / cnt * 1e-3) / 1e9}
+    ob.ob_plan_set_timing(plan, False)
+    if args.copy_probe_mib:
+        kern["torch_copy_probe"] = copy_probe(args.copy_probe_mib, dev)
+    dom = max((k for k in ("server_sumsq", "server_apply", "unpack") if k in kern),
+              key=lambda k: kern[k]["avg_ms"])
+    bpe = bytes_per_elem(w, dom)
+    achieved = bpe * w.n / (kern[dom]["avg_ms"] * 1e-3) / 1e9
+    step_gbps = step_compulsory_bytes(w, "server") * w.n / (ms_per_step * 1e-3) / 1e9
+    return {
+        "metric": METRIC,
+        "value": w.n / (ms_per_step * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32 sign words + f32 scales and error",
+        "data": "synthetic (seeded; two pre-drawn rounds of worker words and scales)",
+        "config": {"workload": w.name, "elements": w.n, "chunks": K, "workers": w.workers,
+                   "step": "server round: ob_server_reduce (2 passes) + ob_unpack"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "bytes_per_elem": bpe, "traffic": load_traffic(dom, w.name)},
+        "step_compulsory_GBps": step_gbps,
+        "step_hbm_frac": step_gbps / PEAK_HBM_GBPS,
+        "timed_step_kinds": {"server_round": args.steps},
+        "dense_step_ms": None,
+        "kernels": kern,
+        "kernel_src_sha": kernel_source_sha(),
+        "cpu_baseline": None,
+    }
 
 
 def main():

@@ -34,6 +34,9 @@ def test_more_than_one_gpu_exits_with_a_message():
     ("bert-base-110M-fp32-lamb", "worker_update", 16.125),
     ("bert-base-110M-fp32-lamb", "compress", 24.125),     # LAMB pass 2: no p
     ("bert-base-110M-fp32-lamb", "lamb_apply", 16.0),
+    ("server-2^28-W8", "server_sumsq", 5.0),              # W = 8 sign bits + the server error
+    ("server-2^28-W8", "server_apply", 9.125),            # + the new error and one bit out
+    ("server-2^28-W8", "unpack", 4.125),
 ])
 def test_bytes_per_element(name, kernel, want):
     assert bench.bytes_per_elem(synth.WORKLOADS[name], kernel) == want
@@ -49,6 +52,15 @@ def test_step_compulsory_bytes():
     w = synth.WORKLOADS["bert-base-110M-fp32"]
     assert bench.step_compulsory_bytes(w, "compressed") == 32.125
     assert bench.step_compulsory_bytes(w, "dense") == 28.0
+    # a server round: W bits + error in, error + 1 bit out; then 1 bit in, fp32 out
+    assert bench.step_compulsory_bytes(synth.WORKLOADS["server-2^28-W8"], "server") == 13.25
+
+
+# Server pass 1 fetches each worker-word line about 1.6 times (nontemporal loads; the four waves of a
+# block each read a quarter of every 128-byte line): 5.64 instead of 5 B per element.  Temporal word
+# loads (5.005 B) and a wave-major mapping (5.20 B) both fetch less and both run slower, so the
+# kernel keeps the extra fetch; its bound is relaxed here and nowhere else.
+MAX_TRAFFIC_RATIO = {"server_sumsq": 1.15}
 
 
 def test_committed_traffic_summaries_parse():
@@ -61,5 +73,5 @@ def test_committed_traffic_summaries_parse():
         lines = [ln for ln in open(os.path.join(d, f)) if ln.startswith("traffic-json:")]
         assert len(lines) == 1, f
         rec = json.loads(lines[0].split(":", 1)[1])
-        assert 0.99 < rec["traffic_over_algorithmic"] < 1.05, (f, rec)
+        assert 0.99 < rec["traffic_over_algorithmic"] < MAX_TRAFFIC_RATIO.get(rec["kernel"], 1.05), (f, rec)
         assert f == f"traffic_{rec['kernel']}_{rec['workload']}.md"
