@@ -615,6 +615,76 @@ def test_deterministic():
     assert var["signs"]
 
 
+@pytest.mark.parametrize("optimizer", ["adam", "lamb"])
+def test_resume_is_bit_identical(optimizer):
+    """Checkpoint / resume: the whole optimizer state is the caller's buffers (err, m, v, p, the
+    non-finite counter) plus the schedule's step counters; the plan holds none of it.  Run 4 steps and
+    save that state to the host, run 4 more; then restore it into fresh buffers with a fresh plan and
+    optimizer and run the same 4 steps: every output of every step is bit-identical.  The schedule
+    crosses the freeze step and a refresh step, and the error buffer is bf16 with stochastic
+    rounding, whose random stream follows the step index."""
+    from adam_ob_compress_amd import schedule
+
+    n, chunk = 1_000_003, 1 << 16
+    cls = schedule.OneBitLamb if optimizer == "lamb" else schedule.OneBitAdam
+    kw = dict(lr=1e-4, clip=5.0, ef_mode=ob.OB_EF_EMA, ef_beta=0.9, int8_signs=True, count_nonfinite=True,
+              freeze_step=2, refresh_period=5, err_rounding="stochastic", sr_seed=0x5EED)
+    gen = torch.Generator(device=DEV)
+    grads = []
+    for s in range(8):
+        gen.manual_seed(1000 + s)
+        grads.append(torch.randn(n, generator=gen, device=DEV) * 1e-3)
+    gen.manual_seed(7)
+    err0 = (torch.randn(n, generator=gen, device=DEV) * 1e-4).to(torch.bfloat16)
+    m0 = torch.zeros(n, device=DEV)
+    v0 = torch.zeros(n, device=DEV)
+    p0 = torch.randn(n, generator=gen, device=DEV) * 0.02
+
+    def outputs(opt, kind):
+        """What a step of this kind writes (a dense step leaves the sign outputs alone)."""
+        out = [opt.err, opt.m, opt.v, opt.p, opt.nonfinite]
+        if kind == "compressed":
+            out += [opt.words, opt.scales, opt.signs]
+        if optimizer == "lamb":
+            out.append(opt.ratios)
+        return [synth.host(t) for t in out]
+
+    def make(state, counters):
+        plan = ob.ob_plan_create(n, chunk_size=chunk)
+        bufs = [torch.from_numpy(a.copy()).to(DEV) for a in state[:4]]
+        bufs[0] = bufs[0].view(torch.bfloat16)          # saved as the bf16 bits (int16)
+        opt = cls(plan, *bufs, **kw)
+        opt.nonfinite.copy_(torch.from_numpy(state[4].astype(np.int64)))
+        opt.step_index, opt.dense_steps = counters
+        return plan, opt
+
+    def save(opt):
+        st = [synth.host(t) for t in (opt.err, opt.m, opt.v, opt.p, opt.nonfinite)]
+        st[0] = st[0].view(np.int16)
+        return st, (opt.step_index, opt.dense_steps)
+
+    plan = ob.ob_plan_create(n, chunk_size=chunk)
+    opt = cls(plan, err0.clone(), m0.clone(), v0.clone(), p0.clone(), **kw)
+    kinds = [opt.step(g) for g in grads[:4]]
+    torch.cuda.synchronize()
+    state, counters = save(opt)
+    ref = []
+    for g in grads[4:]:
+        kinds.append(opt.step(g))
+        torch.cuda.synchronize()
+        ref.append(outputs(opt, kinds[-1]))
+    assert kinds == ["dense", "dense", "compressed", "compressed", "dense", "compressed", "compressed",
+                     "compressed"]
+
+    plan2, opt2 = make(state, counters)
+    for k, g in enumerate(grads[4:]):
+        kind = opt2.step(g)
+        assert kind == kinds[4 + k]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(ref[k], outputs(opt2, kind))):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f"step {4 + k}, output {i}"
+
+
 def test_kernel_timing_api():
     n = 1 << 20
     plan = ob.ob_plan_create(n, chunk_size=1 << 18)
