@@ -106,7 +106,9 @@ struct DeviceGuard {
 
 // Block tables by kernel kind.  Elements per block (from sweeps of 1-128 tiles of 1024 on MI355X):
 //   pass 1 (sums of squares): large blocks, so a chunk has few partial sums: enough blocks to fill
-//     256 CUs several times over, whole tiles, at most 64 tiles;
+//     256 CUs several times over, whole tiles, at most 24 tiles (measured: with 64-tile pass-1 blocks
+//     the pass 2 that follows ran 2% slower on 1.5G- and 6.7G-element buffers, 0.5% on the latter's
+//     whole step; 8-tile blocks slowed pass 1 itself);
 //   compressed pass 2: 4 tiles;  dense step: 2 tiles;  server pass 2 and unpack: 8 tiles.
 // Environment overrides for tuning sweeps (multiples of 1024): OB_BLOCK_ELEMS, OB_BLOCK_ELEMS2,
 // OB_BLOCK_ELEMS_DENSE, OB_BLOCK_ELEMS_SERVER.
@@ -131,7 +133,7 @@ int64_t choose_block_elems(int64_t n, int table)
     const int64_t target_blocks = 8192;
     int64_t e = (n + target_blocks - 1) / target_blocks;
     e = (e + ob::kTile - 1) / ob::kTile * ob::kTile;
-    return std::min<int64_t>(std::max<int64_t>(e, 4 * ob::kTile), 64 * ob::kTile);
+    return std::min<int64_t>(std::max<int64_t>(e, 4 * ob::kTile), 24 * ob::kTile);
 }
 
 void free_plan(ob_plan p)
