@@ -33,8 +33,11 @@ if ROOT not in sys.path:
 METRIC = "elements/s and achieved HBM GB/s (% of peak) of fused 1-bit Adam step, 1 GPU"
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "bert-base-110M-fp32"
+# the kernels and the host code that sizes their launches (block tables): a change to any of them makes
+# the committed counter summaries stale
 KERNEL_SOURCES = ("adam_ob_compress_amd/csrc/ob_compress.hip", "adam_ob_compress_amd/csrc/ob_kernels.hip",
-                  "adam_ob_compress_amd/csrc/ob_device.h", "adam_ob_compress_amd/csrc/ob_internal.h")
+                  "adam_ob_compress_amd/csrc/ob_device.h", "adam_ob_compress_amd/csrc/ob_internal.h",
+                  "adam_ob_compress_amd/csrc/ob_api.cpp")
 
 
 def kernel_source_sha() -> str:
@@ -498,7 +501,11 @@ def traffic_profile(d: str, kernel: str, workload: str) -> str:
         copies = sorted((r for r in rows if "copyBuffer" in r["Kernel_Name"] and r["Grid_Size"] == "131072"),
                         key=lambda r: int(r["Dispatch_Id"]))
         probe = [float(r["Counter_Value"]) for r in copies[-8:]]
-        kern = [float(r["Counter_Value"]) for r in rows if KERNEL_SYMBOL[kernel] in r["Kernel_Name"]]
+        # the workload's own launches: the kernel's largest grid (the warm-up on a small scratch plan
+        # launches the same kernels on small grids)
+        mine = [r for r in rows if KERNEL_SYMBOL[kernel] in r["Kernel_Name"]]
+        top = max((int(r["Grid_Size"]) for r in mine), default=0)
+        kern = [float(r["Counter_Value"]) for r in mine if int(r["Grid_Size"]) == top]
         if not probe or not kern:
             raise SystemExit(f"no {counter} rows for the copy probe or {kernel} under {d}")
         res[counter] = (sum(kern) / len(kern), len(kern), sum(probe) / len(probe) / probe_kib)
@@ -512,7 +519,7 @@ def traffic_profile(d: str, kernel: str, workload: str) -> str:
            "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 4)}
     return f"""# HBM traffic of `{kernel}` on {w.name}
 
-Kernel source sha (ob_compress.hip, ob_kernels.hip, ob_device.h, ob_internal.h): {rec['kernel_src_sha']}.
+Kernel source sha (ob_compress.hip, ob_kernels.hip, ob_device.h, ob_internal.h, ob_api.cpp): {rec['kernel_src_sha']}.
 
 Commands (each its own run on one MI355X, from the repository root, `export TMPDIR=/tmp`):
 
@@ -532,18 +539,28 @@ traffic-json: {json.dumps(rec)}
 """
 
 
+def _grid(r) -> int:
+    if r.get("Grid_Size"):
+        return int(r["Grid_Size"])
+    return int(r.get("Grid_Size_X", 0)) * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1)
+
+
 def rocprof_summary(d: str) -> str:
     out = []
-    stats = sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True))
-    for f in stats:
-        rows = list(csv.DictReader(open(f)))
-        out.append(f"### kernel stats: {os.path.relpath(f, d)}\n")
-        out.append("| kernel | calls | avg us | min us | max us | total % |")
-        out.append("|---|---|---|---|---|---|")
-        for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0))):
-            out.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                       f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                       f"{float(r['Percentage']):.1f} |")
+    # per kernel and grid size from the dispatch trace, so that the warm-up's small launches of the
+    # same kernels are reported apart from the workload's
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)):
+        groups = {}
+        for r in csv.DictReader(open(f)):
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups.setdefault((_short(r["Kernel_Name"]), _grid(r)), []).append(us)
+        total = sum(sum(v) for v in groups.values()) or 1.0
+        out.append(f"### kernel trace by kernel and grid size: {os.path.relpath(f, d)}\n")
+        out.append("| kernel | grid (threads) | calls | avg us | min us | max us | total % |")
+        out.append("|---|---|---|---|---|---|---|")
+        for (k, g), v in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:14]:
+            out.append(f"| {k} | {g} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+                       f"{100.0 * sum(v) / total:.1f} |")
         out.append("")
     ctr = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
     for f in ctr:
