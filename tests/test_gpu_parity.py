@@ -773,6 +773,69 @@ def test_workload_server_2p28_w8():
 
 
 @pytest.mark.slow
+def test_one_chunk_beyond_2_32_elements():
+    """One chunk of 2^32 + 4099 elements (bf16 g, fp32 state; ~78 GB resident), in the launch
+    configuration the bench uses for large buffers (the per-chunk sums before pass 2 run here: the
+    chunk has ~175,000 pass-1 blocks).  The oracle cannot take the chunk whole in test time, so:
+      * the scale against the oracle's sum of squares over host copies of x = g + err, taken in
+        2^28-element pieces (the same double sum in a different grouping; 1 ulp allowed, as for the
+        GPU's own order);
+      * at 8,192 random elements plus the first and last 96: the sign bit against x >= 0, and err, m
+        and p against the oracle's pack / unpack / worker update of those elements given that scale;
+      * the tail word's bits beyond n are 0."""
+    w = dataclasses.replace(synth.GPT2_XL, name="one-chunk-2^32+4099", n=(1 << 32) + 4099, chunk=(1 << 32) + 4099)
+    n = w.n
+    err, m, v, p = synth.draw_state(w, DEV)
+    synth._fill_normal(err, 1e-4, 77, 1, 0)                 # a non-zero error buffer (seeded input)
+    synth._fill_normal(m, 1e-4, 77, 2, 0)
+    g = synth.draw_grad(w, 0, DEV)
+    rng = np.random.default_rng(2024)
+    idx = np.unique(np.concatenate([rng.integers(0, n, 8192), np.arange(96), np.arange(n - 96, n)]))
+    it = torch.from_numpy(idx).to(DEV)
+    g_s = synth.host(g[it]).astype(np.uint32) << 16
+    x_s = (g_s.view(np.float32) + synth.host(err[it])).astype(np.float32)
+    m_s, v_s, p_s = (synth.host(t[it]) for t in (m, v, p))
+    # the oracle's sum of squares of x, piece by piece (ascending within each piece)
+    S = 0.0
+    piece = 1 << 28
+    for a in range(0, n, piece):
+        b = min(n, a + piece)
+        gp = synth.host(g[a:b]).astype(np.uint32) << 16
+        xp = gp.view(np.float32) + synth.host(err[a:b])
+        S += oracle.chunk_sumsq(xp, 0, b - a)
+        del gp, xp
+    scale_ref = np.float32(np.sqrt(S / n))
+
+    plan = ob.ob_plan_create(n, chunk_size=n)
+    words = torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV)
+    scales = torch.zeros(1, dtype=torch.float32, device=DEV)
+    hp = ob.hparams(lr=w.lr, beta1=w.beta1, eps=w.eps)
+    ob.ob_adam_compress_step(plan, g, err, m, v, p, words, scales, hp)
+    torch.cuda.synchronize()
+
+    sc = np.float32(scales[0].item())
+    assert P.ulp_diff(sc, scale_ref) <= 1, (sc, scale_ref)
+    ds = abs(float(sc) - float(scale_ref))
+    wd = synth.host(words[torch.from_numpy(idx // 32).to(DEV)])
+    bits = (wd >> (idx % 32).astype(np.uint32)) & 1
+    assert np.array_equal(bits.astype(bool), x_s >= np.float32(0.0)), "sign bits"
+    last = int(synth.host(words[-1:])[0])
+    assert last >> (n % 32) == 0, "bits beyond n"
+    k = idx.size
+    off = np.asarray([0, k], np.int64)
+    w_ref = oracle.pack(x_s)
+    ghat = oracle.unpack(w_ref, k, off, np.asarray([scale_ref], np.float32))
+    err_ref = (x_s - ghat).astype(np.float32)               # plain error feedback: x - g_hat, one rounding
+    oracle.worker_update(w_ref, np.asarray([scale_ref], np.float32), m_s, v_s, p_s, off,
+                         lr=w.lr, beta1=w.beta1, eps=w.eps)
+    b1, lr, eps = (np.float64(np.float32(t)) for t in (w.beta1, w.lr, w.eps))
+    P.assert_f32_close(synth.host(err[it]), err_ref, "err", ds)
+    P.assert_f32_close(synth.host(m[it]), m_s, "m", ds * (1 - b1))
+    P.assert_f32_close(synth.host(p[it]), p_s, "p", lr * ds * (1 - b1) / (np.sqrt(v_s.astype(np.float64)) + eps))
+    del plan
+
+
+@pytest.mark.slow
 def test_workload_gpt2_1p5b():
     """1,557,611,200 bf16-gradient elements, chunks of 2^24 (93 chunks, ragged tail): 10 compressed
     steps; chunks 0, 1, 46 and the tail chunk 92 checked every step."""
