@@ -512,6 +512,8 @@ def traffic_profile(d: str, kernel: str, workload: str) -> str:
     (fk, fn, ff), (wk, wn, wf) = res["FETCH_SIZE"], res["WRITE_SIZE"]
     traffic = (fk / ff + wk / wf) * 1024
     alg = bytes_per_elem(w, kernel) * w.n
+    if traffic < 0.5 * alg:
+        raise SystemExit(f"{kernel}: no launch of the workload's size under {d} (only the warm-up's?)")
     run_flags = " --split" if kernel.startswith("worker_") else ""   # the split step's kernels
     rec = {"kernel": kernel, "workload": w.name, "kernel_src_sha": kernel_source_sha(),
            "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
