@@ -6,11 +6,16 @@ chunk per tensor).  The schedule's dense steps (step < freeze_step) run first an
 own; then `--warmup` untimed compressed steps; then `--steps` timed steps.  One JSON line is printed.
 
 Inputs are synthetic and resident in HBM before timing starts: a ring of up to 4 pre-drawn gradients
-(seeded) is cycled, so no random generation runs inside the timed region.
+(seeded) is cycled, so no random generation runs inside the timed region.  Before any timing, every
+kernel runs once on a small scratch plan, so no timed launch pays for loading the device code.
+
+Other workloads: --workload NAME (see adam_ob_compress_amd/synth.py: GPT-2-1.5B, Llama-2-7B, LAMB and
+16-bit error variants); --workload 'server-2^28-W8' times a server round (ob_server_reduce + ob_unpack)
+instead of an optimizer step; --split times the worker step split at the exchange.
 
 Other modes:
-  --rocprof-summary DIR   summarise rocprofv3 CSV output found under DIR (kernel stats, and
-                          FETCH_SIZE / WRITE_SIZE counters per dispatch) as markdown on stdout.
+  --rocprof-summary DIR   summarise rocprofv3 CSV output found under DIR (kernel trace per kernel and
+                          grid size, and FETCH_SIZE / WRITE_SIZE counters per dispatch) as markdown.
   --traffic-profile DIR   from the FETCH_SIZE and WRITE_SIZE runs under DIR (made with
                           --copy-probe-mib 1024), write the calibrated HBM traffic of --kernel on
                           --workload as markdown on stdout (the profiles/traffic_*.md format).
