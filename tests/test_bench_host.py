@@ -75,3 +75,75 @@ def test_committed_traffic_summaries_parse():
         rec = json.loads(lines[0].split(":", 1)[1])
         assert 0.99 < rec["traffic_over_algorithmic"] < MAX_TRAFFIC_RATIO.get(rec["kernel"], 1.05), (f, rec)
         assert f == f"traffic_{rec['kernel']}_{rec['workload']}.md"
+
+
+def _counter_csv(path, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+                                           "Counter_Value"])
+        wr.writeheader()
+        for r in rows:
+            wr.writerow(r)
+
+
+def _fake_counter_runs(d, kernel_rows):
+    """FETCH_SIZE and WRITE_SIZE runs as rocprofv3 writes them: 8 copy-probe dispatches (1 GiB read and
+    written, read by the counter at half its size) plus the given kernel dispatches."""
+    for counter, probe_kib in (("FETCH_SIZE", 524288.0), ("WRITE_SIZE", 1048576.0)):
+        rows = [{"Dispatch_Id": i, "Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 131072,
+                 "Counter_Name": counter, "Counter_Value": probe_kib} for i in range(8)]
+        rows += [dict(r, Counter_Name=counter, Counter_Value=r[counter]) for r in kernel_rows]
+        for r in rows:
+            r.pop("FETCH_SIZE", None)
+            r.pop("WRITE_SIZE", None)
+        _counter_csv(os.path.join(d, counter.lower(), "run_counter_collection.csv"), rows)
+
+
+def test_traffic_profile_uses_the_workload_launches_only(tmp_path):
+    """The warm-up's small launches of a kernel are left out of its average; the calibrated bytes
+    then equal what the synthetic counters say the workload's launches moved."""
+    w = synth.WORKLOADS["bert-base-110M-fp32"]
+    alg = bench.bytes_per_elem(w, "compress") * w.n               # bytes per launch
+    fetch_kib = 20.0 * w.n / 1024 / 2                              # 20 B read per element, counted at half
+    write_kib = 12.125 * w.n / 1024
+    big = [{"Dispatch_Id": 100 + i, "Kernel_Name": "void ob::k_compress<GradF32>(...)", "Grid_Size": 6829568,
+            "FETCH_SIZE": fetch_kib, "WRITE_SIZE": write_kib} for i in range(7)]
+    small = [{"Dispatch_Id": 50, "Kernel_Name": "void ob::k_compress<GradF32>(...)", "Grid_Size": 4096,
+              "FETCH_SIZE": 10.0, "WRITE_SIZE": 10.0}]
+    _fake_counter_runs(str(tmp_path), small + big)
+    md = bench.traffic_profile(str(tmp_path), "compress", w.name)
+    rec = json.loads([ln for ln in md.splitlines() if ln.startswith("traffic-json:")][0].split(":", 1)[1])
+    assert abs(rec["bytes_per_launch"] - alg) / alg < 1e-3
+    assert abs(rec["traffic_over_algorithmic"] - 1.0) < 1e-3
+
+
+def test_traffic_profile_refuses_runs_without_a_workload_launch(tmp_path):
+    w = synth.WORKLOADS["bert-base-110M-fp32"]
+    small = [{"Dispatch_Id": 50, "Kernel_Name": "void ob::k_dense<GradF32>(...)", "Grid_Size": 4096,
+              "FETCH_SIZE": 10.0, "WRITE_SIZE": 10.0}]
+    _fake_counter_runs(str(tmp_path), small)
+    with pytest.raises(SystemExit):
+        bench.traffic_profile(str(tmp_path), "dense", w.name)
+
+
+def test_rocprof_summary_groups_by_kernel_and_grid(tmp_path):
+    import csv
+    path = os.path.join(str(tmp_path), "trace", "run_kernel_trace.csv")
+    os.makedirs(os.path.dirname(path))
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X",
+                                           "Grid_Size_Y", "Grid_Size_Z"])
+        wr.writeheader()
+        t = 0
+        for grid, us in ((4096, 2), (6829568, 580), (6829568, 590)):
+            wr.writerow({"Kernel_Name": "void ob::k_compress<GradF32>(...)", "Start_Timestamp": t,
+                         "End_Timestamp": t + us * 1000, "Grid_Size_X": grid, "Grid_Size_Y": 1,
+                         "Grid_Size_Z": 1})
+            t += 10 ** 6
+    md = bench.rocprof_summary(str(tmp_path))
+    rows = [ln for ln in md.splitlines() if ln.startswith("| k_compress")]
+    assert len(rows) == 2
+    assert "| 6829568 | 2 | 585.00 | 580.00 | 590.00 |" in rows[0]
+    assert "| 4096 | 1 | 2.00 |" in rows[1]
