@@ -215,7 +215,15 @@ struct ErrF16 {
     }
     template <class I>
     static __device__ __forceinline__ float load1(const uint16_t* __restrict__ p, I i) { return widen(p[i]); }
-    static __device__ __forceinline__ float rounded(float e) { return static_cast<float>(static_cast<_Float16>(e)); }
+    // e is the fp32 value of a line evaluated in double.  The empty asm keeps it an fp32 register:
+    // without it the compiler fuses the two roundings (double -> fp32 -> fp16) into one software
+    // double -> fp16 rounding, which differs where the fp32 value is an fp16 midpoint that the double
+    // value misses by less than half an fp32 ulp (nearest-even of the fp32 value is the rule here).
+    static __device__ __forceinline__ float rounded(float e)
+    {
+        __asm__ volatile("" : "+v"(e));
+        return static_cast<float>(static_cast<_Float16>(e));
+    }
     // stochastic: lo = |e| truncated to fp16, q its quantum; hi = lo + q iff r*q < (|e| - lo)*65536,
     // taken on the fp32 bits.  |e| >= 2^-14 (fp16 normal): q is 2^13 fp32 quanta, so the fraction is
     // the low 13 significand bits f and the test is r < 8f; the carry of lo + q moves into the next
@@ -408,8 +416,8 @@ template <bool EMA>
 __device__ __forceinline__ uint32_t error_elem(float x, float& e, float scale, const CompressParams& cp)
 {
     const bool b = x >= 0.0f;
-    const float gh = b ? scale : -scale;              // g_hat = dequantize(q)
-    const float delta = x - gh;                       // compensated - g_hat
+    const float gh = b ? scale : -scale;              // the value the bit stands for
+    const float delta = x - gh;                       // what it failed to carry
     if (EMA)
         e = static_cast<float>(cp.ef_beta * static_cast<double>(e) + cp.one_m_ef_beta * static_cast<double>(delta));
     else

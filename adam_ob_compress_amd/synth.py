@@ -147,19 +147,45 @@ def _gen(device, *key) -> torch.Generator:
     return g
 
 
+def _slice_normal(device, sigma: float, key: tuple, s0: int, s1: int) -> torch.Tensor:
+    """Slice [s0, s1) of the N(0, sigma) stream `key` (s0 a multiple of SLICE): its values depend on
+    (key, slice index) only, so one slice can be drawn again on its own."""
+    g = _gen(device, *key, s0 // SLICE)
+    return torch.randn(s1 - s0, generator=g, device=device, dtype=torch.float32) * sigma
+
+
 def _fill_normal(out: torch.Tensor, sigma: float, *key):
     """out[:] = N(0, sigma) drawn slice by slice; values depend on (key, slice index)."""
     n = out.numel()
     for s0 in range(0, n, SLICE):
         s1 = min(n, s0 + SLICE)
-        g = _gen(out.device, *key, s0 // SLICE)
-        out[s0:s1] = torch.randn(s1 - s0, generator=g, device=out.device, dtype=torch.float32) * sigma
+        out[s0:s1] = _slice_normal(out.device, sigma, key, s0, s1)
+
+
+def _window(n: int, a: int, b: int, draw_slice) -> torch.Tensor:
+    """Elements [a, b) of an n-element stream drawn slice by slice: every slice that overlaps the window
+    is drawn again whole by draw_slice(s0, s1), and the overlap is kept."""
+    parts = []
+    for s0 in range(a // SLICE * SLICE, b, SLICE):
+        s1 = min(n, s0 + SLICE)
+        parts.append(draw_slice(s0, s1)[max(a, s0) - s0:min(b, s1) - s0])
+    return parts[0] if len(parts) == 1 else torch.cat(parts)
 
 
 def _sigma_per_tensor(w: Workload) -> np.ndarray:
     """Per-chunk gradient sigma, log-uniform in [1e-4, 1e-2] (fixed for the run)."""
     rng = np.random.default_rng([SEED, S_SIGMA])
     return 10.0 ** rng.uniform(-4.0, -2.0, size=w.n_chunks)
+
+
+def _grad_slice(w: Workload, step: int, device, s0: int, s1: int) -> torch.Tensor:
+    """Slice [s0, s1) of a uniform-sigma gradient: N(0, sigma) with outliers, in w's gradient dtype."""
+    t = _slice_normal(device, w.grad_sigma, (S_GRAD, step), s0, s1)
+    if w.outlier_frac > 0:
+        go = _gen(device, S_OUTLIER, step, s0 // SLICE)
+        hit = torch.rand(s1 - s0, generator=go, device=device) < w.outlier_frac
+        t = torch.where(hit, t * w.outlier_mult, t)
+    return t.to(torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32)
 
 
 def draw_grad(w: Workload, step: int, device, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -179,30 +205,64 @@ def draw_grad(w: Workload, step: int, device, out: torch.Tensor | None = None) -
         return out
     for s0 in range(0, w.n, SLICE):
         s1 = min(w.n, s0 + SLICE)
-        g = _gen(device, S_GRAD, step, s0 // SLICE)
-        t = torch.randn(s1 - s0, generator=g, device=device, dtype=torch.float32) * w.grad_sigma
-        if w.outlier_frac > 0:
-            go = _gen(device, S_OUTLIER, step, s0 // SLICE)
-            hit = torch.rand(s1 - s0, generator=go, device=device) < w.outlier_frac
-            t = torch.where(hit, t * w.outlier_mult, t)
-        out[s0:s1] = t.to(dt)
+        out[s0:s1] = _grad_slice(w, step, device, s0, s1)
     return out
+
+
+def draw_grad_window(w: Workload, step: int, a: int, b: int, device) -> torch.Tensor:
+    """Elements [a, b) of draw_grad(w, step), drawn on their own (a per-tensor-sigma workload: [a, b)
+    must lie in one chunk)."""
+    if w.grad_sigma is not None:
+        return _window(w.n, a, b, lambda s0, s1: _grad_slice(w, step, device, s0, s1))
+    off = w.chunk_offsets()
+    c = int(np.searchsorted(off, a, side="right")) - 1
+    o0, o1 = int(off[c]), int(off[c + 1])
+    assert o0 <= a <= b <= o1, "a per-tensor-sigma window must lie in one chunk"
+    sig = float(_sigma_per_tensor(w)[c])
+    t = _window(o1 - o0, a - o0, b - o0,
+                lambda s0, s1: _slice_normal(device, sig, (S_GRAD, step, c), s0, s1))
+    return t.to(torch.bfloat16) if w.grad_dtype == "bf16" else t
 
 
 ERR_TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
-def draw_state(w: Workload, device):
-    """Initial (err, m, v, p): err = 0 (in w.err_dtype), m = 0, v = |N(0,1e-6)| + 1e-8, p ~ N(0, 0.02)."""
+def _state_slice(w: Workload, which: str, device, s0: int, s1: int, err_sigma: float, m_sigma: float):
+    if which == "err":
+        t = (_slice_normal(device, err_sigma, (S_ERR, 0, 0), s0, s1) if err_sigma > 0
+             else torch.zeros(s1 - s0, dtype=torch.float32, device=device))
+        return t.to(ERR_TORCH_DTYPES[w.err_dtype])
+    if which == "m":
+        return (_slice_normal(device, m_sigma, (S_M, 0, 0), s0, s1) if m_sigma > 0
+                else torch.zeros(s1 - s0, dtype=torch.float32, device=device))
+    if which == "v":
+        return _slice_normal(device, 1e-6, (S_V, 0, 0), s0, s1).abs_().add_(1e-8)
+    return _slice_normal(device, 0.02, (S_P, 0, 0), s0, s1)
+
+
+def draw_state(w: Workload, device, err_sigma: float = 0.0, m_sigma: float = 0.0):
+    """Initial (err, m, v, p): err = 0 (in w.err_dtype), m = 0, v = |N(0,1e-6)| + 1e-8, p ~ N(0, 0.02).
+    err_sigma / m_sigma > 0 draw err ~ N(0, err_sigma) (rounded to w.err_dtype) and m ~ N(0, m_sigma)
+    instead, for checks from a state with every term non-zero."""
     n = w.n
-    err = torch.zeros(n, dtype=ERR_TORCH_DTYPES[w.err_dtype], device=device)
-    m = torch.zeros(n, dtype=torch.float32, device=device)
-    v = torch.empty(n, dtype=torch.float32, device=device)
-    p = torch.empty(n, dtype=torch.float32, device=device)
-    _fill_normal(v, 1e-6, S_V, 0, 0)
-    v.abs_().add_(1e-8)
-    _fill_normal(p, 0.02, S_P, 0, 0)
-    return err, m, v, p
+    out = []
+    for which, dt in (("err", ERR_TORCH_DTYPES[w.err_dtype]), ("m", torch.float32), ("v", torch.float32),
+                      ("p", torch.float32)):
+        t = torch.empty(n, dtype=dt, device=device)
+        if (which == "err" and err_sigma <= 0) or (which == "m" and m_sigma <= 0):
+            t.zero_()
+        else:
+            for s0 in range(0, n, SLICE):
+                s1 = min(n, s0 + SLICE)
+                t[s0:s1] = _state_slice(w, which, device, s0, s1, err_sigma, m_sigma)
+        out.append(t)
+    return tuple(out)
+
+
+def draw_state_window(w: Workload, a: int, b: int, device, err_sigma: float = 0.0, m_sigma: float = 0.0):
+    """Elements [a, b) of draw_state(w, device, err_sigma, m_sigma), drawn on their own."""
+    return tuple(_window(w.n, a, b, lambda s0, s1, k=k: _state_slice(w, k, device, s0, s1, err_sigma, m_sigma))
+                 for k in ("err", "m", "v", "p"))
 
 
 def draw_worker_words(w: Workload, rnd: int, device) -> torch.Tensor:

@@ -12,8 +12,9 @@ and the oracle may run on different chunks in parallel threads (ctypes releases 
 
 Tolerances:
   * packed words and int8 signs: bit-exact;
-  * a 16-bit error buffer: the fp32 bound below plus one unit in the last place of the storage format
-    (the two sides round fp32 values that may differ in their last bits);
+  * a 16-bit error buffer (nearest or stochastic rounding): the stored words bit-equal on every chunk
+    whose scale matched (see assert_err_close); on a chunk whose scale differed by an ulp, the fp32
+    bound below plus one unit in the last place of the storage format;
   * scales: equal, or 1 ulp apart (the double sum of squares is reduced in a different order);
     mismatches are counted and returned;
   * fp32 state: |gpu - ref| <= 2e-6*|ref| + 1e-9 (+ the exact propagation of a scale difference:
@@ -24,6 +25,7 @@ Tolerances:
 """
 from __future__ import annotations
 
+import collections
 import concurrent.futures as cf
 import os
 
@@ -84,18 +86,47 @@ def widen_err(a: np.ndarray) -> np.ndarray:
     return a.astype(np.float32)
 
 
-def assert_err_close(gpu, ref, what, slack=0.0):
-    """Error buffers of any storage format: fp32 by assert_f32_close; 16-bit with one extra ulp."""
+def assert_err_close(gpu, ref, what, slack=0.0, exact=True):
+    """Error buffers of any storage format.
+
+    fp32: assert_f32_close(gpu, ref, what, slack).
+
+    bf16 / fp16: wherever `exact` holds (a bool, or one per element: True where the element's chunk
+    had the same scale on both sides) the stored 16-bit words must be equal; only NaN payloads are not
+    compared (NaN must meet NaN).  With the same scale both sides store the same fp32 value: plain
+    error feedback is one fp32 subtraction, and in the EMA line both products (fp32 x fp32, and
+    1 - ef_beta times fp32) are exact in double, so the line is rounded once in double whether or not
+    the products are fused, then once to fp32.  Rounding that value to nearest-even, or stochastically
+    with the same random bits, has one result, so any other rounding (truncation, ties away from zero,
+    round-half-down, a wrong random stream) is rejected.
+    Elsewhere (the chunk's scale differed by one ulp, moving the fp32 error by up to `slack`): the
+    fp32 bound plus `slack` plus one unit in the last place of the storage format."""
     fmt = err_format(np.asarray(ref))
     assert err_format(np.asarray(gpu)) == fmt, what
     g32, r32 = widen_err(np.asarray(gpu)), widen_err(np.asarray(ref))
     if fmt == "f32":
         return assert_f32_close(g32, r32, what, slack)
+    assert g32.shape == r32.shape, what
+    ex = np.broadcast_to(np.asarray(exact, dtype=bool), r32.shape)
+    if ex.any():
+        gb = np.asarray(gpu).view(np.uint16)[ex]
+        rb = np.asarray(ref).view(np.uint16)[ex]
+        gn, rn = np.isnan(g32[ex]), np.isnan(r32[ex])
+        bad = (gn != rn) | (~rn & (gb != rb))
+        if np.any(bad):
+            k = int(np.argmax(bad))
+            raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} stored {fmt} words differ where the "
+                                 f"scale matched; first: gpu=0x{int(gb[k]):04x} ({g32[ex][k]!r}) "
+                                 f"ref=0x{int(rb[k]):04x} ({r32[ex][k]!r})")
+    rest = ~ex
+    if not rest.any():
+        return
     prec, tiny = _FMT[fmt]
-    ulp = np.abs(r32.astype(np.float64)) * 2.0 ** (1 - prec) + tiny
+    ulp = np.abs(r32[rest].astype(np.float64)) * 2.0 ** (1 - prec) + tiny
     if not np.isscalar(slack):
-        slack = np.asarray(slack, np.float64)
-    assert_f32_close(g32, r32, what, np.where(np.isfinite(ulp), ulp, 0.0) + slack)
+        slack = np.broadcast_to(np.asarray(slack, np.float64), r32.shape)[rest]
+    assert_f32_close(g32[rest], r32[rest], what + " (chunks whose scale differed)",
+                     np.where(np.isfinite(ulp), ulp, 0.0) + slack)
 
 
 class ChunkRef:
@@ -200,10 +231,6 @@ def _compare_one(r, w, kind, err, m, v, p, words, scales, signs, ratios, diag):
             assert abs(gss - rss[0]) <= 1e-10 * rss[0], f"{tag}: error norm^2 {gss} vs {rss[0]}"
             assert int(diag[1][r.c].item()) == int(rpc[0]), f"{tag}: +1 count"
         assert np.array_equal(gv, r.v), f"{tag}: v changed in the compressed step"
-        if w.err_rounding == "stochastic" and d == 0:
-            # same scale -> the same fp32 new error and the same random bits on both sides
-            assert np.array_equal(ge.view(np.uint16), r.err.view(np.uint16)), \
-                f"{tag}: stochastically rounded error differs"
     else:
         assert_f32_close(gv, r.v, f"{tag}: v")
     err_slack = ds * ((1 - eb) if w.ef_mode == 1 else 1.0)
@@ -218,7 +245,7 @@ def _compare_one(r, w, kind, err, m, v, p, words, scales, signs, ratios, diag):
         dr = abs(float(rg) - float(rr)) if np.isfinite(rr) else 0.0
         u = np.abs(r.m.astype(np.float64)) / den     # run_workload's steps have no bias correction
         p_slack = float(abs(rr)) * p_slack + lr * dr * u
-    assert_err_close(ge, r.err, f"{tag}: err", err_slack)
+    assert_err_close(ge, r.err, f"{tag}: err", err_slack, exact=ds == 0.0)
     assert_f32_close(gm, r.m, f"{tag}: m", m_slack)
     assert_f32_close(gp, r.p, f"{tag}: p", p_slack)
     return mism
@@ -264,3 +291,89 @@ def run_workload(w, chunks=None, steps=None, device="cuda:0", log=print, diagnos
         assert int(opt.nonfinite.item()) == nf_ref
     del plan
     return counts
+
+
+def tracked_chunks(K: int, fixed, n_random: int = 6, seed: int = 0) -> list[int]:
+    """The fixed chunks plus n_random others drawn by a seeded generator (the same ones every run), so
+    that a run's checks also reach chunks nobody picked by hand."""
+    rng = np.random.default_rng([synth.SEED, K, seed])
+    rest = np.setdiff1d(np.arange(K), np.asarray(sorted(fixed), dtype=np.int64))
+    pick = rng.choice(rest, size=min(n_random, rest.size), replace=False) if rest.size else []
+    return sorted({int(c) for c in fixed} | {int(c) for c in pick})
+
+
+def _make_optimizer(w, plan, err, m, v, p, diagnostics=False):
+    cls = schedule.OneBitLamb if w.optimizer == "lamb" else schedule.OneBitAdam
+    return cls(plan, err, m, v, p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+               clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta,
+               int8_signs=w.int8_signs, count_nonfinite=True,
+               freeze_step=w.freeze_step, refresh_period=w.refresh_period,
+               diagnostics=diagnostics, err_rounding=w.err_rounding, sr_seed=synth.SR_SEED)
+
+
+def _check_one_chunk(r, g, w, kind, s, opt):
+    r.err_before = r.err.copy()
+    if kind == "compressed":
+        _oracle_compress(r, g, w, s)
+    else:
+        _oracle_dense(r, g, w, False, 0)
+    mism = _compare_one(r, w, kind, opt.err, opt.m, opt.v, opt.p, opt.words, opt.scales, opt.signs,
+                        getattr(opt, "ratios", None), None)
+    return mism, int(r.out.get("nf", 0))
+
+
+def _every_chunk_one_step(w, plan, kind, s, device, err_sigma, m_sigma, log):
+    err, m, v, p = synth.draw_state(w, device, err_sigma, m_sigma)
+    opt = _make_optimizer(w, plan, err, m, v, p)
+    opt.step_index = s
+    g = synth.draw_grad(w, s, device)
+    torch.cuda.synchronize()
+    got = opt.step(g)
+    assert got == kind, f"{w.name}: step index {s} is a {got} step, not {kind}"
+    torch.cuda.synchronize()
+    del g
+    off = w.chunk_offsets()
+    pending = collections.deque()
+    mism = nf = 0
+
+    def drain(limit):
+        nonlocal mism, nf
+        while len(pending) > limit:
+            a, b = pending.popleft().result()
+            mism += a
+            nf += b
+
+    for c in range(w.n_chunks):
+        a, b = int(off[c]), int(off[c + 1])
+        # this chunk's inputs, drawn again on their own: nothing the step wrote reaches the oracle
+        gh = synth.host(synth.draw_grad_window(w, s, a, b, device))
+        st = [synth.host(t) for t in synth.draw_state_window(w, a, b, device, err_sigma, m_sigma)]
+        pending.append(_POOL.submit(_check_one_chunk, ChunkRef(c, a, b, *st), gh, w, kind, s, opt))
+        drain(2 * _POOL._max_workers)
+    drain(0)
+    if kind == "compressed":
+        assert int(opt.nonfinite.item()) == nf, f"{w.name}: non-finite count"
+    log(f"{w.name} {kind} step {s}: all {w.n_chunks} chunks match ({mism} scale ulp mismatches)")
+    return mism
+
+
+def check_every_chunk(w, device="cuda:0", dense_step=None, err_sigma=1e-4, m_sigma=1e-4, log=print):
+    """Every chunk of w against the oracle after one compressed step, and (dense_step: its step index)
+    after one dense step, each over the whole buffer in the bench's launch configuration and from a
+    seeded state with every term non-zero (err ~ N(0, err_sigma) in w's error format, m ~ N(0, m_sigma)).
+    The oracle's inputs for chunk c are drawn again for that chunk alone by synth's window draws, and
+    the chunks are checked in parallel threads, a bounded number at a time, so the host never holds
+    more than a few chunks of state.  Returns the number of chunks whose scale differed by an ulp."""
+    plan = ob.ob_plan_create(w.n, chunk_size=w.chunk if w.offsets is None else 0, chunk_offsets=w.offsets)
+    first = next(t for t in range(w.steps) if schedule.step_kind(t, w.freeze_step, w.refresh_period)
+                 == "compressed")
+    runs = [("compressed", first)]
+    if dense_step is not None:
+        assert schedule.step_kind(dense_step, w.freeze_step, w.refresh_period) == "dense"
+        runs.append(("dense", dense_step))
+    mism = 0
+    for kind, s in runs:
+        mism += _every_chunk_one_step(w, plan, kind, s, device, err_sigma, m_sigma, log)
+        torch.cuda.empty_cache()
+    del plan
+    return mism

@@ -69,7 +69,8 @@ def _compress_vs_oracle(n, chunk, var, seed, steps=1):
         cidx = np.repeat(np.arange(off.size - 1), np.diff(off))
         ds = np.abs(gs.astype(np.float64) - rs.astype(np.float64))[cidx]
         ds = np.where(np.isfinite(ds), ds, 0.0)
-        P.assert_err_close(synth.host(d_err), err, f"{tag}: err", ds * (0.1 if var["ef_mode"] else 1.0))
+        P.assert_err_close(synth.host(d_err), err, f"{tag}: err", ds * (0.1 if var["ef_mode"] else 1.0),
+                           exact=ds == 0.0)
 
         # the update from the oracle's words and scales
         d_m, d_v, d_p = _t(m), _t(v), _t(p)
@@ -221,6 +222,26 @@ def test_lamb_worker_update(n, chunk):
     rr = oracle.lamb_worker_update(rw, rs, m, v, p, off, **HP)
     assert rr[0] == 1.0
     _check_lamb_update(d_m, d_p, d_r, m, p, v, rr, off, HP["lr"], f"lamb worker update n={n}")
+
+
+def test_lamb_worker_update_with_block_knobs(monkeypatch):
+    """The LAMB worker update writes one p^2 partial per compressed-pass-2 block.  With the dense step's
+    blocks set to 8 tiles (a tuning knob read at plan creation) the compressed-pass-2 table is the
+    plan's largest, about twice the dense table; the plan sizes that workspace for it and the update
+    still matches the oracle (the workspace size is fixed by reading ob_plan_create; this is the
+    regression test of that fix)."""
+    monkeypatch.setenv("OB_BLOCK_ELEMS_DENSE", str(8 * 1024))
+    n, chunk = 1_000_003, 1 << 16
+    gnp, err, m, v, p = _small_state(n, 44)
+    off = oracle.uniform_offsets(n, chunk)
+    plan = ob.ob_plan_create(n, chunk_size=chunk)
+    assert plan.block_elems == 4 * 1024
+    rw, rs, _, _ = oracle.worker_compress(gnp, err, off)
+    d_m, d_v, d_p = _t(m), _t(v), _t(p)
+    d_r = torch.full((off.size - 1,), -7.0, dtype=torch.float32, device=DEV)
+    ob.ob_lamb_worker_update(plan, _t(rw), _t(rs), d_m, d_v, d_p, d_r, ob.hparams(**HP))
+    rr = oracle.lamb_worker_update(rw, rs, m, v, p, off, **HP)
+    _check_lamb_update(d_m, d_p, d_r, m, p, v, rr, off, HP["lr"], "lamb worker update, dense blocks of 8 tiles")
 
 
 @pytest.mark.parametrize("W", [1, 4])
