@@ -23,8 +23,14 @@ struct ob_plan_s {
     // plans with more than kFinalizeAt pass-1 blocks in a chunk: per-chunk sums and the identity table
     double* d_chunk_sums = nullptr;  // [K]
     int32_t* d_ident = nullptr;      // [K + 1]: 0, 1, ..., K
-    double* d_partials_w = nullptr;  // LAMB: one per pass-1 or dense block (the larger)
-    double* d_partials_u = nullptr;  // LAMB: one per compressed-pass-2 or dense block (the larger)
+    // LAMB: per-block sums of p^2 (written by pass 1, the dense step and the worker update, each over
+    // its own block table) and of u^2 (compressed pass 2, the dense step, the worker update); each is
+    // sized for the largest table that writes it, and every launch that writes them is checked
+    // against these sizes on the host (lamb_fits)
+    double* d_partials_w = nullptr;
+    double* d_partials_u = nullptr;
+    int64_t n_partials_w = 0;
+    int64_t n_partials_u = 0;
 
     // diagnostics (off until ob_plan_set_diagnostics): workspaces and the caller's output arrays
     double* d_partials_e = nullptr;    // one per pass-1 block
@@ -248,6 +254,15 @@ ob_status check_grad(const void* g, int dt)
 
 }  // namespace
 
+// LAMB launches write one double per block of their table into the plan's p^2 and/or u^2 workspaces;
+// refuse a launch whose table has more blocks than the workspace it writes holds (cannot happen with
+// the sizes ob_plan_create takes, whatever block sizes the tuning knobs choose; kept as a guard).
+static bool lamb_fits(ob_plan p, int table, bool writes_w, bool writes_u)
+{
+    const int64_t k = p->t[table].n_items;
+    return (!writes_w || k <= p->n_partials_w) && (!writes_u || k <= p->n_partials_u);
+}
+
 extern "C" {
 
 const char* ob_status_str(ob_status s)
@@ -359,10 +374,12 @@ ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_off
                 hipSuccess)
                 return fail(e);
         }
-        const size_t nw = std::max(items[T_PASS1].size(), items[T_DENSE].size());
+        const size_t nw = std::max({items[T_PASS1].size(), items[T_COMPRESS].size(), items[T_DENSE].size()});
         const size_t nu = std::max(items[T_COMPRESS].size(), items[T_DENSE].size());
         if ((e = hipMalloc(&p->d_partials_w, nw * sizeof(double))) != hipSuccess) return fail(e);
         if ((e = hipMalloc(&p->d_partials_u, nu * sizeof(double))) != hipSuccess) return fail(e);
+        p->n_partials_w = static_cast<int64_t>(nw);
+        p->n_partials_u = static_cast<int64_t>(nu);
         if ((e = hipMalloc(&p->d_chunk_off, off.size() * sizeof(int64_t))) != hipSuccess) return fail(e);
         if ((e = hipMemcpy(p->d_chunk_off, off.data(), off.size() * sizeof(int64_t), hipMemcpyHostToDevice)) !=
             hipSuccess)
@@ -409,6 +426,50 @@ ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, flo
 
 namespace {
 
+// Arguments of the compressed step after the plan (or n) checks: dtypes already valid, n > 0.
+ob_status check_compress_args(const void* g, ob_dtype g_dtype, const void* err, ob_dtype err_dtype,
+                              const float* m, const float* v, const float* p, const uint32_t* words_out,
+                              const float* scales_out, const int8_t* signs_out, const uint64_t* nonfinite_out,
+                              const ob_hparams* hp)
+{
+    if (ob_status st = check_grad(g, g_dtype)) return st;
+    if (!err || !m || !v || !p || !words_out || !scales_out) return OB_ERR_ARG;
+    if (!aligned(err, err_dtype == OB_F32 ? 16 : 8)) return OB_ERR_ALIGN;
+    if (!aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16)) return OB_ERR_ALIGN;
+    if (!aligned(words_out, 4) || !aligned(scales_out, 4)) return OB_ERR_ALIGN;
+    if (signs_out && !aligned(signs_out, 4)) return OB_ERR_ALIGN;
+    if (nonfinite_out && !aligned(nonfinite_out, 8)) return OB_ERR_ALIGN;
+    if (hp->ef_mode != OB_EF_PLAIN && hp->ef_mode != OB_EF_EMA) return OB_ERR_ARG;
+    if (hp->err_rounding != OB_ROUND_NEAREST && hp->err_rounding != OB_ROUND_STOCHASTIC) return OB_ERR_ARG;
+    if (hp->err_rounding == OB_ROUND_STOCHASTIC && err_dtype == OB_F32) return OB_ERR_ARG;
+    return OB_OK;
+}
+
+hipError_t sumsq_by_format(ob_dtype err_dtype, const ob::PlanDev& pd1, const void* g, int bf, const void* err,
+                           float clip, const float* lamb_p, hipStream_t s)
+{
+    switch (err_dtype) {
+    case OB_BF16: return ob::launch_chunk_sumsq<OB_BF16>(pd1, g, bf, err, clip, lamb_p, s);
+    case OB_F16: return ob::launch_chunk_sumsq<OB_F16>(pd1, g, bf, err, clip, lamb_p, s);
+    default: return ob::launch_chunk_sumsq<OB_F32>(pd1, g, bf, err, clip, lamb_p, s);
+    }
+}
+
+hipError_t compress_by_format(ob_dtype err_dtype, const ob::PlanDev& pd, const void* g, int bf, void* err,
+                              float* m, const float* v, float* p, uint32_t* words, float* scales, int8_t* signs,
+                              unsigned long long* nf, int ema, int lamb, const ob::CompressParams& cp,
+                              hipStream_t s)
+{
+    switch (err_dtype) {
+    case OB_BF16:
+        return ob::launch_compress<OB_BF16>(pd, g, bf, err, m, v, p, words, scales, signs, nf, ema, lamb, cp, s);
+    case OB_F16:
+        return ob::launch_compress<OB_F16>(pd, g, bf, err, m, v, p, words, scales, signs, nf, ema, lamb, cp, s);
+    default:
+        return ob::launch_compress<OB_F32>(pd, g, bf, err, m, v, p, words, scales, signs, nf, ema, lamb, cp, s);
+    }
+}
+
 // Pass-2 view of the plan.  With many partials per chunk, the chunk sums are formed first (one block
 // per chunk) and the view's pass-1 table becomes the identity over them, so that each pass-2 block
 // forms its scale from one partial instead of all of them.
@@ -450,17 +511,11 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
     if (!plan || !hp) return OB_ERR_ARG;
     if (!valid_dtype(g_dtype) || !valid_err_dtype(err_dtype)) return OB_ERR_DTYPE;
     if (plan->n == 0) return OB_OK;
-    if (ob_status st = check_grad(g, g_dtype)) return st;
-    if (!err || !m || !v || !p || !words_out || !scales_out) return OB_ERR_ARG;
-    if (!aligned(err, err_dtype == OB_F32 ? 16 : 8)) return OB_ERR_ALIGN;
-    if (!aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16)) return OB_ERR_ALIGN;
-    if (!aligned(words_out, 4) || !aligned(scales_out, 4)) return OB_ERR_ALIGN;
-    if (signs_out && !aligned(signs_out, 4)) return OB_ERR_ALIGN;
-    if (nonfinite_out && !aligned(nonfinite_out, 8)) return OB_ERR_ALIGN;
-    if (hp->ef_mode != OB_EF_PLAIN && hp->ef_mode != OB_EF_EMA) return OB_ERR_ARG;
-    if (hp->err_rounding != OB_ROUND_NEAREST && hp->err_rounding != OB_ROUND_STOCHASTIC) return OB_ERR_ARG;
-    if (hp->err_rounding == OB_ROUND_STOCHASTIC && err_dtype == OB_F32) return OB_ERR_ARG;
-
+    if (ob_status st = check_compress_args(g, g_dtype, err, err_dtype, m, v, p, words_out, scales_out, signs_out,
+                                           nonfinite_out, hp))
+        return st;
+    if (lamb && (!lamb_fits(plan, T_PASS1, true, false) || !lamb_fits(plan, T_COMPRESS, false, true)))
+        return OB_ERR_ARG;
     const ob::CompressParams cp = compress_params(hp);
 
     DeviceGuard guard(plan->device);
@@ -472,26 +527,13 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
     auto nf = reinterpret_cast<unsigned long long*>(nonfinite_out);
     const float* lamb_p = lamb ? p : nullptr;
     ob_status st = timed(plan, OB_KERNEL_CHUNK_SUMSQ, stream, [&] {
-        switch (err_dtype) {
-        case OB_BF16: return ob::launch_chunk_sumsq<OB_BF16>(pd1, g, bf, err, cp.clip, lamb_p, stream);
-        case OB_F16: return ob::launch_chunk_sumsq<OB_F16>(pd1, g, bf, err, cp.clip, lamb_p, stream);
-        default: return ob::launch_chunk_sumsq<OB_F32>(pd1, g, bf, err, cp.clip, lamb_p, stream);
-        }
+        return sumsq_by_format(err_dtype, pd1, g, bf, err, cp.clip, lamb_p, stream);
     });
     if (st != OB_OK) return st;
     if ((st = pass2_view(plan, T_COMPRESS, stream, &pd)) != OB_OK) return st;
     st = timed(plan, OB_KERNEL_COMPRESS, stream, [&] {
-        switch (err_dtype) {
-        case OB_BF16:
-            return ob::launch_compress<OB_BF16>(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf,
-                                                ema, lamb, cp, stream);
-        case OB_F16:
-            return ob::launch_compress<OB_F16>(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf,
-                                               ema, lamb, cp, stream);
-        default:
-            return ob::launch_compress<OB_F32>(pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf,
-                                               ema, lamb, cp, stream);
-        }
+        return compress_by_format(err_dtype, pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf, ema,
+                                  lamb, cp, stream);
     });
     if (st != OB_OK || !plan->diag_err_sumsq) return st;
     const ob::PlanDev pdd = plan->dev(T_COMPRESS);   // the pass-1 table the error sums were written by
@@ -613,6 +655,7 @@ ob_status ob_lamb_worker_update(ob_plan plan, const uint32_t* words, const float
     if (!words || !scales || !m || !v || !p || !ratios_out) return OB_ERR_ARG;
     if (!aligned(words, 4) || !aligned(scales, 4) || !aligned(ratios_out, 4)) return OB_ERR_ALIGN;
     if (!aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16)) return OB_ERR_ALIGN;
+    if (!lamb_fits(plan, T_COMPRESS, true, true)) return OB_ERR_ARG;
     const ob::CompressParams cp = compress_params(hp);
     DeviceGuard guard(plan->device);
     if (!guard.ok) return OB_ERR_HIP;
@@ -648,6 +691,7 @@ ob_status ob_lamb_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, flo
     if (!m || !v || !p || !ratios_out) return OB_ERR_ARG;
     if (!aligned(m, 16) || !aligned(v, 16) || !aligned(p, 16) || !aligned(ratios_out, 4)) return OB_ERR_ALIGN;
     if (hp->bias_correction && hp->step < 1) return OB_ERR_ARG;
+    if (!lamb_fits(plan, T_DENSE, true, true)) return OB_ERR_ARG;
     const ob::DenseParams dp = dense_params(hp);
     DeviceGuard guard(plan->device);
     if (!guard.ok) return OB_ERR_HIP;
