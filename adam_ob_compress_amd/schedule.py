@@ -35,8 +35,8 @@ class OneBitAdam:
     random bits from (``sr_seed``, the step index).
 
     With ``diagnostics=True`` every compressed step also leaves, per chunk, the squared L2 norm of the
-    error buffer it read and its number of +1 signs ([P1] sec. 6.2 and 8); see ``error_norms``,
-    ``small_error_chunks`` and ``plus_share``.
+    error buffer it read (``err_sumsq``) and its number of +1 signs (``plus_count``) ([P1] sec. 6.2
+    and 8); ``small_error_chunks`` applies the tutorial's warning threshold to them.
     """
 
     def __init__(self, plan: nat.Plan, err, m, v, p, *, lr, beta1=0.9, beta2=0.999, eps=1e-8,
@@ -81,17 +81,12 @@ class OneBitAdam:
         self.step_index += 1
         return kind
 
-    def error_norms(self) -> torch.Tensor:
-        """Per-chunk L2 norm of the error buffer read by the last compressed step."""
-        return torch.sqrt(self.err_sumsq)
-
     def small_error_chunks(self, threshold: float = 1e-6) -> list[int]:
-        """Chunks whose error-buffer norm was below `threshold` ([P1] sec. 6.2's warning)."""
-        return torch.nonzero(self.error_norms() < threshold).flatten().tolist()
-
-    def plus_share(self, chunk_sizes: torch.Tensor) -> torch.Tensor:
-        """Per-chunk share of +1 signs in the last compressed step (about 0.5 for zero-mean data)."""
-        return self.plus_count.double() / chunk_sizes.double()
+        """Chunks whose error buffer, as the last compressed step read it, had an L2 norm below
+        `threshold` ([P1] sec. 6.2's warning).  Host policy over the library's per-chunk sums of
+        squares (``self.err_sumsq``): a norm below t is a sum of squares below t*t, so no arithmetic is
+        done here; the library's outputs (``err_sumsq``, ``plus_count``) are the diagnostics."""
+        return torch.nonzero(self.err_sumsq < threshold * threshold).flatten().tolist()
 
     def _dense(self, g, stream):
         nat.ob_adam_warmup_step(self.plan, g, self.m, self.v, self.p, self.hp, stream)

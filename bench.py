@@ -1,9 +1,12 @@
 #!/usr/bin/env python3
 """Throughput of the 1-bit Adam step on one MI355X.
 
-Default workload: the BERT-base parameter list (197 fp32 tensors, 108,891,648 elements, one scale
-chunk per tensor).  The schedule's dense steps (step < freeze_step) run first and are timed on their
-own; then `--warmup` untimed compressed steps; then `--steps` timed steps.  One JSON line is printed.
+Default workload: a Llama-2-7B-sized flat buffer (6,738,415,616 elements, bf16 gradients, fp32 state,
+scale chunks of 2^24) with the tutorial's variant of the step (clip at 5, EMA error feedback, int8
+signs) and a variance refresh every 16th step.  The schedule's dense steps -- the warmup steps before
+freeze_step (BERT-base) or refresh steps (Llama-2-7B) -- run first and are timed on their own; then
+`--warmup` untimed compressed steps; then `--steps` timed compressed steps, the compressed phase whose
+step time the pages' acceptance table names.  One JSON line is printed.
 
 Inputs are synthetic and resident in HBM before timing starts: a ring of up to 4 pre-drawn gradients
 (seeded) is cycled, so no random generation runs inside the timed region.  Before any timing, every
@@ -37,7 +40,7 @@ if ROOT not in sys.path:
 
 METRIC = "elements/s and achieved HBM GB/s (% of peak) of fused 1-bit Adam step, 1 GPU"
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, published
-DEFAULT_WORKLOAD = "bert-base-110M-fp32"
+DEFAULT_WORKLOAD = "llama2-7B-bf16-ema"
 # the kernels and the host code that sizes their launches (block tables): a change to any of them makes
 # the committed counter summaries stale
 KERNEL_SOURCES = ("adam_ob_compress_amd/csrc/ob_compress.hip", "adam_ob_compress_amd/csrc/ob_kernels.hip",
@@ -114,43 +117,119 @@ def load_traffic(kernel: str, workload: str):
 # CPU baseline: the oracle as it stands, single thread, on a bounded sample
 # ------------------------------------------------------------------------------------------------
 
+def host_info() -> dict:
+    """The host the CPU baseline ran on: logical CPUs, the CPUs this process may use, the CPU model."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+# threads of the all-cores oracle line: the CPUs this process may use, at most 16 (one GPU's share of
+# the host's cores)
+MAX_CPU_THREADS = 16
+
+
+def _sample(w, limit: int):
+    """Whole chunks of w from the start until `limit` elements: (K, n_s, workload of those chunks)."""
+    import dataclasses
+
+    from adam_ob_compress_amd import synth
+
+    off = w.chunk_offsets()
+    K = 1
+    while K < w.n_chunks and off[K] < limit:
+        K += 1
+    n_s = int(off[K])
+    if w.offsets is None:
+        return K, n_s, synth.scaled(w, n_s, w.chunk)
+    return K, n_s, dataclasses.replace(w, n=n_s, offsets=tuple(int(o) for o in off[:K + 1]))
+
+
 def cpu_baseline(w, seconds: float):
+    """The oracle as it stands on a bounded sample of the workload: single thread (the reported value),
+    and the same oracle run chunk-parallel on up to MAX_CPU_THREADS threads (one chunk per task; the
+    oracle releases the GIL) as a second line."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     import oracle
     from adam_ob_compress_amd import synth
 
-    off = w.chunk_offsets()
     # whole chunks from the start until ~2^27 elements (all of BERT-base); 2^25 for the server round,
     # whose oracle runs ~8x slower per element (W workers' bits per element)
-    limit = (1 << 25) if w.workers else (1 << 27)
-    K = 1
-    while K < w.n_chunks and off[K] < limit:
-        K += 1
-    n_s = int(off[K])
-    sub = synth.scaled(w, n_s, w.chunk) if w.offsets is None else None
-    if sub is None:
-        import dataclasses
-        sub = dataclasses.replace(w, n=n_s, offsets=tuple(int(o) for o in off[:K + 1]))
-    offs = sub.chunk_offsets()
+    K, n_s, sub = _sample(w, (1 << 25) if w.workers else (1 << 27))
+    host = host_info()
     if w.workers:
-        return _cpu_baseline_server(w, sub, K, offs, seconds)
+        res = _cpu_baseline_server(w, sub, K, sub.chunk_offsets(), seconds)
+        res["host"] = host
+        return res
+    step = oracle.lamb_compress_step if w.optimizer == "lamb" else oracle.compress_step
+    hp = dict(lr=w.lr, beta1=w.beta1, eps=w.eps, clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta,
+              want_signs=w.int8_signs)
+
+    def sr(s, index0=0):
+        return (dict(stochastic=True, sr_seed=synth.SR_SEED, sr_step=s, sr_index0=index0)
+                if w.err_rounding == "stochastic" else {})
+
+    offs = sub.chunk_offsets()
     err, m, v, p = (synth.host(t) for t in synth.draw_state(sub, "cpu"))
     g = synth.host(synth.draw_grad(sub, 0, "cpu"))
     times = []
     t_end = time.perf_counter() + seconds
     while len(times) < 2 or (time.perf_counter() < t_end and len(times) < 20):
         t0 = time.perf_counter()
-        step = oracle.lamb_compress_step if w.optimizer == "lamb" else oracle.compress_step
-        sr = (dict(stochastic=True, sr_seed=synth.SR_SEED, sr_step=len(times))
-              if w.err_rounding == "stochastic" else {})
-        step(g, err, m, v, p, offs, lr=w.lr, beta1=w.beta1, eps=w.eps, clip=w.clip, ef_mode=w.ef_mode,
-             ef_beta=w.ef_beta, want_signs=w.int8_signs, **sr)
+        step(g, err, m, v, p, offs, **hp, **sr(len(times)))
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
-    return {"value": n_s / t, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(times)} compressed steps of the oracle on the first {K} chunks "
-                      f"({n_s} elements) of {w.name}, single thread, median step {t:.3f} s"}
+    res = {"value": n_s / t, "unit": "elements/s", "cores": 1, "kind": "oracle",
+           "sample": f"{len(times)} compressed steps of the oracle on the first {K} chunks "
+                     f"({n_s} elements) of {w.name}, single thread, median step {t:.3f} s",
+           "host": host}
+    del err, m, v, p, g
+
+    # the same oracle, one chunk per task on all usable CPUs (at most MAX_CPU_THREADS), over as many
+    # chunks as threads when the workload has them
+    threads = max(1, min(MAX_CPU_THREADS, host["usable_cpus"] or 1))
+    if w.n_chunks < 2 or threads < 2:
+        return res
+    Kp, n_p, subp = _sample(w, threads * int(w.chunk_offsets()[1]))
+    Kp = min(Kp, w.n_chunks)
+    offp = subp.chunk_offsets()
+    state = [synth.host(t) for t in synth.draw_state(subp, "cpu")]
+    gp = synth.host(synth.draw_grad(subp, 0, "cpu"))
+    slices = [(int(offp[c]), int(offp[c + 1])) for c in range(Kp)]
+    views = [[a[lo:hi] for a in (gp, *state)] for lo, hi in slices]
+
+    def chunk(c, s):
+        lo, hi = slices[c]
+        gg, ee, mm, vv, pp = views[c]
+        step(gg, ee, mm, vv, pp, np.asarray([0, hi - lo], np.int64), **hp, **sr(s, lo))
+
+    times = []
+    t_end = time.perf_counter() + seconds
+    with cf.ThreadPoolExecutor(max_workers=threads) as pool:
+        while len(times) < 2 or (time.perf_counter() < t_end and len(times) < 20):
+            t0 = time.perf_counter()
+            for f in [pool.submit(chunk, c, len(times)) for c in range(Kp)]:
+                f.result()
+            times.append(time.perf_counter() - t0)
+    tp = float(np.median(times))
+    res["all_cores"] = {"value": n_p / tp, "unit": "elements/s", "cores": min(threads, Kp), "kind": "oracle",
+                        "sample": f"{len(times)} compressed steps of the oracle on the first {Kp} chunks "
+                                  f"({n_p} elements) of {w.name}, one chunk per task on "
+                                  f"{min(threads, Kp)} threads, median step {tp:.3f} s"}
+    return res
 
 
 def _cpu_baseline_server(w, sub, K, offs, seconds):
@@ -205,16 +284,27 @@ def run(args):
           f"block_elems={plan.block_elems}", file=sys.stderr, flush=True)
 
     warm_kernels(w, opt, dev)
-    # the schedule's dense steps before freeze_step (timed on their own with events)
-    dense_ms = None
-    if w.freeze_step:
+    # the schedule's dense steps, timed on their own with events: the warmup steps before freeze_step,
+    # or (a refresh schedule) two of its refresh steps
+    dense_ms, dense_kind, dense_n = None, None, 0
+    if w.freeze_step or w.refresh_period:
         ob.ob_plan_set_timing(plan, True)
-        for s in range(w.freeze_step):
-            opt.step(grads[s % ring])
+        if w.freeze_step:
+            dense_kind = "warmup"
+            for s in range(w.freeze_step):
+                assert opt.step(grads[s % ring]) == "dense"
+        else:
+            dense_kind = f"refresh (every {w.refresh_period}th step)"
+            for r in range(2):
+                opt.step_index = (r + 1) * w.refresh_period - 1
+                assert opt.step(grads[r % ring]) == "dense"
+            opt.step_index = 0
         torch.cuda.synchronize()
-        ms, cnt = ob.ob_plan_read_timing(plan, ob.OB_KERNEL_DENSE)
-        dense_ms = ms / max(cnt, 1)
+        ms, dense_n = ob.ob_plan_read_timing(plan, ob.OB_KERNEL_DENSE)
+        dense_ms = ms / max(dense_n, 1)
         ob.ob_plan_set_timing(plan, False)
+    # the timed steps are the compressed phase; the refresh steps its schedule inserts are timed above
+    opt.refresh_period = 0
 
     step = opt.step
     if args.split:
@@ -291,6 +381,11 @@ def run(args):
         "step_hbm_frac": step_gbps / PEAK_HBM_GBPS,
         "timed_step_kinds": kinds,
         "dense_step_ms": dense_ms,
+        "dense_step": None if dense_ms is None else {
+            "kind": dense_kind, "steps_timed": dense_n, "avg_ms": dense_ms,
+            "elements_per_s": w.n / (dense_ms * 1e-3),
+            "GBps": bytes_per_elem(w, "dense") * w.n / (dense_ms * 1e-3) / 1e9,
+            "bytes_per_elem": bytes_per_elem(w, "dense")},
         "kernels": kern,
         "kernel_src_sha": kernel_source_sha(),
         "cpu_baseline": None,

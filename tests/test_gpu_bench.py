@@ -24,11 +24,12 @@ def _bench(*args):
     return json.loads(lines[0])
 
 
-@pytest.mark.parametrize("args,workload,kernel", [
-    ((), "bert-base-110M-fp32", "compress"),
-    (("--workload", "server-2^28-W8"), "server-2^28-W8", "server_apply"),
+@pytest.mark.parametrize("args,workload,kernel,dense", [
+    ((), "llama2-7B-bf16-ema", "compress", "refresh"),
+    (("--workload", "bert-base-110M-fp32"), "bert-base-110M-fp32", "compress", "warmup"),
+    (("--workload", "server-2^28-W8"), "server-2^28-W8", "server_apply", None),
 ])
-def test_bench_prints_one_json_line(args, workload, kernel):
+def test_bench_prints_one_json_line(args, workload, kernel, dense):
     d = _bench(*args, "--steps", "3", "--warmup", "1", "--no-cpu")
     assert KEYS <= set(d)
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["higher_is_better"] is True
@@ -38,3 +39,7 @@ def test_bench_prints_one_json_line(args, workload, kernel):
     assert rf["bound"] == "hbm" and rf["kernel"] == kernel and rf["peak"] == 8000.0 and rf["unit"] == "GB/s"
     assert 0 < rf["frac"] < 1 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-12
     assert d["cpu_baseline"] is None
+    if dense is not None:
+        # the timed steps are compressed steps; the schedule's dense steps are timed on their own
+        assert d["timed_step_kinds"] == {"dense": 0, "compressed": 3}
+        assert d["dense_step"]["kind"].startswith(dense) and d["dense_step"]["avg_ms"] > 0
