@@ -9,8 +9,17 @@
  *     scale = sqrt(169/4) = 6.5, word 0b1101, err = x - g_hat, m = 0.5 m + 0.5 g_hat,
  *     p -= 0.5 m / (sqrt(v) + 1);
  *   dense step (same page, section "baseline: why Adam is hard to compress"): m = 0.5 g,
- *     v = 0.25 g^2, p = 1 - 0.5 m / sqrt(v).
+ *     v = 0.25 g^2, p = 1 - 0.5 m / sqrt(v);
+ *   server reduce, two workers (same page, 1-bit Adam, compressed_allreduce): words 0b0011 and
+ *     0b0101 with scales 0.5 and 1.5 average to [1, -0.5, 0.5, -1]; plus the server error
+ *     [1, 0.5, -2.5, 0] gives x = [2, 0, -2, -1], scale sqrt(9/4) = 1.5, word 0b0011 and the new
+ *     server error x - g_hat = [0.5, -1.5, -0.5, 0.5]; its unpack is [1.5, 1.5, -1.5, -1.5];
+ *   pack (the sign part of one_bit_quantize; bit j of word w is element 32w + j, 1 for +1, and
+ *     sign(+-0) = +1, sign(NaN) = -1): [1, -1, 0, -0] -> 13 (fp32 and bf16 input),
+ *     [NaN, Inf, -Inf, -1e-45] -> 2, 33 elements of -1 with x[32] = 1 -> [0, 1], 64 elements of 1
+ *     with x[0] = x[31] = x[63] = -1 -> [0x7FFFFFFE, 0x7FFFFFFF].
  */
+#include <math.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -147,6 +156,90 @@ int main(void)
     CHECK_HIP(hipMemcpy(hpp, p, sizeof hpp, hipMemcpyDeviceToHost));
     const float dm[N] = {1, -1, 0.25f, -2}, dv[N] = {1, 1, 0.0625f, 4}, dp[N] = {0.5f, 1.5f, 0.5f, 1.5f};
     if (!same("dense m", hm, dm, N) || !same("dense v", hv, dv, N) || !same("dense p", hpp, dp, N)) return 1;
+
+    /* server reduce over two workers, then the unpack of its words and scale */
+    {
+        uint32_t *ww, *wo;
+        float *wsc, *esrv, *so, *uo;
+        const uint32_t hww[2] = {3u, 5u};
+        const float hws[2] = {0.5f, 1.5f}, he0[N] = {1.0f, 0.5f, -2.5f, 0.0f};
+        CHECK_HIP(hipMalloc((void**)&ww, sizeof hww));
+        CHECK_HIP(hipMalloc((void**)&wsc, sizeof hws));
+        CHECK_HIP(hipMalloc((void**)&esrv, sizeof he0));
+        CHECK_HIP(hipMalloc((void**)&wo, sizeof(uint32_t)));
+        CHECK_HIP(hipMalloc((void**)&so, sizeof(float)));
+        CHECK_HIP(hipMalloc((void**)&uo, N * sizeof(float)));
+        CHECK_HIP(hipMemcpy(ww, hww, sizeof hww, hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemcpy(wsc, hws, sizeof hws, hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemcpy(esrv, he0, sizeof he0, hipMemcpyHostToDevice));
+        CHECK_OB(ob_server_reduce(plan, 2, ww, wsc, esrv, wo, so, NULL));
+        CHECK_OB(ob_unpack(plan, wo, N, so, uo, NULL));
+        CHECK_HIP(hipDeviceSynchronize());
+        uint32_t hwo;
+        float hso, heo[N], huo[N];
+        CHECK_HIP(hipMemcpy(&hwo, wo, sizeof hwo, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(&hso, so, sizeof hso, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(heo, esrv, sizeof heo, hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemcpy(huo, uo, sizeof huo, hipMemcpyDeviceToHost));
+        const float want_se[N] = {0.5f, -1.5f, -0.5f, 0.5f}, want_uo[N] = {1.5f, 1.5f, -1.5f, -1.5f};
+        if (hwo != 3u || hso != 1.5f) {
+            fprintf(stderr, "server: word %u scale %.9g\n", hwo, hso);
+            return 1;
+        }
+        if (!same("server err", heo, want_se, N) || !same("server unpack", huo, want_uo, N)) return 1;
+        if (ob_server_reduce(plan, 0, ww, wsc, esrv, wo, so, NULL) != OB_ERR_ARG) return 1;   /* W = 0 */
+        hipFree(ww);
+        hipFree(wsc);
+        hipFree(esrv);
+        hipFree(wo);
+        hipFree(so);
+        hipFree(uo);
+    }
+
+    /* pack: fp32 and bf16 inputs, zeros, NaN, Inf, a negative denormal, a 33- and a 64-element case */
+    {
+        enum { M = 64 };
+        float* x;
+        uint16_t* xb;
+        uint32_t* pw;
+        CHECK_HIP(hipMalloc((void**)&x, M * sizeof(float)));
+        CHECK_HIP(hipMalloc((void**)&xb, M * sizeof(uint16_t)));
+        CHECK_HIP(hipMalloc((void**)&pw, 2 * sizeof(uint32_t)));
+        float hx[M];
+        uint32_t hpw[2];
+        const float c1[4] = {1.0f, -1.0f, 0.0f, -0.0f}, c2[4] = {NAN, INFINITY, -INFINITY, -1e-45f};
+        const uint16_t c1b[4] = {0x3F80u, 0xBF80u, 0x0000u, 0x8000u};
+        CHECK_HIP(hipMemcpy(x, c1, sizeof c1, hipMemcpyHostToDevice));
+        CHECK_OB(ob_pack(x, OB_F32, 4, pw, NULL));
+        CHECK_HIP(hipMemcpy(hpw, pw, sizeof(uint32_t), hipMemcpyDeviceToHost));
+        if (hpw[0] != 13u) return fprintf(stderr, "pack [1,-1,0,-0] = %u\n", hpw[0]), 1;
+        CHECK_HIP(hipMemcpy(xb, c1b, sizeof c1b, hipMemcpyHostToDevice));
+        CHECK_OB(ob_pack(xb, OB_BF16, 4, pw, NULL));
+        CHECK_HIP(hipMemcpy(hpw, pw, sizeof(uint32_t), hipMemcpyDeviceToHost));
+        if (hpw[0] != 13u) return fprintf(stderr, "pack bf16 [1,-1,0,-0] = %u\n", hpw[0]), 1;
+        CHECK_HIP(hipMemcpy(x, c2, sizeof c2, hipMemcpyHostToDevice));
+        CHECK_OB(ob_pack(x, OB_F32, 4, pw, NULL));
+        CHECK_HIP(hipMemcpy(hpw, pw, sizeof(uint32_t), hipMemcpyDeviceToHost));
+        if (hpw[0] != 2u) return fprintf(stderr, "pack [NaN,Inf,-Inf,-1e-45] = %u\n", hpw[0]), 1;
+        for (int i = 0; i < 33; ++i) hx[i] = -1.0f;
+        hx[32] = 1.0f;
+        CHECK_HIP(hipMemcpy(x, hx, 33 * sizeof(float), hipMemcpyHostToDevice));
+        CHECK_OB(ob_pack(x, OB_F32, 33, pw, NULL));
+        CHECK_HIP(hipMemcpy(hpw, pw, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost));
+        if (hpw[0] != 0u || hpw[1] != 1u) return fprintf(stderr, "pack n=33: %u %u\n", hpw[0], hpw[1]), 1;
+        for (int i = 0; i < M; ++i) hx[i] = 1.0f;
+        hx[0] = hx[31] = hx[63] = -1.0f;
+        CHECK_HIP(hipMemcpy(x, hx, sizeof hx, hipMemcpyHostToDevice));
+        CHECK_OB(ob_pack(x, OB_F32, M, pw, NULL));
+        CHECK_HIP(hipMemcpy(hpw, pw, 2 * sizeof(uint32_t), hipMemcpyDeviceToHost));
+        if (hpw[0] != 0x7FFFFFFEu || hpw[1] != 0x7FFFFFFFu)
+            return fprintf(stderr, "pack n=64: %08x %08x\n", hpw[0], hpw[1]), 1;
+        if (ob_pack(x, (ob_dtype)5, 4, pw, NULL) != OB_ERR_DTYPE) return 1;
+        if (ob_pack((const float*)((const char*)x + 4), OB_F32, 4, pw, NULL) != OB_ERR_ALIGN) return 1;
+        hipFree(x);
+        hipFree(xb);
+        hipFree(pw);
+    }
 
     /* error paths: rejected on the host, nothing enqueued */
     if (ob_adam_compress_step(NULL, g, OB_F32, err, OB_F32, m, v, p, words, scales, NULL, NULL, &hp, NULL) !=

@@ -1,6 +1,7 @@
 """The C ABI from plain C: tests/c_abi_check.c (built by __graft_entry__.build()) allocates with the
-HIP runtime, runs a compressed step, an unpack and a dense step on hand-derived worked examples and
-checks every output for equality, plus error paths.  No Python binding or torch is involved."""
+HIP runtime, runs a compressed step, the same step split at the exchange, an unpack, a dense step, a
+two-worker server reduce and several packs on hand-derived worked examples and checks every output for
+equality, plus error paths.  No Python binding or torch is involved."""
 import os
 import subprocess
 import tempfile
