@@ -391,7 +391,7 @@ static int compress_core(int64_t n, int64_t K, const int64_t* off,
     /* R15: the error as fp32 (exact widening of the stored values). */
     for (int64_t i = 0; i < n; ++i) err[i] = load_err(err_store, err_fmt, i);
 
-    /* compensated = grad (+clip, R7) + error, kept as an fp32 tensor (R4). */
+    /* x: the gradient (clipped, R7) plus the stored error, kept as an fp32 value (R4). */
     for (int64_t i = 0; i < n; ++i) {
         double gi = (double)load_grad(g, g_is_bf16, i);
         if (clip > 0.0f) {
@@ -404,7 +404,7 @@ static int compress_core(int64_t n, int64_t K, const int64_t* off,
         x[i] = (float)(gi + (double)err[i]);
     }
 
-    /* q, scale = one_bit_quantize(compensated): R1 scale per chunk, R2/R3 sign bits. */
+    /* R1: one scale per chunk of x; R2/R3: the sign bits of x, packed over the flat index. */
     for (int64_t c = 0; c < K; ++c)
         scales[c] = or_chunk_scale(x, off[c], off[c + 1]);
     or_pack(x, 0, n, words);
@@ -414,9 +414,10 @@ static int compress_core(int64_t n, int64_t K, const int64_t* off,
     for (int64_t c = 0; c < K; ++c) {
         for (int64_t i = off[c]; i < off[c + 1]; ++i) {
             int b = sign_bit(x[i]);
-            /* g_hat = dequantize(q): +scale or -scale. */
+            /* the chunk's scale carrying the element's sign: the value the bit stands for. */
             float gh = b ? scales[c] : -scales[c];
-            /* error = compensated - g_hat (plain, [P2]/[P3]), or its EMA ([P1] sec. 2.1). */
+            /* R6: what the bit failed to carry, x less that value; plain feedback keeps it, the EMA
+             * rule of [P1] sec. 2.1 blends it with the previous error by ef_beta. */
             float delta = (float)((double)x[i] - (double)gh);
             float e_new;
             if (ef_mode == 1)
@@ -424,9 +425,11 @@ static int compress_core(int64_t n, int64_t K, const int64_t* off,
             else
                 e_new = delta;
             err[i] = e_new;
-            /* m = beta1*m + (1-beta1)*g_hat ([P2]; [P1] sec. 2.2). */
+            /* R5: the first moment moves toward the quantized value, not the raw gradient
+             * ([P1] sec. 2.2; [P2] compressed branch). */
             m[i] = (float)(b1 * (double)m[i] + (1.0 - b1) * (double)gh);
-            /* param -= lr * m / (sqrt(v_frozen) + eps), v untouched ([P2]). */
+            /* the parameter step divides the new first moment by the root of the frozen second
+             * moment (plus eps); v is only read ([P2] compressed branch). */
             if (adam_update)
                 p[i] = (float)((double)p[i] -
                                (double)lr * ((double)m[i] / (sqrt((double)v[i]) + (double)eps)));
@@ -613,7 +616,7 @@ int or_worker_compress(int64_t n, int64_t K, const int64_t* off, const void* g, 
         return OR_ERR_OOM;
     }
     for (int64_t i = 0; i < n; ++i) err[i] = load_err(err_store, err_fmt, i);
-    /* compensated = grad (+clip, R7) + error */
+    /* x: the gradient (clipped, R7) plus the stored error, an fp32 value (R4) */
     for (int64_t i = 0; i < n; ++i) {
         double gi = (double)load_grad(g, g_is_bf16, i);
         if (clip > 0.0f) {
@@ -625,10 +628,10 @@ int or_worker_compress(int64_t n, int64_t K, const int64_t* off, const void* g, 
         }
         x[i] = (float)(gi + (double)err[i]);
     }
-    /* q, scale = one_bit_quantize(compensated) */
+    /* R1 scales and R2/R3 sign bits of x */
     for (int64_t c = 0; c < K; ++c) scales[c] = or_chunk_scale(x, off[c], off[c + 1]);
     or_pack(x, 0, n, words);
-    /* error = compensated - g_hat with the worker's own g_hat (plain), or its EMA */
+    /* R6 with the value the worker's own bits stand for (R10), plain or EMA */
     const double eb = (double)ef_beta;
     for (int64_t c = 0; c < K; ++c) {
         for (int64_t i = off[c]; i < off[c + 1]; ++i) {
@@ -650,7 +653,7 @@ int or_worker_compress(int64_t n, int64_t K, const int64_t* off, const void* g, 
     return OR_OK;
 }
 
-/* (b) g_hat = dequantize(the exchanged words and scales), then m and the frozen-v update. */
+/* (b) the values the exchanged words and scales stand for, then m and the frozen-v update. */
 int or_worker_update(int64_t n, int64_t K, const int64_t* off, const uint32_t* words, const float* scales,
                      float* m, const float* v, float* p, float lr, float beta1, float eps)
 {
