@@ -20,6 +20,7 @@ struct ob_plan_s {
     int64_t* d_chunk_off = nullptr;
     double* d_partials = nullptr;  // one per pass-1 block
     int64_t p1_max = 0;            // most pass-1 blocks in one chunk
+    bool off128 = false;           // every chunk offset is a multiple of 128 elements
     // plans with more than kFinalizeAt pass-1 blocks in a chunk: per-chunk sums and the identity table
     double* d_chunk_sums = nullptr;  // [K]
     int32_t* d_ident = nullptr;      // [K + 1]: 0, 1, ..., K
@@ -342,6 +343,7 @@ ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_off
     }
     for (int64_t c = 0; c < K; ++c)
         p->p1_max = std::max<int64_t>(p->p1_max, first[T_PASS1][c + 1] - first[T_PASS1][c]);
+    p->off128 = std::all_of(off.begin(), off.end() - 1, [](int64_t o) { return o % 128 == 0; });
 
     if (hipGetDevice(&p->device) != hipSuccess) {
         delete p;
@@ -718,7 +720,7 @@ ob_status ob_server_reduce(ob_plan plan, int32_t W, const uint32_t* worker_words
     if (!guard.ok) return OB_ERR_HIP;
     const ob::PlanDev pd1 = plan->dev(T_PASS1);
     ob_status st = timed(plan, OB_KERNEL_SERVER_SUMSQ, stream, [&] {
-        return ob::launch_server_sumsq(pd1, W, worker_words, worker_scales, server_err, stream);
+        return ob::launch_server_sumsq(pd1, W, worker_words, worker_scales, server_err, plan->off128, stream);
     });
     if (st != OB_OK) return st;
     ob::PlanDev pd;

@@ -66,6 +66,14 @@ constexpr int kPlainItem = 16 * kTile;  // elements per block for the plan-less 
 #ifndef OB_NT_SRV2
 #define OB_NT_SRV2 0
 #endif
+//   OB_SRV_LINES                  server pass 1 with whole-line word loads where the layout allows
+//   OB_SRV_LINES_UNROLL           wave tiles (1024 elements) in flight per wave in that kernel
+#ifndef OB_SRV_LINES
+#define OB_SRV_LINES 1
+#endif
+#ifndef OB_SRV_LINES_UNROLL
+#define OB_SRV_LINES_UNROLL 4
+#endif
 #ifndef OB_NT_BITS
 #define OB_NT_BITS 0
 #endif

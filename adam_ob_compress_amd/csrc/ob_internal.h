@@ -99,8 +99,10 @@ hipError_t launch_chunk_sums(const PlanDev& pd, double* sums, hipStream_t s);
 hipError_t launch_trust_ratio(const PlanDev& pd, float* ratios, hipStream_t s);
 hipError_t launch_lamb_apply(const PlanDev& pd, const float* m, const float* v, float* p, const float* ratios,
                              int bias_correction, const LambParams& lp, hipStream_t s);
+// lines_ok: every block of pd starts at a multiple of 128 elements (the whole-line variant of pass 1
+// may then be used when the word rows are 16-byte aligned and W <= 8)
 hipError_t launch_server_sumsq(const PlanDev& pd, int W, const uint32_t* ww, const float* ws,
-                               const float* e, hipStream_t s);
+                               const float* e, bool lines_ok, hipStream_t s);
 hipError_t launch_server_apply(const PlanDev& pd, int W, const uint32_t* ww, const float* ws,
                                float* e, uint32_t* words, float* scales, hipStream_t s);
 hipError_t launch_unpack(const PlanDev* pd, const uint32_t* words, int64_t n, const float* scales,

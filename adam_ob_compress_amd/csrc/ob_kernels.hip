@@ -487,6 +487,106 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
     }
 }
 
+// Server pass 1 with whole-line word loads (W <= 8; chunk offsets multiples of 128 elements and word
+// rows 16-byte aligned, which the host checks before choosing it).  A wave takes 1024 consecutive
+// elements at a time (a "wave tile"): its error values as four 1 KiB runs, 16 bytes per lane, and the
+// W workers' 32 words of the tile with one 16-byte load per lane -- lanes 8r..8r+7 read worker r's
+// 128 bytes, one whole line per row, so a word-load instruction touches only whole lines that no
+// other wave reads.  The words go through a 1 KiB LDS stage of the wave and come back as the 8 words
+// of each lane's 32-element group (one per worker); the lane's nibble of each, packed, is the layout
+// k_server's transpose produces, and from there the averages come from the same table, built by the
+// same code, so x = avg + e is bit for bit pass 2's.  A chunk's last block may end with a partial
+// wave tile; its elements are taken one at a time.
+__global__ __launch_bounds__(kBlock) void k_server_sumsq_lines(PlanDev pd, int W, const uint32_t* __restrict__ ww,
+                                                               int64_t nw, const float* __restrict__ ws,
+                                                               const float* __restrict__ e)
+{
+    typedef unsigned int w4 __attribute__((ext_vector_type(4)));
+    __shared__ double lds[kBlock / 64];
+    __shared__ float table[1 << kWorkerBatch];
+    __shared__ w4 stage[kBlock / 64][64];
+    constexpr bool NTS = OB_NT_SRV, NTW = OB_NT_SRV_WORDS;
+    constexpr int U = OB_SRV_LINES_UNROLL;
+    const Item it = pd.items[blockIdx.x];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int c = it.chunk;
+    const int row = lane >> 3;                        // the worker row this lane loads
+    const bool loads = row < W;
+    const uint32_t* __restrict__ wrow = ww + static_cast<int64_t>(loads ? row : 0) * nw + 4 * (lane & 7);
+    const int ntiles = it.len >> 10;                  // whole wave tiles of the block
+    f4 ev[U][kVec];
+    w4 wv[U];
+    auto load_group = [&](int t0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = t0 + 4 * u;
+            if (t < ntiles) {
+                const int64_t base = it.start + (static_cast<int64_t>(t) << 10);
+#pragma unroll
+                for (int k = 0; k < kVec; ++k) ev[u][k] = ld4<NTS>(e, base + 256 * k + kVec * lane);
+                wv[u] = loads ? ldv<NTW>(reinterpret_cast<const w4*>(wrow + (base >> 5))) : w4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    // the chunk's worker scales, then the first group of loads, then the table (as k_server's prologue)
+    float sc[kWorkerBatch];
+#pragma unroll
+    for (int w = 0; w < kWorkerBatch; ++w) sc[w] = w < W ? ws[static_cast<int64_t>(w) * pd.K + c] : 0.0f;
+    load_group(wave);
+    {
+        const bool pow2 = (W & (W - 1)) == 0;
+        for (int pat = tid; pat < (1 << W); pat += kBlock) {
+            double a = 0.0;
+#pragma unroll
+            for (int w = 0; w < kWorkerBatch; ++w) {
+                if (w >= W) break;
+                const double s = static_cast<double>(sc[w]);
+                a += ((pat >> w) & 1) ? s : -s;
+            }
+            table[pat] = static_cast<float>(pow2 ? a * (1.0 / static_cast<double>(W)) : a / static_cast<double>(W));
+        }
+    }
+    __syncthreads();
+    const uint32_t keep = W < kWorkerBatch ? (1u << (4 * W)) - 1u : 0xFFFFFFFFu;
+    const int sh = 4 * (lane & 7);
+    double acc = 0.0;
+    for (int t0 = wave; t0 < ntiles; t0 += 4 * U) {
+        if (t0 > wave) load_group(t0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (t0 + 4 * u >= ntiles) break;
+            stage[wave][lane] = wv[u];
+            __builtin_amdgcn_wave_barrier();
+            const uint32_t* st = reinterpret_cast<const uint32_t*>(&stage[wave][0]);
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                // this lane's 4 elements of run k lie in word 8k + lane/8 of every row
+                const int wi = 8 * k + (lane >> 3);
+                uint32_t wd = 0;
+#pragma unroll
+                for (int r = 0; r < kWorkerBatch; ++r) wd |= ((st[32 * r + wi] >> sh) & 0xFu) << (4 * r);
+                const uint32_t pats = patterns_of(wd & keep);
+#pragma unroll
+                for (int q = 0; q < kVec; ++q) {
+                    const float x = table[(pats >> (8 * q)) & 0xFFu] + ev[u][k][q];
+                    acc = fma(static_cast<double>(x), static_cast<double>(x), acc);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+    // a partial wave tile at the end of a chunk's last block: one element at a time
+    for (int j = (ntiles << 10) + tid; j < it.len; j += kBlock) {
+        const int64_t i = it.start + j;
+        uint32_t pat = 0;
+        for (int w = 0; w < W; ++w) pat |= ((ww[static_cast<int64_t>(w) * nw + (i >> 5)] >> (i & 31)) & 1u) << w;
+        const float x = table[pat] + e[i];
+        acc = fma(static_cast<double>(x), static_cast<double>(x), acc);
+    }
+    const double s = block_sum(acc, lds);
+    if (tid == 0) pd.partials[blockIdx.x] = s;
+}
+
 // ------------------------------------------------------------------------------------------------
 // unpack + dequantize, and plain pack
 // ------------------------------------------------------------------------------------------------
@@ -738,10 +838,16 @@ hipError_t launch_lamb_apply(const PlanDev& pd, const float* m, const float* v, 
 }
 
 hipError_t launch_server_sumsq(const PlanDev& pd, int W, const uint32_t* ww, const float* ws,
-                               const float* e, hipStream_t s)
+                               const float* e, bool lines_ok, hipStream_t s)
 {
     const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
     const int64_t nw = (pd.n + 31) / 32;
+    // whole-line word loads need 16-byte aligned word rows and blocks starting at multiples of 128
+    // elements (lines_ok: the plan's chunk offsets are multiples of 128)
+    if (OB_SRV_LINES && W <= kWorkerBatch && lines_ok && nw % 4 == 0 && reinterpret_cast<uintptr_t>(ww) % 16 == 0) {
+        hipLaunchKernelGGL(k_server_sumsq_lines, grid, block, 0, s, pd, W, ww, nw, ws, e);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((k_server<false>), grid, block, 0, s, pd, W, ww, nw, ws, const_cast<float*>(e),
                        static_cast<uint32_t*>(nullptr), static_cast<float*>(nullptr));
     return hipGetLastError();

@@ -314,9 +314,13 @@ def test_server_single_huge_chunk(W):
 
 
 def test_server_bruteforce_small():
-    """W <= 8 takes the kernels' per-chunk table of averages, W > 8 the per-element sums."""
+    """W <= 8 takes the kernels' per-chunk table of averages, W > 8 the per-element sums.  Pass 1 takes
+    its whole-line variant where chunk offsets are multiples of 128 and the word rows 16-byte aligned
+    (n = 1000, 70001 and 1052772 here: whole wave tiles, partial ones and both), the per-lane one
+    elsewhere."""
     for W in (1, 2, 3, 5, 8, 9, 16):
-        for n, chunk in ((1, 64), (31, 64), (130, 64), (1000, 128), (5000, 1024), (70001, 1 << 14)):
+        for n, chunk in ((1, 64), (31, 64), (130, 64), (1000, 128), (5000, 1024), (70001, 1 << 14),
+                         (1_052_772, 1 << 16)):
             off = oracle.uniform_offsets(n, chunk)
             K = off.size - 1
             rng = np.random.default_rng([W, n])
