@@ -14,7 +14,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libobadam.so")
 
-OB_OK, OB_ERR_ARG, OB_ERR_ALIGN, OB_ERR_DTYPE, OB_ERR_HIP, OB_ERR_OOM = range(6)
+OB_OK, OB_ERR_ARG, OB_ERR_ALIGN, OB_ERR_DTYPE, OB_ERR_HIP, OB_ERR_OOM, OB_ERR_SIZE = range(7)
+OB_NOALLOC_SCRATCH_BYTES = 64 << 20
 OB_F32, OB_BF16, OB_F16 = 0, 1, 2
 OB_EF_PLAIN, OB_EF_EMA = 0, 1
 OB_ROUND_NEAREST, OB_ROUND_STOCHASTIC = 0, 1
@@ -73,6 +74,7 @@ def lib() -> ctypes.CDLL:
         "ob_plan_block_elems": (I64, [P]),
         "ob_adam_warmup_step": (I32, [P, P, I32, P, P, P, HP, P]),
         "ob_adam_compress_step": (I32, [P, P, I32, P, I32, P, P, P, P, P, P, P, HP, P]),
+        "ob_adam_compress_step_noalloc": (I32, [I64, I64, P, I32, P, I32, P, P, P, P, P, P, P, HP, P]),
         "ob_lamb_compress_step": (I32, [P, P, I32, P, I32, P, P, P, P, P, P, P, P, HP, P]),
         "ob_lamb_warmup_step": (I32, [P, P, I32, P, P, P, P, HP, P]),
         "ob_adam_worker_compress": (I32, [P, P, I32, P, I32, P, P, P, P, HP, P]),
@@ -217,6 +219,25 @@ def ob_adam_compress_step(plan: Plan, g, err, m, v, p, words_out, scales_out, hp
         _dev(p, "p"),
         _dev(words_out, "words_out"), _dev(scales_out, "scales_out"), _dev(signs_out, "signs_out"),
         _dev(nonfinite_out, "nonfinite_out"), ctypes.byref(hp), _stream(stream)), "ob_adam_compress_step")
+
+
+def ob_adam_compress_step_noalloc(n: int, chunk_size: int, g, err, m, v, p, words_out, scales_out,
+                                  hp: ob_hparams, signs_out=None, nonfinite_out=None, stream=None):
+    """ob_adam_compress_step for uniform chunks of chunk_size, without a plan and without any device
+    allocation (the library's static buffer holds the tables and partial sums)."""
+    K = (n + chunk_size - 1) // chunk_size if n > 0 and chunk_size > 0 else 0
+    _want(g, "g", g.dtype, n)
+    _want(err, "err", err.dtype, n)
+    for name, t in (("m", m), ("v", v), ("p", p)):
+        _want(t, name, torch.float32, n)
+    _want(words_out, "words_out", torch.int32, (n + 31) // 32)
+    _want(scales_out, "scales_out", torch.float32, K)
+    _want(signs_out, "signs_out", torch.int8, n)
+    _want(nonfinite_out, "nonfinite_out", torch.int64, 1)
+    _check(lib().ob_adam_compress_step_noalloc(
+        n, chunk_size, _dev(g, "g"), _gdtype(g), _dev(err, "err"), _errdtype(err), _dev(m, "m"), _dev(v, "v"),
+        _dev(p, "p"), _dev(words_out, "words_out"), _dev(scales_out, "scales_out"), _dev(signs_out, "signs_out"),
+        _dev(nonfinite_out, "nonfinite_out"), ctypes.byref(hp), _stream(stream)), "ob_adam_compress_step_noalloc")
 
 
 def ob_adam_worker_compress(plan: Plan, g, err, words_out, scales_out, hp: ob_hparams, signs_out=None,

@@ -16,6 +16,7 @@ UNITS = [
     ("ob_compress.hip", ["-DOB_ERR_FMT=1"]),   # bf16
     ("ob_compress.hip", ["-DOB_ERR_FMT=2"]),   # fp16
     ("ob_kernels.hip", []),
+    ("ob_noalloc.hip", []),
     ("ob_api.cpp", []),
 ]
 BUILD_DIR = os.path.join(PKG, "_build")

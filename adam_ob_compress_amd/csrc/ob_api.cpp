@@ -275,6 +275,7 @@ const char* ob_status_str(ob_status s)
     case OB_ERR_DTYPE: return "unknown dtype";
     case OB_ERR_HIP: return "HIP runtime error";
     case OB_ERR_OOM: return "device allocation failed";
+    case OB_ERR_SIZE: return "problem too large for the no-allocation entry point's static buffer";
     }
     return "unknown status";
 }
@@ -760,6 +761,100 @@ ob_status ob_unpack(ob_plan plan, const uint32_t* words, int64_t n, const float*
     }
     (void)hipGetLastError();
     return ob::launch_unpack(nullptr, words, n, nullptr, out, stream) == hipSuccess ? OB_OK : OB_ERR_HIP;
+}
+
+ob_status ob_adam_compress_step_noalloc(int64_t n, int64_t chunk_size, const void* g, ob_dtype g_dtype,
+                                        void* err, ob_dtype err_dtype, float* m, const float* v, float* p,
+                                        uint32_t* words_out, float* scales_out, int8_t* signs_out,
+                                        uint64_t* nonfinite_out, const ob_hparams* hp, hipStream_t stream)
+{
+    // everything up to the size check is host arithmetic: a rejected call makes no HIP call
+    if (!hp) return OB_ERR_ARG;
+    if (!valid_dtype(g_dtype) || !valid_err_dtype(err_dtype)) return OB_ERR_DTYPE;
+    if (n < 0 || chunk_size <= 0) return OB_ERR_ARG;
+    if (n == 0) return OB_OK;
+    if (ob_status st = check_compress_args(g, g_dtype, err, err_dtype, m, v, p, words_out, scales_out, signs_out,
+                                           nonfinite_out, hp))
+        return st;
+    const int64_t K = (n + chunk_size - 1) / chunk_size;
+    if (K > 1 && chunk_size % 64 != 0) return OB_ERR_ALIGN;
+    if (K > INT32_MAX - 1) return OB_ERR_SIZE;
+
+    // the block tables ob_plan_create would build for these uniform chunks (same block sizes)
+    const int64_t be1 = choose_block_elems(n, T_PASS1), be2 = choose_block_elems(n, T_COMPRESS);
+    const int64_t last = n - (K - 1) * chunk_size;
+    auto blocks = [](int64_t len, int64_t be) { return (len + be - 1) / be; };
+    const int64_t nbf1 = K > 1 ? blocks(chunk_size, be1) : 0, nbf2 = K > 1 ? blocks(chunk_size, be2) : 0;
+    const int64_t n1 = (K - 1) * nbf1 + blocks(last, be1), n2 = (K - 1) * nbf2 + blocks(last, be2);
+    const bool finalize = std::max(nbf1, blocks(last, be1)) > kFinalizeAt;
+
+    // layout of the static buffer: every region starts on a 256-byte boundary
+    int64_t used = 0;
+    auto region = [&](int64_t bytes) {
+        const int64_t at = used;
+        used += (bytes + 255) / 256 * 256;
+        return at;
+    };
+    const int64_t o_items1 = region(n1 * int64_t(sizeof(ob::Item))), o_first1 = region((K + 1) * 4);
+    const int64_t o_items2 = region(n2 * int64_t(sizeof(ob::Item))), o_first2 = region((K + 1) * 4);
+    const int64_t o_off = region((K + 1) * 8), o_part = region(n1 * 8);
+    const int64_t o_sums = finalize ? region(K * 8) : 0, o_ident = finalize ? region((K + 1) * 4) : 0;
+    if (used > ob::kNoallocScratchBytes || n1 > INT32_MAX || n2 > INT32_MAX) return OB_ERR_SIZE;
+
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return OB_ERR_HIP;
+    unsigned char* base = static_cast<unsigned char*>(ob::noalloc_scratch(device));
+    if (!base) return OB_ERR_HIP;
+
+    ob::UniformTables t;
+    t.items1 = reinterpret_cast<ob::Item*>(base + o_items1);
+    t.first1 = reinterpret_cast<int32_t*>(base + o_first1);
+    t.items2 = reinterpret_cast<ob::Item*>(base + o_items2);
+    t.first2 = reinterpret_cast<int32_t*>(base + o_first2);
+    t.off = reinterpret_cast<int64_t*>(base + o_off);
+    t.ident = finalize ? reinterpret_cast<int32_t*>(base + o_ident) : nullptr;
+    t.n = n;
+    t.chunk = chunk_size;
+    t.be1 = be1;
+    t.be2 = be2;
+    t.n1 = n1;
+    t.n2 = n2;
+    t.K = static_cast<int32_t>(K);
+    t.nbf1 = static_cast<int32_t>(nbf1);
+    t.nbf2 = static_cast<int32_t>(nbf2);
+
+    // the views a plan's dev() would give: pass 1 over items1, the fused pass over items2
+    ob::PlanDev pd1 = {};
+    pd1.items = t.items1;
+    pd1.chunk_first = t.first1;
+    pd1.p1_first = t.first1;
+    pd1.chunk_off = t.off;
+    pd1.partials = reinterpret_cast<double*>(base + o_part);
+    pd1.n = n;
+    pd1.n_items = n1;
+    pd1.K = t.K;
+    ob::PlanDev pd2 = pd1;
+    pd2.items = t.items2;
+    pd2.chunk_first = t.first2;
+    pd2.n_items = n2;
+
+    const ob::CompressParams cp = compress_params(hp);
+    const int bf = g_dtype == OB_BF16;
+    const int ema = hp->ef_mode == OB_EF_EMA;
+    auto nf = reinterpret_cast<unsigned long long*>(nonfinite_out);
+    (void)hipGetLastError();
+    if (ob::launch_uniform_tables(t, stream) != hipSuccess) return OB_ERR_HIP;
+    if (sumsq_by_format(err_dtype, pd1, g, bf, err, cp.clip, nullptr, stream) != hipSuccess) return OB_ERR_HIP;
+    if (finalize) {
+        double* sums = reinterpret_cast<double*>(base + o_sums);
+        if (ob::launch_chunk_sums(pd1, sums, stream) != hipSuccess) return OB_ERR_HIP;
+        pd2.p1_first = t.ident;
+        pd2.partials = sums;
+    }
+    return compress_by_format(err_dtype, pd2, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf, ema, 0,
+                              cp, stream) == hipSuccess
+               ? OB_OK
+               : OB_ERR_HIP;
 }
 
 ob_status ob_plan_set_diagnostics(ob_plan plan, double* err_sumsq_out, uint64_t* plus_count_out)

@@ -109,4 +109,26 @@ hipError_t launch_unpack(const PlanDev* pd, const uint32_t* words, int64_t n, co
                          float* out, hipStream_t s);
 hipError_t launch_pack(const void* x, int x_bf16, int64_t n, uint32_t* words, hipStream_t s);
 
+// ---- the no-allocation compressed step (ob_noalloc.hip) ----
+// Bytes of the static device buffer that holds its block tables and per-block sums.
+constexpr int64_t kNoallocScratchBytes = int64_t(64) << 20;
+// This device's address of that buffer (the device must be current), looked up on the first call on
+// each device and kept; nullptr if the lookup failed.
+void* noalloc_scratch(int device);
+// The block tables of uniform chunks (chunk c = [c*chunk, min((c+1)*chunk, n)), K chunks), for two
+// block sizes (pass 1: be1, pass 2: be2), written into device memory by one kernel: items1/first1 and
+// items2/first2 as ob_plan_create builds them on the host, chunk offsets, and (ident != nullptr) the
+// identity table 0..K.  nbf1 / nbf2: blocks of a chunk other than the last.
+struct UniformTables {
+    Item* items1;
+    int32_t* first1;
+    Item* items2;
+    int32_t* first2;
+    int64_t* off;
+    int32_t* ident;
+    int64_t n, chunk, be1, be2, n1, n2;
+    int32_t K, nbf1, nbf2;
+};
+hipError_t launch_uniform_tables(const UniformTables& t, hipStream_t s);
+
 }  // namespace ob

@@ -58,7 +58,8 @@ typedef enum {
     OB_ERR_ALIGN = 2,
     OB_ERR_DTYPE = 3,
     OB_ERR_HIP = 4,
-    OB_ERR_OOM = 5
+    OB_ERR_OOM = 5,
+    OB_ERR_SIZE = 6     /* ob_adam_compress_step_noalloc: the problem needs more than its static buffer */
 } ob_status;
 
 /* Element types.  Gradients and packed inputs: OB_F32 or OB_BF16.  The error buffer of the compressed
@@ -215,6 +216,29 @@ ob_status ob_unpack(ob_plan plan, const uint32_t* words, int64_t n, const float*
                     hipStream_t stream);
 
 const char* ob_status_str(ob_status s);
+
+/* ---- the compressed step without any allocation ----
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  ob_adam_compress_step for uniform chunks of chunk_size elements
+ * (the last chunk ends at n; chunk_size > 0 and, when n > chunk_size, a multiple of 64 -- the chunking
+ * of ob_plan_create with chunk_offsets == NULL), without a plan.  Arguments, layouts, outputs and
+ * errors otherwise as ob_adam_compress_step; the results are bit for bit those of
+ * ob_adam_compress_step with a plan of the same n and chunk_size.
+ * It calls no hipMalloc, hipFree or other allocating routine.  Its block tables and per-block sums of
+ * squares live in a static device buffer of OB_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends; the first call on a device looks up that device's copy.
+ * Each call rewrites the tables it needs (one small kernel ahead of the two passes), so consecutive
+ * calls may change n and chunk_size.  All calls on one GPU share its buffer: calls that may overlap on
+ * one GPU (other streams, other host threads) race and must not be issued; calls on one stream are
+ * ordered.  Space needed: 24 bytes per first-pass block, 16 per 4096-element block of the fused pass,
+ * 16 per chunk (plus 12 per chunk for chunks of more than 4096 first-pass blocks), each region rounded
+ * up to 256 bytes -- with chunks of 2^24 elements about 1.3e10 elements fit.  A larger problem returns
+ * OB_ERR_SIZE before any HIP call.  No diagnostics and no timing (those belong to a plan). */
+#define OB_NOALLOC_SCRATCH_BYTES (64ll << 20)
+ob_status ob_adam_compress_step_noalloc(int64_t n, int64_t chunk_size, const void* g, ob_dtype g_dtype,
+                                        void* err, ob_dtype err_dtype, float* m, const float* v, float* p,
+                                        uint32_t* words_out, float* scales_out, int8_t* signs_out,
+                                        uint64_t* nonfinite_out, const ob_hparams* hp, hipStream_t stream);
 
 /* ---- kernel timing (measurement support) ----
  * With timing on, every call made with this plan records a hipEvent pair around each kernel it

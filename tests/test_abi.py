@@ -33,9 +33,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
-        assert ob.ob_status_str(s)
+    for s in range(7):
+        assert ob.ob_status_str(s) != "unknown status"
     assert "align" in ob.ob_status_str(2)
+    assert "static buffer" in ob.ob_status_str(6)
 
 
 def test_hparams_layout_matches_header():
@@ -74,6 +75,19 @@ def test_validation_before_any_gpu_work(lib):
     assert lib.ob_plan_create(200, 0, short, 2, ctypes.byref(h)) == 1
     empty_chunk = (ctypes.c_int64 * 4)(0, 64, 64, 200)
     assert lib.ob_plan_create(200, 0, empty_chunk, 3, ctypes.byref(h)) == 1
+    # the no-allocation step: argument and size checks are host arithmetic, made before any HIP call
+    args = (P(0x1000), 0, P(0x2000), 0, P(0x3000), P(0x4000), P(0x5000), P(0x6000), P(0x7000), None, None,
+            ctypes.byref(hp), None)
+    assert lib.ob_adam_compress_step_noalloc(0, 64, *args) == 0                 # n = 0 is a no-op
+    assert lib.ob_adam_compress_step_noalloc(-1, 64, *args) == 1
+    assert lib.ob_adam_compress_step_noalloc(1000, 0, *args) == 1
+    assert lib.ob_adam_compress_step_noalloc(1000, 100, *args) == 2             # interior boundary 100
+    assert lib.ob_adam_compress_step_noalloc(1000, 64, P(0x1004), *args[1:]) == 2
+    assert lib.ob_adam_compress_step_noalloc(1000, 64, None, *args[1:]) == 1
+    # 2^37 elements: about 33.6 million 4096-element blocks of the fused pass need 537 MB of tables
+    assert lib.ob_adam_compress_step_noalloc(1 << 37, 1 << 24, *args) == 6
+    # 2^30 elements in chunks of 64: 16.8 million chunks
+    assert lib.ob_adam_compress_step_noalloc(1 << 30, 64, *args) == 6
     assert lib.ob_plan_destroy(None) == 1
     assert lib.ob_plan_num_chunks(None) == -1
     d = ctypes.c_double()

@@ -1,0 +1,97 @@
+"""The compressed step without any allocation (ob_adam_compress_step_noalloc), marked gpu.
+
+Called through the C ABI (the ctypes binding), it must give bit for bit the outputs of
+ob_adam_compress_step with a plan of the same n and chunk size -- the same kernels over the same
+block tables, the tables and partial sums living in the library's static device buffer instead of the
+plan's allocations.  Each case makes calls in a row on one stream, later ones smaller than the first
+(the buffer then still holds the first call's larger tables), and then the first size again.
+"""
+import numpy as np
+import pytest
+import torch
+
+import adam_ob_compress_amd as ob
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    ob.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _state(n, gdt, edt, seed):
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    g = torch.randn(n, generator=gen, device=DEV) * (20.0 if gdt == "bf16" else 1e-3)
+    err = torch.randn(n, generator=gen, device=DEV) * 1e-3
+    m = torch.randn(n, generator=gen, device=DEV) * 1e-4
+    v = torch.randn(n, generator=gen, device=DEV).abs() * 1e-6 + 1e-8
+    p = torch.randn(n, generator=gen, device=DEV) * 0.02
+    g = g.to(torch.bfloat16) if gdt == "bf16" else g
+    err = err.to({"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[edt])
+    return g, err, m, v, p
+
+
+def _bits(t):
+    t = t.contiguous()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.view(torch.int16)
+    return t.cpu().numpy().view(np.uint8)
+
+
+def _one(n, chunk, gdt, edt, ema, clip, signs, sr, seed):
+    g, err, m, v, p = _state(n, gdt, edt, seed)
+    hp = ob.hparams(lr=1e-4, clip=clip, ef_mode=ob.OB_EF_EMA if ema else ob.OB_EF_PLAIN, ef_beta=0.9,
+                    err_rounding=ob.OB_ROUND_STOCHASTIC if sr else ob.OB_ROUND_NEAREST, sr_seed=0x5EED,
+                    step=3)
+    K = (n + chunk - 1) // chunk
+    outs = []
+    for noalloc in (False, True):
+        e, mm, pp = err.clone(), m.clone(), p.clone()
+        words = torch.full(((n + 31) // 32,), -1, dtype=torch.int32, device=DEV)
+        scales = torch.full((K,), -1.0, dtype=torch.float32, device=DEV)
+        sg = torch.zeros(n, dtype=torch.int8, device=DEV) if signs else None
+        nf = torch.zeros(1, dtype=torch.int64, device=DEV)
+        if noalloc:
+            ob.ob_adam_compress_step_noalloc(n, chunk, g, e, mm, v, pp, words, scales, hp, sg, nf)
+        else:
+            plan = ob.ob_plan_create(n, chunk_size=chunk)
+            ob.ob_adam_compress_step(plan, g, e, mm, v, pp, words, scales, hp, sg, nf)
+        torch.cuda.synchronize()
+        outs.append([_bits(t) for t in (e, mm, pp, words, scales, nf) + ((sg,) if signs else ())])
+        if not noalloc:
+            plan.destroy()
+    names = ("err", "m", "p", "words", "scales", "nonfinite", "signs")
+    for name, a, b in zip(names, *outs):
+        assert np.array_equal(a, b), f"n={n} chunk={chunk} {gdt}/{edt}: {name} differs from the plan's step"
+    return outs[1]
+
+
+# (n, chunk, g dtype, error dtype, EMA, clip, int8 signs, stochastic rounding)
+SEQUENCES = {
+    # one chunk of more than 4096 first-pass blocks (its sum formed by the per-chunk kernel), then
+    # smaller buffers in several chunks with ragged tails, then the first again
+    "huge-chunk-then-smaller": [
+        (17_000_003, 17_000_003, "bf16", "f16", True, 5.0, True, False),
+        (1_000_003, 1 << 16, "f32", "f32", False, 0.0, False, False),
+        (130, 64, "f32", "bf16", True, 0.0, True, True),
+        (17_000_003, 17_000_003, "bf16", "f16", True, 5.0, True, False),
+    ],
+    # many chunks, then one chunk, then a tiny buffer
+    "many-chunks-then-smaller": [
+        (5_000_000, 1 << 14, "f32", "bf16", False, 0.0, True, True),
+        (300_037, 300_037, "bf16", "f32", True, 5.0, False, False),
+        (33, 64, "f32", "f32", False, 0.0, True, False),
+    ],
+}
+
+
+@pytest.mark.parametrize("name", sorted(SEQUENCES))
+def test_noalloc_step_equals_the_plan_step(name):
+    for k, case in enumerate(SEQUENCES[name]):
+        _one(*case, seed=100 + k)
