@@ -55,5 +55,20 @@ def build(verbose: bool = False, extra: list[str] | None = None, out: str | None
     return target
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "ob_probe.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libobprobe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the measurement probe (a nontemporal copy kernel that bench.py's counter calibration
+    runs) into its own library; the optimizer library never loads it."""
+    cmd = [HIPCC, *FLAGS, "-o", PROBE_LIB + ".tmp", PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True, extra=sys.argv[1:])

@@ -240,15 +240,18 @@ def _state_slice(w: Workload, which: str, device, s0: int, s1: int, err_sigma: f
     return _slice_normal(device, 0.02, (S_P, 0, 0), s0, s1)
 
 
-def draw_state(w: Workload, device, err_sigma: float = 0.0, m_sigma: float = 0.0):
+def draw_state(w: Workload, device, err_sigma: float = 0.0, m_sigma: float = 0.0, out=None):
     """Initial (err, m, v, p): err = 0 (in w.err_dtype), m = 0, v = |N(0,1e-6)| + 1e-8, p ~ N(0, 0.02).
     err_sigma / m_sigma > 0 draw err ~ N(0, err_sigma) (rounded to w.err_dtype) and m ~ N(0, m_sigma)
-    instead, for checks from a state with every term non-zero."""
+    instead, for checks from a state with every term non-zero.  out: four tensors of n elements (err in
+    w.err_dtype, the others fp32) to fill in place instead of allocating."""
     n = w.n
+    given = out
     out = []
-    for which, dt in (("err", ERR_TORCH_DTYPES[w.err_dtype]), ("m", torch.float32), ("v", torch.float32),
-                      ("p", torch.float32)):
-        t = torch.empty(n, dtype=dt, device=device)
+    for k, (which, dt) in enumerate((("err", ERR_TORCH_DTYPES[w.err_dtype]), ("m", torch.float32),
+                                     ("v", torch.float32), ("p", torch.float32))):
+        t = torch.empty(n, dtype=dt, device=device) if given is None else given[k]
+        assert t.dtype == dt and t.numel() == n
         if (which == "err" and err_sigma <= 0) or (which == "m" and m_sigma <= 0):
             t.zero_()
         else:

@@ -270,9 +270,14 @@ def run(args):
     if w.workers:
         return w, run_server(args, w)
     plan = ob.ob_plan_create(w.n, chunk_size=w.chunk if w.offsets is None else 0, chunk_offsets=w.offsets)
-    err, m, v, p = synth.draw_state(w, dev)
     ring = 1 if w.n > (1 << 31) else min(4, max(1, args.steps))
-    grads = [synth.draw_grad(w, s, dev) for s in range(ring)]
+    if args.slab:
+        err, m, v, p, grads = slab_buffers(w, ring, dev, args.slab_stagger)
+        synth.draw_state(w, dev, out=(err, m, v, p))
+        grads = [synth.draw_grad(w, s, dev, out=grads[s]) for s in range(ring)]
+    else:
+        err, m, v, p = synth.draw_state(w, dev)
+        grads = [synth.draw_grad(w, s, dev) for s in range(ring)]
     cls = schedule.OneBitLamb if w.optimizer == "lamb" else schedule.OneBitAdam
     opt = cls(plan, err, m, v, p, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                               clip=w.clip, ef_mode=w.ef_mode, ef_beta=w.ef_beta, int8_signs=w.int8_signs,
@@ -340,7 +345,7 @@ def run(args):
     ob.ob_plan_set_timing(plan, False)
 
     if args.copy_probe_mib:
-        kern["torch_copy_probe"] = copy_probe(args.copy_probe_mib, dev)
+        kern["copy_probes"] = copy_probe(args.copy_probe_mib, dev)
 
     # the dominant kernel of the timed steps: the longest per launch (the fused pass 2 for 1-bit Adam)
     dom = max((k for k in ("compress", "lamb_apply", "worker_compress", "worker_update") if k in kern),
@@ -373,7 +378,8 @@ def run(args):
                    "error_feedback": "ema" if w.ef_mode else "plain", "int8_signs": w.int8_signs,
                    "freeze_step": w.freeze_step, "refresh_period": w.refresh_period,
                    "block_elems": plan.block_elems, "work_blocks": plan.num_blocks,
-                   "diagnostics": bool(args.diagnostics), "split": bool(args.split)},
+                   "diagnostics": bool(args.diagnostics), "split": bool(args.split),
+                   "slab": bool(args.slab), "slab_stagger": args.slab_stagger if args.slab else None},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
                      "bytes_per_elem": bpe, "traffic": traffic},
@@ -391,6 +397,32 @@ def run(args):
         "cpu_baseline": None,
     }
     return w, res
+
+
+SLAB_ALIGN = 2 << 20
+
+
+def slab_buffers(w, ring: int, dev: str, stagger: int = 0):
+    """err, m, v, p and `ring` gradients carved from one device allocation, each at a 2 MiB-aligned
+    offset plus j * stagger bytes for array j (an allocation-strategy experiment: all arrays then come
+    from one allocation, at chosen distances from each other)."""
+    import torch
+
+    from adam_ob_compress_amd import synth
+
+    kinds = [synth.ERR_TORCH_DTYPES[w.err_dtype]] + [torch.float32] * 3
+    kinds += [torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32] * ring
+    sizes = [w.n * torch.empty(0, dtype=k).element_size() for k in kinds]
+    assert stagger % 256 == 0
+    offs, total = [], 0
+    for j, b in enumerate(sizes):
+        offs.append(total + j * stagger)
+        total += (b + SLAB_ALIGN - 1) // SLAB_ALIGN * SLAB_ALIGN
+    total += len(sizes) * stagger
+    slab = torch.empty(total + SLAB_ALIGN, dtype=torch.uint8, device=dev)
+    shift = (-slab.data_ptr()) % SLAB_ALIGN
+    views = [slab[shift + o:shift + o + b].view(k) for o, b, k in zip(offs, sizes, kinds)]
+    return views[0], views[1], views[2], views[3], views[4:]
 
 
 def warm_kernels(w, opt, dev: str):
@@ -425,23 +457,42 @@ def warm_kernels(w, opt, dev: str):
 
 
 def copy_probe(mib: int, dev: str) -> dict:
-    """A plain torch copy of `mib` MiB (3 untimed + 5 timed): the counters' calibration run, and a
-    practical bandwidth reference."""
+    """Copies of `mib` MiB, each 3 untimed + 5 timed: a plain torch copy (ordinary loads and stores)
+    and the probe library's copy with nontemporal loads and stores (the library's streaming kernels'
+    access kind).  They are the counters' calibration runs and practical bandwidth references."""
+    import ctypes
+
     import torch
+
+    from adam_ob_compress_amd import build
 
     nb = mib << 20
     src = torch.empty(nb // 4, dtype=torch.float32, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    for _ in range(5):
-        dst.copy_(src)
-    ev1.record()
-    torch.cuda.synchronize()
-    return {"bytes_per_launch": 2 * nb, "GBps": 2 * nb / (ev0.elapsed_time(ev1) / 5 * 1e-3) / 1e9}
+    probe = ctypes.CDLL(build.PROBE_LIB)
+    probe.ob_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    probe.ob_probe_copy.restype = ctypes.c_int
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def nt_copy():
+        rc = probe.ob_probe_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nb, 1, stream)
+        if rc != 0:
+            raise RuntimeError(f"ob_probe_copy failed ({rc})")
+
+    out = {}
+    for name, copy in (("torch_copy", lambda: dst.copy_(src)), ("nontemporal_copy", nt_copy)):
+        for _ in range(3):
+            copy()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(5):
+            copy()
+        ev1.record()
+        torch.cuda.synchronize()
+        out[name] = {"bytes_per_launch": 2 * nb, "GBps": 2 * nb / (ev0.elapsed_time(ev1) / 5 * 1e-3) / 1e9}
+    assert torch.equal(src, dst)
+    return out
 
 
 def run_server(args, w):
@@ -488,7 +539,7 @@ def run_server(args, w):
                           "GBps": bytes_per_elem(w, name) * w.n / (ms / cnt * 1e-3) / 1e9}
     ob.ob_plan_set_timing(plan, False)
     if args.copy_probe_mib:
-        kern["torch_copy_probe"] = copy_probe(args.copy_probe_mib, dev)
+        kern["copy_probes"] = copy_probe(args.copy_probe_mib, dev)
     dom = max((k for k in ("server_sumsq", "server_apply", "unpack") if k in kern),
               key=lambda k: kern[k]["avg_ms"])
     bpe = bytes_per_elem(w, dom)
@@ -531,10 +582,15 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also run a plain torch copy of this many MiB (counter calibration)")
+                    help="also copy this many MiB with torch and with the probe's nontemporal "
+                         "copy (counter calibration)")
     ap.add_argument("--split", action="store_true",
                     help="time the worker step split at the exchange (worker compress + worker update, "
                          "one worker) instead of the fused compressed step")
+    ap.add_argument("--slab", action="store_true",
+                    help="place the state arrays and gradients in one allocation at 2 MiB-aligned offsets")
+    ap.add_argument("--slab-stagger", type=int, default=0,
+                    help="with --slab: array j starts j times this many bytes (a multiple of 256) later")
     ap.add_argument("--diagnostics", action="store_true",
                     help="also compute the per-chunk error norm and +1 count in every compressed step")
     ap.add_argument("--rocprof-summary", metavar="DIR")
@@ -588,28 +644,42 @@ def _counter_rows(d: str, counter: str):
                 yield r
 
 
+# Kernels whose streaming loads are nontemporal (their counters are calibrated on the probe's
+# nontemporal copy); the others (server pass 2) use ordinary loads (calibrated on the torch copy).
+NONTEMPORAL_KERNELS = {"compress", "chunk_sumsq", "dense", "worker_compress", "worker_update", "lamb_apply",
+                       "server_sumsq", "unpack"}
+# the probes of --copy-probe-mib 1024: (name, kernel-name fragment, grid in threads)
+COPY_PROBES = (("torch copy", "copyBuffer", 131072), ("nontemporal copy", "k_probe_copy<true>", 16777216))
+
+
 def traffic_profile(d: str, kernel: str, workload: str) -> str:
     """Calibrated HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE runs under d."""
     from adam_ob_compress_amd import synth
 
     w = synth.WORKLOADS[workload]
-    probe_kib = 1 << 20  # the --copy-probe-mib 1024 copy reads and writes 1 GiB each
-    res = {}
+    probe_kib = 1 << 20  # the --copy-probe-mib 1024 copies read and write 1 GiB each
+    res, factors = {}, {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         rows = list(_counter_rows(d, counter))
-        # the probe is the run's last 8 copy dispatches of grid 131072 (3 warm-up + 5 timed copies)
-        copies = sorted((r for r in rows if "copyBuffer" in r["Kernel_Name"] and r["Grid_Size"] == "131072"),
-                        key=lambda r: int(r["Dispatch_Id"]))
-        probe = [float(r["Counter_Value"]) for r in copies[-8:]]
+        # each probe's dispatches are the run's last 8 of its kernel and grid (3 warm-up + 5 timed)
+        for pname, frag, grid in COPY_PROBES:
+            copies = sorted((r for r in rows if frag in r["Kernel_Name"] and int(r["Grid_Size"]) == grid),
+                            key=lambda r: int(r["Dispatch_Id"]))
+            vals = [float(r["Counter_Value"]) for r in copies[-8:]]
+            if vals:
+                factors.setdefault(pname, {})[counter] = sum(vals) / len(vals) / probe_kib
         # the workload's own launches: the kernel's largest grid (the warm-up on a small scratch plan
         # launches the same kernels on small grids)
         mine = [r for r in rows if KERNEL_SYMBOL[kernel] in r["Kernel_Name"]]
         top = max((int(r["Grid_Size"]) for r in mine), default=0)
         kern = [float(r["Counter_Value"]) for r in mine if int(r["Grid_Size"]) == top]
-        if not probe or not kern:
+        if not kern or "torch copy" not in factors or counter not in factors["torch copy"]:
             raise SystemExit(f"no {counter} rows for the copy probe or {kernel} under {d}")
-        res[counter] = (sum(kern) / len(kern), len(kern), sum(probe) / len(probe) / probe_kib)
-    (fk, fn, ff), (wk, wn, wf) = res["FETCH_SIZE"], res["WRITE_SIZE"]
+        res[counter] = (sum(kern) / len(kern), len(kern))
+    nt = "nontemporal copy" in factors and len(factors["nontemporal copy"]) == 2
+    used = "nontemporal copy" if nt and kernel in NONTEMPORAL_KERNELS else "torch copy"
+    ff, wf = factors[used]["FETCH_SIZE"], factors[used]["WRITE_SIZE"]
+    (fk, fn), (wk, wn) = res["FETCH_SIZE"], res["WRITE_SIZE"]
     traffic = (fk / ff + wk / wf) * 1024
     alg = bytes_per_elem(w, kernel) * w.n
     if traffic < 0.5 * alg:
@@ -617,8 +687,13 @@ def traffic_profile(d: str, kernel: str, workload: str) -> str:
     run_flags = " --split" if kernel.startswith("worker_") else ""   # the split step's kernels
     rec = {"kernel": kernel, "workload": w.name, "kernel_src_sha": kernel_source_sha(),
            "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
-           "fetch_factor": round(ff, 5), "write_factor": round(wf, 5), "bytes_per_launch": round(traffic),
+           "calibration": used, "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
+           "factors": {k: {c: round(v, 5) for c, v in f.items()} for k, f in factors.items()},
+           "bytes_per_launch": round(traffic),
            "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 4)}
+    cal = "\n".join(f"| {k} | {f.get('FETCH_SIZE', float('nan')) * probe_kib:,.1f} | "
+                     f"{f.get('WRITE_SIZE', float('nan')) * probe_kib:,.1f} | {f.get('FETCH_SIZE', float('nan')):.5f} | "
+                     f"{f.get('WRITE_SIZE', float('nan')):.5f} |" for k, f in factors.items())
     return f"""# HBM traffic of `{kernel}` on {w.name}
 
 Kernel source sha (ob_compress.hip, ob_kernels.hip, ob_device.h, ob_internal.h, ob_api.cpp): {rec['kernel_src_sha']}.
@@ -629,9 +704,16 @@ Commands (each its own run on one MI355X, from the repository root, `export TMPD
     rocprofv3 --pmc WRITE_SIZE -d rocprof_out/write -o run --output-format csv -- python bench.py --workload {w.name}{run_flags} --steps 5 --warmup 2 --no-cpu --copy-probe-mib 1024
     python bench.py --traffic-profile rocprof_out --kernel {kernel} --workload {w.name}
 
-Calibration: the run also copies 1 GiB with torch (`__amd_rocclr_copyBuffer`, grid 131072), which
-reads and writes 1,048,576 KiB.  The counters read {ff * probe_kib:,.1f} KiB (FETCH_SIZE) and
-{wf * probe_kib:,.1f} KiB (WRITE_SIZE) per such dispatch: fetch factor {ff:.5f}, write factor {wf:.5f}.
+Calibration: the run also copies 1 GiB twice over -- with torch (`__amd_rocclr_copyBuffer`, grid
+131072, ordinary loads and stores) and with the probe library's copy (`k_probe_copy<true>`, grid
+16777216, 16-byte lanes with nontemporal loads and stores) -- each reading and writing 1,048,576 KiB
+per dispatch.  Counter readings per such dispatch and the factors they give:
+
+| copy | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch factor | write factor |
+|---|---|---|---|---|
+{cal}
+
+`{kernel}` is calibrated with the {used} (its streaming accesses are {"nontemporal" if used == "nontemporal copy" else "ordinary"}).
 
 | kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/launch (calibrated) | algorithmic bytes/launch | ratio |
 |---|---|---|---|---|---|---|

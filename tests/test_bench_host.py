@@ -88,12 +88,15 @@ def _counter_csv(path, rows):
             wr.writerow(r)
 
 
-def _fake_counter_runs(d, kernel_rows):
-    """FETCH_SIZE and WRITE_SIZE runs as rocprofv3 writes them: 8 copy-probe dispatches (1 GiB read and
-    written, read by the counter at half its size) plus the given kernel dispatches."""
-    for counter, probe_kib in (("FETCH_SIZE", 524288.0), ("WRITE_SIZE", 1048576.0)):
+def _fake_counter_runs(d, kernel_rows, nt_fetch_kib=524288.0):
+    """FETCH_SIZE and WRITE_SIZE runs as rocprofv3 writes them: 8 dispatches of each copy probe (1 GiB
+    read and written; the torch copy's fetch read by the counter at half its size, the nontemporal
+    copy's at nt_fetch_kib) plus the given kernel dispatches."""
+    for counter, probe_kib, nt_kib in (("FETCH_SIZE", 524288.0, nt_fetch_kib), ("WRITE_SIZE", 1048576.0, 1048576.0)):
         rows = [{"Dispatch_Id": i, "Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 131072,
                  "Counter_Name": counter, "Counter_Value": probe_kib} for i in range(8)]
+        rows += [{"Dispatch_Id": 10 + i, "Kernel_Name": "void (anonymous namespace)::k_probe_copy<true>(...)",
+                  "Grid_Size": 16777216, "Counter_Name": counter, "Counter_Value": nt_kib} for i in range(8)]
         rows += [dict(r, Counter_Name=counter, Counter_Value=r[counter]) for r in kernel_rows]
         for r in rows:
             r.pop("FETCH_SIZE", None)
@@ -117,6 +120,23 @@ def test_traffic_profile_uses_the_workload_launches_only(tmp_path):
     rec = json.loads([ln for ln in md.splitlines() if ln.startswith("traffic-json:")][0].split(":", 1)[1])
     assert abs(rec["bytes_per_launch"] - alg) / alg < 1e-3
     assert abs(rec["traffic_over_algorithmic"] - 1.0) < 1e-3
+
+
+def test_traffic_profile_takes_the_nontemporal_calibration_for_nontemporal_kernels(tmp_path):
+    """A nontemporal copy whose fetch reads at the full 1 GiB sets the fetch factor to 1 for the
+    nontemporal kernels (compress), while server pass 2 (ordinary loads) keeps the torch copy's 0.5."""
+    w = synth.WORKLOADS["bert-base-110M-fp32"]
+    fetch_kib = 20.0 * w.n / 1024                                  # 20 B read per element, counted in full
+    write_kib = 12.125 * w.n / 1024
+    big = [{"Dispatch_Id": 100 + i, "Kernel_Name": "void ob::k_compress<GradF32>(...)", "Grid_Size": 6829568,
+            "FETCH_SIZE": fetch_kib, "WRITE_SIZE": write_kib} for i in range(7)]
+    _fake_counter_runs(str(tmp_path), big, nt_fetch_kib=1048576.0)
+    rec = json.loads([ln for ln in bench.traffic_profile(str(tmp_path), "compress", w.name).splitlines()
+                      if ln.startswith("traffic-json:")][0].split(":", 1)[1])
+    assert rec["calibration"] == "nontemporal copy" and rec["fetch_factor"] == 1.0
+    assert abs(rec["traffic_over_algorithmic"] - 1.0) < 1e-3
+    assert rec["factors"]["torch copy"]["FETCH_SIZE"] == 0.5
+    assert "server_apply" not in bench.NONTEMPORAL_KERNELS
 
 
 def test_traffic_profile_refuses_runs_without_a_workload_launch(tmp_path):
