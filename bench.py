@@ -622,7 +622,8 @@ def main():
 # ------------------------------------------------------------------------------------------------
 
 def _short(name: str) -> str:
-    for key in ("k_chunk_sumsq", "k_compress", "k_dense", "k_server", "k_unpack", "k_pack", "k_lamb_apply",
+    for key in ("k_chunk_sumsq", "k_compress", "k_dense", "k_server_sumsq_lines", "k_server", "k_unpack", "k_pack",
+                "k_lamb_apply",
                 "k_trust_ratio", "k_diag_reduce", "k_scale_finalize", "k_worker_compress", "k_worker_update"):
         if key in name:
             tmpl = name.split(key, 1)[1]
@@ -630,8 +631,11 @@ def _short(name: str) -> str:
     return name[:80]
 
 
+# the kernel names each timing kind covers (server pass 1: the whole-line kernel where the layout allows
+# it, the per-lane one elsewhere)
 KERNEL_SYMBOL = {"compress": "k_compress<", "chunk_sumsq": "k_chunk_sumsq<", "dense": "k_dense<",
-                 "server_sumsq": "k_server<false>", "server_apply": "k_server<true>", "unpack": "k_unpack",
+                 "server_sumsq": ("k_server_sumsq_lines", "k_server<false>"), "server_apply": "k_server<true>",
+                 "unpack": "k_unpack",
                  "lamb_apply": "k_lamb_apply<", "trust_ratio": "k_trust_ratio", "diag": "k_diag_reduce",
                  "scale": "k_scale_finalize", "worker_compress": "k_worker_compress<",
                  "worker_update": "k_worker_update"}
@@ -670,7 +674,8 @@ def traffic_profile(d: str, kernel: str, workload: str) -> str:
                 factors.setdefault(pname, {})[counter] = sum(vals) / len(vals) / probe_kib
         # the workload's own launches: the kernel's largest grid (the warm-up on a small scratch plan
         # launches the same kernels on small grids)
-        mine = [r for r in rows if KERNEL_SYMBOL[kernel] in r["Kernel_Name"]]
+        syms = KERNEL_SYMBOL[kernel] if isinstance(KERNEL_SYMBOL[kernel], tuple) else (KERNEL_SYMBOL[kernel],)
+        mine = [r for r in rows if any(sym in r["Kernel_Name"] for sym in syms)]
         top = max((int(r["Grid_Size"]) for r in mine), default=0)
         kern = [float(r["Counter_Value"]) for r in mine if int(r["Grid_Size"]) == top]
         if not kern or "torch copy" not in factors or counter not in factors["torch copy"]:
