@@ -335,22 +335,27 @@ def _every_chunk_one_step(w, plan, kind, s, device, err_sigma, m_sigma, log):
     off = w.chunk_offsets()
     pending = collections.deque()
     mism = nf = 0
+    inflight = 0      # elements of the chunks queued or being checked (host memory ~100 B each)
 
-    def drain(limit):
-        nonlocal mism, nf
-        while len(pending) > limit:
-            a, b = pending.popleft().result()
+    def drain(max_tasks, max_elems):
+        nonlocal mism, nf, inflight
+        while pending and (len(pending) > max_tasks or inflight > max_elems):
+            fut, size = pending.popleft()
+            a, b = fut.result()
             mism += a
             nf += b
+            inflight -= size
 
     for c in range(w.n_chunks):
         a, b = int(off[c]), int(off[c + 1])
+        # bound the host memory: at most 2 chunks per thread and 2^29 elements in flight
+        drain(2 * _POOL._max_workers - 1, (1 << 29) - (b - a))
         # this chunk's inputs, drawn again on their own: nothing the step wrote reaches the oracle
         gh = synth.host(synth.draw_grad_window(w, s, a, b, device))
         st = [synth.host(t) for t in synth.draw_state_window(w, a, b, device, err_sigma, m_sigma)]
-        pending.append(_POOL.submit(_check_one_chunk, ChunkRef(c, a, b, *st), gh, w, kind, s, opt))
-        drain(2 * _POOL._max_workers)
-    drain(0)
+        pending.append((_POOL.submit(_check_one_chunk, ChunkRef(c, a, b, *st), gh, w, kind, s, opt), b - a))
+        inflight += b - a
+    drain(0, 0)
     if kind == "compressed":
         assert int(opt.nonfinite.item()) == nf, f"{w.name}: non-finite count"
     log(f"{w.name} {kind} step {s}: all {w.n_chunks} chunks match ({mism} scale ulp mismatches)")

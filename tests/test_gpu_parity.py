@@ -727,6 +727,15 @@ def test_workload_bert_base_16bit_error(edt):
     assert counts["dense"] == 5 and counts["compressed"] == 20
 
 
+@pytest.mark.parametrize("name", ["bert-base-110M-fp32-err-bf16", "bert-base-110M-fp32-err-f16",
+                                  "bert-base-110M-fp32-err-bf16-sr", "bert-base-110M-fp32-lamb"])
+def test_workload_bert_base_variants_every_chunk(name):
+    """BERT-base's variants, every one of the 197 chunks (layers, for LAMB): after the first compressed
+    step (step index 5) and after a dense step (index 0), each over the whole buffer from a seeded state
+    with a non-zero error buffer and momentum; LAMB's ratios included."""
+    P.check_every_chunk(synth.WORKLOADS[name], dense_step=0, log=lambda *_: None)
+
+
 def test_workload_server_2p28_w8():
     """n = 2^28, W = 8, chunks of 2^20: 10 rounds of server reduce + unpack; the server error carries
     across rounds.  Round 0 (server error 0, seeded worker words and scales) checks all 256 chunks;
@@ -874,6 +883,17 @@ def test_workload_llama2_7b_every_chunk():
     variance refresh (step index 15, t = 16), each over the whole buffer from a seeded state with a
     non-zero error buffer and momentum."""
     P.check_every_chunk(synth.LLAMA2_7B, dense_step=15, log=lambda *_: None)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["llama2-7B-bf16-lamb", "gpt2-1.5B-bf16-err-bf16"])
+def test_workload_large_variants_every_chunk(name):
+    """Every chunk of 1-bit LAMB on Llama-2-7B's 291 layers (ratios included; the two 131M-element
+    layers take the per-chunk sums kernel) and of GPT-2-1.5B with a bf16 error buffer, after the first
+    compressed step over the whole buffer from a seeded state.  (LAMB's dense step on these layers is
+    checked every step on the tracked layers of test_workload_llama2_7b_lamb; checking it on every
+    layer too would double this test's ~75 s of host copies.)"""
+    P.check_every_chunk(synth.WORKLOADS[name], log=lambda *_: None)
 
 
 @pytest.mark.slow
