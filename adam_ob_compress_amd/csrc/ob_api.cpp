@@ -318,28 +318,18 @@ ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_off
     p->n = n;
     p->K = static_cast<int32_t>(K);
 
-    // block tables: consecutive blocks per chunk
+    // block tables: consecutive blocks per chunk, checked against what the kernels assume before any
+    // of them reaches the device
     std::vector<ob::Item> items[kTables];
     std::vector<int32_t> first[kTables];
     for (int pass = 0; pass < kTables; ++pass) {
         ob_plan_s::Table& t = p->t[pass];
         t.block_elems = choose_block_elems(n, pass);
-        first[pass].assign(static_cast<size_t>(K) + 1, 0);
-        for (int64_t c = 0; c < K; ++c) {
-            first[pass][c] = static_cast<int32_t>(items[pass].size());
-            for (int64_t s = off[c]; s < off[c + 1]; s += t.block_elems) {
-                ob::Item it;
-                it.start = s;
-                it.len = static_cast<int32_t>(std::min<int64_t>(t.block_elems, off[c + 1] - s));
-                it.chunk = static_cast<int32_t>(c);
-                items[pass].push_back(it);
-                if (items[pass].size() > static_cast<size_t>(INT32_MAX)) {
-                    delete p;
-                    return OB_ERR_ARG;
-                }
-            }
+        if (!ob::build_block_table(off, t.block_elems, items[pass], first[pass]) ||
+            ob::check_block_table(off, t.block_elems, items[pass], first[pass]) != nullptr) {
+            delete p;
+            return OB_ERR_ARG;
         }
-        first[pass][K] = static_cast<int32_t>(items[pass].size());
         t.n_items = static_cast<int64_t>(items[pass].size());
     }
     for (int64_t c = 0; c < K; ++c)

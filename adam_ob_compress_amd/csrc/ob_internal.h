@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ob_tables.h"
+
 namespace ob {
 
 // Launch geometry of every per-element kernel: 256 threads (four 64-wide waves), each lane owning
@@ -12,14 +14,6 @@ namespace ob {
 constexpr int kBlock = 256;
 constexpr int kVec = 4;
 constexpr int kTile = kBlock * kVec;
-
-// One work block: a contiguous run of elements inside one chunk.  Blocks of a chunk are consecutive,
-// start at multiples of 64 elements and (except a chunk's last) hold a whole number of tiles.
-struct Item {
-    int64_t start;
-    int32_t len;
-    int32_t chunk;
-};
 
 // Device-side view of a plan for one launch.  Pass-1 kernels (sums of squares) and pass-2 kernels
 // (everything that needs a chunk's scale, and the dense step) use different block tables: pass 1

@@ -20,25 +20,11 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
-__device__ __forceinline__ Item uniform_item(int64_t j, int64_t be, int32_t nbf, const UniformTables& t)
-{
-    // blocks of chunk c are [c * nbf, (c + 1) * nbf) for every chunk but the last
-    int64_t c = t.K > 1 ? j / nbf : 0;
-    if (c > t.K - 1) c = t.K - 1;
-    const int64_t start = c * t.chunk + (j - c * nbf) * be;
-    const int64_t end = c == t.K - 1 ? t.n : (c + 1) * t.chunk;
-    Item it;
-    it.start = start;
-    it.len = static_cast<int32_t>(end - start < be ? end - start : be);
-    it.chunk = static_cast<int32_t>(c);
-    return it;
-}
-
 __global__ __launch_bounds__(kBlock) void k_uniform_tables(UniformTables t)
 {
     const int64_t j = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
-    if (j < t.n1) t.items1[j] = uniform_item(j, t.be1, t.nbf1, t);
-    if (j < t.n2) t.items2[j] = uniform_item(j, t.be2, t.nbf2, t);
+    if (j < t.n1) t.items1[j] = uniform_item(j, t.n, t.chunk, t.K, t.be1, t.nbf1);
+    if (j < t.n2) t.items2[j] = uniform_item(j, t.n, t.chunk, t.K, t.be2, t.nbf2);
     if (j <= t.K) {
         const int32_t c = static_cast<int32_t>(j);
         t.first1[j] = c < t.K ? c * t.nbf1 : static_cast<int32_t>(t.n1);
