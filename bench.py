@@ -45,7 +45,7 @@ DEFAULT_WORKLOAD = "llama2-7B-bf16-ema"
 # the committed counter summaries stale
 KERNEL_SOURCES = ("adam_ob_compress_amd/csrc/ob_compress.hip", "adam_ob_compress_amd/csrc/ob_kernels.hip",
                   "adam_ob_compress_amd/csrc/ob_device.h", "adam_ob_compress_amd/csrc/ob_internal.h",
-                  "adam_ob_compress_amd/csrc/ob_api.cpp")
+                  "adam_ob_compress_amd/csrc/ob_tables.h", "adam_ob_compress_amd/csrc/ob_api.cpp")
 
 
 def kernel_source_sha() -> str:
@@ -701,7 +701,7 @@ def traffic_profile(d: str, kernel: str, workload: str) -> str:
                      f"{f.get('WRITE_SIZE', float('nan')):.5f} |" for k, f in factors.items())
     return f"""# HBM traffic of `{kernel}` on {w.name}
 
-Kernel source sha (ob_compress.hip, ob_kernels.hip, ob_device.h, ob_internal.h, ob_api.cpp): {rec['kernel_src_sha']}.
+Kernel source sha (ob_compress.hip, ob_kernels.hip, ob_device.h, ob_internal.h, ob_tables.h, ob_api.cpp): {rec['kernel_src_sha']}.
 
 Commands (each its own run on one MI355X, from the repository root, `export TMPDIR=/tmp`):
 
