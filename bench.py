@@ -367,13 +367,14 @@ def run(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": (("bf16 grads + f32 state" if w.grad_dtype == "bf16" else "f32")
-                  + ("" if w.err_dtype == "f32" else f", {w.err_dtype} error buffer")
-                  + (" (stochastic rounding)" if w.err_rounding == "stochastic" else "")),
-        "data": "synthetic (seeded; ring of pre-drawn gradients)",
+        # the arithmetic: compensation and the stored state in fp32, each formula line evaluated in
+        # fp64 and rounded once (the storage types are in config)
+        "dtype": "f32",
+        "data": f"synthetic (seeded; {ring} pre-drawn gradient{'s' if ring > 1 else ''} cycled)",
         "config": {"workload": w.name, "elements": w.n, "chunks": plan.num_chunks,
                    "optimizer": "1-bit " + ("LAMB" if w.optimizer == "lamb" else "Adam"),
                    "grad_dtype": w.grad_dtype, "err_dtype": w.err_dtype, "err_rounding": w.err_rounding,
+                   "state_dtype": "f32", "formula_dtype": "f64",
                    "clip": w.clip,
                    "error_feedback": "ema" if w.ef_mode else "plain", "int8_signs": w.int8_signs,
                    "freeze_step": w.freeze_step, "refresh_period": w.refresh_period,
