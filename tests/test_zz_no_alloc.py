@@ -4,7 +4,8 @@ Called through the C ABI (the ctypes binding), it must give bit for bit the outp
 ob_adam_compress_step with a plan of the same n and chunk size -- the same kernels over the same
 block tables, the tables and partial sums living in the library's static device buffer instead of the
 plan's allocations.  Each case makes calls in a row on one stream, later ones smaller than the first
-(the buffer then still holds the first call's larger tables), and then the first size again.
+(the buffer then still holds the first call's larger tables), and then the first size again.  The
+step is also captured into a HIP graph and replayed.
 """
 import numpy as np
 import pytest
@@ -95,3 +96,58 @@ SEQUENCES = {
 def test_noalloc_step_equals_the_plan_step(name):
     for k, case in enumerate(SEQUENCES[name]):
         _one(*case, seed=100 + k)
+
+
+def test_noalloc_step_under_graph_capture():
+    """The reason the entry point exists: captured once into a HIP graph (its table kernel and both passes,
+    nothing allocated while capturing) and replayed with new gradients copied in between, every replay
+    gives bit for bit what the same step gives eagerly."""
+    n, chunk = 3 * (1 << 20) + 4096, 1 << 20
+    K = (n + chunk - 1) // chunk
+    hp = ob.hparams(lr=1e-4, clip=5.0, ef_mode=ob.OB_EF_EMA, ef_beta=0.9)
+    gen = torch.Generator(device=DEV)
+    grads = []
+    for s in range(4):
+        gen.manual_seed(500 + s)
+        grads.append((torch.randn(n, generator=gen, device=DEV) * 20.0).to(torch.bfloat16))
+
+    def buffers(seed):
+        _, err, m, v, p = _state(n, "bf16", "f16", seed)
+        return dict(err=err, m=m, v=v, p=p,
+                    words=torch.zeros((n + 31) // 32, dtype=torch.int32, device=DEV),
+                    scales=torch.zeros(K, dtype=torch.float32, device=DEV),
+                    signs=torch.zeros(n, dtype=torch.int8, device=DEV),
+                    nf=torch.zeros(1, dtype=torch.int64, device=DEV))
+
+    def step(b, g):
+        ob.ob_adam_compress_step_noalloc(n, chunk, g, b["err"], b["m"], b["v"], b["p"], b["words"], b["scales"],
+                                         hp, b["signs"], b["nf"])
+
+    def snapshot(b):
+        return [_bits(b[k]) for k in ("err", "m", "p", "words", "scales", "signs", "nf")]
+
+    a = buffers(9)
+    eager = []
+    for s in range(4):
+        step(a, grads[s])
+        torch.cuda.synchronize()
+        eager.append(snapshot(a))
+
+    b = buffers(9)
+    g_in = torch.empty_like(grads[0])
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        g_in.copy_(grads[0])
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            step(b, g_in)
+    torch.cuda.synchronize()
+    for s in range(4):
+        g_in.copy_(grads[s])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, x, y in zip(("err", "m", "p", "words", "scales", "signs", "nonfinite"), snapshot(b), eager[s]):
+            assert np.array_equal(x, y), f"replay {s}: {name} differs from the eager step"
