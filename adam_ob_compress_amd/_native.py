@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         "ob_plan_num_chunks": (I64, [P]),
         "ob_plan_num_blocks": (I64, [P]),
         "ob_plan_block_elems": (I64, [P]),
+        "ob_plan_num_groups": (I64, [P, I32, I32, I32]),
         "ob_adam_warmup_step": (I32, [P, P, I32, P, P, P, HP, P]),
         "ob_adam_compress_step": (I32, [P, P, I32, P, I32, P, P, P, P, P, P, P, HP, P]),
         "ob_adam_compress_step_noalloc": (I32, [I64, I64, P, I32, P, I32, P, P, P, P, P, P, P, HP, P]),
@@ -168,6 +169,10 @@ class Plan:
     @property
     def block_elems(self) -> int:
         return int(lib().ob_plan_block_elems(self.handle))
+
+    def num_groups(self, g_dtype: int, err_dtype: int = OB_F32, lamb: bool = False) -> int:
+        """Launches of each of the compressed step's two kernels per step (its chunk groups)."""
+        return int(lib().ob_plan_num_groups(self.handle, g_dtype, err_dtype, 1 if lamb else 0))
 
     def destroy(self):
         if self.handle:

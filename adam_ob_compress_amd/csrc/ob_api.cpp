@@ -39,6 +39,14 @@ struct ob_plan_s {
     double* diag_err_sumsq = nullptr;
     unsigned long long* diag_plus = nullptr;
 
+    // Chunk groups of the compressed step's two passes.  Pass 2 re-reads g and err, which pass 1 has
+    // just read; run over consecutive chunks whose pass-1 bytes about fit in the GPU's last-level cache
+    // (the Infinity Cache, 256 MB on MI355X), pass 1 then pass 2 per group serves most of that re-read
+    // from the cache instead of HBM.  groups[w]: the groups when pass 1 reads w bytes per element (g,
+    // err and, for LAMB, p: 4 to 12); one group of all chunks when grouping is off.
+    int64_t group_bytes = 0;
+    std::vector<ob::ChunkGroup> groups[13];
+
     // block tables, one per kernel kind (kTables)
     struct Table {
         int64_t block_elems = 0;
@@ -52,6 +60,7 @@ struct ob_plan_s {
     struct Rec {
         int kernel;
         hipEvent_t a, b;
+        bool owns_a;   // false: a is the previous record's b (a chained launch), pooled with that record
     };
     std::vector<Rec> pending;
     std::vector<hipEvent_t> pool;
@@ -76,6 +85,7 @@ struct ob_plan_s {
         pd.n = n;
         pd.n_items = t[table].n_items;
         pd.K = K;
+        pd.item0 = 0;
         return pd;
     }
 };
@@ -89,6 +99,14 @@ constexpr int64_t kMaxBlockElems = int64_t(1) << 20;
 // Measured: at 1,761 partials (BERT-base's embedding) the in-block reduction is still the faster; the
 // extra launch is for chunks so large that every block re-adding their partials would dominate.
 constexpr int64_t kFinalizeAt = 16 * ob::kBlock;
+
+// Pass-1 bytes per chunk group (the compressed step's passes run group by group).  Measured on MI355X
+// (interleaved A/B in one process, outputs bit-identical): 320 MB groups took the Llama-2-7B-sized
+// step (6.7G elements, bf16 g) from 39.9 to 37.7 ms and the GPT-2-1.5B-sized one from 8.78 to 8.20 ms;
+// 192 and 400 MB were 1-2% slower than 320, 64 MB (one chunk per group) slower than no groups at all,
+// and the same groups with nontemporal pass-1 loads (which do not stay in the cache) slower too.
+// OB_GROUP_BYTES overrides (0 = one launch per pass).
+constexpr int64_t kGroupBytes = int64_t(320) << 20;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -143,6 +161,26 @@ int64_t choose_block_elems(int64_t n, int table)
     return std::min<int64_t>(std::max<int64_t>(e, 4 * ob::kTile), 24 * ob::kTile);
 }
 
+int64_t group_budget()
+{
+    if (const char* env = std::getenv("OB_GROUP_BYTES")) return std::max<long long>(0, std::atoll(env));
+    return kGroupBytes;
+}
+
+// Bytes per element that pass 1 reads: g, the error buffer and (LAMB) p.
+int pass1_width(int g_dtype, int err_dtype, int lamb)
+{
+    return (g_dtype == OB_BF16 ? 2 : 4) + (err_dtype == OB_F32 ? 4 : 2) + (lamb ? 4 : 0);
+}
+
+// A launch over blocks [i0, i0 + count) of the view's table.
+ob::PlanDev group_view(ob::PlanDev pd, int32_t i0, int32_t count)
+{
+    pd.item0 = i0;
+    pd.n_items = count;
+    return pd;
+}
+
 void free_plan(ob_plan p)
 {
     if (!p) return;
@@ -182,24 +220,36 @@ hipEvent_t take_event(ob_plan p)
     return e;
 }
 
-// Enqueue one kernel via `launch`, bracketed by events when timing is on.
+// Enqueue one kernel via `launch`, bracketed by events when timing is on.  chain != nullptr: launches
+// of one call that follow each other on the stream with nothing in between share events -- a launch
+// starts at the event that ended the previous one (*chain, if set) and leaves its own end event in
+// *chain -- so a call with many launches (the compressed step's chunk groups) records one event per
+// launch instead of two.
 template <class F>
-ob_status timed(ob_plan p, int kernel, hipStream_t s, F&& launch)
+ob_status timed(ob_plan p, int kernel, hipStream_t s, F&& launch, hipEvent_t* chain = nullptr)
 {
     hipEvent_t a = nullptr, b = nullptr;
+    bool owns_a = true;
     if (p && p->timing) {
-        a = take_event(p);
+        if (chain && *chain) {
+            a = *chain;
+            owns_a = false;
+        } else {
+            a = take_event(p);
+        }
         b = take_event(p);
-        if (a && b) (void)hipEventRecord(a, s);
+        if (a && b && owns_a) (void)hipEventRecord(a, s);
     }
     (void)hipGetLastError();  // clear a stale error so the check below sees this launch only
     const hipError_t err = launch();
     if (a && b) {
         (void)hipEventRecord(b, s);
-        p->pending.push_back({kernel, a, b});
+        p->pending.push_back({kernel, a, b, owns_a});
+        if (chain) *chain = b;
     } else {
-        if (a) p->pool.push_back(a);
+        if (a && owns_a) p->pool.push_back(a);
         if (b) p->pool.push_back(b);
+        if (chain) *chain = nullptr;
     }
     return err == hipSuccess ? OB_OK : OB_ERR_HIP;
 }
@@ -215,7 +265,7 @@ ob_status drain_timing(ob_plan p)
             p->total_ms[r.kernel] += ms;
             p->launches[r.kernel] += 1;
         }
-        p->pool.push_back(r.a);
+        if (r.owns_a) p->pool.push_back(r.a);
         p->pool.push_back(r.b);
     }
     p->pending.clear();
@@ -335,6 +385,17 @@ ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_off
     for (int64_t c = 0; c < K; ++c)
         p->p1_max = std::max<int64_t>(p->p1_max, first[T_PASS1][c + 1] - first[T_PASS1][c]);
     p->off128 = std::all_of(off.begin(), off.end() - 1, [](int64_t o) { return o % 128 == 0; });
+    // chunk groups (none while any chunk needs its sums formed by a launch of their own)
+    p->group_bytes = group_budget();
+    const bool grouping = p->group_bytes > 0 && p->p1_max <= kFinalizeAt;
+    for (int w = 4; w <= 12; w += 2) {
+        const int64_t max_elems = grouping ? std::max<int64_t>(1, p->group_bytes / w) : 0;
+        ob::build_chunk_groups(off, first[T_PASS1], first[T_COMPRESS], max_elems, p->groups[w]);
+        if (ob::check_chunk_groups(off, first[T_PASS1], first[T_COMPRESS], max_elems, p->groups[w]) != nullptr) {
+            delete p;
+            return OB_ERR_ARG;
+        }
+    }
 
     if (hipGetDevice(&p->device) != hipSuccess) {
         delete p;
@@ -394,6 +455,11 @@ int64_t ob_plan_num_elements(ob_plan plan) { return plan ? plan->n : -1; }
 int64_t ob_plan_num_chunks(ob_plan plan) { return plan ? plan->K : -1; }
 int64_t ob_plan_num_blocks(ob_plan plan) { return plan ? plan->t[T_COMPRESS].n_items : -1; }
 int64_t ob_plan_block_elems(ob_plan plan) { return plan ? plan->t[T_COMPRESS].block_elems : -1; }
+int64_t ob_plan_num_groups(ob_plan plan, ob_dtype g_dtype, ob_dtype err_dtype, int32_t lamb)
+{
+    if (!plan || !valid_dtype(g_dtype) || !valid_err_dtype(err_dtype)) return -1;
+    return static_cast<int64_t>(plan->groups[pass1_width(g_dtype, err_dtype, lamb)].size());
+}
 
 ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* m, float* v, float* p,
                               const ob_hparams* hp, hipStream_t stream)
@@ -466,13 +532,14 @@ hipError_t compress_by_format(ob_dtype err_dtype, const ob::PlanDev& pd, const v
 // Pass-2 view of the plan.  With many partials per chunk, the chunk sums are formed first (one block
 // per chunk) and the view's pass-1 table becomes the identity over them, so that each pass-2 block
 // forms its scale from one partial instead of all of them.
-ob_status pass2_view(ob_plan plan, int table, hipStream_t stream, ob::PlanDev* out)
+ob_status pass2_view(ob_plan plan, int table, hipStream_t stream, ob::PlanDev* out, hipEvent_t* chain = nullptr)
 {
     *out = plan->dev(table);
     if (plan->p1_max <= kFinalizeAt) return OB_OK;
     const ob::PlanDev pd1 = plan->dev(T_PASS1);
-    const ob_status st = timed(plan, OB_KERNEL_SCALE, stream,
-                               [&] { return ob::launch_chunk_sums(pd1, plan->d_chunk_sums, stream); });
+    const ob_status st = timed(
+        plan, OB_KERNEL_SCALE, stream, [&] { return ob::launch_chunk_sums(pd1, plan->d_chunk_sums, stream); },
+        chain);
     out->p1_first = plan->d_ident;
     out->partials = plan->d_chunk_sums;
     return st;
@@ -519,16 +586,28 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
     const int ema = hp->ef_mode == OB_EF_EMA;
     auto nf = reinterpret_cast<unsigned long long*>(nonfinite_out);
     const float* lamb_p = lamb ? p : nullptr;
-    ob_status st = timed(plan, OB_KERNEL_CHUNK_SUMSQ, stream, [&] {
-        return sumsq_by_format(err_dtype, pd1, g, bf, err, cp.clip, lamb_p, stream);
-    });
-    if (st != OB_OK) return st;
-    if ((st = pass2_view(plan, T_COMPRESS, stream, &pd)) != OB_OK) return st;
-    st = timed(plan, OB_KERNEL_COMPRESS, stream, [&] {
-        return compress_by_format(err_dtype, pd, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf, ema,
-                                  lamb, cp, stream);
-    });
-    if (st != OB_OK || !plan->diag_err_sumsq) return st;
+    ob_status st = OB_OK;
+    hipEvent_t chain = nullptr;
+    for (const ob::ChunkGroup& gr : plan->groups[pass1_width(g_dtype, err_dtype, lamb)]) {
+        st = timed(
+            plan, OB_KERNEL_CHUNK_SUMSQ, stream,
+            [&] {
+                return sumsq_by_format(err_dtype, group_view(pd1, gr.i1, gr.n1), g, bf, err, cp.clip, lamb_p,
+                                       stream);
+            },
+            &chain);
+        if (st != OB_OK) return st;
+        if ((st = pass2_view(plan, T_COMPRESS, stream, &pd, &chain)) != OB_OK) return st;
+        st = timed(
+            plan, OB_KERNEL_COMPRESS, stream,
+            [&] {
+                return compress_by_format(err_dtype, group_view(pd, gr.i2, gr.n2), g, bf, err, m, v, p, words_out,
+                                          scales_out, signs_out, nf, ema, lamb, cp, stream);
+            },
+            &chain);
+        if (st != OB_OK) return st;
+    }
+    if (!plan->diag_err_sumsq) return st;
     const ob::PlanDev pdd = plan->dev(T_COMPRESS);   // the pass-1 table the error sums were written by
     return timed(plan, OB_KERNEL_DIAG, stream, [&] {
         return ob::launch_diag_reduce(pdd, plan->diag_err_sumsq, plan->diag_plus, stream);
@@ -598,29 +677,36 @@ ob_status ob_adam_worker_compress(ob_plan plan, const void* g, ob_dtype g_dtype,
     const int bf = g_dtype == OB_BF16;
     const int ema = hp->ef_mode == OB_EF_EMA;
     auto nf = reinterpret_cast<unsigned long long*>(nonfinite_out);
-    ob_status st = timed(plan, OB_KERNEL_CHUNK_SUMSQ, stream, [&] {
-        switch (err_dtype) {
-        case OB_BF16: return ob::launch_chunk_sumsq<OB_BF16>(pd1, g, bf, err, cp.clip, nullptr, stream);
-        case OB_F16: return ob::launch_chunk_sumsq<OB_F16>(pd1, g, bf, err, cp.clip, nullptr, stream);
-        default: return ob::launch_chunk_sumsq<OB_F32>(pd1, g, bf, err, cp.clip, nullptr, stream);
-        }
-    });
-    if (st != OB_OK) return st;
-    ob::PlanDev pd;
-    if ((st = pass2_view(plan, T_COMPRESS, stream, &pd)) != OB_OK) return st;
-    return timed(plan, OB_KERNEL_WORKER_COMPRESS, stream, [&] {
-        switch (err_dtype) {
-        case OB_BF16:
-            return ob::launch_worker_compress<OB_BF16>(pd, g, bf, err, words_out, scales_out, signs_out, nf, ema, cp,
-                                                       stream);
-        case OB_F16:
-            return ob::launch_worker_compress<OB_F16>(pd, g, bf, err, words_out, scales_out, signs_out, nf, ema, cp,
-                                                      stream);
-        default:
-            return ob::launch_worker_compress<OB_F32>(pd, g, bf, err, words_out, scales_out, signs_out, nf, ema, cp,
-                                                      stream);
-        }
-    });
+    ob_status st = OB_OK;
+    hipEvent_t chain = nullptr;
+    for (const ob::ChunkGroup& gr : plan->groups[pass1_width(g_dtype, err_dtype, 0)]) {
+        st = timed(
+            plan, OB_KERNEL_CHUNK_SUMSQ, stream,
+            [&] {
+                return sumsq_by_format(err_dtype, group_view(pd1, gr.i1, gr.n1), g, bf, err, cp.clip, nullptr,
+                                       stream);
+            },
+            &chain);
+        if (st != OB_OK) return st;
+        ob::PlanDev pd;
+        if ((st = pass2_view(plan, T_COMPRESS, stream, &pd, &chain)) != OB_OK) return st;
+        const ob::PlanDev pg = group_view(pd, gr.i2, gr.n2);
+        st = timed(plan, OB_KERNEL_WORKER_COMPRESS, stream, [&] {
+            switch (err_dtype) {
+            case OB_BF16:
+                return ob::launch_worker_compress<OB_BF16>(pg, g, bf, err, words_out, scales_out, signs_out, nf, ema,
+                                                           cp, stream);
+            case OB_F16:
+                return ob::launch_worker_compress<OB_F16>(pg, g, bf, err, words_out, scales_out, signs_out, nf, ema,
+                                                          cp, stream);
+            default:
+                return ob::launch_worker_compress<OB_F32>(pg, g, bf, err, words_out, scales_out, signs_out, nf, ema,
+                                                          cp, stream);
+            }
+        }, &chain);
+        if (st != OB_OK) return st;
+    }
+    return st;
 }
 
 ob_status ob_adam_worker_update(ob_plan plan, const uint32_t* words, const float* scales, float* m,
@@ -834,17 +920,31 @@ ob_status ob_adam_compress_step_noalloc(int64_t n, int64_t chunk_size, const voi
     auto nf = reinterpret_cast<unsigned long long*>(nonfinite_out);
     (void)hipGetLastError();
     if (ob::launch_uniform_tables(t, stream) != hipSuccess) return OB_ERR_HIP;
-    if (sumsq_by_format(err_dtype, pd1, g, bf, err, cp.clip, nullptr, stream) != hipSuccess) return OB_ERR_HIP;
-    if (finalize) {
+    if (finalize) {   // chunks too large to share the cache: whole-buffer passes, with per-chunk sums
+        if (sumsq_by_format(err_dtype, pd1, g, bf, err, cp.clip, nullptr, stream) != hipSuccess) return OB_ERR_HIP;
         double* sums = reinterpret_cast<double*>(base + o_sums);
         if (ob::launch_chunk_sums(pd1, sums, stream) != hipSuccess) return OB_ERR_HIP;
         pd2.p1_first = t.ident;
         pd2.partials = sums;
+        return compress_by_format(err_dtype, pd2, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf, ema,
+                                  0, cp, stream) == hipSuccess
+                   ? OB_OK
+                   : OB_ERR_HIP;
     }
-    return compress_by_format(err_dtype, pd2, g, bf, err, m, v, p, words_out, scales_out, signs_out, nf, ema, 0,
-                              cp, stream) == hipSuccess
-               ? OB_OK
-               : OB_ERR_HIP;
+    // chunk groups of q chunks (the plan's greedy grouping, for equal chunks; the last group takes the rest)
+    const int64_t budget = group_budget();
+    const int64_t max_elems = budget > 0 ? std::max<int64_t>(1, budget / pass1_width(g_dtype, err_dtype, 0)) : 0;
+    const int64_t q = max_elems > 0 ? std::max<int64_t>(1, max_elems / chunk_size) : K;
+    for (int64_t c0 = 0; c0 < K; c0 += q) {
+        const ob::ChunkGroup gr = ob::uniform_chunk_group(c0, q, K, nbf1, n1, nbf2, n2);
+        if (sumsq_by_format(err_dtype, group_view(pd1, gr.i1, gr.n1), g, bf, err, cp.clip, nullptr, stream) !=
+            hipSuccess)
+            return OB_ERR_HIP;
+        if (compress_by_format(err_dtype, group_view(pd2, gr.i2, gr.n2), g, bf, err, m, v, p, words_out, scales_out,
+                               signs_out, nf, ema, 0, cp, stream) != hipSuccess)
+            return OB_ERR_HIP;
+    }
+    return OB_OK;
 }
 
 ob_status ob_plan_set_diagnostics(ob_plan plan, double* err_sumsq_out, uint64_t* plus_count_out)

@@ -48,7 +48,8 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
                                                         const float* __restrict__ p)
 {
     __shared__ double lds[kBlock / 64];
-    const Item it = pd.items[blockIdx.x];
+    const int blk = pd.item0 + static_cast<int>(blockIdx.x);
+    const Item it = pd.items[blk];
     const int tid = threadIdx.x;
     double acc = 0.0, accw = 0.0, acce = 0.0;
     constexpr int U = OB_P1_UNROLL;
@@ -100,14 +101,14 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
         }
     }
     const double s = block_sum(acc, lds);
-    if (tid == 0) pd.partials[blockIdx.x] = s;
+    if (tid == 0) pd.partials[blk] = s;
     if (LAMB) {
         const double sw = block_sum(accw, lds);
-        if (tid == 0) pd.partials_w[blockIdx.x] = sw;
+        if (tid == 0) pd.partials_w[blk] = sw;
     }
     if (DIAG) {
         const double se = block_sum(acce, lds);
-        if (tid == 0) pd.partials_e[blockIdx.x] = se;
+        if (tid == 0) pd.partials_e[blk] = se;
     }
 }
 
@@ -126,7 +127,8 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
                                                      CompressParams cp)
 {
     __shared__ double lds[kBlock / 64];
-    const Item it = pd.items[blockIdx.x];
+    const int blk = pd.item0 + static_cast<int>(blockIdx.x);
+    const Item it = pd.items[blk];
     const int tid = threadIdx.x;
     constexpr int U = OB_P2_UNROLL;
     f4 gv[U], ev[U], mv[U], vv[U], pv[U];
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
     };
     // the chunk's scale, reduced while the block's first group of tiles is in flight
     const float scale = chunk_scale_overlapped(pd, it.chunk, lds, U * kTile <= it.len, [&] { load_group(0); });
-    if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
+    if (tid == 0 && blk == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
 
     uint32_t nf = 0, plus = 0;
     double usq = 0.0;
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
     if (pd.partials_b != nullptr) {   // diagnostics: +1 signs of the block (nib holds valid elements only)
         __shared__ uint32_t ldsb[kBlock / 64];
         const uint32_t t = block_sum_u32(plus, ldsb);
-        if (tid == 0) pd.partials_b[blockIdx.x] = t;
+        if (tid == 0) pd.partials_b[blk] = t;
     }
     if (NONFIN) {
         __shared__ uint32_t ldsu[kBlock / 64];
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
     }
     if (LAMB) {
         const double su = block_sum(usq, lds);
-        if (tid == 0) pd.partials_u[blockIdx.x] = su;
+        if (tid == 0) pd.partials_u[blk] = su;
     }
 }
 
@@ -254,7 +256,8 @@ __global__ __launch_bounds__(kBlock) void k_worker_compress(PlanDev pd, const ty
                                                             CompressParams cp)
 {
     __shared__ double lds[kBlock / 64];
-    const Item it = pd.items[blockIdx.x];
+    const int blk = pd.item0 + static_cast<int>(blockIdx.x);
+    const Item it = pd.items[blk];
     const int tid = threadIdx.x;
     constexpr int U = OB_P2_UNROLL;
     f4 gv[U], ev[U];
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(kBlock) void k_worker_compress(PlanDev pd, const ty
     };
     // the chunk's scale, reduced while the block's first group of tiles is in flight
     const float scale = chunk_scale_overlapped(pd, it.chunk, lds, U * kTile <= it.len, [&] { load_group(0); });
-    if (tid == 0 && static_cast<int>(blockIdx.x) == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
+    if (tid == 0 && blk == pd.chunk_first[it.chunk]) scales[it.chunk] = scale;
     uint32_t nf = 0;
     int base = 0;
     for (; base + U * kTile <= it.len; base += U * kTile) {

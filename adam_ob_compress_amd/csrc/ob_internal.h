@@ -36,8 +36,12 @@ struct PlanDev {
     double* partials_e;
     uint32_t* partials_b;
     int64_t n;
-    int64_t n_items;
+    int64_t n_items;            // blocks of this launch: items [item0, item0 + n_items)
     int32_t K;
+    // index in `items` of this launch's first block; its per-block results go to the same index of the
+    // partials arrays.  Non-zero only for the chunk-group launches of the compressed step's two passes
+    // (k_chunk_sumsq, k_compress, k_worker_compress); every other kernel takes 0.
+    int32_t item0;
 };
 
 struct CompressParams {

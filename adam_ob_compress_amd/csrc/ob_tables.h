@@ -79,4 +79,67 @@ inline const char* check_block_table(const std::vector<int64_t>& off, int64_t bl
     return nullptr;
 }
 
+// Chunk groups.  The compressed step runs its two passes group by group: pass 1 over the group's
+// chunks, then pass 2 over the same chunks while what pass 1 read is still in the last-level cache.
+// A group is consecutive chunks [c0, c1), its blocks [i1, i1 + n1) of the pass-1 table and
+// [i2, i2 + n2) of the pass-2 table (f1 / f2: those tables' first-block indexes).
+struct ChunkGroup {
+    int32_t c0, c1;
+    int32_t i1, n1;
+    int32_t i2, n2;
+};
+
+inline ChunkGroup chunk_group(int64_t c0, int64_t c1, const std::vector<int32_t>& f1, const std::vector<int32_t>& f2)
+{
+    return {static_cast<int32_t>(c0), static_cast<int32_t>(c1), f1[c0], f1[c1] - f1[c0], f2[c0], f2[c1] - f2[c0]};
+}
+
+// Greedy groups: each as many chunks as keep it within max_elems elements (a larger chunk is a group of
+// its own); max_elems <= 0 gives one group of all chunks.
+inline void build_chunk_groups(const std::vector<int64_t>& off, const std::vector<int32_t>& f1,
+                               const std::vector<int32_t>& f2, int64_t max_elems, std::vector<ChunkGroup>& out)
+{
+    const int64_t K = static_cast<int64_t>(off.size()) - 1;
+    out.clear();
+    for (int64_t c0 = 0; c0 < K;) {
+        int64_t c1 = max_elems > 0 ? c0 + 1 : K;
+        while (c1 < K && off[c1 + 1] - off[c0] <= max_elems) ++c1;
+        out.push_back(chunk_group(c0, c1, f1, f2));
+        c0 = c1;
+    }
+}
+
+// For K uniform chunks (nbf blocks in each but the last; n_1 / n_2 blocks in all): the group of q chunks
+// starting at chunk c0 (the last group takes what is left).
+constexpr ChunkGroup uniform_chunk_group(int64_t c0, int64_t q, int64_t K, int64_t nbf1, int64_t n_1, int64_t nbf2,
+                                         int64_t n_2)
+{
+    const int64_t c1 = c0 + q < K ? c0 + q : K;
+    const int64_t e1 = c1 < K ? c1 * nbf1 : n_1, e2 = c1 < K ? c1 * nbf2 : n_2;
+    return {static_cast<int32_t>(c0),           static_cast<int32_t>(c1),
+            static_cast<int32_t>(c0 * nbf1),    static_cast<int32_t>(e1 - c0 * nbf1),
+            static_cast<int32_t>(c0 * nbf2),    static_cast<int32_t>(e2 - c0 * nbf2)};
+}
+
+// nullptr if `groups` cover every chunk once, in order, each within max_elems elements unless it is a
+// single chunk (max_elems <= 0: no limit), with block ranges that are exactly their chunks' blocks in
+// both tables; otherwise what is wrong.
+inline const char* check_chunk_groups(const std::vector<int64_t>& off, const std::vector<int32_t>& f1,
+                                      const std::vector<int32_t>& f2, int64_t max_elems,
+                                      const std::vector<ChunkGroup>& groups)
+{
+    const int64_t K = static_cast<int64_t>(off.size()) - 1;
+    int64_t next = 0;
+    for (const ChunkGroup& g : groups) {
+        if (g.c0 != next) return "groups do not cover the chunks in order";
+        if (g.c1 <= g.c0 || g.c1 > K) return "an empty or overlong group";
+        if (max_elems > 0 && g.c1 - g.c0 > 1 && off[g.c1] - off[g.c0] > max_elems)
+            return "a group of several chunks passes the element limit";
+        if (g.i1 != f1[g.c0] || g.n1 != f1[g.c1] - f1[g.c0]) return "a group's pass-1 blocks are not its chunks'";
+        if (g.i2 != f2[g.c0] || g.n2 != f2[g.c1] - f2[g.c0]) return "a group's pass-2 blocks are not its chunks'";
+        next = g.c1;
+    }
+    return next == K ? nullptr : "groups do not reach the last chunk";
+}
+
 }  // namespace ob

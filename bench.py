@@ -336,23 +336,15 @@ def run(args):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    kern = {}
-    for kid, name in ob.KERNEL_NAMES.items():
-        ms, cnt = ob.ob_plan_read_timing(plan, kid)
-        if cnt:
-            kern[name] = {"avg_ms": ms / cnt, "launches": cnt,
-                          "GBps": bytes_per_elem(w, name) * w.n / (ms / cnt * 1e-3) / 1e9}
+    kern = kernel_times(plan, w.n, args.steps, w)
     ob.ob_plan_set_timing(plan, False)
 
     if args.copy_probe_mib:
         kern["copy_probes"] = copy_probe(args.copy_probe_mib, dev)
 
-    # the dominant kernel of the timed steps: the longest per launch (the fused pass 2 for 1-bit Adam)
+    # the dominant kernel of the timed steps: the most time per step (the fused pass 2 for 1-bit Adam)
     dom = max((k for k in ("compress", "lamb_apply", "worker_compress", "worker_update") if k in kern),
-              key=lambda k: kern[k]["avg_ms"])
-    avg = kern[dom]["avg_ms"]
-    bpe = bytes_per_elem(w, dom)
-    achieved = bpe * w.n / (avg * 1e-3) / 1e9
+              key=lambda k: kern[k]["ms_per_step"])
     traffic = load_traffic(dom, w.name)
     value = w.n / (ms_per_step * 1e-3)
     step_gbps = step_compulsory_bytes(w, "compressed") * w.n / (ms_per_step * 1e-3) / 1e9
@@ -381,9 +373,7 @@ def run(args):
                    "block_elems": plan.block_elems, "work_blocks": plan.num_blocks,
                    "diagnostics": bool(args.diagnostics), "split": bool(args.split),
                    "slab": bool(args.slab), "slab_stagger": args.slab_stagger if args.slab else None},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "bytes_per_elem": bpe, "traffic": traffic},
+        "roofline": roofline_of(kern, dom, w, traffic),
         "step_compulsory_GBps": step_gbps,
         "step_hbm_frac": step_gbps / PEAK_HBM_GBPS,
         "timed_step_kinds": kinds,
@@ -398,6 +388,35 @@ def run(args):
         "cpu_baseline": None,
     }
     return w, res
+
+
+def kernel_times(plan, n: int, steps: int, w) -> dict:
+    """Per kernel kind, from the plan's event timing over `steps` timed steps: launches, average launch
+    duration, and the kernel's time per step.  A kernel launched once per chunk group runs several times a
+    step; its rate is the step's algorithmic bytes over its time per step, which is the same as the
+    average elements per launch over the average launch duration."""
+    from adam_ob_compress_amd import _native as ob
+
+    kern = {}
+    for kid, name in ob.KERNEL_NAMES.items():
+        ms, cnt = ob.ob_plan_read_timing(plan, kid)
+        if cnt:
+            per_step = ms / steps
+            kern[name] = {"avg_ms": ms / cnt, "launches": cnt, "launches_per_step": cnt / steps,
+                          "ms_per_step": per_step,
+                          "GBps": bytes_per_elem(w, name) * n / (per_step * 1e-3) / 1e9}
+    return kern
+
+
+def roofline_of(kern: dict, dom: str, w, traffic) -> dict:
+    """The roofline record of the dominant kernel (see kernel_times for the per-launch reading)."""
+    k = kern[dom]
+    bpe = bytes_per_elem(w, dom)
+    elems = w.n / k["launches_per_step"]
+    achieved = bpe * elems / (k["avg_ms"] * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS, "bytes_per_elem": bpe, "launches_per_step": k["launches_per_step"],
+            "elements_per_launch": elems, "avg_launch_ms": k["avg_ms"], "traffic": traffic}
 
 
 SLAB_ALIGN = 2 << 20
@@ -435,7 +454,7 @@ def warm_kernels(w, opt, dev: str):
     import adam_ob_compress_amd as ob
     from adam_ob_compress_amd import schedule
 
-    n = 1 << 16
+    n = WARM_N
     plan = ob.ob_plan_create(n, chunk_size=1 << 14)
     gdt = torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32
     edt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.err_dtype]
@@ -532,19 +551,12 @@ def run_server(args, w):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kern = {}
-    for kid, name in ob.KERNEL_NAMES.items():
-        ms, cnt = ob.ob_plan_read_timing(plan, kid)
-        if cnt:
-            kern[name] = {"avg_ms": ms / cnt, "launches": cnt,
-                          "GBps": bytes_per_elem(w, name) * w.n / (ms / cnt * 1e-3) / 1e9}
+    kern = kernel_times(plan, w.n, args.steps, w)
     ob.ob_plan_set_timing(plan, False)
     if args.copy_probe_mib:
         kern["copy_probes"] = copy_probe(args.copy_probe_mib, dev)
     dom = max((k for k in ("server_sumsq", "server_apply", "unpack") if k in kern),
-              key=lambda k: kern[k]["avg_ms"])
-    bpe = bytes_per_elem(w, dom)
-    achieved = bpe * w.n / (kern[dom]["avg_ms"] * 1e-3) / 1e9
+              key=lambda k: kern[k]["ms_per_step"])
     step_gbps = step_compulsory_bytes(w, "server") * w.n / (ms_per_step * 1e-3) / 1e9
     return {
         "metric": METRIC,
@@ -561,9 +573,7 @@ def run_server(args, w):
         "data": "synthetic (seeded; two pre-drawn rounds of worker words and scales)",
         "config": {"workload": w.name, "elements": w.n, "chunks": K, "workers": w.workers,
                    "step": "server round: ob_server_reduce (2 passes) + ob_unpack"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                     "bytes_per_elem": bpe, "traffic": load_traffic(dom, w.name)},
+        "roofline": roofline_of(kern, dom, w, load_traffic(dom, w.name)),
         "step_compulsory_GBps": step_gbps,
         "step_hbm_frac": step_gbps / PEAK_HBM_GBPS,
         "timed_step_kinds": {"server_round": args.steps},
@@ -657,11 +667,55 @@ NONTEMPORAL_KERNELS = {"compress", "chunk_sumsq", "dense", "worker_compress", "w
 COPY_PROBES = (("torch copy", "copyBuffer", 131072), ("nontemporal copy", "k_probe_copy<true>", 16777216))
 
 
+# the counter runs' timed steps (their commands pass --steps 5)
+PMC_STEPS = 5
+# kernels launched once per chunk group of the compressed step
+GROUPED_KERNELS = {"chunk_sumsq", "compress", "worker_compress"}
+
+
+# the library's default pass-1 bytes per chunk group (OB_GROUP_BYTES overrides it, as in the library)
+GROUP_BYTES = 320 << 20
+
+
+def chunk_groups(w, lamb: bool = False) -> list:
+    """The chunk groups [(c0, c1), ...] the library's compressed step runs its two kernels over for
+    workload w (host arithmetic, no GPU): consecutive chunks while their pass-1 bytes (g, err and, for
+    LAMB, p) stay within the budget, a larger chunk alone; one group when grouping is off or a chunk has
+    more than 4096 pass-1 blocks (then the library forms per-chunk sums first).  tests/test_gpu_bench.py
+    checks it against ob_plan_num_groups for every workload."""
+    off = [int(o) for o in w.chunk_offsets()]
+    K = len(off) - 1
+    budget = int(os.environ.get("OB_GROUP_BYTES", GROUP_BYTES))
+    width = (2 if w.grad_dtype == "bf16" else 4) + (4 if w.err_dtype == "f32" else 2) + (4 if lamb else 0)
+    be1 = int(os.environ.get("OB_BLOCK_ELEMS", 0))
+    if not (be1 >= 1024 and be1 <= (1 << 20) and be1 % 1024 == 0):
+        be1 = min(max(-(-(-(-w.n // 8192)) // 1024) * 1024, 4096), 24576)
+    p1_max = max(-(-(off[c + 1] - off[c]) // be1) for c in range(K))
+    max_elems = max(1, budget // width) if budget > 0 and p1_max <= 4096 else 0
+    out, c0 = [], 0
+    while c0 < K:
+        c1 = c0 + 1 if max_elems > 0 else K
+        while c1 < K and off[c1 + 1] - off[c0] <= max_elems:
+            c1 += 1
+        out.append((c0, c1))
+        c0 = c1
+    return out
+
+
+def launches_per_step(w, kernel: str) -> int:
+    """Launches of `kernel` in one step of workload w: the chunk groups for the compressed step's two
+    kernels, else 1."""
+    if kernel not in GROUPED_KERNELS:
+        return 1
+    return len(chunk_groups(w, lamb=w.optimizer == "lamb" and kernel != "worker_compress"))
+
+
 def traffic_profile(d: str, kernel: str, workload: str) -> str:
     """Calibrated HBM bytes per launch of `kernel` from FETCH_SIZE / WRITE_SIZE runs under d."""
     from adam_ob_compress_amd import synth
 
     w = synth.WORKLOADS[workload]
+    groups = launches_per_step(w, kernel)
     probe_kib = 1 << 20  # the --copy-probe-mib 1024 copies read and write 1 GiB each
     res, factors = {}, {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -673,30 +727,44 @@ def traffic_profile(d: str, kernel: str, workload: str) -> str:
             vals = [float(r["Counter_Value"]) for r in copies[-8:]]
             if vals:
                 factors.setdefault(pname, {})[counter] = sum(vals) / len(vals) / probe_kib
-        # the workload's own launches: the kernel's largest grid (the warm-up on a small scratch plan
-        # launches the same kernels on small grids)
         syms = KERNEL_SYMBOL[kernel] if isinstance(KERNEL_SYMBOL[kernel], tuple) else (KERNEL_SYMBOL[kernel],)
-        mine = [r for r in rows if any(sym in r["Kernel_Name"] for sym in syms)]
-        top = max((int(r["Grid_Size"]) for r in mine), default=0)
-        kern = [float(r["Counter_Value"]) for r in mine if int(r["Grid_Size"]) == top]
-        if not kern or "torch copy" not in factors or counter not in factors["torch copy"]:
+        mine = sorted((r for r in rows if any(sym in r["Kernel_Name"] for sym in syms)),
+                      key=lambda r: int(r["Dispatch_Id"]))
+        if groups > 1:
+            # launched once per chunk group: the timed steps' launches are the kernel's last
+            # PMC_STEPS * groups dispatches
+            kern = [float(r["Counter_Value"]) for r in mine[-PMC_STEPS * groups:]]
+            ok = len(kern) == PMC_STEPS * groups
+        else:
+            # the workload's own launches: the kernel's largest grid (the warm-up on a small scratch
+            # plan launches the same kernels on small grids)
+            top = max((int(r["Grid_Size"]) for r in mine), default=0)
+            kern = [float(r["Counter_Value"]) for r in mine if int(r["Grid_Size"]) == top]
+            ok = bool(kern)
+        if not ok or "torch copy" not in factors or counter not in factors["torch copy"]:
             raise SystemExit(f"no {counter} rows for the copy probe or {kernel} under {d}")
-        res[counter] = (sum(kern) / len(kern), len(kern))
+        # KiB per step of the workload, and the dispatches that gave it
+        res[counter] = (sum(kern) / len(kern) * groups, len(kern))
     nt = "nontemporal copy" in factors and len(factors["nontemporal copy"]) == 2
     used = "nontemporal copy" if nt and kernel in NONTEMPORAL_KERNELS else "torch copy"
     ff, wf = factors[used]["FETCH_SIZE"], factors[used]["WRITE_SIZE"]
     (fk, fn), (wk, wn) = res["FETCH_SIZE"], res["WRITE_SIZE"]
-    traffic = (fk / ff + wk / wf) * 1024
+    traffic = (fk / ff + wk / wf) * 1024            # HBM bytes per step
     alg = bytes_per_elem(w, kernel) * w.n
     if traffic < 0.5 * alg:
         raise SystemExit(f"{kernel}: no launch of the workload's size under {d} (only the warm-up's?)")
+    fk, wk = fk / groups, wk / groups                # per launch from here on
     run_flags = " --split" if kernel.startswith("worker_") else ""   # the split step's kernels
     rec = {"kernel": kernel, "workload": w.name, "kernel_src_sha": kernel_source_sha(),
            "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
            "calibration": used, "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
            "factors": {k: {c: round(v, 5) for c, v in f.items()} for k, f in factors.items()},
-           "bytes_per_launch": round(traffic),
-           "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 4)}
+           "launches_per_step": groups, "bytes_per_step": round(traffic),
+           "bytes_per_launch": round(traffic / groups),
+           "algorithmic_bytes_per_launch": round(alg / groups), "traffic_over_algorithmic": round(traffic / alg, 4)}
+    group_note = "" if groups == 1 else (
+        f"`{kernel}` runs once per chunk group, {groups} launches per step: the figures below are the\n"
+        f"last {PMC_STEPS} steps' {PMC_STEPS * groups} dispatches (the timed ones), summed per step and divided by {groups}.\n\n")
     cal = "\n".join(f"| {k} | {f.get('FETCH_SIZE', float('nan')) * probe_kib:,.1f} | "
                      f"{f.get('WRITE_SIZE', float('nan')) * probe_kib:,.1f} | {f.get('FETCH_SIZE', float('nan')):.5f} | "
                      f"{f.get('WRITE_SIZE', float('nan')):.5f} |" for k, f in factors.items())
@@ -721,9 +789,9 @@ per dispatch.  Counter readings per such dispatch and the factors they give:
 
 `{kernel}` is calibrated with the {used} (its streaming accesses are {"nontemporal" if used == "nontemporal copy" else "ordinary"}).
 
-| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/launch (calibrated) | algorithmic bytes/launch | ratio |
+{group_note}| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | HBM bytes/launch (calibrated) | algorithmic bytes/launch | ratio |
 |---|---|---|---|---|---|---|
-| {kernel} | {fn} / {wn} | {fk:,.1f} | {wk:,.1f} | {traffic:,.0f} | {alg:,.0f} ({bytes_per_elem(w, kernel)} B x n) | {traffic / alg:.4f} |
+| {kernel} | {fn} / {wn} | {fk:,.1f} | {wk:,.1f} | {traffic / groups:,.0f} | {alg / groups:,.0f} ({bytes_per_elem(w, kernel)} B x n{" / " + str(groups) if groups > 1 else ""}) | {traffic / alg:.4f} |
 
 traffic-json: {json.dumps(rec)}
 """
@@ -733,6 +801,12 @@ def _grid(r) -> int:
     if r.get("Grid_Size"):
         return int(r["Grid_Size"])
     return int(r.get("Grid_Size_X", 0)) * int(r.get("Grid_Size_Y", 1) or 1) * int(r.get("Grid_Size_Z", 1) or 1)
+
+
+# the largest grid (threads) of a library kernel in warm_kernels' scratch plan of WARM_N elements: the
+# dense table's blocks of 2 tiles (2048 elements), 256 threads each
+WARM_N = 1 << 16
+WARM_GRID = WARM_N // 2048 * 256
 
 
 def rocprof_summary(d: str) -> str:
@@ -752,6 +826,20 @@ def rocprof_summary(d: str) -> str:
             out.append(f"| {k} | {g} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
                        f"{100.0 * sum(v) / total:.1f} |")
         out.append("")
+        # the library's kernels over all their launches on the workload (the compressed step's two
+        # kernels run once per chunk group, with grids that differ between groups); the bench's warm-up
+        # on a scratch plan launches them with grids of at most WARM_GRID threads
+        lib_k = {}
+        for (k, g), v in groups.items():
+            if k.startswith("k_") and g > WARM_GRID:
+                lib_k.setdefault(k, []).extend(v)
+        if lib_k:
+            out.append(f"### library kernels over all launches with grids above {WARM_GRID} threads (the workload's)\n")
+            out.append("| kernel | calls | avg us | total us |")
+            out.append("|---|---|---|---|")
+            for k, v in sorted(lib_k.items(), key=lambda kv: -sum(kv[1])):
+                out.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {sum(v):.1f} |")
+            out.append("")
     ctr = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
     for f in ctr:
         agg = {}

@@ -110,6 +110,15 @@ int64_t ob_plan_num_elements(ob_plan plan);   /* -1 for a NULL plan */
 int64_t ob_plan_num_chunks(ob_plan plan);     /* -1 for a NULL plan */
 int64_t ob_plan_num_blocks(ob_plan plan);     /* work blocks = grid size of the per-element kernels */
 int64_t ob_plan_block_elems(ob_plan plan);    /* elements per work block (except chunk tails) */
+/* Chunk groups of the compressed step (ob_adam_compress_step, ob_lamb_compress_step with lamb != 0,
+ * ob_adam_worker_compress): the step runs its two kernels group by group, each group being consecutive
+ * chunks whose bytes read by the first kernel (g, err and, for LAMB, p) stay within a budget sized to
+ * the GPU's last-level cache (320 MB; the environment variable OB_GROUP_BYTES, read when the plan is
+ * created, overrides it and 0 turns grouping off), so that the second kernel re-reads them from that
+ * cache.  A chunk above the budget is a group of its own; plans whose chunks need a per-chunk sums
+ * launch (more than 4096 first-kernel blocks in a chunk) are one group.  Returns the number of groups,
+ * i.e. the launches of each of the two kernels per step; -1 for a NULL plan or an invalid dtype. */
+int64_t ob_plan_num_groups(ob_plan plan, ob_dtype g_dtype, ob_dtype err_dtype, int32_t lamb);
 
 /* Dense Adam step ([P2] baseline section; the step used before freeze_step in [P2] 1-bit Adam and for
  * the variance refresh of [P2] 0/1 Adam):
@@ -124,7 +133,8 @@ ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, flo
  *   g' = clip(widen(g));  x = g' + err (fp32);  words = pack(sign(x));  scales_c per chunk;
  *   g_hat = +-scale_c;  err = x - g_hat (PLAIN) or ef_beta*err + (1-ef_beta)*(x - g_hat) (EMA);
  *   m = beta1*m + (1-beta1)*g_hat;  p -= lr * m / (sqrt(v) + eps)  (v frozen, read only).
- * Runs two kernels: a per-chunk sum of squares, then one fused streaming pass.
+ * Runs two kernels: a per-chunk sum of squares, then one fused streaming pass, one pair of launches
+ * per chunk group (ob_plan_num_groups; the results do not depend on the grouping).
  * g: n elements (read only); err: n elements of err_dtype, in place; m, p: fp32[n] in place;
  * v: fp32[n] read only; words_out: uint32[ceil(n/32)]; scales_out: fp32[K];
  * err_dtype ([P3] Q&A on error-feedback memory): OB_F32, or OB_BF16 / OB_F16 -- the stored error is
@@ -228,7 +238,8 @@ const char* ob_status_str(ob_status s);
  * squares live in a static device buffer of OB_NOALLOC_SCRATCH_BYTES that the library holds on every
  * GPU it runs on until the process ends; the first call on a device looks up that device's copy.
  * Each call rewrites the tables it needs (one small kernel ahead of the two passes), so consecutive
- * calls may change n and chunk_size.  All calls on one GPU share its buffer: calls that may overlap on
+ * calls may change n and chunk_size.  The two passes run by chunk groups as in ob_adam_compress_step
+ * (groups of equal numbers of chunks within the same budget, OB_GROUP_BYTES read on every call).  All calls on one GPU share its buffer: calls that may overlap on
  * one GPU (other streams, other host threads) race and must not be issued; calls on one stream are
  * ordered.  Space needed: 24 bytes per first-pass block, 16 per 4096-element block of the fused pass,
  * 16 per chunk (plus 12 per chunk for chunks of more than 4096 first-pass blocks), each region rounded
@@ -241,10 +252,12 @@ ob_status ob_adam_compress_step_noalloc(int64_t n, int64_t chunk_size, const voi
                                         uint64_t* nonfinite_out, const ob_hparams* hp, hipStream_t stream);
 
 /* ---- kernel timing (measurement support) ----
- * With timing on, every call made with this plan records a hipEvent pair around each kernel it
- * launches, on the call's stream.  ob_plan_read_timing waits for the recorded events and returns the
- * summed milliseconds and launch count of one kernel kind since timing was switched on.  The events
- * are created with hipEventDisableSystemFence: they measure time only and order no memory. */
+ * With timing on, every call made with this plan records hipEvents around each kernel it launches, on
+ * the call's stream: a pair per launch, except that the launches a compressed step makes one after the
+ * other for its chunk groups share them (each starts at the event that ended the one before), one
+ * event per launch.  ob_plan_read_timing waits for the recorded events and returns the summed
+ * milliseconds and launch count of one kernel kind since timing was switched on.  The events are
+ * created with hipEventDisableSystemFence: they measure time only and order no memory. */
 typedef enum {
     OB_KERNEL_CHUNK_SUMSQ = 0,     /* compressed step (Adam or LAMB), pass 1 */
     OB_KERNEL_COMPRESS = 1,        /* compressed step (Adam or LAMB), pass 2 (fused streaming pass) */

@@ -6,7 +6,12 @@
 // table as ob_plan_create does and requires ob::check_block_table to accept it; for uniform shapes it
 // also requires ob::uniform_item (the no-allocation kernel's formula) to give every block of it.  Then
 // it plants mistakes in tables (a block moved, dropped, duplicated, retagged, shortened; first[]
-// shifted) and requires the checker to reject each.  Prints "table_check ok" and the counts.
+// shifted) and requires the checker to reject each.  Then the chunk groups of the compressed step's
+// passes, for pairs of pass-1 / pass-2 block sizes and several element limits: ob::build_chunk_groups
+// must pass ob::check_chunk_groups and be greedy (each group but the last would pass the limit with
+// its next chunk); for uniform shapes ob::uniform_chunk_group (the no-allocation path's groups) must
+// pass too; planted group mistakes must be rejected.  Prints "table_check ok" and the counts.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -19,6 +24,8 @@
 
 static const int64_t kBlockSizes[] = {1024, 2048, 4096, 8192, 24576, 1 << 20};
 
+static const int64_t kGroupLimits[] = {0, 1, 64, 5000, 1 << 16, 1 << 20, 1 << 24, int64_t(1) << 26};
+
 static int fail(const char* what, const std::string& shape, int64_t be)
 {
     std::fprintf(stderr, "FAIL: %s (shape %s, block %lld)\n", what, shape.c_str(), static_cast<long long>(be));
@@ -28,7 +35,7 @@ static int fail(const char* what, const std::string& shape, int64_t be)
 int main()
 {
     std::string line;
-    long shapes = 0, tables = 0, blocks = 0, planted = 0;
+    long shapes = 0, tables = 0, blocks = 0, planted = 0, group_sets = 0;
     while (std::getline(std::cin, line)) {
         if (line.empty()) continue;
         std::istringstream in(line);
@@ -97,8 +104,62 @@ int main()
                 ++planted;
             }
         }
+        // chunk groups over a pass-1 and a pass-2 table
+        const int64_t K = static_cast<int64_t>(off.size()) - 1;
+        const int64_t pairs[][2] = {{24576, 4096}, {4096, 4096}, {1 << 20, 2048}};
+        for (const auto& pr : pairs) {
+            std::vector<ob::Item> it1, it2;
+            std::vector<int32_t> f1, f2;
+            if (!ob::build_block_table(off, pr[0], it1, f1) || !ob::build_block_table(off, pr[1], it2, f2))
+                return fail("build refused", shape, pr[0]);
+            for (int64_t lim : kGroupLimits) {
+                std::vector<ob::ChunkGroup> gs;
+                ob::build_chunk_groups(off, f1, f2, lim, gs);
+                if (const char* why = ob::check_chunk_groups(off, f1, f2, lim, gs)) return fail(why, shape, lim);
+                ++group_sets;
+                for (size_t j = 0; j + 1 < gs.size(); ++j)
+                    if (off[gs[j].c1 + 1] - off[gs[j].c0] <= lim) return fail("a group is not greedy", shape, lim);
+                if (lim <= 0 && gs.size() != (K > 0 ? 1u : 0u)) return fail("no limit but several groups", shape, lim);
+                if (uniform && K > 0) {
+                    const int64_t nbf1 = K > 1 ? (chunk + pr[0] - 1) / pr[0] : 0;
+                    const int64_t nbf2 = K > 1 ? (chunk + pr[1] - 1) / pr[1] : 0;
+                    const int64_t q = lim > 0 ? std::max<int64_t>(1, lim / chunk) : K;
+                    std::vector<ob::ChunkGroup> us;
+                    for (int64_t c0 = 0; c0 < K; c0 += q)
+                        us.push_back(ob::uniform_chunk_group(c0, q, K, nbf1, static_cast<int64_t>(it1.size()), nbf2,
+                                                             static_cast<int64_t>(it2.size())));
+                    if (const char* why = ob::check_chunk_groups(off, f1, f2, lim, us))
+                        return fail(why, shape, lim);
+                    ++group_sets;
+                }
+                // planted mistakes
+                std::vector<std::vector<ob::ChunkGroup>> bad;
+                auto t = gs;
+                t.pop_back();
+                bad.push_back(t);                                        // last group dropped
+                t = gs;
+                t[0].n1 += 1;
+                bad.push_back(t);                                        // one pass-1 block too many
+                t = gs;
+                t[0].i2 += 1;
+                bad.push_back(t);                                        // pass-2 range shifted
+                if (gs.size() >= 2) {
+                    t = gs;
+                    t[0].c1 -= 1;
+                    bad.push_back(t);                                    // a chunk left out
+                    t = gs;
+                    t[0] = ob::chunk_group(gs[0].c0, gs[1].c1, f1, f2);
+                    t.erase(t.begin() + 1);
+                    if (lim > 0) bad.push_back(t);                       // two groups merged past the limit
+                }
+                for (auto& b : bad) {
+                    if (!ob::check_chunk_groups(off, f1, f2, lim, b)) return fail("a planted group mistake passed", shape, lim);
+                    ++planted;
+                }
+            }
+        }
     }
-    std::printf("table_check ok: %ld shapes, %ld tables, %ld blocks, %ld planted mistakes rejected\n", shapes,
-                tables, blocks, planted);
+    std::printf("table_check ok: %ld shapes, %ld tables, %ld blocks, %ld group sets, %ld planted mistakes rejected\n",
+                shapes, tables, blocks, group_sets, planted);
     return 0;
 }

@@ -104,9 +104,11 @@ def _fake_counter_runs(d, kernel_rows, nt_fetch_kib=524288.0):
         _counter_csv(os.path.join(d, counter.lower(), "run_counter_collection.csv"), rows)
 
 
-def test_traffic_profile_uses_the_workload_launches_only(tmp_path):
+def test_traffic_profile_uses_the_workload_launches_only(tmp_path, monkeypatch):
     """The warm-up's small launches of a kernel are left out of its average; the calibrated bytes
-    then equal what the synthetic counters say the workload's launches moved."""
+    then equal what the synthetic counters say the workload's launches moved (one launch per step:
+    chunk groups off)."""
+    monkeypatch.setenv("OB_GROUP_BYTES", "0")
     w = synth.WORKLOADS["bert-base-110M-fp32"]
     alg = bench.bytes_per_elem(w, "compress") * w.n               # bytes per launch
     fetch_kib = 20.0 * w.n / 1024 / 2                              # 20 B read per element, counted at half
@@ -122,9 +124,10 @@ def test_traffic_profile_uses_the_workload_launches_only(tmp_path):
     assert abs(rec["traffic_over_algorithmic"] - 1.0) < 1e-3
 
 
-def test_traffic_profile_takes_the_nontemporal_calibration_for_nontemporal_kernels(tmp_path):
+def test_traffic_profile_takes_the_nontemporal_calibration_for_nontemporal_kernels(tmp_path, monkeypatch):
     """A nontemporal copy whose fetch reads at the full 1 GiB sets the fetch factor to 1 for the
     nontemporal kernels (compress), while server pass 2 (ordinary loads) keeps the torch copy's 0.5."""
+    monkeypatch.setenv("OB_GROUP_BYTES", "0")
     w = synth.WORKLOADS["bert-base-110M-fp32"]
     fetch_kib = 20.0 * w.n / 1024                                  # 20 B read per element, counted in full
     write_kib = 12.125 * w.n / 1024
@@ -137,6 +140,61 @@ def test_traffic_profile_takes_the_nontemporal_calibration_for_nontemporal_kerne
     assert abs(rec["traffic_over_algorithmic"] - 1.0) < 1e-3
     assert rec["factors"]["torch copy"]["FETCH_SIZE"] == 0.5
     assert "server_apply" not in bench.NONTEMPORAL_KERNELS
+
+
+def test_traffic_profile_of_a_grouped_kernel_sums_the_timed_steps_launches(tmp_path):
+    """A kernel launched once per chunk group: the last PMC_STEPS * groups dispatches are the timed
+    steps'; their sum per step is the step's bytes, reported per launch as that over the groups.  The
+    earlier dispatches (warm-up steps with other sizes, the scratch plan) do not count."""
+    w = synth.WORKLOADS["gpt2-1.5B-bf16"]
+    groups = bench.launches_per_step(w, "compress")
+    assert groups == len(bench.chunk_groups(w)) > 1
+    bpe = bench.bytes_per_elem(w, "compress")
+    sizes = [int(w.chunk_offsets()[c1] - w.chunk_offsets()[c0]) for c0, c1 in bench.chunk_groups(w)]
+    assert sum(sizes) == w.n
+    rows, i = [], 0
+    for step in range(2 + bench.PMC_STEPS):
+        for el in sizes:
+            scale = 1.0 if step >= 2 else 3.0            # the warm-up steps' values must be ignored
+            rows.append({"Dispatch_Id": 100 + i, "Kernel_Name": "void ob::k_compress<GradBF16>(...)",
+                         "Grid_Size": el // 4096 * 256, "FETCH_SIZE": scale * 18.0 * el / 1024 / 2,
+                         "WRITE_SIZE": scale * 12.125 * el / 1024})
+            i += 1
+    rows.append({"Dispatch_Id": 50, "Kernel_Name": "void ob::k_compress<GradBF16>(...)", "Grid_Size": 4096,
+                 "FETCH_SIZE": 1e9, "WRITE_SIZE": 1e9})
+    _fake_counter_runs(str(tmp_path), rows)
+    rec = json.loads([ln for ln in bench.traffic_profile(str(tmp_path), "compress", w.name).splitlines()
+                      if ln.startswith("traffic-json:")][0].split(":", 1)[1])
+    assert rec["launches_per_step"] == groups
+    assert abs(rec["traffic_over_algorithmic"] - 1.0) < 1e-3
+    assert abs(rec["bytes_per_step"] - bpe * w.n) / (bpe * w.n) < 1e-3
+    assert abs(rec["bytes_per_launch"] * groups - rec["bytes_per_step"]) <= groups
+
+
+def test_chunk_groups_follow_the_budget():
+    """Greedy: each group but the last would pass the budget with its next chunk; no group of several
+    chunks passes it; OB_GROUP_BYTES=0 gives one group."""
+    for name in ("bert-base-110M-fp32", "gpt2-1.5B-bf16", "llama2-7B-bf16-ema", "server-2^28-W8"):
+        w = synth.WORKLOADS[name]
+        off = w.chunk_offsets()
+        width = (2 if w.grad_dtype == "bf16" else 4) + (4 if w.err_dtype == "f32" else 2)
+        lim = bench.GROUP_BYTES // width
+        gs = bench.chunk_groups(w)
+        assert gs[0][0] == 0 and gs[-1][1] == len(off) - 1
+        assert all(a[1] == b[0] for a, b in zip(gs, gs[1:]))
+        for c0, c1 in gs:
+            assert c1 - c0 == 1 or off[c1] - off[c0] <= lim
+        for c0, c1 in gs[:-1]:
+            assert off[c1 + 1] - off[c0] > lim
+    old = os.environ.get("OB_GROUP_BYTES")
+    os.environ["OB_GROUP_BYTES"] = "0"
+    try:
+        assert len(bench.chunk_groups(synth.WORKLOADS["llama2-7B-bf16-ema"])) == 1
+    finally:
+        if old is None:
+            del os.environ["OB_GROUP_BYTES"]
+        else:
+            os.environ["OB_GROUP_BYTES"] = old
 
 
 def test_traffic_profile_refuses_runs_without_a_workload_launch(tmp_path):
@@ -164,6 +222,8 @@ def test_rocprof_summary_groups_by_kernel_and_grid(tmp_path):
             t += 10 ** 6
     md = bench.rocprof_summary(str(tmp_path))
     rows = [ln for ln in md.splitlines() if ln.startswith("| k_compress")]
-    assert len(rows) == 2
+    assert len(rows) == 3
     assert "| 6829568 | 2 | 585.00 | 580.00 | 590.00 |" in rows[0]
     assert "| 4096 | 1 | 2.00 |" in rows[1]
+    # the per-kernel line over the workload's launches leaves the warm-up's small grid out
+    assert rows[2] == "| k_compress<GradF32>(...) | 2 | 585.00 | 1170.0 |"

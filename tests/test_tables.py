@@ -1,7 +1,9 @@
 """The plan's work-block tables on the CPU: tests/table_check.cpp (g++, no HIP) builds them as
 ob_plan_create does for every workload's chunking and many random ones, at six block sizes, and checks
 what the kernels assume of them (ob_tables.h's check_block_table, which ob_plan_create also runs);
-for uniform chunks, the no-allocation kernel's per-block formula must reproduce every block."""
+for uniform chunks, the no-allocation kernel's per-block formula must reproduce every block.  It also
+checks the chunk groups the compressed step's passes run over (greedy, covering, with each group's
+block ranges those of its chunks in both tables; the no-allocation path's uniform groups too)."""
 import os
 import subprocess
 import tempfile
@@ -44,4 +46,4 @@ def test_block_tables_hold_what_the_kernels_assume():
         r = subprocess.run([exe], input=_shapes(), capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr
     assert r.stdout.startswith("table_check ok"), r.stdout
-    assert "planted mistakes rejected" in r.stdout
+    assert "planted mistakes rejected" in r.stdout and "group sets" in r.stdout

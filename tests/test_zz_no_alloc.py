@@ -5,7 +5,9 @@ ob_adam_compress_step with a plan of the same n and chunk size -- the same kerne
 block tables, the tables and partial sums living in the library's static device buffer instead of the
 plan's allocations.  Each case makes calls in a row on one stream, later ones smaller than the first
 (the buffer then still holds the first call's larger tables), and then the first size again.  The
-step is also captured into a HIP graph and replayed.
+same with small chunk-group budgets (both steps then run their passes group by group, the plan's
+greedy groups against the no-allocation step's equal groups), and the step captured into a HIP graph
+and replayed.
 """
 import numpy as np
 import pytest
@@ -96,6 +98,16 @@ SEQUENCES = {
 def test_noalloc_step_equals_the_plan_step(name):
     for k, case in enumerate(SEQUENCES[name]):
         _one(*case, seed=100 + k)
+
+
+def test_noalloc_step_by_groups_equals_the_plan_step(monkeypatch):
+    """OB_GROUP_BYTES of a few chunks: many groups on both sides.  The last case's plan puts its three
+    chunks (the last one short) in one group where the no-allocation step makes two."""
+    monkeypatch.setenv("OB_GROUP_BYTES", "200000")
+    _one(5_000_000, 1 << 14, "f32", "bf16", False, 0.0, True, True, seed=7)
+    _one(1_000_003, 1 << 16, "f32", "f32", True, 5.0, True, False, seed=8)
+    monkeypatch.setenv("OB_GROUP_BYTES", str(8 * (2 * 16384 + 1000)))
+    _one(2 * 16384 + 1000, 16384, "f32", "f32", True, 0.0, False, False, seed=9)
 
 
 def test_noalloc_step_under_graph_capture():
