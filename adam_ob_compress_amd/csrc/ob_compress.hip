@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
                 else
                     *sp = signs4(nib);
             }
-            store_word(words, i, nib, true);
+            store_word<OB_NT_BITS>(words, i, nib, true);
             plus += __builtin_popcount(nib);
         }
     }
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kBlock) void k_compress(PlanDev pd, const typename 
                 if (NONFIN) nf += __builtin_isfinite(e) ? 0u : 1u;
             }
         }
-        store_word(words, i, nib, 32 * (tid >> 3) < rem);
+        store_word<OB_NT_BITS>(words, i, nib, 32 * (tid >> 3) < rem);
         plus += __builtin_popcount(nib);
     }
     if (pd.partials_b != nullptr) {   // diagnostics: +1 signs of the block (nib holds valid elements only)
@@ -291,8 +291,14 @@ __global__ __launch_bounds__(kBlock) void k_worker_compress(PlanDev pd, const ty
                 nf += __builtin_isfinite(e) ? 0u : 1u;
             }
             E::template store4<OB_NT_ST>(err, i, ev[u]);
-            if (signs) *reinterpret_cast<uint32_t*>(signs + i) = signs4(nib);
-            store_word(words, i, nib, true);
+            if (signs) {
+                uint32_t* sp = reinterpret_cast<uint32_t*>(signs + i);
+                if (OB_NT_BITS)
+                    __builtin_nontemporal_store(signs4(nib), sp);
+                else
+                    *sp = signs4(nib);
+            }
+            store_word<OB_NT_BITS>(words, i, nib, true);
         }
     }
     for (; base < it.len; base += kTile) {
@@ -313,7 +319,7 @@ __global__ __launch_bounds__(kBlock) void k_worker_compress(PlanDev pd, const ty
             if (signs) signs[i + k] = b ? int8_t(1) : int8_t(-1);
             nf += __builtin_isfinite(e) ? 0u : 1u;
         }
-        store_word(words, i, nib, 32 * (tid >> 3) < rem);
+        store_word<OB_NT_BITS>(words, i, nib, 32 * (tid >> 3) < rem);
     }
     if (nonfinite) {
         __shared__ uint32_t ldsu[kBlock / 64];

@@ -63,7 +63,9 @@ constexpr int kPlainItem = 16 * kTile;  // elements per block for the plan-less 
 #define OB_UNPACK_UNROLL 4
 #endif
 //   OB_NT_SRV2                    nontemporal loads and stores in server pass 2
-//   OB_NT_BITS                    nontemporal stores of packed words and int8 signs
+//   OB_NT_BITS                    nontemporal stores of the compressed step's packed words and int8
+//                                 signs (on: lines written with ordinary stores stay in the caches and
+//                                 are written back while the next chunk group's pass 1 reads)
 #ifndef OB_NT_SRV2
 #define OB_NT_SRV2 0
 #endif
@@ -76,7 +78,7 @@ constexpr int kPlainItem = 16 * kTile;  // elements per block for the plan-less 
 #define OB_SRV_LINES_UNROLL 4
 #endif
 #ifndef OB_NT_BITS
-#define OB_NT_BITS 0
+#define OB_NT_BITS 1
 #endif
 
 // ------------------------------------------------------------------------------------------------
@@ -385,13 +387,14 @@ __device__ __forceinline__ uint32_t or8(uint32_t v)
 }
 
 // Lane tid holds the 4 sign bits of elements i..i+3 (i = tile start + 4*tid, tile start a multiple of
-// 32).  Lanes 8k..8k+7 together hold the 32 bits of one word; lane 8k writes it if `valid`.
-template <class I>
+// 32).  Lanes 8k..8k+7 together hold the 32 bits of one word; lane 8k writes it if `valid`, with a
+// nontemporal store when NT.
+template <bool NT, class I>
 __device__ __forceinline__ void store_word(uint32_t* __restrict__ words, I i, uint32_t nib, bool valid)
 {
     const uint32_t w = or8(nib << (4 * (threadIdx.x & 7)));
     if ((threadIdx.x & 7) == 0 && valid) {
-        if (OB_NT_BITS)
+        if (NT)
             __builtin_nontemporal_store(w, words + (i >> 5));
         else
             words[i >> 5] = w;

@@ -466,7 +466,7 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
         for (int u = 0; u < U; ++u) {
             const int64_t i = it.start + base + u * kTile + kVec * tid;
             const uint32_t nib = tile(i, kVec, grp_e[u], grp_w[u]);
-            if (APPLY) store_word(words, i, nib, true);
+            if (APPLY) store_word<OB_NT_SRV2>(words, i, nib, true);
         }
     }
     // the rest, one (possibly ragged) tile at a time
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(kBlock) void k_server(PlanDev pd, int W, const uint
         if (cnt >= kVec) ev = ld4<NTS>(e, i);
         const uint32_t wd = (tabulate && group_valid) ? load_word(i) : 0u;
         const uint32_t nib = tile(i, cnt, ev, wd);
-        if (APPLY) store_word(words, i, nib, group_valid);
+        if (APPLY) store_word<OB_NT_SRV2>(words, i, nib, group_valid);
     }
     if (!APPLY) {
         const double s = block_sum(acc, lds);
@@ -666,7 +666,7 @@ __global__ __launch_bounds__(kBlock) void k_pack(const typename G::T* __restrict
             for (int k = 0; k < kVec; ++k)
                 if (k < cnt) nib |= (G::load1(x, i + k) >= 0.0f ? 1u : 0u) << k;
         }
-        store_word(words, i, nib, 32 * (tid >> 3) < rem);
+        store_word<false>(words, i, nib, 32 * (tid >> 3) < rem);
     }
 }
 
