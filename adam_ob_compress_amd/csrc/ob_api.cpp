@@ -102,9 +102,10 @@ constexpr int64_t kFinalizeAt = 16 * ob::kBlock;
 
 // Pass-1 bytes per chunk group (the compressed step's passes run group by group).  Measured on MI355X
 // (interleaved A/B in one process, outputs bit-identical): 320 MB groups took the Llama-2-7B-sized
-// step (6.7G elements, bf16 g) from 39.9 to 37.7 ms and the GPT-2-1.5B-sized one from 8.78 to 8.20 ms;
-// 192 and 400 MB were 1-2% slower than 320, 64 MB (one chunk per group) slower than no groups at all,
-// and the same groups with nontemporal pass-1 loads (which do not stay in the cache) slower too.
+// step (6.7G elements, bf16 g) from 40.8 to 37.9 ms, the GPT-2-1.5B-sized one from 8.75 to 8.35 ms and
+// the BERT-base-sized one from 0.705 to 0.672 ms; 192 and 400 MB were 1-2% slower than 320, 64 MB (one
+// chunk per group) no faster than no groups at all, and the same groups with nontemporal pass-1 loads
+// (which do not stay in the cache) slower than no groups.
 // OB_GROUP_BYTES overrides (0 = one launch per pass).
 constexpr int64_t kGroupBytes = int64_t(320) << 20;
 
