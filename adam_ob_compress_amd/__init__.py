@@ -10,7 +10,7 @@ from ._native import (  # noqa: F401
     OB_KERNEL_CHUNK_SUMSQ,
     OB_KERNEL_COMPRESS, OB_KERNEL_DENSE, OB_KERNEL_DIAG, OB_KERNEL_LAMB_APPLY, OB_KERNEL_SERVER_APPLY,
     OB_KERNEL_SERVER_SUMSQ, OB_KERNEL_TRUST_RATIO, OB_KERNEL_UNPACK, LIB_PATH, ObError, Plan, hparams,
-    OB_ERR_SIZE, OB_NOALLOC_SCRATCH_BYTES,
+    OB_ERR_OOM, OB_ERR_SIZE, OB_NOALLOC_SCRATCH_BYTES,
     lib, ob_adam_compress_step, ob_adam_compress_step_noalloc, ob_adam_warmup_step, ob_adam_worker_compress,
     ob_adam_worker_update,
     ob_hparams, ob_lamb_compress_step, ob_lamb_worker_update,

@@ -331,8 +331,14 @@ const char* ob_status_str(ob_status s)
     return "unknown status";
 }
 
-ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_offsets, int64_t n_chunks,
-                         ob_plan* out)
+}  // extern "C"
+
+namespace {
+
+// ob_plan_create's body.  p: the plan being built, owned here until it is handed out in *out (every
+// return that fails frees it first), so that the caller can free it if an exception escapes.
+ob_status plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_offsets, int64_t n_chunks, ob_plan* out,
+                      ob_plan& p)
 {
     if (!out) return OB_ERR_ARG;
     *out = nullptr;
@@ -364,7 +370,7 @@ ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_off
     }
     const int64_t K = static_cast<int64_t>(off.size()) - 1;
 
-    ob_plan p = new (std::nothrow) ob_plan_s;
+    p = new (std::nothrow) ob_plan_s;
     if (!p) return OB_ERR_OOM;
     p->n = n;
     p->K = static_cast<int32_t>(K);
@@ -444,12 +450,33 @@ ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_off
     return OB_OK;
 }
 
-ob_status ob_plan_destroy(ob_plan plan)
+}  // namespace
+
+extern "C" {
+
+ob_status ob_plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_offsets, int64_t n_chunks,
+                         ob_plan* out)
 {
+    ob_plan p = nullptr;
+    try {
+        return plan_create(n, chunk_size, chunk_offsets, n_chunks, out, p);
+    } catch (...) {
+        // a host allocation of the tables or groups failed (the only exceptions here): free what the
+        // plan holds so far and report it like a failed device allocation
+        if (p) free_plan(p);
+        if (out) *out = nullptr;
+        return OB_ERR_OOM;
+    }
+}
+
+ob_status ob_plan_destroy(ob_plan plan)
+try {
     if (!plan) return OB_ERR_ARG;
     DeviceGuard g(plan->device);
     free_plan(plan);
     return OB_OK;
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 int64_t ob_plan_num_elements(ob_plan plan) { return plan ? plan->n : -1; }
@@ -464,7 +491,7 @@ int64_t ob_plan_num_groups(ob_plan plan, ob_dtype g_dtype, ob_dtype err_dtype, i
 
 ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* m, float* v, float* p,
                               const ob_hparams* hp, hipStream_t stream)
-{
+try {
     if (!plan || !hp) return OB_ERR_ARG;
     if (!valid_dtype(g_dtype)) return OB_ERR_DTYPE;
     if (plan->n == 0) return OB_OK;
@@ -480,6 +507,8 @@ ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, flo
     const int bf = g_dtype == OB_BF16;
     return timed(plan, OB_KERNEL_DENSE, stream,
                  [&] { return ob::launch_dense(pd, g, bf, m, v, p, 0, dp, stream); });
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 }  // extern "C"
@@ -650,15 +679,17 @@ ob_status ob_adam_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, v
                                 float* m, const float* v, float* p, uint32_t* words_out, float* scales_out,
                                 int8_t* signs_out, uint64_t* nonfinite_out, const ob_hparams* hp,
                                 hipStream_t stream)
-{
+try {
     return compress_passes(plan, g, g_dtype, err, err_dtype, m, v, p, words_out, scales_out, signs_out,
                            nonfinite_out, hp, 0, stream);
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_adam_worker_compress(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
                                   uint32_t* words_out, float* scales_out, int8_t* signs_out,
                                   uint64_t* nonfinite_out, const ob_hparams* hp, hipStream_t stream)
-{
+try {
     if (!plan || !hp) return OB_ERR_ARG;
     if (!valid_dtype(g_dtype) || !valid_err_dtype(err_dtype)) return OB_ERR_DTYPE;
     if (plan->n == 0) return OB_OK;
@@ -708,11 +739,13 @@ ob_status ob_adam_worker_compress(ob_plan plan, const void* g, ob_dtype g_dtype,
         if (st != OB_OK) return st;
     }
     return st;
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_adam_worker_update(ob_plan plan, const uint32_t* words, const float* scales, float* m,
                                 const float* v, float* p, const ob_hparams* hp, hipStream_t stream)
-{
+try {
     if (!plan || !hp) return OB_ERR_ARG;
     if (plan->n == 0) return OB_OK;
     if (!words || !scales || !m || !v || !p) return OB_ERR_ARG;
@@ -724,12 +757,14 @@ ob_status ob_adam_worker_update(ob_plan plan, const uint32_t* words, const float
     const ob::PlanDev pd = plan->dev(T_COMPRESS);
     return timed(plan, OB_KERNEL_WORKER_UPDATE, stream,
                  [&] { return ob::launch_worker_update(pd, words, scales, m, v, p, 0, cp, stream); });
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_lamb_worker_update(ob_plan plan, const uint32_t* words, const float* scales, float* m,
                                 const float* v, float* p, float* ratios_out, const ob_hparams* hp,
                                 hipStream_t stream)
-{
+try {
     if (!plan || !hp) return OB_ERR_ARG;
     if (plan->n == 0) return OB_OK;
     if (!words || !scales || !m || !v || !p || !ratios_out) return OB_ERR_ARG;
@@ -744,13 +779,15 @@ ob_status ob_lamb_worker_update(ob_plan plan, const uint32_t* words, const float
                          [&] { return ob::launch_worker_update(pd, words, scales, m, v, p, 1, cp, stream); });
     if (st != OB_OK) return st;
     return lamb_finish(plan, T_COMPRESS, T_COMPRESS, m, v, p, ratios_out, 0, lamb_params(hp, 1.0, 1.0), stream);
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_lamb_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, void* err, ob_dtype err_dtype,
                                 float* m, const float* v, float* p, uint32_t* words_out, float* scales_out,
                                 float* ratios_out, int8_t* signs_out, uint64_t* nonfinite_out,
                                 const ob_hparams* hp, hipStream_t stream)
-{
+try {
     if (!plan || !hp) return OB_ERR_ARG;
     if (plan->n > 0 && (!ratios_out || !aligned(ratios_out, 4))) return ratios_out ? OB_ERR_ALIGN : OB_ERR_ARG;
     ob_status st = compress_passes(plan, g, g_dtype, err, err_dtype, m, v, p, words_out, scales_out, signs_out,
@@ -759,11 +796,13 @@ ob_status ob_lamb_compress_step(ob_plan plan, const void* g, ob_dtype g_dtype, v
     DeviceGuard guard(plan->device);
     if (!guard.ok) return OB_ERR_HIP;
     return lamb_finish(plan, T_PASS1, T_COMPRESS, m, v, p, ratios_out, 0, lamb_params(hp, 1.0, 1.0), stream);
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_lamb_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* m, float* v, float* p,
                               float* ratios_out, const ob_hparams* hp, hipStream_t stream)
-{
+try {
     if (!plan || !hp) return OB_ERR_ARG;
     if (!valid_dtype(g_dtype)) return OB_ERR_DTYPE;
     if (plan->n == 0) return OB_OK;
@@ -782,11 +821,13 @@ ob_status ob_lamb_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, flo
     if (st != OB_OK) return st;
     return lamb_finish(plan, T_DENSE, T_DENSE, m, v, p, ratios_out, dp.bias_correction,
                        lamb_params(hp, dp.bc1, dp.bc2), stream);
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_server_reduce(ob_plan plan, int32_t W, const uint32_t* worker_words, const float* worker_scales,
                            float* server_err, uint32_t* words_out, float* scales_out, hipStream_t stream)
-{
+try {
     if (!plan) return OB_ERR_ARG;
     if (W < 1 || W > 1024) return OB_ERR_ARG;
     if (plan->n == 0) return OB_OK;
@@ -807,10 +848,12 @@ ob_status ob_server_reduce(ob_plan plan, int32_t W, const uint32_t* worker_words
         return ob::launch_server_apply(pd, W, worker_words, worker_scales, server_err, words_out, scales_out,
                                        stream);
     });
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_pack(const void* x, ob_dtype x_dtype, int64_t n, uint32_t* words_out, hipStream_t stream)
-{
+try {
     if (!valid_dtype(x_dtype)) return OB_ERR_DTYPE;
     if (n < 0) return OB_ERR_ARG;
     if (n == 0) return OB_OK;
@@ -818,11 +861,13 @@ ob_status ob_pack(const void* x, ob_dtype x_dtype, int64_t n, uint32_t* words_ou
     if (!aligned(x, x_dtype == OB_BF16 ? 8 : 16) || !aligned(words_out, 4)) return OB_ERR_ALIGN;
     (void)hipGetLastError();
     return ob::launch_pack(x, x_dtype == OB_BF16, n, words_out, stream) == hipSuccess ? OB_OK : OB_ERR_HIP;
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_unpack(ob_plan plan, const uint32_t* words, int64_t n, const float* scales, float* out,
                     hipStream_t stream)
-{
+try {
     if (n < 0) return OB_ERR_ARG;
     if (scales && !plan) return OB_ERR_ARG;
     if (plan && plan->n != n) return OB_ERR_ARG;
@@ -838,13 +883,15 @@ ob_status ob_unpack(ob_plan plan, const uint32_t* words, int64_t n, const float*
     }
     (void)hipGetLastError();
     return ob::launch_unpack(nullptr, words, n, nullptr, out, stream) == hipSuccess ? OB_OK : OB_ERR_HIP;
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_adam_compress_step_noalloc(int64_t n, int64_t chunk_size, const void* g, ob_dtype g_dtype,
                                         void* err, ob_dtype err_dtype, float* m, const float* v, float* p,
                                         uint32_t* words_out, float* scales_out, int8_t* signs_out,
                                         uint64_t* nonfinite_out, const ob_hparams* hp, hipStream_t stream)
-{
+try {
     // everything up to the size check is host arithmetic: a rejected call makes no HIP call
     if (!hp) return OB_ERR_ARG;
     if (!valid_dtype(g_dtype) || !valid_err_dtype(err_dtype)) return OB_ERR_DTYPE;
@@ -946,10 +993,12 @@ ob_status ob_adam_compress_step_noalloc(int64_t n, int64_t chunk_size, const voi
             return OB_ERR_HIP;
     }
     return OB_OK;
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_plan_set_diagnostics(ob_plan plan, double* err_sumsq_out, uint64_t* plus_count_out)
-{
+try {
     if (!plan) return OB_ERR_ARG;
     if ((err_sumsq_out == nullptr) != (plus_count_out == nullptr)) return OB_ERR_ARG;
     if (err_sumsq_out && (!aligned(err_sumsq_out, 8) || !aligned(plus_count_out, 8))) return OB_ERR_ALIGN;
@@ -969,10 +1018,12 @@ ob_status ob_plan_set_diagnostics(ob_plan plan, double* err_sumsq_out, uint64_t*
     plan->diag_err_sumsq = err_sumsq_out;
     plan->diag_plus = reinterpret_cast<unsigned long long*>(plus_count_out);
     return OB_OK;
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_plan_set_timing(ob_plan plan, int32_t enable)
-{
+try {
     if (!plan) return OB_ERR_ARG;
     DeviceGuard guard(plan->device);
     ob_status st = drain_timing(plan);
@@ -982,16 +1033,20 @@ ob_status ob_plan_set_timing(ob_plan plan, int32_t enable)
         plan->launches[k] = 0;
     }
     return st;
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 ob_status ob_plan_read_timing(ob_plan plan, int32_t kernel, double* total_ms, int64_t* launches)
-{
+try {
     if (!plan || kernel < 0 || kernel >= OB_KERNEL_COUNT || !total_ms || !launches) return OB_ERR_ARG;
     DeviceGuard guard(plan->device);
     const ob_status st = drain_timing(plan);
     *total_ms = plan->total_ms[kernel];
     *launches = plan->launches[kernel];
     return st;
+} catch (...) {
+    return OB_ERR_OOM;  // host allocation failures are the only exceptions here
 }
 
 }  // extern "C"

@@ -35,7 +35,8 @@
  * returns a status without touching the GPU: OB_ERR_ARG (null required pointer, bad size, bad chunk
  * table, W < 1, n differs from the plan), OB_ERR_ALIGN (pointer or chunk-boundary alignment),
  * OB_ERR_DTYPE (unknown dtype).  A failed launch returns OB_ERR_HIP; faults during execution surface
- * at the caller's next synchronisation.  OB_ERR_OOM: a plan allocation failed.  n = 0 is a no-op.
+ * at the caller's next synchronisation.  OB_ERR_OOM: an allocation failed (a plan's device memory, or
+ * host memory for its tables or for timing records).  n = 0 is a no-op.
  * No C++ exception crosses the ABI and nothing aborts.  NaN and Inf propagate per IEEE.
  *
  * Threads and streams: distinct plans are independent.  A plan holds a small workspace (one double

@@ -99,3 +99,26 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises((ValueError, RuntimeError)):
         ob.ob_pack(torch.zeros(64), torch.zeros(2, dtype=torch.int32))
+
+
+def test_host_allocation_failure_is_a_status_not_an_abort():
+    """No C++ exception crosses the ABI: a plan whose host-side tables do not fit (2^38 elements under
+    a 4 GiB address-space limit, in a child process) returns OB_ERR_OOM with *out = NULL, where an
+    escaping std::bad_alloc would abort the process."""
+    import subprocess
+    import sys
+    import textwrap
+
+    code = textwrap.dedent(f"""
+        import ctypes, resource
+        resource.setrlimit(resource.RLIMIT_AS, (4 << 30, 4 << 30))
+        L = ctypes.CDLL({ob.LIB_PATH!r})
+        L.ob_plan_create.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.POINTER(ctypes.c_void_p)]
+        h = ctypes.c_void_p(1)
+        print(L.ob_plan_create(1 << 38, 1 << 20, None, 0, ctypes.byref(h)), h.value)
+    """)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    status, handle = r.stdout.split()
+    assert int(status) == ob.OB_ERR_OOM and handle == "None"
