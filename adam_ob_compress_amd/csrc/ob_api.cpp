@@ -858,6 +858,7 @@ try {
     if (n < 0) return OB_ERR_ARG;
     if (n == 0) return OB_OK;
     if (!x || !words_out) return OB_ERR_ARG;
+    if (n > int64_t(INT32_MAX) * ob::kPlainItem) return OB_ERR_ARG;
     if (!aligned(x, x_dtype == OB_BF16 ? 8 : 16) || !aligned(words_out, 4)) return OB_ERR_ALIGN;
     (void)hipGetLastError();
     return ob::launch_pack(x, x_dtype == OB_BF16, n, words_out, stream) == hipSuccess ? OB_OK : OB_ERR_HIP;
@@ -881,6 +882,7 @@ try {
         return timed(plan, OB_KERNEL_UNPACK, stream,
                      [&] { return ob::launch_unpack(&pd, words, n, scales, out, stream); });
     }
+    if (n > int64_t(INT32_MAX) * ob::kPlainItem) return OB_ERR_ARG;
     (void)hipGetLastError();
     return ob::launch_unpack(nullptr, words, n, nullptr, out, stream) == hipSuccess ? OB_OK : OB_ERR_HIP;
 } catch (...) {

@@ -12,7 +12,6 @@ namespace {
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 
-constexpr int kPlainItem = 16 * kTile;  // elements per block for the plan-less pack/unpack
 
 // Tuning knobs (compile-time; every setting computes the same results):
 //   OB_P1_UNROLL / OB_P2_UNROLL   tiles in flight per loop trip in pass 1 / pass 2

@@ -14,6 +14,9 @@ namespace ob {
 constexpr int kBlock = 256;
 constexpr int kVec = 4;
 constexpr int kTile = kBlock * kVec;
+// elements per block of the plan-less pack and unpack (their grid is n / kPlainItem blocks, so n is at
+// most INT32_MAX * kPlainItem)
+constexpr int kPlainItem = 16 * kTile;
 
 // Device-side view of a plan for one launch.  Pass-1 kernels (sums of squares) and pass-2 kernels
 // (everything that needs a chunk's scale, and the dense step) use different block tables: pass 1

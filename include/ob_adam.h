@@ -217,12 +217,14 @@ ob_status ob_lamb_worker_update(ob_plan plan, const uint32_t* words, const float
                                 const float* v, float* p, float* ratios_out, const ob_hparams* hp,
                                 hipStream_t stream);
 
-/* Pack signs of x (OB_F32 or OB_BF16, n elements) into ceil(n/32) words ([P2] one_bit_quantize, sign part). */
+/* Pack signs of x (OB_F32 or OB_BF16, n elements) into ceil(n/32) words ([P2] one_bit_quantize, sign part).
+ * n at most (2^31 - 1) * 16384 (one block per 16384 elements); OB_ERR_ARG beyond. */
 ob_status ob_pack(const void* x, ob_dtype x_dtype, int64_t n, uint32_t* words_out, hipStream_t stream);
 
 /* Unpack + dequantize ([P2] dequantize): out_i = bit(i) ? s_c : -s_c, s_c = scales[c] for the plan's
  * chunk c of i; with scales == NULL, s = 1 and plan may be NULL.  With scales, plan is required and n
- * must equal the plan's n.  out: fp32[n]. */
+ * must equal the plan's n.  out: fp32[n].  Without a plan's tables (scales == NULL) n is at most
+ * (2^31 - 1) * 16384, as for ob_pack. */
 ob_status ob_unpack(ob_plan plan, const uint32_t* words, int64_t n, const float* scales, float* out,
                     hipStream_t stream);
 

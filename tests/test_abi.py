@@ -60,6 +60,11 @@ def test_validation_before_any_gpu_work(lib):
     assert lib.ob_pack(None, 0, -1, None, None) == 1
     assert lib.ob_unpack(None, None, 0, None, None, None) == 0
     assert lib.ob_unpack(None, P(0x1000), 64, P(0x2000), P(0x3000), None) == 1   # scales need a plan
+    # plan-less pack / unpack: a grid of n / 16384 blocks must fit 2^31 - 1
+    too_many = ((1 << 31) - 1) * 16384 + 1
+    assert lib.ob_pack(P(0x1000), 0, too_many, P(0x2000), None) == 1
+    assert lib.ob_unpack(None, P(0x1000), too_many, None, P(0x3000), None) == 1
+    assert lib.ob_plan_num_groups(None, 0, 0, 0) == -1
     hp = ob.hparams()
     assert lib.ob_adam_compress_step(None, P(0x1000), 0, None, 0, None, None, None, None, None, None,
                                      None, ctypes.byref(hp), None) == 1
