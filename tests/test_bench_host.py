@@ -227,3 +227,17 @@ def test_rocprof_summary_groups_by_kernel_and_grid(tmp_path):
     assert "| 4096 | 1 | 2.00 |" in rows[1]
     # the per-kernel line over the workload's launches leaves the warm-up's small grid out
     assert rows[2] == "| k_compress<GradF32>(...) | 2 | 585.00 | 1170.0 |"
+
+
+def test_roofline_of_a_grouped_kernel_is_the_steps_bytes_over_its_time():
+    """A kernel launched G times a step: achieved = B/elem x (n / G) / average launch time, which is
+    the step's algorithmic bytes over the kernel's time per step."""
+    w = synth.WORKLOADS["llama2-7B-bf16-ema"]
+    G, avg_ms = 134, 0.225
+    kern = {"compress": {"avg_ms": avg_ms, "launches": 20 * G, "launches_per_step": float(G),
+                         "ms_per_step": avg_ms * G}}
+    r = bench.roofline_of(kern, "compress", w, None)
+    per_step = bench.bytes_per_elem(w, "compress") * w.n / (avg_ms * G * 1e-3) / 1e9
+    assert abs(r["achieved"] - per_step) / per_step < 1e-12
+    assert r["frac"] == r["achieved"] / bench.PEAK_HBM_GBPS
+    assert r["launches_per_step"] == G and abs(r["elements_per_launch"] * G - w.n) < 1e-3
