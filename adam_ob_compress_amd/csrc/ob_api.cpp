@@ -42,10 +42,12 @@ struct ob_plan_s {
     // Chunk groups of the compressed step's two passes.  Pass 2 re-reads g and err, which pass 1 has
     // just read; run over consecutive chunks whose pass-1 bytes about fit in the GPU's last-level cache
     // (the Infinity Cache, 256 MB on MI355X), pass 1 then pass 2 per group serves most of that re-read
-    // from the cache instead of HBM.  groups[w]: the groups when pass 1 reads w bytes per element (g,
-    // err and, for LAMB, p: 4 to 12); one group of all chunks when grouping is off.
+    // from the cache instead of HBM.  groups[w]: the groups when pass 1 reads w bytes per element (g
+    // and err: 4, 6 or 8); one group of all chunks when grouping is off.  whole: one group of all
+    // chunks, for 1-bit LAMB (its pass 1 also reads p, and groups measured no faster there).
     int64_t group_bytes = 0;
-    std::vector<ob::ChunkGroup> groups[13];
+    std::vector<ob::ChunkGroup> groups[9];
+    std::vector<ob::ChunkGroup> whole;
 
     // block tables, one per kernel kind (kTables)
     struct Table {
@@ -168,10 +170,12 @@ int64_t group_budget()
     return kGroupBytes;
 }
 
-// Bytes per element that pass 1 reads: g, the error buffer and (LAMB) p.
-int pass1_width(int g_dtype, int err_dtype, int lamb)
+// The chunk groups a compressed step runs its two passes over: by the bytes per element pass 1 reads
+// (g and the error buffer), or one group for 1-bit LAMB.
+const std::vector<ob::ChunkGroup>& step_groups(ob_plan p, int g_dtype, int err_dtype, int lamb)
 {
-    return (g_dtype == OB_BF16 ? 2 : 4) + (err_dtype == OB_F32 ? 4 : 2) + (lamb ? 4 : 0);
+    if (lamb) return p->whole;
+    return p->groups[(g_dtype == OB_BF16 ? 2 : 4) + (err_dtype == OB_F32 ? 4 : 2)];
 }
 
 // A launch over blocks [i0, i0 + count) of the view's table.
@@ -395,7 +399,7 @@ ob_status plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_offset
     // chunk groups (none while any chunk needs its sums formed by a launch of their own)
     p->group_bytes = group_budget();
     const bool grouping = p->group_bytes > 0 && p->p1_max <= kFinalizeAt;
-    for (int w = 4; w <= 12; w += 2) {
+    for (int w = 4; w <= 8; w += 2) {
         const int64_t max_elems = grouping ? std::max<int64_t>(1, p->group_bytes / w) : 0;
         ob::build_chunk_groups(off, first[T_PASS1], first[T_COMPRESS], max_elems, p->groups[w]);
         if (ob::check_chunk_groups(off, first[T_PASS1], first[T_COMPRESS], max_elems, p->groups[w]) != nullptr) {
@@ -403,6 +407,7 @@ ob_status plan_create(int64_t n, int64_t chunk_size, const int64_t* chunk_offset
             return OB_ERR_ARG;
         }
     }
+    ob::build_chunk_groups(off, first[T_PASS1], first[T_COMPRESS], 0, p->whole);
 
     if (hipGetDevice(&p->device) != hipSuccess) {
         delete p;
@@ -486,7 +491,7 @@ int64_t ob_plan_block_elems(ob_plan plan) { return plan ? plan->t[T_COMPRESS].bl
 int64_t ob_plan_num_groups(ob_plan plan, ob_dtype g_dtype, ob_dtype err_dtype, int32_t lamb)
 {
     if (!plan || !valid_dtype(g_dtype) || !valid_err_dtype(err_dtype)) return -1;
-    return static_cast<int64_t>(plan->groups[pass1_width(g_dtype, err_dtype, lamb)].size());
+    return static_cast<int64_t>(step_groups(plan, g_dtype, err_dtype, lamb).size());
 }
 
 ob_status ob_adam_warmup_step(ob_plan plan, const void* g, ob_dtype g_dtype, float* m, float* v, float* p,
@@ -534,13 +539,14 @@ ob_status check_compress_args(const void* g, ob_dtype g_dtype, const void* err, 
     return OB_OK;
 }
 
+// nt: nontemporal loads, for a pass 1 over all chunks at once (no chunk groups)
 hipError_t sumsq_by_format(ob_dtype err_dtype, const ob::PlanDev& pd1, const void* g, int bf, const void* err,
-                           float clip, const float* lamb_p, hipStream_t s)
+                           float clip, const float* lamb_p, bool nt, hipStream_t s)
 {
     switch (err_dtype) {
-    case OB_BF16: return ob::launch_chunk_sumsq<OB_BF16>(pd1, g, bf, err, clip, lamb_p, s);
-    case OB_F16: return ob::launch_chunk_sumsq<OB_F16>(pd1, g, bf, err, clip, lamb_p, s);
-    default: return ob::launch_chunk_sumsq<OB_F32>(pd1, g, bf, err, clip, lamb_p, s);
+    case OB_BF16: return ob::launch_chunk_sumsq<OB_BF16>(pd1, g, bf, err, clip, lamb_p, nt, s);
+    case OB_F16: return ob::launch_chunk_sumsq<OB_F16>(pd1, g, bf, err, clip, lamb_p, nt, s);
+    default: return ob::launch_chunk_sumsq<OB_F32>(pd1, g, bf, err, clip, lamb_p, nt, s);
     }
 }
 
@@ -618,11 +624,13 @@ ob_status compress_passes(ob_plan plan, const void* g, ob_dtype g_dtype, void* e
     const float* lamb_p = lamb ? p : nullptr;
     ob_status st = OB_OK;
     hipEvent_t chain = nullptr;
-    for (const ob::ChunkGroup& gr : plan->groups[pass1_width(g_dtype, err_dtype, lamb)]) {
+    const std::vector<ob::ChunkGroup>& groups = step_groups(plan, g_dtype, err_dtype, lamb);
+    const bool whole = groups.size() == 1;   // one pass 1 over everything: nontemporal loads
+    for (const ob::ChunkGroup& gr : groups) {
         st = timed(
             plan, OB_KERNEL_CHUNK_SUMSQ, stream,
             [&] {
-                return sumsq_by_format(err_dtype, group_view(pd1, gr.i1, gr.n1), g, bf, err, cp.clip, lamb_p,
+                return sumsq_by_format(err_dtype, group_view(pd1, gr.i1, gr.n1), g, bf, err, cp.clip, lamb_p, whole,
                                        stream);
             },
             &chain);
@@ -711,11 +719,13 @@ try {
     auto nf = reinterpret_cast<unsigned long long*>(nonfinite_out);
     ob_status st = OB_OK;
     hipEvent_t chain = nullptr;
-    for (const ob::ChunkGroup& gr : plan->groups[pass1_width(g_dtype, err_dtype, 0)]) {
+    const std::vector<ob::ChunkGroup>& groups = step_groups(plan, g_dtype, err_dtype, 0);
+    const bool whole = groups.size() == 1;   // one pass 1 over everything: nontemporal loads
+    for (const ob::ChunkGroup& gr : groups) {
         st = timed(
             plan, OB_KERNEL_CHUNK_SUMSQ, stream,
             [&] {
-                return sumsq_by_format(err_dtype, group_view(pd1, gr.i1, gr.n1), g, bf, err, cp.clip, nullptr,
+                return sumsq_by_format(err_dtype, group_view(pd1, gr.i1, gr.n1), g, bf, err, cp.clip, nullptr, whole,
                                        stream);
             },
             &chain);
@@ -971,7 +981,8 @@ try {
     (void)hipGetLastError();
     if (ob::launch_uniform_tables(t, stream) != hipSuccess) return OB_ERR_HIP;
     if (finalize) {   // chunks too large to share the cache: whole-buffer passes, with per-chunk sums
-        if (sumsq_by_format(err_dtype, pd1, g, bf, err, cp.clip, nullptr, stream) != hipSuccess) return OB_ERR_HIP;
+        if (sumsq_by_format(err_dtype, pd1, g, bf, err, cp.clip, nullptr, true, stream) != hipSuccess)
+            return OB_ERR_HIP;
         double* sums = reinterpret_cast<double*>(base + o_sums);
         if (ob::launch_chunk_sums(pd1, sums, stream) != hipSuccess) return OB_ERR_HIP;
         pd2.p1_first = t.ident;
@@ -983,12 +994,14 @@ try {
     }
     // chunk groups of q chunks (the plan's greedy grouping, for equal chunks; the last group takes the rest)
     const int64_t budget = group_budget();
-    const int64_t max_elems = budget > 0 ? std::max<int64_t>(1, budget / pass1_width(g_dtype, err_dtype, 0)) : 0;
+    const int64_t width = (g_dtype == OB_BF16 ? 2 : 4) + (err_dtype == OB_F32 ? 4 : 2);
+    const int64_t max_elems = budget > 0 ? std::max<int64_t>(1, budget / width) : 0;
     const int64_t q = max_elems > 0 ? std::max<int64_t>(1, max_elems / chunk_size) : K;
+    const bool whole = q >= K;   // one group: nontemporal pass-1 loads
     for (int64_t c0 = 0; c0 < K; c0 += q) {
         const ob::ChunkGroup gr = ob::uniform_chunk_group(c0, q, K, nbf1, n1, nbf2, n2);
-        if (sumsq_by_format(err_dtype, group_view(pd1, gr.i1, gr.n1), g, bf, err, cp.clip, nullptr, stream) !=
-            hipSuccess)
+        if (sumsq_by_format(err_dtype, group_view(pd1, gr.i1, gr.n1), g, bf, err, cp.clip, nullptr, whole,
+                            stream) != hipSuccess)
             return OB_ERR_HIP;
         if (compress_by_format(err_dtype, group_view(pd2, gr.i2, gr.n2), g, bf, err, m, v, p, words_out, scales_out,
                                signs_out, nf, ema, 0, cp, stream) != hipSuccess)

@@ -47,7 +47,9 @@ namespace {
 // (LAMB: and of the parameters, for the layer's ||w||; DIAG: and of the error buffer read)
 // ------------------------------------------------------------------------------------------------
 
-template <class G, class E, bool CLIP, bool LAMB, bool DIAG>
+// NT: nontemporal loads (a single launch over the whole buffer, whose reads pass 2 gets from HBM anyway);
+// ordinary ones when the launch covers one chunk group, so that pass 2 finds its lines in the cache.
+template <class G, class E, bool CLIP, bool LAMB, bool DIAG, bool NT>
 __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typename G::T* __restrict__ g,
                                                         const typename E::T* __restrict__ err, float clip,
                                                         const float* __restrict__ p)
@@ -64,9 +66,9 @@ __global__ __launch_bounds__(kBlock) void k_chunk_sumsq(PlanDev pd, const typena
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t i = it.start + base + u * kTile + kVec * tid;
-            gv[u] = G::template load4<OB_NT_P1>(g, i);
-            ev[u] = E::template load4<OB_NT_P1>(err, i);
-            if (LAMB) pv[u] = ld4<OB_NT_P1>(p, i);
+            gv[u] = G::template load4<NT>(g, i);
+            ev[u] = E::template load4<NT>(err, i);
+            if (LAMB) pv[u] = ld4<NT>(p, i);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -341,12 +343,15 @@ __global__ __launch_bounds__(kBlock) void k_worker_compress(PlanDev pd, const ty
 
 namespace {
 template <class G, class E>
-void sumsq_dispatch(int sel, dim3 grid, dim3 block, hipStream_t s, const PlanDev& pd, const typename G::T* g,
-                    const typename E::T* err, float clip, const float* p)
+void sumsq_dispatch(int sel, bool nt, dim3 grid, dim3 block, hipStream_t s, const PlanDev& pd,
+                    const typename G::T* g, const typename E::T* err, float clip, const float* p)
 {
-#define OB_CASE(k, CL, LA, DG)                                                                        \
-    case k:                                                                                            \
-        hipLaunchKernelGGL((k_chunk_sumsq<G, E, CL, LA, DG>), grid, block, 0, s, pd, g, err, clip, p); \
+#define OB_CASE(k, CL, LA, DG)                                                                              \
+    case k:                                                                                                  \
+        if (nt)                                                                                              \
+            hipLaunchKernelGGL((k_chunk_sumsq<G, E, CL, LA, DG, true>), grid, block, 0, s, pd, g, err, clip, p);  \
+        else                                                                                                 \
+            hipLaunchKernelGGL((k_chunk_sumsq<G, E, CL, LA, DG, false>), grid, block, 0, s, pd, g, err, clip, p); \
         break;
     switch (sel) {
         OB_CASE(0, false, false, false)
@@ -364,16 +369,18 @@ void sumsq_dispatch(int sel, dim3 grid, dim3 block, hipStream_t s, const PlanDev
 
 template <int EF>
 hipError_t launch_chunk_sumsq(const PlanDev& pd, const void* g, int g_bf16, const void* err_v, float clip,
-                              const float* lamb_p, hipStream_t s)
+                              const float* lamb_p, int nontemporal, hipStream_t s)
 {
     using E = typename ErrOf<EF>::type;
     auto err = static_cast<const typename E::T*>(err_v);
     const dim3 grid(static_cast<unsigned>(pd.n_items)), block(kBlock);
     const int sel = (clip > 0.0f ? 1 : 0) | (lamb_p ? 2 : 0) | (pd.partials_e ? 4 : 0);
     if (g_bf16)
-        sumsq_dispatch<GradBF16, E>(sel, grid, block, s, pd, static_cast<const uint16_t*>(g), err, clip, lamb_p);
+        sumsq_dispatch<GradBF16, E>(sel, nontemporal != 0, grid, block, s, pd, static_cast<const uint16_t*>(g), err,
+                                    clip, lamb_p);
     else
-        sumsq_dispatch<GradF32, E>(sel, grid, block, s, pd, static_cast<const float*>(g), err, clip, lamb_p);
+        sumsq_dispatch<GradF32, E>(sel, nontemporal != 0, grid, block, s, pd, static_cast<const float*>(g), err,
+                                   clip, lamb_p);
     return hipGetLastError();
 }
 
@@ -515,7 +522,7 @@ hipError_t launch_worker_compress(const PlanDev& pd, const void* g, int g_bf16, 
 
 // the error format this translation unit is compiled for
 template hipError_t launch_chunk_sumsq<OB_ERR_FMT>(const PlanDev&, const void*, int, const void*, float,
-                                                   const float*, hipStream_t);
+                                                   const float*, int, hipStream_t);
 template hipError_t launch_compress<OB_ERR_FMT>(const PlanDev&, const void*, int, void*, float*, const float*,
                                                 float*, uint32_t*, float*, int8_t*, unsigned long long*, int,
                                                 int, const CompressParams&, hipStream_t);

@@ -15,8 +15,6 @@ typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 
 // Tuning knobs (compile-time; every setting computes the same results):
 //   OB_P1_UNROLL / OB_P2_UNROLL   tiles in flight per loop trip in pass 1 / pass 2
-//   OB_NT_P1                      nontemporal loads in pass 1 (off: pass 1's reads are to stay in the
-//                                 last-level cache for the pass 2 that follows on the same chunk group)
 //   OB_NT_P2                      nontemporal loads of the pass-2 inputs (read once more, then dead)
 //   OB_NT_ST                      nontemporal stores of the pass-2 outputs
 #ifndef OB_P1_UNROLL
@@ -24,9 +22,6 @@ typedef unsigned int u2 __attribute__((ext_vector_type(2)));
 #endif
 #ifndef OB_P2_UNROLL
 #define OB_P2_UNROLL 4
-#endif
-#ifndef OB_NT_P1
-#define OB_NT_P1 0
 #endif
 #ifndef OB_NT_P2
 #define OB_NT_P2 1

@@ -66,10 +66,12 @@ struct LambParams {
 
 // Compressed-step launchers for error-buffer format EF (0 fp32, 1 bf16, 2 fp16); ob_compress.hip,
 // built once per format, instantiates each.
-// lamb_p != nullptr: also the per-block sum of p^2 (LAMB), into pd.partials_w.
+// lamb_p != nullptr: also the per-block sum of p^2 (LAMB), into pd.partials_w.  nontemporal != 0:
+// nontemporal loads (a launch over all chunks at once); 0: ordinary loads, which leave the lines in the
+// last-level cache for the pass 2 that follows on the same chunk group.
 template <int EF>
 hipError_t launch_chunk_sumsq(const PlanDev& pd, const void* g, int g_bf16, const void* err, float clip,
-                              const float* lamb_p, hipStream_t s);
+                              const float* lamb_p, int nontemporal, hipStream_t s);
 // lamb != 0: no parameter update; the per-block sum of u^2 goes to pd.partials_u (p is not touched).
 template <int EF>
 hipError_t launch_compress(const PlanDev& pd, const void* g, int g_bf16, void* err, float* m, const float* v,

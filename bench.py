@@ -679,14 +679,16 @@ GROUP_BYTES = 320 << 20
 
 def chunk_groups(w, lamb: bool = False) -> list:
     """The chunk groups [(c0, c1), ...] the library's compressed step runs its two kernels over for
-    workload w (host arithmetic, no GPU): consecutive chunks while their pass-1 bytes (g, err and, for
-    LAMB, p) stay within the budget, a larger chunk alone; one group when grouping is off or a chunk has
-    more than 4096 pass-1 blocks (then the library forms per-chunk sums first).  tests/test_gpu_bench.py
-    checks it against ob_plan_num_groups for every workload."""
+    workload w (host arithmetic, no GPU): consecutive chunks while their pass-1 bytes (g and err) stay
+    within the budget, a larger chunk alone; one group for 1-bit LAMB, when grouping is off, or when a
+    chunk has more than 4096 pass-1 blocks (then the library forms per-chunk sums first).
+    tests/test_gpu_groups.py checks it against ob_plan_num_groups for every workload."""
     off = [int(o) for o in w.chunk_offsets()]
     K = len(off) - 1
+    if lamb:                       # 1-bit LAMB runs one group
+        return [(0, K)]
     budget = int(os.environ.get("OB_GROUP_BYTES", GROUP_BYTES))
-    width = (2 if w.grad_dtype == "bf16" else 4) + (4 if w.err_dtype == "f32" else 2) + (4 if lamb else 0)
+    width = (2 if w.grad_dtype == "bf16" else 4) + (4 if w.err_dtype == "f32" else 2)
     be1 = int(os.environ.get("OB_BLOCK_ELEMS", 0))
     if not (be1 >= 1024 and be1 <= (1 << 20) and be1 % 1024 == 0):
         be1 = min(max(-(-(-(-w.n // 8192)) // 1024) * 1024, 4096), 24576)

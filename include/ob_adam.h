@@ -111,14 +111,15 @@ int64_t ob_plan_num_elements(ob_plan plan);   /* -1 for a NULL plan */
 int64_t ob_plan_num_chunks(ob_plan plan);     /* -1 for a NULL plan */
 int64_t ob_plan_num_blocks(ob_plan plan);     /* work blocks = grid size of the per-element kernels */
 int64_t ob_plan_block_elems(ob_plan plan);    /* elements per work block (except chunk tails) */
-/* Chunk groups of the compressed step (ob_adam_compress_step, ob_lamb_compress_step with lamb != 0,
- * ob_adam_worker_compress): the step runs its two kernels group by group, each group being consecutive
- * chunks whose bytes read by the first kernel (g, err and, for LAMB, p) stay within a budget sized to
- * the GPU's last-level cache (320 MB; the environment variable OB_GROUP_BYTES, read when the plan is
- * created, overrides it and 0 turns grouping off), so that the second kernel re-reads them from that
- * cache.  A chunk above the budget is a group of its own; plans whose chunks need a per-chunk sums
- * launch (more than 4096 first-kernel blocks in a chunk) are one group.  Returns the number of groups,
- * i.e. the launches of each of the two kernels per step; -1 for a NULL plan or an invalid dtype. */
+/* Chunk groups of the compressed step (ob_adam_compress_step, ob_adam_worker_compress): the step runs
+ * its two kernels group by group, each group being consecutive chunks whose bytes read by the first
+ * kernel (g and err) stay within a budget sized to the GPU's last-level cache (320 MB; the environment
+ * variable OB_GROUP_BYTES, read when the plan is created, overrides it and 0 turns grouping off), so
+ * that the second kernel re-reads them from that cache.  A chunk above the budget is a group of its
+ * own; plans whose chunks need a per-chunk sums launch (more than 4096 first-kernel blocks in a chunk)
+ * are one group, and so is 1-bit LAMB (lamb != 0: ob_lamb_compress_step, whose first kernel also reads
+ * p).  Returns the number of groups, i.e. the launches of each of the two kernels per step; -1 for a
+ * NULL plan or an invalid dtype. */
 int64_t ob_plan_num_groups(ob_plan plan, ob_dtype g_dtype, ob_dtype err_dtype, int32_t lamb);
 
 /* Dense Adam step ([P2] baseline section; the step used before freeze_step in [P2] 1-bit Adam and for
