@@ -23,10 +23,11 @@
 //     LDS across the four waves); pass 2 reduces the chunk's partials in a fixed order at its start
 //     (every block of the chunk gets bit-identical scales), then does the fused streaming update;
 //   * the host runs the two passes over groups of consecutive chunks sized to the Infinity Cache, so
-//     that pass 2's re-read of g and err comes from the cache: pass 1 loads with ordinary (allocating)
-//     loads, pass 2 with nontemporal ones; a launch covers blocks [item0, item0 + n_items) of the
-//     plan-wide table and writes its per-block results at their plan-wide index, so the results do not
-//     depend on the grouping;
+//     that pass 2's re-read of g and err comes from the cache: pass 1 then loads with ordinary
+//     (allocating) loads (nontemporal ones when a single launch covers all chunks), pass 2 with
+//     nontemporal ones; a launch covers blocks [item0, item0 + n_items) of the plan-wide table and
+//     writes its per-block results at their plan-wide index, so the results do not depend on the
+//     grouping;
 //   * sign bits: each lane forms a 4-bit nibble; an OR across 8 neighbouring lanes with DPP row
 //     permutes (no LDS) builds the 32-bit word of 32 consecutive elements, written by one lane;
 //   * all fp32 arithmetic is plain IEEE (no fast-math, denormals kept: a negative denormal must give
