@@ -190,7 +190,7 @@ void free_plan(ob_plan p)
 {
     if (!p) return;
     for (auto& r : p->pending) {
-        (void)hipEventDestroy(r.a);
+        if (r.owns_a) (void)hipEventDestroy(r.a);   // a chained record's a is the previous record's b
         (void)hipEventDestroy(r.b);
     }
     for (auto e : p->pool) (void)hipEventDestroy(e);

@@ -136,3 +136,26 @@ def test_timing_of_grouped_launches(monkeypatch):
     span = a.elapsed_time(b)
     assert ms_c + ms_s <= span * 1.001 + 0.005, (ms_c, ms_s, span)
     plan.destroy()
+
+
+def test_destroy_with_undrained_grouped_timing(monkeypatch):
+    """A plan destroyed with grouped launches' timing records still pending (never read): each shared
+    event is destroyed once, and a new plan's timing works after it."""
+    monkeypatch.setenv("OB_GROUP_BYTES", "1")
+    n, chunk = 1 << 20, 1 << 18
+    d = [torch.ones(n, dtype=torch.float32, device=T.DEV) for _ in range(5)]
+    words = torch.zeros(n // 32, dtype=torch.int32, device=T.DEV)
+    scales = torch.zeros(n // chunk, dtype=torch.float32, device=T.DEV)
+    for _ in range(3):
+        plan = ob.ob_plan_create(n, chunk_size=chunk)
+        assert plan.num_groups(ob.OB_F32, ob.OB_F32) == 4
+        ob.ob_plan_set_timing(plan, True)
+        ob.ob_adam_compress_step(plan, *d, words, scales, ob.hparams())
+        torch.cuda.synchronize()
+        plan.destroy()
+    plan = ob.ob_plan_create(n, chunk_size=chunk)
+    ob.ob_plan_set_timing(plan, True)
+    ob.ob_adam_compress_step(plan, *d, words, scales, ob.hparams())
+    ms, cnt = ob.ob_plan_read_timing(plan, ob.OB_KERNEL_COMPRESS)
+    assert cnt == 4 and ms > 0
+    plan.destroy()
